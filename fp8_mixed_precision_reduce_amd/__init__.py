@@ -1,0 +1,268 @@
+"""Python binding of libfp8lin.so, the MI355X FP8 linear layer with per-tensor
+delayed scaling.
+
+Argument marshalling only: each function takes torch tensors that already live
+on the GPU, passes their data pointers, sizes and the current HIP stream to the
+C entry point of the same name (include/fp8lin.h) and raises Fp8LinError on a
+non-zero status.  Every step of the computation runs in the library's HIP
+kernels; torch only provides device memory and streams.
+
+The library must be built (python -m fp8_mixed_precision_reduce_amd.build or
+__graft_entry__.build()); importing this package without it raises
+ImportError -- there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8lin.so")
+
+# ---- constants mirrored from include/fp8lin.h
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_ARG, ERR_HIP, ERR_UNSUPPORTED = range(8)
+F32, BF16, E4M3, E5M2 = 0, 1, 2, 3
+FORMAT_E4M3, FORMAT_HYBRID = 0, 1
+AMAX_MAX = 0
+EPI_GELU, EPI_ACCUMULATE, EPI_FAST_ACCUM = 1, 2, 4
+KIND_NAMES = ["amax", "cast", "cast_transpose", "dequant", "scale_update", "gemm", "dbias", "other"]
+ABI_VERSION = 1
+
+FUNCTIONS = [
+    "fp8lin_abi_version", "fp8lin_last_error", "fp8lin_status_name", "fp8lin_dbias_workspace_bytes",
+    "fp8_amax", "fp8_amax_scale_update", "fp8_cast", "fp8_cast_transpose", "fp8_cast_transpose_dgelu",
+    "fp8_dequant", "fp8_gemm", "fp8_linear_fwd", "fp8_linear_bwd", "fp8lin_timing_enable", "fp8lin_timing_read",
+]
+
+
+class Fp8LinError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class Recipe(ctypes.Structure):
+    """DelayedScaling recipe: format, amax history length, amax algorithm,
+    margin, and whether the layer GEMMs use the fast (FP8 matrix-core) sums."""
+    _fields_ = [("format", ctypes.c_int32), ("history_len", ctypes.c_int32),
+                ("amax_compute_algo", ctypes.c_int32), ("margin", ctypes.c_int32),
+                ("fast_accum", ctypes.c_int32)]
+
+    def __init__(self, format=FORMAT_HYBRID, history_len=16, amax_compute_algo=AMAX_MAX, margin=0, fast_accum=0):
+        super().__init__(format, history_len, amax_compute_algo, margin, int(bool(fast_accum)))
+
+
+class _MetaC(ctypes.Structure):
+    _fields_ = [("amax_history", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("scale_inv", ctypes.c_void_p)]
+
+
+class _SavedC(ctypes.Structure):
+    _fields_ = [("xq", ctypes.c_void_p), ("xq_t", ctypes.c_void_p), ("wq", ctypes.c_void_p),
+                ("wq_t", ctypes.c_void_p), ("sinv", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m fp8_mixed_precision_reduce_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    sig = {
+        "fp8lin_abi_version": (I32, []),
+        "fp8lin_last_error": (ctypes.c_char_p, []),
+        "fp8lin_status_name": (ctypes.c_char_p, [I32]),
+        "fp8lin_dbias_workspace_bytes": (I64, [I64, I64]),
+        "fp8_amax": (I32, [P, I32, I64, P, P]),
+        "fp8_amax_scale_update": (I32, [P, P, P, P, I32, ctypes.POINTER(Recipe), P]),
+        "fp8_cast": (I32, [P, I32, I64, I32, P, P, P, P]),
+        "fp8_cast_transpose": (I32, [P, I32, I64, I64, I32, P, P, P, P, P, P, P]),
+        "fp8_cast_transpose_dgelu": (I32, [P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, P]),
+        "fp8_dequant": (I32, [P, I32, I64, P, P, I32, P]),
+        "fp8_gemm": (I32, [P, I32, P, I32, I64, I64, I64, P, P, P, I32, I32, P, I32, P, P, P]),
+        "fp8_linear_fwd": (I32, [I64, I64, I64, P, I32, P, I32, P, I32, I32, P, I32, P, P,
+                                 ctypes.POINTER(Recipe), ctypes.POINTER(_MetaC), ctypes.POINTER(_MetaC),
+                                 ctypes.POINTER(_SavedC), P]),
+        "fp8_linear_bwd": (I32, [I64, I64, I64, P, I32, P, P, ctypes.POINTER(Recipe), ctypes.POINTER(_MetaC),
+                                 ctypes.POINTER(_SavedC), P, P, P, I32, P, I32, P, P, P]),
+        "fp8lin_timing_enable": (I32, [I32]),
+        "fp8lin_timing_read": (I32, [P, P, I32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.fp8lin_abi_version() != ABI_VERSION:
+        raise ImportError(f"libfp8lin ABI {lib.fp8lin_abi_version()} != binding ABI {ABI_VERSION}")
+    return lib
+
+
+_lib = _load()
+
+
+def _status_name(s):
+    return _lib.fp8lin_status_name(s).decode()
+
+
+def _check(status):
+    if status != OK:
+        raise Fp8LinError(status, _lib.fp8lin_last_error().decode())
+
+
+def _p(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"expected a float32 or bfloat16 tensor, got {t.dtype}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def library():
+    """The loaded ctypes library (for callers that marshal raw pointers)."""
+    return _lib
+
+
+# ------------------------------------------------------------------- state
+
+class Meta:
+    """Delayed-scaling state of one tensor in device memory: amax history
+    (float[L], slot 0 = current step), scale and scale_inv (start at 1)."""
+
+    def __init__(self, history_len, fmt, device="cuda"):
+        self.fmt = fmt
+        self.amax_history = torch.zeros(history_len, dtype=torch.float32, device=device)
+        self.scale = torch.ones(1, dtype=torch.float32, device=device)
+        self.scale_inv = torch.ones(1, dtype=torch.float32, device=device)
+
+    def c(self):
+        return _MetaC(self.amax_history.data_ptr(), self.scale.data_ptr(), self.scale_inv.data_ptr())
+
+
+class MetaBank:
+    """The metas of n tensors in three contiguous buffers, so that one
+    fp8_amax_scale_update call updates all of them."""
+
+    def __init__(self, formats, history_len, device="cuda"):
+        n = len(formats)
+        self.formats = bytes(formats)
+        self.history_len = history_len
+        self.amax_history = torch.zeros(n, history_len, dtype=torch.float32, device=device)
+        self.scale = torch.ones(n, dtype=torch.float32, device=device)
+        self.scale_inv = torch.ones(n, dtype=torch.float32, device=device)
+
+    def meta(self, i):
+        m = Meta.__new__(Meta)
+        m.fmt = self.formats[i]
+        m.amax_history = self.amax_history[i]
+        m.scale = self.scale[i:i + 1]
+        m.scale_inv = self.scale_inv[i:i + 1]
+        return m
+
+    def update(self, recipe, stream=None):
+        fp8_amax_scale_update(self.amax_history, self.scale, self.scale_inv, self.formats, recipe, stream)
+
+
+class Saved:
+    """Buffers a forward pass leaves for its backward pass (FP8 copies of X
+    and W, row-major and transposed, and their inverse scales)."""
+
+    def __init__(self, m, n, k, device="cuda", transposes=True):
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.xq = torch.empty(m, k, **u8)
+        self.wq = torch.empty(n, k, **u8)
+        self.xq_t = torch.empty(k, m, **u8) if transposes else None
+        self.wq_t = torch.empty(k, n, **u8) if transposes else None
+        self.sinv = torch.empty(2, dtype=torch.float32, device=device)
+
+    def c(self):
+        return _SavedC(self.xq.data_ptr(), self.xq_t.data_ptr() if self.xq_t is not None else None,
+                       self.wq.data_ptr(), self.wq_t.data_ptr() if self.wq_t is not None else None,
+                       self.sinv.data_ptr())
+
+
+# ------------------------------------------------------------ entry points
+
+def fp8_amax(x, amax_slot, stream=None):
+    _check(_lib.fp8_amax(_p(x), _dt(x), x.numel(), _p(amax_slot), _stream(stream)))
+
+
+def fp8_amax_scale_update(amax_history, scale, scale_inv, formats, recipe, stream=None):
+    fm = (ctypes.c_uint8 * len(formats)).from_buffer_copy(bytes(formats))
+    _check(_lib.fp8_amax_scale_update(_p(amax_history), _p(scale), _p(scale_inv), ctypes.cast(fm, ctypes.c_void_p),
+                                      len(formats), ctypes.byref(recipe), _stream(stream)))
+
+
+def fp8_cast(x, fmt, scale, q, amax_slot=None, stream=None):
+    _check(_lib.fp8_cast(_p(x), _dt(x), x.numel(), fmt, _p(scale), _p(q), _p(amax_slot), _stream(stream)))
+
+
+def fp8_cast_transpose(x, fmt, scale, q, q_t, amax_slot=None, dbias=None, dbias_ws=None, stream=None):
+    rows, cols = x.shape
+    _check(_lib.fp8_cast_transpose(_p(x), _dt(x), rows, cols, fmt, _p(scale), _p(q), _p(q_t), _p(amax_slot),
+                                   _p(dbias), _p(dbias_ws), _stream(stream)))
+
+
+def fp8_cast_transpose_dgelu(dh, z, fmt, scale, q, q_t, amax_slot=None, dbias=None, dbias_ws=None, dz_out=None,
+                             stream=None):
+    rows, cols = dh.shape
+    _check(_lib.fp8_cast_transpose_dgelu(_p(dh), _p(z), _dt(dh), rows, cols, fmt, _p(scale), _p(q), _p(q_t),
+                                         _p(amax_slot), _p(dbias), _p(dbias_ws), _p(dz_out), _stream(stream)))
+
+
+def fp8_dequant(q, fmt, scale_inv, out, stream=None):
+    _check(_lib.fp8_dequant(_p(q), fmt, q.numel(), _p(scale_inv), _p(out), _dt(out), _stream(stream)))
+
+
+def fp8_gemm(a, a_fmt, b, b_fmt, sinv_a, sinv_b, d, bias=None, epilogue=0, aux=None, amax_d=None, stream=None):
+    m, k = a.shape
+    n = b.shape[0]
+    bias_dt = _dt(bias) if bias is not None else F32
+    _check(_lib.fp8_gemm(_p(a), a_fmt, _p(b), b_fmt, m, n, k, _p(sinv_a), _p(sinv_b), _p(bias), bias_dt, epilogue,
+                         _p(d), _dt(d), _p(aux), _p(amax_d), _stream(stream)))
+
+
+def fp8_linear_fwd(x, w, y, recipe, mx, mw, saved, bias=None, epilogue=0, y_aux=None, y_amax_slot=None,
+                   stream=None):
+    m, k = x.shape
+    n = w.shape[0]
+    bias_dt = _dt(bias) if bias is not None else F32
+    cx, cw, cs = mx.c(), mw.c(), saved.c()
+    _check(_lib.fp8_linear_fwd(m, n, k, _p(x), _dt(x), _p(w), _dt(w), _p(bias), bias_dt, epilogue, _p(y), _dt(y),
+                               _p(y_aux), _p(y_amax_slot), ctypes.byref(recipe), ctypes.byref(cx), ctypes.byref(cw),
+                               ctypes.byref(cs), _stream(stream)))
+
+
+def fp8_linear_bwd(dy, k, recipe, mdy, saved, dyq_ws=None, dyq_t_ws=None, dx=None, dw=None, accumulate_dw=False,
+                   dbias=None, dbias_ws=None, gelu_z=None, dz_out=None, stream=None):
+    m, n = dy.shape
+    dx_dt = _dt(dx) if dx is not None else F32
+    cm, cs = mdy.c(), saved.c()
+    _check(_lib.fp8_linear_bwd(m, n, k, _p(dy), _dt(dy), _p(gelu_z), _p(dz_out), ctypes.byref(recipe),
+                               ctypes.byref(cm), ctypes.byref(cs), _p(dyq_ws), _p(dyq_t_ws), _p(dx), dx_dt, _p(dw),
+                               int(bool(accumulate_dw)), _p(dbias), _p(dbias_ws), _stream(stream)))
+
+
+def dbias_workspace_bytes(rows, cols):
+    return _lib.fp8lin_dbias_workspace_bytes(rows, cols)
+
+
+def timing_enable(capacity):
+    _check(_lib.fp8lin_timing_enable(capacity))
+
+
+def timing_read(max_records=1 << 16):
+    """[(kind_name, ms), ...] of the launches recorded since timing_enable."""
+    kinds = (ctypes.c_int32 * max_records)()
+    ms = (ctypes.c_float * max_records)()
+    n = _lib.fp8lin_timing_read(ctypes.cast(kinds, ctypes.c_void_p), ctypes.cast(ms, ctypes.c_void_p), max_records)
+    return [(KIND_NAMES[kinds[i]], ms[i]) for i in range(n)]

@@ -1,0 +1,445 @@
+// extern "C" entry points of libfp8lin: argument validation (on the host,
+// before anything is enqueued), dispatch to the kernel launchers, the layer
+// compositions, error reporting and the optional launch timer.
+//
+// Every entry point follows the same shape: validate -> launch(es) on the
+// caller's stream -> return a status.  No entry point synchronises, allocates
+// device memory, or lets a C++ exception escape.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/fp8lin.h"
+#include "common.h"
+
+namespace fp8lin {
+
+// ------------------------------------------------------------ error reporting
+namespace {
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int32_t ok() {
+    g_err[0] = '\0';
+    return FP8LIN_OK;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(FP8LIN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool is_hp(int32_t dt) { return dt == FP8LIN_F32 || dt == FP8LIN_BF16; }
+bool is_fp8(int32_t dt) { return dt == FP8LIN_E4M3 || dt == FP8LIN_E5M2; }
+int64_t elem_size(int32_t dt) { return dt == FP8LIN_F32 ? 4 : dt == FP8LIN_BF16 ? 2 : 1; }
+
+// [lo, hi) byte ranges of two buffers overlap?
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kMaxK = int64_t(1) << 23;
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+}  // namespace
+
+// ---------------------------------------------------------------- launch timer
+namespace {
+struct Timer {
+    std::mutex mu;
+    std::vector<hipEvent_t> ev;     // 2 per record
+    std::vector<int32_t> kinds;
+    int32_t used = 0;
+    int32_t capacity = 0;
+    int32_t pending_kind = -1;
+};
+Timer g_timer;
+}  // namespace
+
+void timing_before(int kind, hipStream_t stream) {
+    if (g_timer.capacity == 0) return;
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    if (g_timer.used >= g_timer.capacity) return;
+    hipEventRecord(g_timer.ev[2 * g_timer.used], stream);
+    g_timer.pending_kind = kind;
+}
+
+void timing_after(hipStream_t stream) {
+    if (g_timer.capacity == 0) return;
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    if (g_timer.pending_kind < 0) return;
+    hipEventRecord(g_timer.ev[2 * g_timer.used + 1], stream);
+    g_timer.kinds[g_timer.used] = g_timer.pending_kind;
+    g_timer.pending_kind = -1;
+    ++g_timer.used;
+}
+
+}  // namespace fp8lin
+
+using namespace fp8lin;
+
+extern "C" {
+
+int32_t fp8lin_abi_version(void) { return FP8LIN_ABI_VERSION; }
+
+const char* fp8lin_last_error(void) { return g_err; }
+
+const char* fp8lin_status_name(int32_t s) {
+    switch (s) {
+        case FP8LIN_OK: return "FP8LIN_OK";
+        case FP8LIN_ERR_NULL: return "FP8LIN_ERR_NULL";
+        case FP8LIN_ERR_SHAPE: return "FP8LIN_ERR_SHAPE";
+        case FP8LIN_ERR_ALIGN: return "FP8LIN_ERR_ALIGN";
+        case FP8LIN_ERR_DTYPE: return "FP8LIN_ERR_DTYPE";
+        case FP8LIN_ERR_ARG: return "FP8LIN_ERR_ARG";
+        case FP8LIN_ERR_HIP: return "FP8LIN_ERR_HIP";
+        case FP8LIN_ERR_UNSUPPORTED: return "FP8LIN_ERR_UNSUPPORTED";
+        default: return "FP8LIN_UNKNOWN_STATUS";
+    }
+}
+
+int64_t fp8lin_dbias_workspace_bytes(int64_t rows, int64_t cols) {
+    return cast_transpose_dbias_ws_bytes(rows, cols);
+}
+
+int32_t fp8lin_timing_enable(int32_t capacity) {
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    for (hipEvent_t e : g_timer.ev) hipEventDestroy(e);
+    g_timer.ev.clear();
+    g_timer.kinds.clear();
+    g_timer.used = 0;
+    g_timer.capacity = 0;
+    g_timer.pending_kind = -1;
+    if (capacity < 0 || capacity > (1 << 20)) return fail(FP8LIN_ERR_ARG, "timing capacity %d out of range", capacity);
+    if (capacity == 0) return ok();
+    g_timer.ev.resize(2 * (size_t)capacity);
+    g_timer.kinds.assign(capacity, 0);
+    for (auto& e : g_timer.ev) {
+        const hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) {
+            g_timer.ev.clear();
+            return hip_status(r, "hipEventCreate");
+        }
+    }
+    g_timer.capacity = capacity;
+    return ok();
+}
+
+int32_t fp8lin_timing_read(int32_t* kinds, float* ms, int32_t max) {
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    const int32_t n = g_timer.used < max ? g_timer.used : max;
+    for (int32_t i = 0; i < n; ++i) {
+        hipEventSynchronize(g_timer.ev[2 * i + 1]);
+        float t = 0.0f;
+        hipEventElapsedTime(&t, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]);
+        if (kinds) kinds[i] = g_timer.kinds[i];
+        if (ms) ms[i] = t;
+    }
+    g_timer.used = 0;
+    return n;
+}
+
+// ------------------------------------------------------------------- amax
+int32_t fp8_amax(const void* x, int32_t x_dtype, int64_t n, float* amax_slot, void* stream) {
+    if (!is_hp(x_dtype)) return fail(FP8LIN_ERR_DTYPE, "fp8_amax: x_dtype %d must be F32 or BF16", x_dtype);
+    if (n < 0 || n > kMaxElems) return fail(FP8LIN_ERR_SHAPE, "fp8_amax: n=%lld out of range", (long long)n);
+    if (!amax_slot || (n > 0 && !x)) return fail(FP8LIN_ERR_NULL, "fp8_amax: null pointer");
+    if (!aligned(x, 16) || !aligned(amax_slot, 4)) return fail(FP8LIN_ERR_ALIGN, "fp8_amax: misaligned pointer");
+    return hip_status(launch_amax(x, x_dtype, n, amax_slot, as_stream(stream)), "fp8_amax");
+}
+
+// ----------------------------------------------------------- scale update
+int32_t fp8_amax_scale_update(float* amax_history, float* scale, float* scale_inv, const uint8_t* formats,
+                              int32_t n_tensors, const fp8lin_recipe* recipe, void* stream) {
+    if (!amax_history || !scale || !scale_inv || !formats || !recipe)
+        return fail(FP8LIN_ERR_NULL, "fp8_amax_scale_update: null pointer");
+    if (n_tensors < 1 || n_tensors > 4096)
+        return fail(FP8LIN_ERR_SHAPE, "fp8_amax_scale_update: n_tensors=%d not in [1, 4096]", n_tensors);
+    if (recipe->history_len < 1 || recipe->history_len > 65536)
+        return fail(FP8LIN_ERR_ARG, "fp8_amax_scale_update: history_len=%d not in [1, 65536]", recipe->history_len);
+    if (recipe->margin < 0 || recipe->margin > 127)
+        return fail(FP8LIN_ERR_ARG, "fp8_amax_scale_update: margin=%d not in [0, 127]", recipe->margin);
+    if (recipe->amax_compute_algo != FP8LIN_AMAX_MAX)
+        return fail(FP8LIN_ERR_UNSUPPORTED, "fp8_amax_scale_update: amax_compute_algo %d (only max)",
+                    recipe->amax_compute_algo);
+    for (int32_t t = 0; t < n_tensors; ++t)
+        if (!is_fp8(formats[t]))
+            return fail(FP8LIN_ERR_DTYPE, "fp8_amax_scale_update: formats[%d]=%d is not E4M3/E5M2", t, formats[t]);
+    if (!aligned(amax_history, 4) || !aligned(scale, 4) || !aligned(scale_inv, 4))
+        return fail(FP8LIN_ERR_ALIGN, "fp8_amax_scale_update: misaligned pointer");
+    const int64_t hb = (int64_t)n_tensors * recipe->history_len * 4, sb = (int64_t)n_tensors * 4;
+    if (overlap(amax_history, hb, scale, sb) || overlap(amax_history, hb, scale_inv, sb) ||
+        overlap(scale, sb, scale_inv, sb))
+        return fail(FP8LIN_ERR_ARG, "fp8_amax_scale_update: history, scale and scale_inv overlap");
+    return hip_status(launch_scale_update(amax_history, scale, scale_inv, formats, n_tensors, recipe->history_len,
+                                          recipe->margin, as_stream(stream)),
+                      "fp8_amax_scale_update");
+}
+
+// ------------------------------------------------------------------- cast
+int32_t fp8_cast(const void* x, int32_t x_dtype, int64_t n, int32_t fp8_dtype, const float* scale, uint8_t* q,
+                 float* amax_slot, void* stream) {
+    if (!is_hp(x_dtype)) return fail(FP8LIN_ERR_DTYPE, "fp8_cast: x_dtype %d must be F32 or BF16", x_dtype);
+    if (!is_fp8(fp8_dtype)) return fail(FP8LIN_ERR_DTYPE, "fp8_cast: fp8_dtype %d must be E4M3 or E5M2", fp8_dtype);
+    if (n < 0 || n > kMaxElems) return fail(FP8LIN_ERR_SHAPE, "fp8_cast: n=%lld out of range", (long long)n);
+    if (!scale || (n > 0 && (!x || !q))) return fail(FP8LIN_ERR_NULL, "fp8_cast: null pointer");
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4) || !aligned(amax_slot, 4))
+        return fail(FP8LIN_ERR_ALIGN, "fp8_cast: misaligned pointer");
+    if (overlap(x, n * elem_size(x_dtype), q, n))
+        return fail(FP8LIN_ERR_ARG, "fp8_cast: output overlaps input");
+    return hip_status(launch_cast(x, x_dtype, n, fp8_dtype, scale, q, amax_slot, as_stream(stream)), "fp8_cast");
+}
+
+namespace {
+int32_t check_ct(const char* fn, const void* x, const void* z, int32_t x_dtype, int64_t rows, int64_t cols,
+                 int32_t fp8_dtype, const float* scale, uint8_t* q, uint8_t* q_t, float* amax_slot, float* dbias,
+                 float* dbias_ws, void* dz_out, bool need_qt = true) {
+    if (!is_hp(x_dtype)) return fail(FP8LIN_ERR_DTYPE, "%s: x_dtype %d must be F32 or BF16", fn, x_dtype);
+    if (!is_fp8(fp8_dtype)) return fail(FP8LIN_ERR_DTYPE, "%s: fp8_dtype %d must be E4M3 or E5M2", fn, fp8_dtype);
+    if (rows < 0 || cols < 0 || rows % 16 || cols % 16 || rows * cols > kMaxElems)
+        return fail(FP8LIN_ERR_SHAPE, "%s: rows=%lld cols=%lld must be >= 0 multiples of 16", fn, (long long)rows,
+                    (long long)cols);
+    const int64_t n = rows * cols;
+    if (!scale || (n > 0 && (!x || (need_qt && !q_t)))) return fail(FP8LIN_ERR_NULL, "%s: null pointer", fn);
+    if (dbias && cols > 0 && !dbias_ws && rows > 0) return fail(FP8LIN_ERR_NULL, "%s: dbias needs dbias_ws", fn);
+    if (!aligned(x, 16) || !aligned(z, 16) || !aligned(q, 16) || !aligned(q_t, 16) || !aligned(dz_out, 16) ||
+        !aligned(scale, 4) || !aligned(amax_slot, 4) || !aligned(dbias, 4) || !aligned(dbias_ws, 4))
+        return fail(FP8LIN_ERR_ALIGN, "%s: misaligned pointer", fn);
+    const int64_t xb = n * elem_size(x_dtype);
+    const int64_t wsb = cast_transpose_dbias_ws_bytes(rows, cols);
+    const void* outs[4] = {q, q_t, dz_out, dbias ? (const void*)dbias_ws : nullptr};
+    const int64_t ob[4] = {n, n, xb, wsb};
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(outs[i], ob[i], x, xb) || overlap(outs[i], ob[i], z, z ? xb : 0))
+            return fail(FP8LIN_ERR_ARG, "%s: an output overlaps an input", fn);
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], ob[i], outs[j], ob[j])) return fail(FP8LIN_ERR_ARG, "%s: outputs overlap", fn);
+    }
+    if (dbias && (overlap(dbias, cols * 4, x, xb) || overlap(dbias, cols * 4, dbias_ws, wsb)))
+        return fail(FP8LIN_ERR_ARG, "%s: dbias overlaps another buffer", fn);
+    return FP8LIN_OK;
+}
+}  // namespace
+
+int32_t fp8_cast_transpose(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int32_t fp8_dtype,
+                           const float* scale, uint8_t* q, uint8_t* q_t, float* amax_slot, float* dbias,
+                           float* dbias_ws, void* stream) {
+    const int32_t v = check_ct("fp8_cast_transpose", x, nullptr, x_dtype, rows, cols, fp8_dtype, scale, q, q_t,
+                               amax_slot, dbias, dbias_ws, nullptr);
+    if (v != FP8LIN_OK) return v;
+    return hip_status(launch_cast_transpose(x, nullptr, x_dtype, rows, cols, fp8_dtype, scale, q, q_t, amax_slot,
+                                            dbias, dbias_ws, nullptr, as_stream(stream)),
+                      "fp8_cast_transpose");
+}
+
+int32_t fp8_cast_transpose_dgelu(const void* dh, const void* z, int32_t x_dtype, int64_t rows, int64_t cols,
+                                 int32_t fp8_dtype, const float* scale, uint8_t* q, uint8_t* q_t, float* amax_slot,
+                                 float* dbias, float* dbias_ws, void* dz_out, void* stream) {
+    if (rows * cols > 0 && !z) return fail(FP8LIN_ERR_NULL, "fp8_cast_transpose_dgelu: z is null");
+    const int32_t v = check_ct("fp8_cast_transpose_dgelu", dh, z, x_dtype, rows, cols, fp8_dtype, scale, q, q_t,
+                               amax_slot, dbias, dbias_ws, dz_out);
+    if (v != FP8LIN_OK) return v;
+    return hip_status(launch_cast_transpose(dh, z, x_dtype, rows, cols, fp8_dtype, scale, q, q_t, amax_slot, dbias,
+                                            dbias_ws, dz_out, as_stream(stream)),
+                      "fp8_cast_transpose_dgelu");
+}
+
+// ---------------------------------------------------------------- dequant
+int32_t fp8_dequant(const uint8_t* q, int32_t fp8_dtype, int64_t n, const float* scale_inv, void* out,
+                    int32_t out_dtype, void* stream) {
+    if (!is_fp8(fp8_dtype)) return fail(FP8LIN_ERR_DTYPE, "fp8_dequant: fp8_dtype %d must be E4M3 or E5M2", fp8_dtype);
+    if (!is_hp(out_dtype)) return fail(FP8LIN_ERR_DTYPE, "fp8_dequant: out_dtype %d must be F32 or BF16", out_dtype);
+    if (n < 0 || n > kMaxElems) return fail(FP8LIN_ERR_SHAPE, "fp8_dequant: n=%lld out of range", (long long)n);
+    if (!scale_inv || (n > 0 && (!q || !out))) return fail(FP8LIN_ERR_NULL, "fp8_dequant: null pointer");
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(scale_inv, 4))
+        return fail(FP8LIN_ERR_ALIGN, "fp8_dequant: misaligned pointer");
+    if (overlap(q, n, out, n * elem_size(out_dtype))) return fail(FP8LIN_ERR_ARG, "fp8_dequant: output overlaps input");
+    return hip_status(launch_dequant(q, fp8_dtype, n, scale_inv, out, out_dtype, as_stream(stream)), "fp8_dequant");
+}
+
+// ------------------------------------------------------------------- GEMM
+namespace {
+int32_t check_gemm(const char* fn, const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_dtype, int64_t m,
+                   int64_t n, int64_t k, const float* sinv_a, const float* sinv_b, const void* bias,
+                   int32_t bias_dtype, int32_t epilogue, void* d, int32_t d_dtype, void* aux, float* amax_d) {
+    if (!is_fp8(a_dtype) || !is_fp8(b_dtype))
+        return fail(FP8LIN_ERR_DTYPE, "%s: operand types %d, %d must be E4M3/E5M2", fn, a_dtype, b_dtype);
+    if (!is_hp(d_dtype)) return fail(FP8LIN_ERR_DTYPE, "%s: output type %d must be F32 or BF16", fn, d_dtype);
+    if (bias && !is_hp(bias_dtype)) return fail(FP8LIN_ERR_DTYPE, "%s: bias type %d must be F32 or BF16", fn, bias_dtype);
+    if (m < 0 || n < 0 || k < 0 || m % 16 || n % 16 || k % 16 || k >= kMaxK || m > (int64_t(1) << 31) ||
+        n > (int64_t(1) << 31) || m * n > kMaxElems)
+        return fail(FP8LIN_ERR_SHAPE, "%s: m=%lld n=%lld k=%lld must be >= 0 multiples of 16, k < 2^23", fn,
+                    (long long)m, (long long)n, (long long)k);
+    if (epilogue & ~(FP8LIN_EPI_GELU | FP8LIN_EPI_ACCUMULATE | FP8LIN_EPI_FAST_ACCUM))
+        return fail(FP8LIN_ERR_ARG, "%s: unknown epilogue flags 0x%x", fn, epilogue);
+    if ((epilogue & FP8LIN_EPI_GELU) && (epilogue & FP8LIN_EPI_ACCUMULATE))
+        return fail(FP8LIN_ERR_ARG, "%s: GELU and ACCUMULATE cannot be combined", fn);
+    if ((epilogue & FP8LIN_EPI_ACCUMULATE) && d_dtype != FP8LIN_F32)
+        return fail(FP8LIN_ERR_DTYPE, "%s: ACCUMULATE needs an F32 output", fn);
+    if (aux && !(epilogue & FP8LIN_EPI_GELU)) return fail(FP8LIN_ERR_ARG, "%s: aux is only written with GELU", fn);
+    if (!sinv_a || !sinv_b) return fail(FP8LIN_ERR_NULL, "%s: null scale pointer", fn);
+    if (m * n > 0 && !d) return fail(FP8LIN_ERR_NULL, "%s: null output", fn);
+    if (m * n * k > 0 && (!a || !b)) return fail(FP8LIN_ERR_NULL, "%s: null operand", fn);
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(aux, 16) || !aligned(bias, 16) ||
+        !aligned(sinv_a, 4) || !aligned(sinv_b, 4) || !aligned(amax_d, 4))
+        return fail(FP8LIN_ERR_ALIGN, "%s: misaligned pointer", fn);
+    const int64_t db = m * n * elem_size(d_dtype);
+    const void* ins[3] = {a, b, bias};
+    const int64_t ib[3] = {m * k, n * k, bias ? n * elem_size(bias_dtype) : 0};
+    for (int i = 0; i < 3; ++i)
+        if (overlap(d, db, ins[i], ib[i]) || overlap(aux, aux ? db : 0, ins[i], ib[i]))
+            return fail(FP8LIN_ERR_ARG, "%s: an output overlaps an input", fn);
+    if (overlap(d, db, aux, aux ? db : 0)) return fail(FP8LIN_ERR_ARG, "%s: d and aux overlap", fn);
+    return FP8LIN_OK;
+}
+}  // namespace
+
+int32_t fp8_gemm(const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_dtype, int64_t m, int64_t n, int64_t k,
+                 const float* sinv_a, const float* sinv_b, const void* bias, int32_t bias_dtype, int32_t epilogue,
+                 void* d, int32_t d_dtype, void* aux, float* amax_d, void* stream) {
+    const int32_t v = check_gemm("fp8_gemm", a, a_dtype, b, b_dtype, m, n, k, sinv_a, sinv_b, bias, bias_dtype,
+                                 epilogue, d, d_dtype, aux, amax_d);
+    if (v != FP8LIN_OK) return v;
+    return hip_status(launch_gemm(a, a_dtype, b, b_dtype, m, n, k, sinv_a, sinv_b, bias, bias_dtype, epilogue, d,
+                                  d_dtype, aux, amax_d, as_stream(stream)),
+                      "fp8_gemm");
+}
+
+// ---------------------------------------------------------- linear layer
+namespace {
+int32_t check_recipe(const char* fn, const fp8lin_recipe* r) {
+    if (!r) return fail(FP8LIN_ERR_NULL, "%s: null recipe", fn);
+    if (r->format != FP8LIN_FORMAT_E4M3 && r->format != FP8LIN_FORMAT_HYBRID)
+        return fail(FP8LIN_ERR_ARG, "%s: recipe format %d", fn, r->format);
+    if (r->amax_compute_algo != FP8LIN_AMAX_MAX)
+        return fail(FP8LIN_ERR_UNSUPPORTED, "%s: amax_compute_algo %d (only max)", fn, r->amax_compute_algo);
+    return FP8LIN_OK;
+}
+
+int32_t check_meta(const char* fn, const char* which, const fp8lin_meta* mt) {
+    if (!mt || !mt->amax_history || !mt->scale || !mt->scale_inv)
+        return fail(FP8LIN_ERR_NULL, "%s: meta %s has a null pointer", fn, which);
+    if (!aligned(mt->amax_history, 4) || !aligned(mt->scale, 4) || !aligned(mt->scale_inv, 4))
+        return fail(FP8LIN_ERR_ALIGN, "%s: meta %s misaligned", fn, which);
+    return FP8LIN_OK;
+}
+}  // namespace
+
+int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x_dtype, const void* w,
+                       int32_t w_dtype, const void* bias, int32_t bias_dtype, int32_t epilogue, void* y,
+                       int32_t y_dtype, void* y_aux, float* y_amax_slot, const fp8lin_recipe* recipe,
+                       const fp8lin_meta* mx, const fp8lin_meta* mw, const fp8lin_saved* saved, void* stream) {
+    const char* fn = "fp8_linear_fwd";
+    int32_t v;
+    if ((v = check_recipe(fn, recipe)) || (v = check_meta(fn, "x", mx)) || (v = check_meta(fn, "w", mw))) return v;
+    if (!saved || !saved->xq || !saved->wq || !saved->sinv) return fail(FP8LIN_ERR_NULL, "%s: saved needs xq, wq, sinv", fn);
+    if (!is_hp(x_dtype) || !is_hp(w_dtype)) return fail(FP8LIN_ERR_DTYPE, "%s: x/w types must be F32 or BF16", fn);
+    if (epilogue & ~FP8LIN_EPI_GELU) return fail(FP8LIN_ERR_ARG, "%s: the forward epilogue is 0 or GELU", fn);
+    const int32_t fast = recipe->fast_accum ? FP8LIN_EPI_FAST_ACCUM : 0;
+    if (m < 0 || n < 0 || k < 0 || m % 16 || n % 16 || k % 16)
+        return fail(FP8LIN_ERR_SHAPE, "%s: m=%lld n=%lld k=%lld must be >= 0 multiples of 16", fn, (long long)m,
+                    (long long)n, (long long)k);
+    if (m * k > 0 && !x) return fail(FP8LIN_ERR_NULL, "%s: null x", fn);
+    if (n * k > 0 && !w) return fail(FP8LIN_ERR_NULL, "%s: null w", fn);
+    if (!aligned(saved->sinv, 4)) return fail(FP8LIN_ERR_ALIGN, "%s: saved->sinv misaligned", fn);
+    // Validate every sub-call before launching any of them.
+    if ((v = check_ct(fn, x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx->scale, saved->xq, saved->xq_t,
+                      mx->amax_history, nullptr, nullptr, nullptr, false)))
+        return v;
+    if ((v = check_ct(fn, w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw->scale, saved->wq, saved->wq_t,
+                      mw->amax_history, nullptr, nullptr, nullptr, false)))
+        return v;
+    if ((v = check_gemm(fn, saved->xq, FP8LIN_E4M3, saved->wq, FP8LIN_E4M3, m, n, k, saved->sinv, saved->sinv + 1,
+                        bias, bias_dtype, epilogue | fast, y, y_dtype, y_aux, y_amax_slot)))
+        return v;
+    if (overlap(y, m * n * elem_size(y_dtype), x, m * k * elem_size(x_dtype)) ||
+        overlap(y, m * n * elem_size(y_dtype), w, n * k * elem_size(w_dtype)))
+        return fail(FP8LIN_ERR_ARG, "%s: y overlaps an input", fn);
+
+    hipStream_t s = as_stream(stream);
+    hipError_t e;
+    if (saved->xq_t) e = launch_cast_transpose(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx->scale, saved->xq,
+                                               saved->xq_t, mx->amax_history, nullptr, nullptr, nullptr, s);
+    else e = launch_cast(x, x_dtype, m * k, FP8LIN_E4M3, mx->scale, saved->xq, mx->amax_history, s);
+    if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast X");
+    if (saved->wq_t) e = launch_cast_transpose(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw->scale, saved->wq,
+                                               saved->wq_t, mw->amax_history, nullptr, nullptr, nullptr, s);
+    else e = launch_cast(w, w_dtype, n * k, FP8LIN_E4M3, mw->scale, saved->wq, mw->amax_history, s);
+    if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast W");
+    e = launch_copy_scalars(mx->scale_inv, mw->scale_inv, saved->sinv, s);
+    if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: save scale_inv");
+    e = launch_gemm(saved->xq, FP8LIN_E4M3, saved->wq, FP8LIN_E4M3, m, n, k, saved->sinv, saved->sinv + 1, bias,
+                    bias_dtype, epilogue | fast, y, y_dtype, y_aux, y_amax_slot, s);
+    return hip_status(e, "fp8_linear_fwd: gemm");
+}
+
+int32_t fp8_linear_bwd(int64_t m, int64_t n, int64_t k, const void* dy, int32_t dy_dtype, const void* gelu_z,
+                       void* dz_out, const fp8lin_recipe* recipe, const fp8lin_meta* mdy, const fp8lin_saved* saved,
+                       uint8_t* dyq_ws, uint8_t* dyq_t_ws, void* dx, int32_t dx_dtype, float* dw,
+                       int32_t accumulate_dw, float* dbias, float* dbias_ws, void* stream) {
+    const char* fn = "fp8_linear_bwd";
+    int32_t v;
+    if ((v = check_recipe(fn, recipe)) || (v = check_meta(fn, "dy", mdy))) return v;
+    if (!saved || !saved->sinv) return fail(FP8LIN_ERR_NULL, "%s: saved needs sinv", fn);
+    if (!is_hp(dy_dtype)) return fail(FP8LIN_ERR_DTYPE, "%s: dy type must be F32 or BF16", fn);
+    if (dz_out && !gelu_z) return fail(FP8LIN_ERR_ARG, "%s: dz_out needs gelu_z", fn);
+    if (m < 0 || n < 0 || k < 0 || m % 16 || n % 16 || k % 16)
+        return fail(FP8LIN_ERR_SHAPE, "%s: m=%lld n=%lld k=%lld must be >= 0 multiples of 16", fn, (long long)m,
+                    (long long)n, (long long)k);
+    if (m * n > 0 && !dy) return fail(FP8LIN_ERR_NULL, "%s: null dy", fn);
+    if (dx && (!dyq_ws || !saved->wq_t)) return fail(FP8LIN_ERR_NULL, "%s: dx needs dyq_ws and saved->wq_t", fn);
+    if (dw && (!dyq_t_ws || !saved->xq_t)) return fail(FP8LIN_ERR_NULL, "%s: dw needs dyq_t_ws and saved->xq_t", fn);
+    if (!dx && !dw && !dbias) return ok();
+    const int32_t gfmt = recipe->format == FP8LIN_FORMAT_HYBRID ? FP8LIN_E5M2 : FP8LIN_E4M3;
+    const int32_t fast = recipe->fast_accum ? FP8LIN_EPI_FAST_ACCUM : 0;
+    // Row-major codes feed dgrad, transposed codes feed wgrad; each is written
+    // only when its GEMM is wanted.
+    uint8_t* qr = dx ? dyq_ws : nullptr;
+    uint8_t* qt = dw ? dyq_t_ws : nullptr;
+    if ((v = check_ct(fn, dy, gelu_z, dy_dtype, m, n, gfmt, mdy->scale, qr, qt, mdy->amax_history, dbias, dbias_ws,
+                      dz_out, false)))
+        return v;
+    if (dx && (v = check_gemm(fn, dyq_ws, gfmt, saved->wq_t, FP8LIN_E4M3, m, k, n, mdy->scale_inv, saved->sinv + 1,
+                              nullptr, FP8LIN_F32, fast, dx, dx_dtype, nullptr, nullptr)))
+        return v;
+    if (dw && (v = check_gemm(fn, dyq_t_ws, gfmt, saved->xq_t, FP8LIN_E4M3, n, k, m, mdy->scale_inv, saved->sinv,
+                              nullptr, FP8LIN_F32, (accumulate_dw ? FP8LIN_EPI_ACCUMULATE : 0) | fast, dw, FP8LIN_F32,
+                              nullptr, nullptr)))
+        return v;
+    if (dx && dw && overlap(dx, m * k * elem_size(dx_dtype), dw, n * k * 4))
+        return fail(FP8LIN_ERR_ARG, "%s: dx and dw overlap", fn);
+
+    hipStream_t s = as_stream(stream);
+    hipError_t e = launch_cast_transpose(dy, gelu_z, dy_dtype, m, n, gfmt, mdy->scale, qr, qt, mdy->amax_history,
+                                         dbias, dbias_ws, dz_out, s);
+    if (e != hipSuccess) return hip_status(e, "fp8_linear_bwd: cast dY");
+    if (dx) {
+        e = launch_gemm(dyq_ws, gfmt, saved->wq_t, FP8LIN_E4M3, m, k, n, mdy->scale_inv, saved->sinv + 1, nullptr,
+                        FP8LIN_F32, fast, dx, dx_dtype, nullptr, nullptr, s);
+        if (e != hipSuccess) return hip_status(e, "fp8_linear_bwd: dgrad");
+    }
+    if (dw) {
+        e = launch_gemm(dyq_t_ws, gfmt, saved->xq_t, FP8LIN_E4M3, n, k, m, mdy->scale_inv, saved->sinv, nullptr,
+                        FP8LIN_F32, (accumulate_dw ? FP8LIN_EPI_ACCUMULATE : 0) | fast, dw, FP8LIN_F32, nullptr,
+                        nullptr, s);
+        if (e != hipSuccess) return hip_status(e, "fp8_linear_bwd: wgrad");
+    }
+    return ok();
+}
+
+}  // extern "C"

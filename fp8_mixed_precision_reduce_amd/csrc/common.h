@@ -1,0 +1,191 @@
+// Device helpers and launcher declarations shared by the kernels of libfp8lin.
+//
+// Everything here is written for gfx950 (CDNA4): 64-lane waves, the OCP FP8
+// hardware converts, DPP lane shuffles, buffer resources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8lin {
+
+enum Dtype : int32_t { kF32 = 0, kBF16 = 1, kE4M3 = 2, kE5M2 = 3 };
+
+// Kinds of kernels, as reported by the event timer.
+enum Kind : int32_t { kKindAmax = 0, kKindCast = 1, kKindCastT = 2, kKindDequant = 3,
+                      kKindScaleUpdate = 4, kKindGemm = 5, kKindDbias = 6, kKindOther = 7 };
+
+// Host side: record events around a launch when timing is enabled.
+void timing_before(int kind, hipStream_t stream);
+void timing_after(hipStream_t stream);
+
+// ------------------------------------------------------------------ launchers
+// Each returns the hipError_t of its launch.  Arguments are validated by the
+// C entry points before these are called.
+hipError_t launch_amax(const void* x, int dtype, int64_t n, float* slot, hipStream_t s);
+hipError_t launch_cast(const void* x, int dtype, int64_t n, int fmt, const float* scale,
+                       uint8_t* q, float* slot, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* q, int fmt, int64_t n, const float* sinv, void* out,
+                          int out_dtype, hipStream_t s);
+hipError_t launch_scale_update(float* hist, float* scale, float* sinv, const uint8_t* fmts,
+                               int32_t n, int32_t L, int32_t margin, hipStream_t s);
+hipError_t launch_copy_scalars(const float* a, const float* b, float* dst2, hipStream_t s);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_t rows, int64_t cols,
+                                 int fmt, const float* scale, uint8_t* q, uint8_t* qt, float* slot,
+                                 float* dbias, float* dbias_ws, void* dz_out, hipStream_t s);
+int64_t cast_transpose_dbias_ws_bytes(int64_t rows, int64_t cols);
+hipError_t launch_gemm(const uint8_t* a, int afmt, const uint8_t* b, int bfmt, int64_t m, int64_t n,
+                       int64_t k, const float* sinv_a, const float* sinv_b, const void* bias,
+                       int bias_dtype, int epilogue, void* d, int d_dtype, void* aux, float* amax,
+                       hipStream_t s);
+
+#ifdef __HIPCC__
+// ------------------------------------------------------------ device helpers
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Two fp32 values to two bf16 (round to nearest-even) packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float round_to_bf16(float v) {
+    return bf16_to_f32(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+}
+
+template <int FMT> struct Fp8Max;
+template <> struct Fp8Max<kE4M3> { static constexpr float value = 448.0f; };
+template <> struct Fp8Max<kE5M2> { static constexpr float value = 57344.0f; };
+
+// Saturating clamp that lets NaN through: |p| >= max -> +-max.
+template <int FMT>
+__device__ __forceinline__ float sat_fp8(float p) {
+    return fabsf(p) >= Fp8Max<FMT>::value ? copysignf(Fp8Max<FMT>::value, p) : p;
+}
+
+// Encode four fp32 values (already scaled) into four codes, byte i = value i.
+// The hardware converts round to nearest-even; the clamp gives saturation and
+// NaN is mapped to sign|0x7F explicitly.
+template <int FMT>
+__device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
+    const float sa = sat_fp8<FMT>(a), sb = sat_fp8<FMT>(b), sc = sat_fp8<FMT>(c), sd = sat_fp8<FMT>(d);
+    int v;
+    if constexpr (FMT == kE4M3) {
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(sa, sb, 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(sc, sd, v, true);
+    } else {
+        v = __builtin_amdgcn_cvt_pk_bf8_f32(sa, sb, 0, false);
+        v = __builtin_amdgcn_cvt_pk_bf8_f32(sc, sd, v, true);
+    }
+    uint32_t r = (uint32_t)v;
+    const bool na = a != a, nb = b != b, nc = c != c, nd = d != d;
+    if (__builtin_expect(na | nb | nc | nd, 0)) {
+        const uint32_t nan_mask = (na ? 0xFFu : 0u) | (nb ? 0xFF00u : 0u) | (nc ? 0xFF0000u : 0u) |
+                                  (nd ? 0xFF000000u : 0u);
+        const uint32_t signs = ((__float_as_uint(a) >> 31) << 7) | ((__float_as_uint(b) >> 31) << 15) |
+                               ((__float_as_uint(c) >> 31) << 23) | ((__float_as_uint(d) >> 31) << 31);
+        r = (r & ~nan_mask) | (nan_mask & (0x7F7F7F7Fu | signs));
+    }
+    return r;
+}
+
+// Decode four codes (bytes of w) to fp32, exactly.
+template <int FMT>
+__device__ __forceinline__ void dec4(uint32_t w, float out[4]) {
+    f32x2 lo, hi;
+    if constexpr (FMT == kE4M3) {
+        lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+        hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    } else {
+        lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+        hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+    }
+    out[0] = lo.x; out[1] = lo.y; out[2] = hi.x; out[3] = hi.y;
+}
+
+// |x| as an unsigned bit pattern: the amax statistic compares these.
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// Max over the 64 lanes of a wave: DPP within each row of 16 lanes, then the
+// four row results through readlane.  Every lane returns the wave maximum.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// Max-merge a per-thread amax into a device slot: one atomic per workgroup.
+// `red` is LDS scratch of at least (blockDim.x / 64) words.  All threads of
+// the block must call it.
+__device__ __forceinline__ void block_amax_merge(uint32_t v, float* slot, uint32_t* red) {
+    v = wave_max_u32(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t m = 0;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = max(m, red[w]);
+        if (m != 0u) atomicMax(reinterpret_cast<unsigned int*>(slot), m);
+    }
+}
+
+// Load 16 consecutive elements (16-byte aligned) as fp32.
+template <int DT>
+__device__ __forceinline__ void load16(const void* base, int64_t idx, float v[16]) {
+    if constexpr (DT == kF32) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + idx);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 u = p[j];
+            v[4 * j + 0] = __uint_as_float(u.x); v[4 * j + 1] = __uint_as_float(u.y);
+            v[4 * j + 2] = __uint_as_float(u.z); v[4 * j + 3] = __uint_as_float(u.w);
+        }
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint4 u = p[j];
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[8 * j + 2 * h + 0] = __uint_as_float(w[h] << 16);
+                v[8 * j + 2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
+            }
+        }
+    }
+}
+
+// Encode 16 fp32 values times `s` into 16 codes.
+template <int FMT>
+__device__ __forceinline__ uint4 scale_enc16(const float v[16], float s) {
+    uint4 r;
+    r.x = enc4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+    r.y = enc4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+    r.z = enc4<FMT>(v[8] * s, v[9] * s, v[10] * s, v[11] * s);
+    r.w = enc4<FMT>(v[12] * s, v[13] * s, v[14] * s, v[15] * s);
+    return r;
+}
+
+// gelu'(z) = Phi(z) + z * phi(z), fp32, with Phi through erfc so the negative
+// tail keeps its relative precision.
+__device__ __forceinline__ float gelu_grad_f32(float z) {
+    const float cdf = 0.5f * erfcf(-z * 0.70710678118654752f);
+    const float pdf = expf(-0.5f * z * z) * 0.39894228040143268f;
+    return cdf + z * pdf;
+}
+
+__device__ __forceinline__ float gelu_f32(float z) {
+    return 0.5f * z * erfcf(-z * 0.70710678118654752f);
+}
+#endif  // __HIPCC__
+
+}  // namespace fp8lin

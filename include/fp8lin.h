@@ -1,0 +1,328 @@
+/*
+ * fp8lin.h -- C ABI of libfp8lin.so: an FP8 linear layer with per-tensor
+ * delayed scaling for AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations come from (titles as published):
+ *   [TE-KR]  "Transformer Engine으로 FP8 사용하기" (coniverse.tistory.com)
+ *   [MP-KR]  "LLM) Mixed-Precision 개념 및 학습 방법 알아보기" (data-newbie.tistory.com)
+ *   [PT-VI]  "Các kiểu dữ liệu FP8 gốc của PyTorch" (hotroai.com)
+ *   [TE-RU]  "Как работает FP8 quantization на H100 (Transformer Engine)?" (aivaro.ru)
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Pointers are DEVICE pointers unless the comment says "host".  Tensors are
+ *   dense and row-major.  FP8 tensors are one byte per element (OCP E4M3 or
+ *   OCP E5M2 codes).  bf16 tensors are 16-bit bfloat16 bit patterns.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *   call only enqueues work on that stream and returns; no call synchronises.
+ *   Scales and amaxes live in device memory, so delayed scaling never needs a
+ *   host round trip.
+ * - The library allocates no device memory.  The caller owns every buffer.
+ *   Inputs are read-only; the only buffers written are the outputs a call
+ *   names, the amax slots it max-merges into, and (fp8_amax_scale_update only)
+ *   the metas.  Outputs must not overlap inputs.
+ * - Tensor base pointers must be 16-byte aligned (FP8LIN_ERR_ALIGN); scalar
+ *   pointers (scale, amax slot, ...) 4-byte aligned.
+ * - Arguments are validated on the host before anything is enqueued; a call
+ *   that returns an error has had no effect.  A failed launch returns
+ *   FP8LIN_ERR_HIP.  fp8lin_last_error() describes the last failure of the
+ *   calling thread.  Faults inside a kernel surface at the caller's next
+ *   synchronisation, as usual in HIP.
+ * - An "amax slot" is a float holding a non-negative value (or NaN).  Calls
+ *   max-merge into it: slot = max(slot, amax) compared as IEEE bit patterns of
+ *   |x| (so the order of merges does not matter and NaN/Inf propagate).
+ */
+#ifndef FP8LIN_H
+#define FP8LIN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8LIN_ABI_VERSION 1
+
+/* Status codes returned by every call. */
+enum {
+    FP8LIN_OK = 0,
+    FP8LIN_ERR_NULL = 1,        /* a required pointer is NULL */
+    FP8LIN_ERR_SHAPE = 2,       /* a size is negative, too large, or not a multiple of 16 where required */
+    FP8LIN_ERR_ALIGN = 3,       /* a pointer is not aligned as required */
+    FP8LIN_ERR_DTYPE = 4,       /* an element type or format is not accepted by this call */
+    FP8LIN_ERR_ARG = 5,         /* any other invalid argument (flags, history length, margin, aliasing) */
+    FP8LIN_ERR_HIP = 6,         /* the HIP runtime refused a launch */
+    FP8LIN_ERR_UNSUPPORTED = 7  /* a valid request this build does not implement */
+};
+
+/* Element types. */
+enum {
+    FP8LIN_F32 = 0,
+    FP8LIN_BF16 = 1,
+    FP8LIN_E4M3 = 2,            /* OCP E4M3: finite + NaN, max 448  ([TE-KR] "Introduction to FP8") */
+    FP8LIN_E5M2 = 3             /* OCP E5M2: IEEE-like, max 57344    ([TE-KR] "Introduction to FP8") */
+};
+
+/* Recipe formats ([TE-KR] "FP8 사용방안(recipe)": Format.HYBRID uses E4M3 in the
+ * forward pass and E5M2 in the backward pass; [TE-RU] section 4). */
+enum {
+    FP8LIN_FORMAT_E4M3 = 0,     /* every tensor E4M3 */
+    FP8LIN_FORMAT_HYBRID = 1    /* forward tensors E4M3, gradients E5M2 */
+};
+
+/* amax_compute_algo: the only algorithm the pages name is "max" over the history. */
+enum { FP8LIN_AMAX_MAX = 0 };
+
+/* GEMM epilogue / mode flags. */
+enum {
+    FP8LIN_EPI_GELU = 1,        /* out = gelu(y), gelu(y) = y * Phi(y) (exact erf form) */
+    FP8LIN_EPI_ACCUMULATE = 2,  /* out += y (fp32 outputs only, no GELU) */
+    FP8LIN_EPI_FAST_ACCUM = 4   /* native FP8 matrix-core dot products: twice the rate, but the
+                                   hardware sums each group of 8 products with ~14 bits kept
+                                   below the group's largest product (not fp32-exact).  Without
+                                   this flag the products are formed exactly and summed in fp32. */
+};
+
+/* Delayed-scaling recipe ([TE-KR] "FP8 사용방안(recipe)", [TE-RU] section 10:
+ * DelayedScaling(fp8_format, amax_history_len, amax_compute_algo)).  `margin`
+ * divides the scale by 2^margin (0 <= margin <= 127).  `fast_accum` != 0 makes
+ * the layer calls run their GEMMs with FP8LIN_EPI_FAST_ACCUM. */
+typedef struct {
+    int32_t format;             /* FP8LIN_FORMAT_* */
+    int32_t history_len;        /* amax history length L >= 1 */
+    int32_t amax_compute_algo;  /* FP8LIN_AMAX_MAX */
+    int32_t margin;
+    int32_t fast_accum;
+} fp8lin_recipe;
+
+/* Per-tensor scaling state ([TE-KR] "Scaling factor" strategy: delayed scaling
+ * keeps a history of earlier amaxes as extra state of the FP8 operator).  All
+ * three are device pointers: amax_history float[L] in logical order (slot 0 =
+ * the current step's amax), scale and scale_inv one float each. */
+typedef struct {
+    float* amax_history;
+    float* scale;
+    float* scale_inv;
+} fp8lin_meta;
+
+/* What the forward pass leaves for the backward pass ([TE-KR] "Backward Pass
+ * 처리": backward runs at the precision fixed in the forward, i.e. on the FP8
+ * copies and factors taken there).  Device pointers:
+ *   xq [M][K], xq_t [K][M], wq [N][K], wq_t [K][N]  FP8 codes (E4M3)
+ *   sinv float[2]: scale_inv of X and of W as they were at the forward pass.
+ * xq_t and wq_t may be NULL for inference (no transposes are produced). */
+typedef struct {
+    uint8_t* xq;
+    uint8_t* xq_t;
+    uint8_t* wq;
+    uint8_t* wq_t;
+    float* sinv;
+} fp8lin_saved;
+
+/* ------------------------------------------------------------------------ */
+
+/* FP8LIN_ABI_VERSION of the loaded library. */
+int32_t fp8lin_abi_version(void);
+
+/* Message describing the last failed call of the calling thread ("" if none).
+ * The string is owned by the library and valid until the thread's next call. */
+const char* fp8lin_last_error(void);
+
+/* Name of a status code ("FP8LIN_OK", ...). */
+const char* fp8lin_status_name(int32_t status);
+
+/* Bytes of workspace fp8_cast_transpose / fp8_linear_bwd need for a bias
+ * gradient of a [rows][cols] tensor (0 if rows or cols is 0). */
+int64_t fp8lin_dbias_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * fp8_amax -- max-merge amax(x) = max |x_i| into *amax_slot.
+ * [TE-KR] "Scaling factor" strategy: scaling is driven by a tensor's absolute
+ * maximum; just-in-time scaling measures it on every use.
+ *   x         [n] elements of x_dtype (FP8LIN_F32 or FP8LIN_BF16); n >= 0
+ *   amax_slot device float, max-merged (bit-pattern max of |x|)
+ */
+int32_t fp8_amax(const void* x, int32_t x_dtype, int64_t n, float* amax_slot, void* stream);
+
+/*
+ * fp8_amax_scale_update -- the per-step delayed-scaling update of n tensors in
+ * one launch.  [TE-KR] "Scaling factor" strategy (delayed scaling uses the
+ * amaxes of earlier iterations kept as a history); [TE-KR] "FP8 사용방안
+ * (recipe)" (amax_compute_algo "max"); [PT-VI] training script (the history
+ * and scale update runs once per step after backward, before the optimizer);
+ * [TE-RU] section 3 (the tensor is multiplied by the factor before the FP8
+ * rounding and the result divided by it after the GEMM).
+ * For each tensor t, with h = amax_history + t*L:
+ *   A = max over the finite entries of h[0..L-1]
+ *   if A > 0:  s = fl32(fl32(fp8_max(fmt[t]) / A) * 2^-margin), s = FLT_MAX if
+ *              that overflowed; if s > 0: scale[t] = s, scale_inv[t] = fl32(1/s)
+ *   (otherwise scale[t] and scale_inv[t] are kept);
+ *   then h rolls one slot: h[i] = h[i-1] (i = L-1..1), h[0] = 0.
+ *   amax_history  device float[n][L], updated in place
+ *   scale, scale_inv device float[n], updated in place
+ *   formats       HOST uint8[n], each FP8LIN_E4M3 or FP8LIN_E5M2 (fp8_max 448 or 57344)
+ *   recipe        HOST; uses history_len (L), margin and amax_compute_algo
+ * 1 <= n <= 4096, 1 <= L <= 65536.
+ */
+int32_t fp8_amax_scale_update(float* amax_history, float* scale, float* scale_inv,
+                              const uint8_t* formats, int32_t n_tensors,
+                              const fp8lin_recipe* recipe, void* stream);
+
+/*
+ * fp8_cast -- q = enc_F(fl32(x * scale)) elementwise, with amax(x) fused.
+ * [TE-KR] "FP8 자동변환(Autocasting)": inputs are converted to FP8 and their
+ * amax recorded in the same step; [TE-RU] section 3.  enc_F is the saturating
+ * round-to-nearest-even encode of format F (fp32 product first, no FMA; NaN ->
+ * sign|0x7F; +-Inf and |p| >= fp8_max -> +-max; FP8 subnormals kept; sign of
+ * zero kept).
+ *   x         [n] of x_dtype (F32 or BF16), n >= 0 (any n, no multiple-of-16 rule)
+ *   fp8_dtype FP8LIN_E4M3 or FP8LIN_E5M2
+ *   scale     device float
+ *   q         [n] codes
+ *   amax_slot device float or NULL
+ */
+int32_t fp8_cast(const void* x, int32_t x_dtype, int64_t n, int32_t fp8_dtype,
+                 const float* scale, uint8_t* q, float* amax_slot, void* stream);
+
+/*
+ * fp8_cast_transpose -- fp8_cast of a [rows][cols] tensor that writes the codes
+ * both row-major (q [rows][cols]) and transposed (q_t [cols][rows]), so each
+ * backward GEMM finds its operand contiguous along the reduced dimension.
+ * Optionally also the bias gradient dbias[c] = sum_r x[r][c] (fp32).
+ * [TE-KR] "Backward Pass 처리" (backward consumes the forward's FP8 copies);
+ * [PT-VI] torch._scaled_mm example (the second operand enters transposed).
+ *   rows, cols  >= 0 and multiples of 16 ([TE-KR] caution note: FP8 linear
+ *               layers need both dimensions divisible by 16)
+ *   q           [rows][cols] or NULL (only the transpose is written)
+ *   q_t         [cols][rows]
+ *   amax_slot   device float or NULL
+ *   dbias       device float[cols] or NULL (overwritten, not accumulated)
+ *   dbias_ws    workspace of fp8lin_dbias_workspace_bytes(rows, cols) bytes;
+ *               required when dbias != NULL, else ignored
+ */
+int32_t fp8_cast_transpose(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                           int32_t fp8_dtype, const float* scale, uint8_t* q, uint8_t* q_t,
+                           float* amax_slot, float* dbias, float* dbias_ws, void* stream);
+
+/*
+ * fp8_cast_transpose_dgelu -- the cast-transpose of the gradient entering a
+ * GeLU: dz = round_x(dh * gelu'(z)) is formed on the fly (fp32 math, rounded to
+ * the element type of dh), then cast and transposed as fp8_cast_transpose does;
+ * amax and dbias are of dz.  gelu'(z) = Phi(z) + z * phi(z).
+ *   dh, z       [rows][cols] of x_dtype (F32 or BF16); z is the pre-GeLU value
+ *   dz_out      [rows][cols] of x_dtype or NULL (the rounded dz, for inspection)
+ *   other arguments as in fp8_cast_transpose
+ */
+int32_t fp8_cast_transpose_dgelu(const void* dh, const void* z, int32_t x_dtype,
+                                 int64_t rows, int64_t cols, int32_t fp8_dtype,
+                                 const float* scale, uint8_t* q, uint8_t* q_t,
+                                 float* amax_slot, float* dbias, float* dbias_ws,
+                                 void* dz_out, void* stream);
+
+/*
+ * fp8_dequant -- out = round_out(fl32(dec_F(q) * scale_inv)) elementwise.
+ * [TE-RU] section 3: after the FP8 operation the factor is divided back out;
+ * [TE-KR] "정확도(Precision)": the FP8-representable copy of a tensor.
+ *   q         [n] codes of fp8_dtype, n >= 0
+ *   scale_inv device float
+ *   out       [n] of out_dtype (F32, or BF16 rounded to nearest-even)
+ */
+int32_t fp8_dequant(const uint8_t* q, int32_t fp8_dtype, int64_t n, const float* scale_inv,
+                    void* out, int32_t out_dtype, void* stream);
+
+/*
+ * fp8_gemm -- the scaled FP8 GEMM with fp32 accumulation and a fused epilogue:
+ *   y[i][j] = (sum_k dec(a[i][k]) * dec(b[j][k])) * sinv_a * sinv_b + bias[j]
+ *   d[i][j] = gelu(y) | y | d[i][j] + y   (per `epilogue`), rounded to d_dtype
+ * [PT-VI] torch._scaled_mm example: two FP8 operands (the second transposed),
+ * their scales, an optional bias, an output type, and the output's amax;
+ * [MP-KR] "Accumulation into FP32"; [TE-RU] section 3 (inverse scaling after
+ * the GEMM).  Both operands are contiguous along k ("TN").
+ *   a [m][k], b [n][k]  codes; (a_dtype, b_dtype) in {E4M3, E5M2}^2
+ *   m, n, k    >= 0 and multiples of 16; k < 2^23
+ *   sinv_a, sinv_b  device floats
+ *   bias       device [n] of bias_dtype (F32 or BF16) or NULL
+ *   epilogue   0, FP8LIN_EPI_GELU or FP8LIN_EPI_ACCUMULATE, optionally | FP8LIN_EPI_FAST_ACCUM
+ *   d          [m][n] of d_dtype (F32 or BF16; ACCUMULATE needs F32)
+ *   aux        [m][n] of d_dtype or NULL: y before GeLU (only with GELU)
+ *   amax_d     device float or NULL: max-merged amax of d as written
+ */
+int32_t fp8_gemm(const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_dtype,
+                 int64_t m, int64_t n, int64_t k, const float* sinv_a, const float* sinv_b,
+                 const void* bias, int32_t bias_dtype, int32_t epilogue,
+                 void* d, int32_t d_dtype, void* aux, float* amax_d, void* stream);
+
+/*
+ * fp8_linear_fwd -- forward of Y = X W^T + b on FP8 copies of X and W.
+ * [TE-KR] "FP8 자동변환(Autocasting)": every input is cast to FP8, its amax
+ * recorded and the factor applied; [TE-KR] "Using FP8 with Transformer
+ * Engine" (a Linear(768, 768, bias=True) on a 1024x768 input).
+ * Steps (all on `stream`): cast(-transpose) X -> saved->xq (+ xq_t) with
+ * mx->scale, amax(X) into mx->amax_history[0]; the same for W with mw;
+ * saved->sinv = {*mx->scale_inv, *mw->scale_inv}; then fp8_gemm(xq, wq) with
+ * sinv = saved->sinv, bias and epilogue, into y (and y_aux, y_amax_slot).
+ * The forward format is E4M3 under both recipe formats.
+ *   m, n, k   X [m][k], W [n][k], Y [m][n]; multiples of 16
+ *   x_dtype, w_dtype  F32 or BF16;  bias: [n] of bias_dtype or NULL
+ *   epilogue  0 or FP8LIN_EPI_GELU (then y_aux, if not NULL, gets y before GeLU)
+ *   y_dtype   F32 or BF16
+ *   mx, mw    HOST structs of device pointers (metas of X and W)
+ *   saved     HOST struct of device pointers; xq, wq, sinv required
+ */
+int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k,
+                       const void* x, int32_t x_dtype, const void* w, int32_t w_dtype,
+                       const void* bias, int32_t bias_dtype, int32_t epilogue,
+                       void* y, int32_t y_dtype, void* y_aux, float* y_amax_slot,
+                       const fp8lin_recipe* recipe, const fp8lin_meta* mx, const fp8lin_meta* mw,
+                       const fp8lin_saved* saved, void* stream);
+
+/*
+ * fp8_linear_bwd -- backward of the FP8 linear from the forward's saved state.
+ * [TE-KR] "Backward Pass 처리" (precision fixed by the forward; gradients in
+ * E5M2 under HYBRID per "Introduction to FP8"); [MP-KR] "FP32 Master Copy of
+ * Weights" (weight gradients feed fp32 masters).
+ * Steps: cast-transpose dY (format E5M2 under HYBRID, E4M3 otherwise) with
+ * mdy->scale into dyq_ws / dyq_t_ws, amax(dY) into mdy->amax_history[0],
+ * optional dbias = column sums of dY; then
+ *   dX [m][k] = (dYq . Wq)   = fp8_gemm(dyq [m][n], wq_t [k][n]) * sinv_dy * saved->sinv[1]
+ *   dW [n][k] = (dYq^T . Xq) = fp8_gemm(dyq_t [n][m], xq_t [k][m]) * sinv_dy * saved->sinv[0]
+ * If gelu_z is not NULL, dy is the gradient with respect to gelu(Z) of a layer
+ * whose forward used FP8LIN_EPI_GELU with pre-activation Z = gelu_z ([m][n],
+ * dy's type); the gradient cast is then dZ = round(dy * gelu'(Z)) (see
+ * fp8_cast_transpose_dgelu) and dbias is of dZ.
+ *   dy        [m][n] of dy_dtype (F32 or BF16)
+ *   dz_out    [m][n] of dy_dtype or NULL (only with gelu_z)
+ *   mdy       HOST struct of device pointers (meta of the gradient)
+ *   saved     HOST struct from the forward; wq_t needed for dX, xq_t for dW
+ *   dyq_ws    [m][n] bytes (needed when dx != NULL), dyq_t_ws [n][m] bytes (needed when dw != NULL)
+ *   dx        [m][k] of dx_dtype (F32 or BF16) or NULL
+ *   dw        [n][k] float or NULL; accumulate_dw != 0 adds into it
+ *   dbias     float[n] or NULL; dbias_ws as in fp8_cast_transpose
+ */
+int32_t fp8_linear_bwd(int64_t m, int64_t n, int64_t k,
+                       const void* dy, int32_t dy_dtype, const void* gelu_z, void* dz_out,
+                       const fp8lin_recipe* recipe, const fp8lin_meta* mdy, const fp8lin_saved* saved,
+                       uint8_t* dyq_ws, uint8_t* dyq_t_ws,
+                       void* dx, int32_t dx_dtype, float* dw, int32_t accumulate_dw,
+                       float* dbias, float* dbias_ws, void* stream);
+
+/*
+ * Kernel timing.  fp8lin_timing_enable(capacity) makes the library record a
+ * pair of HIP events around each of its next `capacity` kernel launches
+ * (0 disables and frees the events).  fp8lin_timing_read waits for the
+ * recorded events and returns, for up to `max` launches, the kernel kind
+ * (FP8LIN_KIND_*) and the elapsed milliseconds; it returns the count and
+ * resets the record.  Events are host-side objects; no device memory is used.
+ */
+enum {
+    FP8LIN_KIND_AMAX = 0, FP8LIN_KIND_CAST = 1, FP8LIN_KIND_CAST_TRANSPOSE = 2,
+    FP8LIN_KIND_DEQUANT = 3, FP8LIN_KIND_SCALE_UPDATE = 4, FP8LIN_KIND_GEMM = 5,
+    FP8LIN_KIND_DBIAS = 6, FP8LIN_KIND_OTHER = 7
+};
+int32_t fp8lin_timing_enable(int32_t capacity);
+int32_t fp8lin_timing_read(int32_t* kinds, float* ms, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8LIN_H */

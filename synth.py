@@ -1,0 +1,100 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module holds only input recipes -- shapes, value distributions and seeds --
+and none of the FP8 method's arithmetic.  Values are drawn with torch's seeded
+generators (on the CPU for small tensors, on the GPU for large ones) and then
+rounded once to the element type.  Both the HIP path and the oracle consume the
+same tensors (the oracle after a copy to the host).
+
+Seed of a tensor: 12345 + 1000 * config + 10 * iteration + tensor_id (12345 is
+the seed of the pages' Linear(768, 768) example).
+
+Workloads:
+  linear768  X f32 1024x768 ~ U[0,1), W f32 768x768 and b f32 768 ~ U(-1/sqrt(768), 1/sqrt(768)),
+             dY f32 1024x768 ~ N(0,1) * 2^-20 (fresh X and dY each iteration)
+  mlp        tokens 8192, hidden 4096, FFN 14336; X bf16 N(0,1) with round(0.001*4096) = 4
+             outlier channels scaled x50 (chosen by a seeded permutation); W1 bf16 14336x4096 and
+             W2 bf16 4096x14336 ~ N(0, 0.02); dY bf16 8192x4096 ~ N(0,1)
+  quant      bf16 16384x16384; row r has magnitude 2^u_r, u_r ~ U[-20, 10], times N(0,1) values
+"""
+import math
+
+import torch
+
+SEED0 = 12345
+
+
+def seed_of(config, iteration, tensor_id):
+    return SEED0 + 1000 * config + 10 * iteration + tensor_id
+
+
+def _gen(seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def uniform(shape, lo, hi, seed, dtype=torch.float32, device="cpu"):
+    u = torch.rand(shape, generator=_gen(seed, device), device=device, dtype=torch.float32)
+    return (u * (hi - lo) + lo).to(dtype)
+
+
+def normal(shape, std, seed, dtype=torch.float32, device="cpu"):
+    x = torch.randn(shape, generator=_gen(seed, device), device=device, dtype=torch.float32)
+    return (x * std).to(dtype)
+
+
+# ------------------------------------------------------------ linear768 ----
+
+LINEAR768 = dict(m=1024, n=768, k=768, history_len=16)
+
+
+def linear768_weights(device="cpu", m=1024, n=768, k=768):
+    a = 1.0 / math.sqrt(k)
+    w = uniform((n, k), -a, a, seed_of(1, 0, 1), device=device)
+    b = uniform((n,), -a, a, seed_of(1, 0, 2), device=device)
+    return w, b
+
+
+def linear768_x(iteration, device="cpu", m=1024, k=768):
+    return uniform((m, k), 0.0, 1.0, seed_of(2, iteration, 0), device=device)
+
+
+def linear768_dy(iteration, device="cpu", m=1024, n=768):
+    return normal((m, n), 2.0 ** -20, seed_of(2, iteration, 3), device=device)
+
+
+# ------------------------------------------------------------------ mlp ----
+
+MLP = dict(m=8192, hidden=4096, ffn=14336, history_len=1024)
+
+
+def mlp_inputs(iteration=0, device="cpu", m=8192, hidden=4096, ffn=14336):
+    """X (with outlier channels), W1, W2 and the upstream gradient dY, all bf16."""
+    x = normal((m, hidden), 1.0, seed_of(3, iteration, 0), device=device)
+    n_out = round(0.001 * hidden)
+    perm = torch.randperm(hidden, generator=_gen(seed_of(3, 0, 9), "cpu"))
+    cols = perm[:n_out].to(device)
+    x[:, cols] *= 50.0
+    x = x.to(torch.bfloat16)
+    w1 = normal((ffn, hidden), 0.02, seed_of(3, 0, 1), torch.bfloat16, device)
+    w2 = normal((hidden, ffn), 0.02, seed_of(3, 0, 2), torch.bfloat16, device)
+    dy = normal((m, hidden), 1.0, seed_of(3, iteration, 3), torch.bfloat16, device)
+    return x, w1, w2, dy
+
+
+def mlp_outlier_channels(hidden=4096):
+    n_out = round(0.001 * hidden)
+    perm = torch.randperm(hidden, generator=_gen(seed_of(3, 0, 9), "cpu"))
+    return perm[:n_out]
+
+
+# ---------------------------------------------------------------- quant ----
+
+QUANT = dict(rows=16384, cols=16384, history_len=1024)
+
+
+def quant_tensor(device="cpu", rows=16384, cols=16384):
+    u = uniform((rows, 1), -20.0, 10.0, seed_of(4, 0, 1), device=device)
+    x = normal((rows, cols), 1.0, seed_of(4, 0, 0), device=device)
+    return (x * torch.exp2(u)).to(torch.bfloat16)

@@ -1,0 +1,82 @@
+"""Shared helpers of the GPU parity tests: tensor <-> numpy marshalling and the
+comparison rules.
+
+Comparison rules (the tolerances are stated here, once):
+* casts, transposes, amaxes, histories, scales, dequant: bit-exact (NaN codes
+  compared bit-exact too; NaN floats compared as "both NaN").
+* GEMM with fp32 output: ||gpu - oracle||_F / ||oracle||_F <= 1e-5 against
+  the oracle's fp64 result (exact zero when the oracle's result is zero).
+* GEMM with bf16 output: every element with |y| >= 2^-8 * RMS(y) is within one
+  bf16 ulp of the oracle's round-to-nearest-even bf16, and the normwise error
+  of the bf16 output is <= 2^-8 (bf16's unit roundoff is 2^-9).
+"""
+import numpy as np
+import torch
+
+GEMM_F32_RTOL = 1e-5
+
+
+def np_of(t):
+    """Host numpy copy; bf16 becomes its uint16 bit patterns."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def dev(a, device="cuda"):
+    """numpy -> device tensor; uint16 arrays are taken as bf16 bit patterns."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def bf16_bits_to_f64(h):
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_bits_equal(got, want, what=""):
+    got, want = np.asarray(got), np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if got.dtype == np.float32:
+        gb, wb = got.view(np.uint32), want.view(np.uint32)
+        both_nan = np.isnan(got) & np.isnan(want)
+        bad = (gb != wb) & ~both_nan
+    else:
+        bad = got != want
+    if bad.any():
+        idx = np.argwhere(bad)[:8]
+        raise AssertionError(f"{what}: {int(bad.sum())} mismatches, first at {idx.tolist()}: "
+                             f"got {got[tuple(idx.T)]} want {want[tuple(idx.T)]}")
+
+
+def assert_gemm_f32(got, want64, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    den = np.linalg.norm(want64)
+    if den == 0.0:
+        assert np.all(got == 0.0), what
+        return 0.0
+    err = np.linalg.norm(got - want64) / den
+    assert err <= GEMM_F32_RTOL, f"{what}: normwise relative error {err:.3e} > {GEMM_F32_RTOL}"
+    return err
+
+
+def _bf16_key(bits):
+    v = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    return np.where(v & 0x8000, -(v & 0x7FFF), v & 0x7FFF)
+
+
+def assert_gemm_bf16(got_bits, want64, oracle, what=""):
+    ref_bits = oracle.bf16_from_f64(want64)
+    rms = np.sqrt(np.mean(want64 ** 2)) if want64.size else 0.0
+    big = np.abs(want64) >= 2.0 ** -8 * rms
+    ulps = np.abs(_bf16_key(got_bits) - _bf16_key(ref_bits))
+    bad = big & (ulps > 1)
+    if bad.any():
+        idx = np.argwhere(bad)[:8]
+        raise AssertionError(f"{what}: {int(bad.sum())} elements beyond 1 bf16 ulp, first {idx.tolist()}")
+    den = np.linalg.norm(want64)
+    if den > 0:
+        err = np.linalg.norm(bf16_bits_to_f64(got_bits) - want64) / den
+        assert err <= 2.0 ** -8, f"{what}: bf16 normwise error {err:.3e}"

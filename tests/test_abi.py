@@ -1,0 +1,153 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments on the host before launching
+anything (so these checks need no device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+F = pytest.importorskip("fp8_mixed_precision_reduce_amd")
+L = F.library()
+P = ctypes.c_void_p
+
+A16 = P(1 << 20)          # fake, 16-byte aligned device addresses (never dereferenced)
+B16 = P(1 << 24)
+C16 = P(1 << 28)
+ODD = P((1 << 20) + 4)    # 4-byte aligned, not 16-byte aligned
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "fp8lin.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fp8\w*)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = _header_functions()
+    assert len(names) >= 13
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(F.FUNCTIONS)
+
+
+def test_abi_version_and_status_names():
+    assert L.fp8lin_abi_version() == 1
+    assert L.fp8lin_status_name(0) == b"FP8LIN_OK"
+    assert L.fp8lin_status_name(2) == b"FP8LIN_ERR_SHAPE"
+    assert L.fp8lin_status_name(99) == b"FP8LIN_UNKNOWN_STATUS"
+
+
+def test_dbias_workspace_size():
+    assert L.fp8lin_dbias_workspace_bytes(0, 64) == 0
+    assert L.fp8lin_dbias_workspace_bytes(128, 64) == 64 * 4
+    assert L.fp8lin_dbias_workspace_bytes(1024, 768) == 8 * 768 * 4
+
+
+def _err(status):
+    assert status != 0
+    assert L.fp8lin_last_error()        # a message is left for the caller
+    return status
+
+
+def test_amax_and_cast_validation():
+    assert _err(L.fp8_amax(A16, 7, 16, B16, None)) == F.ERR_DTYPE
+    assert _err(L.fp8_amax(A16, F.F32, -1, B16, None)) == F.ERR_SHAPE
+    assert _err(L.fp8_amax(None, F.F32, 16, B16, None)) == F.ERR_NULL
+    assert _err(L.fp8_amax(ODD, F.F32, 16, B16, None)) == F.ERR_ALIGN
+    assert L.fp8_amax(A16, F.F32, 0, B16, None) == F.OK                  # empty: nothing to do
+    assert _err(L.fp8_cast(A16, F.F32, 16, F.F32, B16, C16, None, None)) == F.ERR_DTYPE
+    assert _err(L.fp8_cast(A16, F.BF16, 16, F.E4M3, None, C16, None, None)) == F.ERR_NULL
+    assert _err(L.fp8_cast(A16, F.F32, 64, F.E4M3, B16, P((1 << 20) + 16), None, None)) == F.ERR_ARG  # overlap
+    assert L.fp8_cast(A16, F.F32, 0, F.E5M2, B16, C16, None, None) == F.OK
+
+
+def test_cast_transpose_validation():
+    ct = L.fp8_cast_transpose
+    assert _err(ct(A16, F.BF16, 17, 32, F.E4M3, B16, C16, P(1 << 30), None, None, None, None)) == F.ERR_SHAPE
+    assert _err(ct(A16, F.BF16, 32, 24, F.E4M3, B16, C16, P(1 << 30), None, None, None, None)) == F.ERR_SHAPE
+    assert _err(ct(A16, F.BF16, 32, 32, F.E4M3, B16, C16, None, None, None, None, None)) == F.ERR_NULL
+    assert _err(ct(A16, F.BF16, 32, 32, F.E4M3, B16, C16, P(1 << 30), None, P(1 << 31), None, None)) == F.ERR_NULL
+    assert _err(ct(A16, F.BF16, 32, 32, F.E4M3, B16, ODD, P(1 << 30), None, None, None, None)) == F.ERR_ALIGN
+    assert _err(ct(A16, F.BF16, 32, 32, F.E4M3, B16, C16, C16, None, None, None, None)) == F.ERR_ARG
+    assert ct(A16, F.BF16, 0, 32, F.E4M3, B16, C16, P(1 << 30), None, None, None, None) == F.OK
+    dg = L.fp8_cast_transpose_dgelu
+    assert _err(dg(A16, None, F.BF16, 32, 32, F.E5M2, B16, C16, P(1 << 30), None, None, None, None, None)) == F.ERR_NULL
+
+
+def test_dequant_validation():
+    assert _err(L.fp8_dequant(A16, F.BF16, 16, B16, C16, F.F32, None)) == F.ERR_DTYPE
+    assert _err(L.fp8_dequant(A16, F.E4M3, 16, B16, C16, F.E5M2, None)) == F.ERR_DTYPE
+    assert _err(L.fp8_dequant(A16, F.E4M3, 16, None, C16, F.F32, None)) == F.ERR_NULL
+    assert L.fp8_dequant(A16, F.E4M3, 0, B16, C16, F.F32, None) == F.OK
+
+
+def _gemm(m=64, n=64, k=64, a_dt=F.E4M3, b_dt=F.E4M3, d_dt=F.F32, epi=0, aux=None, bias=None, bias_dt=F.F32,
+          d=P(1 << 30), sa=P(1 << 32), sb=P(1 << 33)):
+    return L.fp8_gemm(A16, a_dt, B16, b_dt, m, n, k, sa, sb, bias, bias_dt, epi, d, d_dt, aux, None, None)
+
+
+def test_gemm_validation():
+    assert _err(_gemm(m=65)) == F.ERR_SHAPE
+    assert _err(_gemm(k=1 << 23)) == F.ERR_SHAPE
+    assert _err(_gemm(a_dt=F.F32)) == F.ERR_DTYPE
+    assert _err(_gemm(d_dt=F.E4M3)) == F.ERR_DTYPE
+    assert _err(_gemm(epi=8)) == F.ERR_ARG
+    assert _err(_gemm(epi=3)) == F.ERR_ARG
+    assert _err(_gemm(epi=2, d_dt=F.BF16)) == F.ERR_DTYPE
+    assert _err(_gemm(aux=P(1 << 34))) == F.ERR_ARG                    # aux only with GELU
+    assert _err(_gemm(sa=None)) == F.ERR_NULL
+    assert _err(_gemm(d=P((1 << 20) + 8))) == F.ERR_ALIGN
+    assert _err(_gemm(d=P((1 << 20) + 16))) == F.ERR_ARG               # d overlaps A
+    assert _gemm(m=0) == F.OK
+
+
+def _recipe(**kw):
+    return F.Recipe(**kw)
+
+
+def test_scale_update_validation():
+    fm = (ctypes.c_uint8 * 2)(F.E4M3, F.E5M2)
+    upd = L.fp8_amax_scale_update
+    r = _recipe(history_len=16)
+    assert _err(upd(A16, B16, C16, ctypes.cast(fm, P), 0, ctypes.byref(r), None)) == F.ERR_SHAPE
+    assert _err(upd(A16, B16, C16, ctypes.cast(fm, P), 2, ctypes.byref(_recipe(history_len=0)), None)) == F.ERR_ARG
+    assert _err(upd(A16, B16, C16, ctypes.cast(fm, P), 2, ctypes.byref(_recipe(margin=200)), None)) == F.ERR_ARG
+    assert _err(upd(A16, B16, C16, ctypes.cast(fm, P), 2, ctypes.byref(_recipe(amax_compute_algo=1)),
+                    None)) == F.ERR_UNSUPPORTED
+    bad = (ctypes.c_uint8 * 2)(F.E4M3, F.F32)
+    assert _err(upd(A16, B16, C16, ctypes.cast(bad, P), 2, ctypes.byref(r), None)) == F.ERR_DTYPE
+    assert _err(upd(A16, A16, C16, ctypes.cast(fm, P), 2, ctypes.byref(r), None)) == F.ERR_ARG      # overlap
+    assert _err(upd(None, B16, C16, ctypes.cast(fm, P), 2, ctypes.byref(r), None)) == F.ERR_NULL
+
+
+def test_linear_validation():
+    r = _recipe()
+    meta = F._MetaC(1 << 36, (1 << 36) + 4096, (1 << 36) + 8192)
+    saved = F._SavedC(1 << 37, 1 << 38, 1 << 39, 1 << 40, 1 << 41)
+    fwd = L.fp8_linear_fwd
+    args = [A16, F.F32, B16, F.F32, None, F.F32, 0, C16, F.F32, None, None, ctypes.byref(r), ctypes.byref(meta),
+            ctypes.byref(meta), ctypes.byref(saved), None]
+    assert _err(fwd(64, 64, 60, *args)) == F.ERR_SHAPE
+    args_acc = list(args)
+    args_acc[6] = F.EPI_ACCUMULATE
+    assert _err(fwd(64, 64, 64, *args_acc)) == F.ERR_ARG
+    no_saved = list(args)
+    no_saved[14] = None
+    assert _err(fwd(64, 64, 64, *no_saved)) == F.ERR_NULL
+    bwd = L.fp8_linear_bwd
+    saved_no_t = F._SavedC(1 << 37, None, 1 << 39, None, 1 << 41)
+    assert _err(bwd(64, 64, 64, A16, F.F32, None, None, ctypes.byref(r), ctypes.byref(meta),
+                    ctypes.byref(saved_no_t), B16, C16, P(1 << 42), F.F32, None, 0, None, None, None)) == F.ERR_NULL
+    assert _err(bwd(64, 64, 64, A16, F.F32, None, P(1 << 42), ctypes.byref(r), ctypes.byref(meta),
+                    ctypes.byref(saved), B16, C16, None, F.F32, None, 0, None, None, None)) == F.ERR_ARG
+    bad_fmt = _recipe(format=5)
+    assert _err(bwd(64, 64, 64, A16, F.F32, None, None, ctypes.byref(bad_fmt), ctypes.byref(meta),
+                    ctypes.byref(saved), B16, C16, None, F.F32, None, 0, None, None, None)) == F.ERR_ARG
+
+
+def test_timing_toggle():
+    assert L.fp8lin_timing_enable(-1) == F.ERR_ARG
+    assert L.fp8lin_timing_enable(0) == F.OK

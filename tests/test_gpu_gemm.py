@@ -1,0 +1,189 @@
+"""GPU parity: the FP8 GEMM and its epilogues against the oracle's fp64 GEMM.
+
+Shapes cover all three tile configurations (64, 128 and 256 square tiles),
+ragged M/N/K tails (multiples of 16 that are not multiples of the tile), K=0,
+both operand-format pairs of the layer (E4M3 x E4M3, E5M2 x E4M3) and the two
+the layer does not use.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_mixed_precision_reduce_amd as F
+from helpers import assert_bits_equal, assert_gemm_bf16, assert_gemm_f32, dev, np_of
+
+pytestmark = pytest.mark.gpu
+PAIRS = [((F.E4M3, 0), (F.E4M3, 0)), ((F.E5M2, 1), (F.E4M3, 0)), ((F.E4M3, 0), (F.E5M2, 1)),
+         ((F.E5M2, 1), (F.E5M2, 1))]
+
+
+def _scalar(v):
+    return torch.tensor([v], dtype=torch.float32, device="cuda")
+
+
+def _codes(oracle, rng, shape, fmt, spread=4.0):
+    x = (rng.standard_normal(shape) * np.exp2(rng.uniform(-spread, spread, shape))).astype(np.float32)
+    return oracle.cast(x, fmt, 1.0)
+
+
+def _run(a, af, b, bf, sa, sb, out_dtype=torch.float32, bias=None, epilogue=0, aux=False, d0=None):
+    m, n = a.shape[0], b.shape[0]
+    d = d0.clone() if d0 is not None else torch.empty(m, n, dtype=out_dtype, device="cuda")
+    ax = torch.empty(m, n, dtype=out_dtype, device="cuda") if aux else None
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    F.fp8_gemm(dev(a), af, dev(b), bf, _scalar(sa), _scalar(sb), d, bias=bias, epilogue=epilogue, aux=ax,
+               amax_d=amax)
+    return d, ax, amax
+
+
+SHAPES = [(16, 16, 16), (64, 64, 128), (80, 48, 400), (272, 528, 400), (1024, 768, 768), (1040, 1536, 1168),
+          (4096, 4096, 256)]
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2", "e5m2xe5m2"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_f32_matches_oracle(oracle, pair, shape):
+    (af, oaf), (bf, obf) = pair
+    m, n, k = shape
+    rng = np.random.default_rng(m + 3 * n + 7 * k + af)
+    a = _codes(oracle, rng, (m, k), oaf)
+    b = _codes(oracle, rng, (n, k), obf)
+    sa, sb = np.float32(0.0371), np.float32(1.73)
+    d, _, amax = _run(a, af, b, bf, float(sa), float(sb))
+    rows = np.unique(np.concatenate([np.arange(min(m, 64)), rng.integers(0, m, 64), [m - 1]]))
+    want = oracle.gemm(a, oaf, b, obf, sa, sb, rows=rows)
+    got = np_of(d)
+    assert_gemm_f32(got[rows], want, f"{shape}")
+    assert_bits_equal(np_of(amax)[0], np.float32(np.max(np.abs(got))), "output amax")
+
+
+@pytest.mark.parametrize("shape", [(272, 528, 400), (2048, 2048, 512)], ids=lambda s: "x".join(map(str, s)))
+def test_gemm_bias_gelu_aux_bf16(oracle, shape):
+    m, n, k = shape
+    rng = np.random.default_rng(k)
+    a = _codes(oracle, rng, (m, k), 0)
+    b = _codes(oracle, rng, (n, k), 0)
+    bias = rng.standard_normal(n).astype(np.float32)
+    sa, sb = np.float32(0.02), np.float32(0.05)
+    d, aux, amax = _run(a, F.E4M3, b, F.E4M3, float(sa), float(sb), torch.bfloat16, bias=dev(bias),
+                        epilogue=F.EPI_GELU, aux=True)
+    rows = np.unique(np.concatenate([np.arange(32), rng.integers(0, m, 48), [m - 1]]))
+    y, pre = oracle.gemm(a, 0, b, 0, sa, sb, bias.astype(np.float64), gelu=True, rows=rows, want_pre=True)
+    assert_gemm_bf16(np_of(d)[rows], y, oracle, "gelu(y)")
+    assert_gemm_bf16(np_of(aux)[rows], pre, oracle, "pre-gelu aux")
+    got = np_of(d)
+    assert_bits_equal(np_of(amax)[0], np.float32(np.max(np.abs(oracle.bf16_to_f64(got)))), "amax of bf16 out")
+
+
+def test_gemm_bf16_bias_and_accumulate(oracle):
+    m, n, k = 320, 256, 272
+    rng = np.random.default_rng(1)
+    a = _codes(oracle, rng, (m, k), 1)
+    b = _codes(oracle, rng, (n, k), 0)
+    bias16 = oracle.bf16_from_f32(rng.standard_normal(n).astype(np.float32))
+    d, _, _ = _run(a, F.E5M2, b, F.E4M3, 0.5, 0.25, torch.float32, bias=dev(bias16))
+    want = oracle.gemm(a, 1, b, 0, 0.5, 0.25, oracle.bf16_to_f64(bias16))
+    assert_gemm_f32(np_of(d), want, "bf16 bias")
+    d0 = torch.from_numpy(rng.standard_normal((m, n)).astype(np.float32)).cuda()
+    d, _, _ = _run(a, F.E5M2, b, F.E4M3, 0.5, 0.25, d0=d0, epilogue=F.EPI_ACCUMULATE)
+    want = oracle.gemm(a, 1, b, 0, 0.5, 0.25) + np_of(d0).astype(np.float64)
+    assert_gemm_f32(np_of(d), want, "accumulate")
+
+
+def test_gemm_empty_k_writes_bias(oracle):
+    m, n = 48, 64
+    bias = np.arange(n, dtype=np.float32)
+    d = torch.full((m, n), 7.0, device="cuda")
+    a = torch.empty(m, 0, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, 0, dtype=torch.uint8, device="cuda")
+    F.fp8_gemm(a, F.E4M3, b, F.E4M3, _scalar(1.0), _scalar(1.0), d, bias=dev(bias))
+    assert np.array_equal(np_of(d), np.tile(bias, (m, 1)))
+
+
+def test_gemm_deterministic(oracle):
+    rng = np.random.default_rng(2)
+    a = _codes(oracle, rng, (1024, 2048), 0)
+    b = _codes(oracle, rng, (1536, 2048), 0)
+    d1, _, m1 = _run(a, F.E4M3, b, F.E4M3, 1.0, 1.0)
+    d2, _, m2 = _run(a, F.E4M3, b, F.E4M3, 1.0, 1.0)
+    assert torch.equal(d1.view(torch.int32), d2.view(torch.int32)) and torch.equal(m1, m2)
+
+
+@pytest.mark.parametrize("which", ["fc1", "fc2_dgrad", "fc1_wgrad"])
+def test_gemm_full_size_mlp_shapes_sampled(oracle, which):
+    """The MLP block's GEMM shapes at full size, in the launch configuration the
+    benchmark times; the oracle recomputes 24 sampled rows."""
+    m, n, k, af, oaf = {"fc1": (8192, 14336, 4096, F.E4M3, 0),
+                        "fc2_dgrad": (8192, 14336, 4096, F.E5M2, 1),
+                        "fc1_wgrad": (14336, 4096, 8192, F.E5M2, 1)}[which]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(m + n + k)
+    a32 = torch.randn(m, k, device="cuda", generator=g)
+    b32 = torch.randn(n, k, device="cuda", generator=g) * 0.02
+    a = torch.empty(m, k, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, k, dtype=torch.uint8, device="cuda")
+    F.fp8_cast(a32, af, _scalar(8.0), a)
+    F.fp8_cast(b32, F.E4M3, _scalar(2000.0), b)
+    del a32, b32
+    d = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    F.fp8_gemm(a, af, b, F.E4M3, _scalar(0.125), _scalar(1 / 2000.0), d)
+    rows = np.random.default_rng(0).choice(m, 24, replace=False)
+    a_np = np_of(a)
+    want = oracle.gemm(a_np, oaf, np_of(b), 0, np.float32(0.125), np.float32(1 / 2000.0), rows=rows)
+    assert_gemm_bf16(np_of(d)[rows], want, oracle, which)
+    # the same GEMM with fp32 output meets the normwise 1e-5 bound before rounding
+    d32 = torch.empty(m, n, dtype=torch.float32, device="cuda")
+    F.fp8_gemm(a, af, b, F.E4M3, _scalar(0.125), _scalar(1 / 2000.0), d32)
+    assert_gemm_f32(np_of(d32)[rows], want, which + " f32")
+
+
+def test_gemm_identity_over_every_code(oracle):
+    """A row holding every finite code times an identity returns each decoded
+    value exactly; a NaN or Inf operand makes its whole output row NaN."""
+    for af, of in ((F.E4M3, 0), (F.E5M2, 1)):
+        k = 256
+        vals = np.array([oracle.decode(c, of) for c in range(256)])
+        codes = np.where(np.isfinite(vals), np.arange(256), 0).astype(np.uint8)
+        a = np.tile(codes, (16, 1))
+        a[15, 7] = 0x7F                                              # NaN in both formats
+        ident = np.zeros((k, k), np.uint8)
+        ident[np.arange(k), np.arange(k)] = 0x38                    # E4M3 1.0
+        d, _, _ = _run(a, af, ident, F.E4M3, 1.0, 1.0)
+        got = np_of(d).astype(np.float64)
+        want = np.where(np.isfinite(vals), vals, 0.0)
+        assert np.array_equal(got[:15], np.tile(want, (15, 1)))
+        assert np.all(np.isnan(got[15]))
+
+
+def _group_bound(a_dec, b_dec, k):
+    """Per-output bound of the fast path: each group of 8 consecutive k loses
+    at most 2^-10 of its largest |product| (about 14 bits kept below it)."""
+    g = (k + 7) // 8
+    pad = g * 8 - k
+    ap = np.pad(a_dec, ((0, 0), (0, pad)))
+    bp = np.pad(b_dec, ((0, 0), (0, pad)))
+    out = np.zeros((a_dec.shape[0], b_dec.shape[0]))
+    for j in range(g):
+        pa = np.abs(ap[:, 8 * j:8 * j + 8])
+        pb = np.abs(bp[:, 8 * j:8 * j + 8])
+        out += np.max(pa[:, None, :] * pb[None, :, :], axis=2)
+    return 2.0 ** -10 * out
+
+
+@pytest.mark.parametrize("pair", PAIRS[:2], ids=["e4m3xe4m3", "e5m2xe4m3"])
+@pytest.mark.parametrize("shape", [(64, 64, 128), (272, 528, 400), (1024, 1024, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gemm_fast_accum_within_group_truncation_bound(oracle, pair, shape):
+    (af, oaf), (bf, obf) = pair
+    m, n, k = shape
+    rng = np.random.default_rng(m + n + k)
+    a = _codes(oracle, rng, (m, k), oaf)
+    b = _codes(oracle, rng, (n, k), obf)
+    sa, sb = np.float32(0.5), np.float32(0.25)
+    d, _, _ = _run(a, af, b, bf, float(sa), float(sb), epilogue=F.EPI_FAST_ACCUM)
+    rows = rng.choice(m, min(m, 32), replace=False)
+    want = oracle.gemm(a, oaf, b, obf, sa, sb, rows=rows)
+    ta, tb = oracle.decode_table(oaf), oracle.decode_table(obf)
+    bound = 2 * _group_bound(ta[a[rows]], tb[b], k) * float(sa) * float(sb) + 1e-6 * np.abs(want) + 1e-30
+    err = np.abs(np_of(d)[rows].astype(np.float64) - want)
+    assert np.all(err <= bound), float(np.max(err / bound))
