@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 delayed-scaling linear on one MI355X.
+
+Workload (one "step" = every step of the hot path once): the FP8 MLP block
+FC1 -> GeLU -> FC2 of a transformer layer, one GPU's share: 8192 tokens,
+hidden 4096, FFN 14336, bf16 activations (0.1% outlier channels x50) and
+weights, HYBRID formats (E4M3 forward, E5M2 gradients), delayed scaling with
+an amax history of 1024 and the "max" algorithm.  Per step:
+  forward  FC1: amax+cast-transpose X and W1, FP8 GEMM + GeLU epilogue -> H (bf16), Z
+           FC2: amax+cast-transpose H and W2, FP8 GEMM -> Y (bf16)
+  backward FC2: amax+cast-transpose dY (E5M2), dgrad -> dH (bf16), wgrad -> dW2 (fp32)
+           FC1: GeLU backward fused into the amax+cast-transpose of dZ, dgrad -> dX, wgrad -> dW1
+  update   one fp8_amax_scale_update over the 6 tensors' histories.
+6 GEMMs of 2*8192*4096*14336 flop each = 5.77e12 flop per step.
+
+Prints one JSON line.  `value` is TFLOP/s of the whole step (inputs resident
+in HBM).  `roofline` is the GEMM kernel: algorithmic flop per launch over its
+average launch time, measured with HIP events around each launch (recorded by
+the library on the launch stream) during a second pass of the same steps.
+`cpu_baseline` times the CPU oracle on a 1024-token slice of the same step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M, HID, FFN, HIST = 8192, 4096, 14336, 1024
+GEMM_FLOP = 2.0 * M * HID * FFN
+STEP_FLOP = 6 * GEMM_FLOP
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense f16/bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def _exit_multi_gpu(n):
+    print(f"bench.py runs on one GPU only (asked for {n}); the multi-GPU path is not part of this build.",
+          file=sys.stderr, flush=True)
+    sys.exit(2)
+
+
+class MlpBlock:
+    """Buffers and metas of the MLP block; step() enqueues one fwd+bwd+update."""
+
+    def __init__(self, F, torch, fast_accum=False):
+        import synth
+        self.F, self.torch = F, torch
+        dev = "cuda"
+        self.x, self.w1, self.w2, self.dy = synth.mlp_inputs(0, device=dev)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty(M, FFN, **bf)
+        self.z = torch.empty(M, FFN, **bf)
+        self.y = torch.empty(M, HID, **bf)
+        self.dh = torch.empty(M, FFN, **bf)
+        self.dx = torch.empty(M, HID, **bf)
+        self.dw1 = torch.empty(FFN, HID, dtype=torch.float32, device=dev)
+        self.dw2 = torch.empty(HID, FFN, dtype=torch.float32, device=dev)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        self.gq2, self.gqt2 = torch.empty(M, HID, **u8), torch.empty(HID, M, **u8)
+        self.gq1, self.gqt1 = torch.empty(M, FFN, **u8), torch.empty(FFN, M, **u8)
+        self.s1 = F.Saved(M, FFN, HID, device=dev)
+        self.s2 = F.Saved(M, HID, FFN, device=dev)
+        self.bank = F.MetaBank([F.E4M3, F.E4M3, F.E4M3, F.E4M3, F.E5M2, F.E5M2], HIST, device=dev)
+        self.mx, self.mw1, self.mh, self.mw2, self.mdy, self.mdz = (self.bank.meta(i) for i in range(6))
+        self.recipe = F.Recipe(F.FORMAT_HYBRID, HIST, F.AMAX_MAX, 0, fast_accum)
+
+    def step(self):
+        F, r = self.F, self.recipe
+        F.fp8_linear_fwd(self.x, self.w1, self.h, r, self.mx, self.mw1, self.s1, epilogue=F.EPI_GELU, y_aux=self.z)
+        F.fp8_linear_fwd(self.h, self.w2, self.y, r, self.mh, self.mw2, self.s2)
+        F.fp8_linear_bwd(self.dy, FFN, r, self.mdy, self.s2, self.gq2, self.gqt2, dx=self.dh, dw=self.dw2)
+        F.fp8_linear_bwd(self.dh, HID, r, self.mdz, self.s1, self.gq1, self.gqt1, dx=self.dx, dw=self.dw1,
+                         gelu_z=self.z)
+        self.bank.update(r)
+
+    @staticmethod
+    def cast_bytes_per_step():
+        """Algorithmic HBM bytes of the cast kernels in one step."""
+        ct = lambda r, c: r * c * (2 + 2)          # read bf16, write codes and transposed codes
+        return (ct(M, HID) + ct(FFN, HID) + ct(M, FFN) + ct(HID, FFN) + ct(M, HID)
+                + M * FFN * (2 + 2 + 2))           # dgelu: read dH and Z, write codes twice
+
+
+def time_steps(block, torch, steps):
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        block.step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def kernel_breakdown(block, F, torch, steps):
+    """Per-kind launch times over `steps` further steps (HIP events recorded
+    by the library around each of its launches, on the launch stream)."""
+    F.timing_enable(64 * steps)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        block.step()
+    torch.cuda.synchronize()
+    rec = F.timing_read(64 * steps)
+    F.timing_enable(0)
+    out = {}
+    for kind, ms in rec:
+        n, tot = out.get(kind, (0, 0.0))
+        out[kind] = (n + 1, tot + ms)
+    return out
+
+
+def cpu_baseline(torch, rows=1024):
+    """The CPU oracle on a `rows`-token slice of the same step (full weights)."""
+    import numpy as np
+
+    import oracle as O
+    import synth
+    x, w1, w2, dy = synth.mlp_inputs(0, device="cuda")
+    to16 = lambda t: t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    xs, dys, w1n, w2n = to16(x[:rows]), to16(dy[:rows]), to16(w1), to16(w2)
+    del x, w1, w2, dy
+    t0 = time.perf_counter()
+    O.mlp_step(xs, w1n, w2n, dys, O.mlp_metas(HIST))
+    dt = time.perf_counter() - t0
+    flop = 6 * 2.0 * rows * HID * FFN
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"MLP block fwd+bwd+update on {rows} of {M} tokens (hidden {HID}, FFN {FFN}, full "
+                      f"weights, history {HIST}); {dt:.2f} s for {flop:.3g} flop"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fast-accum", action="store_true", help="time the fast-accumulation GEMMs as the main value")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        _exit_multi_gpu(args.gpus)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        _exit_multi_gpu(int(os.environ["WORLD_SIZE"]))
+
+    import torch
+
+    import fp8_mixed_precision_reduce_amd as F
+
+    block = MlpBlock(F, torch, fast_accum=args.fast_accum)
+    for _ in range(args.warmup):
+        block.step()
+    ms = time_steps(block, torch, args.steps)
+    kb = kernel_breakdown(block, F, torch, args.steps)
+    n_g, t_g = kb.get("gemm", (1, float("nan")))
+    gemm_ms = t_g / n_g
+    gemm_tflops = GEMM_FLOP / (gemm_ms * 1e-3) / 1e12
+    cast_ms = sum(kb.get(k, (0, 0.0))[1] for k in ("cast_transpose", "cast")) / args.steps
+    cast_gbs = MlpBlock.cast_bytes_per_step() / (cast_ms * 1e-3) / 1e9
+
+    # the other accumulation mode, for reference
+    other = MlpBlock(F, torch, fast_accum=not args.fast_accum)
+    for _ in range(2):
+        other.step()
+    other_ms = time_steps(other, torch, max(3, args.steps // 2))
+    del other
+
+    value = STEP_FLOP / (ms * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if args.fast_accum else PEAK_F16_TFLOPS
+    line = {
+        "metric": "FP8 linear fwd+bwd TFLOP/s (% FP8 MFMA peak); cast/amax GB/s (% HBM)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {
+            "workload": "FP8 MLP block fwd+bwd (FC1-GeLU-FC2), tokens 8192, hidden 4096, FFN 14336, HYBRID "
+                        "E4M3/E5M2, delayed scaling, amax history 1024, max",
+            "global_batch": M, "hidden": HID, "ffn": FFN, "history_len": HIST,
+            "gemm_inner_product": "fast: native fp8 MFMA" if args.fast_accum
+            else "exact: fp8 codes decoded to f16, f16 MFMA, fp32 accumulation",
+            "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / peak, 4),
+            "traffic": None,
+            "kernel": "k_gemm (fp8 GEMM, 256x256 tiles)",
+            "per_launch_flop": GEMM_FLOP,
+            "avg_launch_ms": round(gemm_ms, 4),
+        },
+        "kernels_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in sorted(kb.items())},
+        "cast_kernels": {"achieved_gbs": round(cast_gbs, 1), "peak_gbs": PEAK_HBM_GBS,
+                         "frac": round(cast_gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_step": MlpBlock.cast_bytes_per_step()},
+        ("exact_accum" if args.fast_accum else "fast_accum"): {
+            "ms_per_step": round(other_ms, 4), "tflops": round(STEP_FLOP / (other_ms * 1e-3) / 1e12, 2)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(torch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -396,3 +396,31 @@ def linear_bwd(dy, saved, mg, rows_dx=None, rows_dw=None):
     dx = gemm(gq, mg.fmt, saved["wqt"], saved["fmt_w"], mg.scale_inv, saved["sinv_w"], rows=rows_dx)
     dw = gemm(gqt, mg.fmt, saved["xqt"], saved["fmt_x"], mg.scale_inv, saved["sinv_x"], rows=rows_dw)
     return dict(gq=gq, gqt=gqt, sinv_g=np.float32(mg.scale_inv), dx=dx, dw=dw, dbias=colsum(dy))
+
+
+def mlp_step(x, w1, w2, dy, metas, rows_w=None):
+    """One forward + backward step of the FP8 MLP block FC1 -> GeLU -> FC2
+    (no biases), HYBRID formats, followed by the delayed-scaling update.
+
+    x [m][h], w1 [f][h], w2 [h][f], dy [m][h] as bf16 bit patterns (uint16);
+    metas: dict of Meta for 'x', 'w1', 'h', 'w2', 'dy', 'dz'.  The GeLU output
+    H, its input Z, dH and dZ are rounded to bf16 between the steps, as the
+    layer stores them.  rows_w (optional) restricts the weight-gradient rows
+    that are computed.  Returns every intermediate.
+    """
+    fw1 = linear_fwd(x, w1, metas["x"], metas["w1"], gelu_=True)
+    h = bf16_from_f64(fw1["y"])
+    z = bf16_from_f64(fw1["pre"])
+    fw2 = linear_fwd(h, w2, metas["h"], metas["w2"])
+    bw2 = linear_bwd(dy, fw2, metas["dy"], rows_dw=rows_w)
+    dh = bf16_from_f64(bw2["dx"])
+    dz = gelu_bwd(dh, z)
+    bw1 = linear_bwd(dz, fw1, metas["dz"], rows_dw=rows_w)
+    update_metas([metas[k] for k in ("x", "w1", "h", "w2", "dy", "dz")])
+    return dict(fw1=fw1, fw2=fw2, bw1=bw1, bw2=bw2, h=h, z=z, y=bf16_from_f64(fw2["y"]), dh=dh, dz=dz,
+                dx=bf16_from_f64(bw1["dx"]), dw1=bw1["dw"], dw2=bw2["dw"])
+
+
+def mlp_metas(hist_len):
+    return {"x": Meta(hist_len, E4M3), "w1": Meta(hist_len, E4M3), "h": Meta(hist_len, E4M3),
+            "w2": Meta(hist_len, E4M3), "dy": Meta(hist_len, E5M2), "dz": Meta(hist_len, E5M2)}
