@@ -27,12 +27,20 @@
 // Tiling.  Both operands are contiguous along k ("TN").  A workgroup of 4
 // waves (2 x 2) computes a BM x BN tile; each wave owns MB x NB blocks of
 // 32 x 32.  k advances in stages of 128 bytes through a double-buffered LDS
-// tile; global loads for the next stage go through buffer resources
-// (out-of-range rows and the k tail read as zero) into registers while the
-// current stage is multiplied.  LDS rows are 128 bytes; the 16-byte chunk
-// index is XOR-swizzled with (row & 7) and the 8-byte half with bit 3 of the
-// row, so 16-byte accesses of 8 consecutive rows and 8-byte accesses of 16
-// consecutive rows each touch distinct banks.  The MFMA takes the B tile as
+// tile.  The next stage is fetched while the current one is multiplied, with
+// buffer loads that write straight into LDS (buffer_load_dwordx4 ... lds: no
+// staging registers, out-of-range rows and the k tail read as zero).  LDS rows
+// are 128 bytes with the 16-byte chunk index XOR-swizzled by (row >> 1) & 7,
+// so a DMA wave-instruction fills 8 rows and the 16-byte fragment reads of 16
+// consecutive rows (one LDS cycle on gfx950's 64 banks) hit 16 distinct bank
+// groups; with a (row & 7) swizzle the counters showed 2-way conflicts.  Each lane reads 16 bytes
+// of k per fragment: the exact path splits them into two f16 MFMAs (bytes
+// 0-7 and 8-15; A and B use the same split, so the k order inside an MFMA is
+// only permuted), the fast path reads 32 bytes per 64-k MFMA.  Fragments of
+// the next k block are read before the current block's MFMAs are issued, and
+// the next stage's DMA instructions are spread over the k blocks so that no
+// burst of them stalls the wave's MFMA issue.
+// The MFMA takes the B tile as
 // its first operand, so each lane's accumulators run along n: four
 // consecutive outputs of one row, written with one 16-byte (fp32) or 8-byte
 // (bf16) store.  Tiles are rasterised in groups of 8 tile-rows, and the
@@ -69,20 +77,26 @@ struct GemmParams {
     int32_t bias_dtype, d_dtype, epilogue;
 };
 
-template <int MB, int NB>
+// WM x WN waves, each owning MB x NB blocks of 32 x 32.
+template <int WM, int WN, int MB, int NB>
 struct TileCfg {
-    static constexpr int BM = 2 * 32 * MB;
-    static constexpr int BN = 2 * 32 * NB;
-    static constexpr int A_LD = BM * kBK / 16 / kThreads;   // 16-byte chunks per thread per stage
-    static constexpr int B_LD = BN * kBK / 16 / kThreads;
+    static constexpr int WAVES = WM * WN;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int BM = WM * 32 * MB;
+    static constexpr int BN = WN * 32 * NB;
     static constexpr int STAGE = (BM + BN) * kBK;           // LDS bytes per stage
+    static constexpr int A_DMA = BM / 8 / WAVES;            // 1 KiB DMA wave-instructions per stage
+    static constexpr int B_DMA = BN / 8 / WAVES;
 };
 
-// Byte offset of the 16-byte chunk `chunk` of LDS row `row`; the two 8-byte
-// halves of a chunk are stored swapped when bit 3 of the row is set.
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
-__device__ __forceinline__ int half_swap(int row) { return (row >> 3) & 1; }
-__device__ __forceinline__ uint4 swap_halves(uint4 v, int sw) { return sw ? make_uint4(v.z, v.w, v.x, v.y) : v; }
+// Byte offset of the 16-byte chunk `chunk` of LDS row `row`.  The LDS serves
+// 16 lanes of a 16-byte read per cycle from 64 banks (256 bytes, two rows);
+// swizzling by (row >> 1) & 7 puts the same logical chunk of 16 consecutive
+// rows into 16 distinct bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kBK + ((chunk ^ swz(row)) << 4); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Eight FP8 codes (k order) to eight f16 values, exactly.
 template <int FMT>
@@ -102,8 +116,10 @@ __device__ __forceinline__ v8h dec8_f16(uint2 raw) {
     return v8h{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+// One wave-instruction of the stage DMA: lane l's 16 bytes land at
+// lds_base + 16 * l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_base, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, off, 0, 0, 0);
 }
 
 // MFMA format selector of an FP8 operand.
@@ -128,21 +144,21 @@ __device__ __forceinline__ void tile_coords(int32_t tiles_m, int32_t tiles_n, in
     tn = rem / gsize;
 }
 
-template <int MB, int NB, int AF, int BF, bool FAST>
-__global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST>
+__global__ void __launch_bounds__(64 * WM * WN, (WM * WN * MB * NB >= 64 ? (WM * WN) / 4 : 2))
 k_gemm(GemmParams p) {
-    using C = TileCfg<MB, NB>;
+    using C = TileCfg<WM, WN, MB, NB>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
-    __shared__ uint32_t red[kThreads / 64];
+    __shared__ uint32_t red[C::WAVES];
 
     int tm, tn;
     tile_coords(p.tiles_m, p.tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     const int64_t M = p.m, N = p.n, K = p.k;
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave % WM, wn = wave / WM;
     const int g = lane >> 5, r32 = lane & 31;
 
     // Buffer resources over this tile's rows of A and B.
@@ -152,37 +168,28 @@ k_gemm(GemmParams p) {
     const __amdgpu_buffer_rsrc_t rb_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.b + n0 * K), (short)0, (int)(rows_b * (uint32_t)K), 0x00020000);
 
-    const int chunk = t & 7, row_base = t >> 3;     // this thread's chunk column and first row
-    uint4 ga[C::A_LD], gb[C::B_LD];
-
-    auto gload = [&](int kt) {
-        const uint32_t kb = (uint32_t)kt * kBK + chunk * 16;
-        const bool kok = kb < (uint32_t)K;
-#pragma unroll
-        for (int i = 0; i < C::A_LD; ++i) {
-            const uint32_t row = row_base + 32 * i;
-            ga[i] = buf_load16(ra_rsrc, kok ? row * (uint32_t)K + kb : 0x80000000u);
-        }
-#pragma unroll
-        for (int i = 0; i < C::B_LD; ++i) {
-            const uint32_t row = row_base + 32 * i;
-            gb[i] = buf_load16(rb_rsrc, kok ? row * (uint32_t)K + kb : 0x80000000u);
-        }
-    };
-    auto lstore = [&](int stage) {
+    // Stage DMA: wave-instruction i of wave w fills rows 8 (w + W i) .. +7 (W =
+    // waves per workgroup); lane l lands at physical chunk l % 8 of row
+    // row = 8 (w + W i) + l / 8, i.e. it loads logical chunk (l % 8) ^ swz(row).
+    const int lrow = lane >> 3, lpc = lane & 7;
+    // DMA wave-instruction q of a stage: q < A_DMA fills A rows, the rest B rows.
+    auto dma_part = [&](int kt, int stage, int q0, int q1) {
         uint8_t* sa = smem + stage * C::STAGE;
         uint8_t* sb = sa + C::BM * kBK;
+        const uint32_t k0 = (uint32_t)kt * kBK;
 #pragma unroll
-        for (int i = 0; i < C::A_LD; ++i) {
-            const int row = row_base + 32 * i;
-            *reinterpret_cast<uint4*>(sa + lds_off(row, chunk)) = swap_halves(ga[i], half_swap(row));
-        }
-#pragma unroll
-        for (int i = 0; i < C::B_LD; ++i) {
-            const int row = row_base + 32 * i;
-            *reinterpret_cast<uint4*>(sb + lds_off(row, chunk)) = swap_halves(gb[i], half_swap(row));
+        for (int q = 0; q < C::A_DMA + C::B_DMA; ++q) {
+            if (q < q0 || q >= q1) continue;
+            const bool is_a = q < C::A_DMA;
+            const int i = is_a ? q : q - C::A_DMA;
+            const int row = 8 * (wave + C::WAVES * i) + lrow;
+            const uint32_t kb = k0 + (uint32_t)((lpc ^ swz(row)) << 4);
+            const uint32_t off = (uint32_t)row * (uint32_t)K + kb;
+            dma16(is_a ? ra_rsrc : rb_rsrc, (is_a ? sa : sb) + (row - lrow) * kBK,
+                  kb < (uint32_t)K ? off : 0x80000000u);
         }
     };
+    constexpr int NDMA = C::A_DMA + C::B_DMA;
 
     v16f acc[MB][NB];
 #pragma unroll
@@ -194,34 +201,47 @@ k_gemm(GemmParams p) {
 
     const int nk = (int)((K + kBK - 1) / kBK);
     if (nk > 0) {
-        gload(0);
-        lstore(0);
+        dma_part(0, 0, 0, NDMA);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
     for (int kt = 0; kt < nk; ++kt) {
         const int stage = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+        const bool more = kt + 1 < nk;     // the next stage's DMA is spread over this stage's k blocks
         const uint8_t* sa = smem + stage * C::STAGE;
         const uint8_t* sb = sa + C::BM * kBK;
         if constexpr (FAST) {
-#pragma unroll
-            for (int ks = 0; ks < kBK / 64; ++ks) {
-                v8i af[MB], bf[NB];
-                const int c0 = ks * 4 + g * 2;
+            // 64-k blocks: lane group g holds k = 64 kb + 32 g .. +31 (chunks 4 kb + 2 g, +1).
+            uint4 alo[MB], ahi[MB], blo[NB], bhi[NB];
+            auto rd = [&](int kb) {
+                const int c0 = kb * 4 + g * 2;
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
                     const int row = wm * MB * 32 + i * 32 + r32;
-                    const uint4 lo = swap_halves(*reinterpret_cast<const uint4*>(sa + lds_off(row, c0)), half_swap(row));
-                    const uint4 hi = swap_halves(*reinterpret_cast<const uint4*>(sa + lds_off(row, c0 + 1)), half_swap(row));
-                    af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    alo[i] = *reinterpret_cast<const uint4*>(sa + lds_off(row, c0));
+                    ahi[i] = *reinterpret_cast<const uint4*>(sa + lds_off(row, c0 + 1));
                 }
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int row = wn * NB * 32 + j * 32 + r32;
-                    const uint4 lo = swap_halves(*reinterpret_cast<const uint4*>(sb + lds_off(row, c0)), half_swap(row));
-                    const uint4 hi = swap_halves(*reinterpret_cast<const uint4*>(sb + lds_off(row, c0 + 1)), half_swap(row));
-                    bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    blo[j] = *reinterpret_cast<const uint4*>(sb + lds_off(row, c0));
+                    bhi[j] = *reinterpret_cast<const uint4*>(sb + lds_off(row, c0 + 1));
                 }
+            };
+            rd(0);
+#pragma unroll
+            for (int kb = 0; kb < kBK / 64; ++kb) {
+                v8i af[MB], bf[NB];
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    af[i] = v8i{(int)alo[i].x, (int)alo[i].y, (int)alo[i].z, (int)alo[i].w,
+                                (int)ahi[i].x, (int)ahi[i].y, (int)ahi[i].z, (int)ahi[i].w};
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    bf[j] = v8i{(int)blo[j].x, (int)blo[j].y, (int)blo[j].z, (int)blo[j].w,
+                                (int)bhi[j].x, (int)bhi[j].y, (int)bhi[j].z, (int)bhi[j].w};
+                if (kb + 1 < kBK / 64) rd(kb + 1);
+                if (more) dma_part(kt + 1, stage ^ 1, kb * NDMA / (kBK / 64), (kb + 1) * NDMA / (kBK / 64));
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -230,30 +250,49 @@ k_gemm(GemmParams p) {
                             bf[j], af[i], acc[i][j], MfmaFmt<BF>::value, MfmaFmt<AF>::value, 0, 0, 0, 0);
             }
         } else {
-            // k steps of 16: lane group g holds k = 8g .. 8g+7 of the step.
+            // 32-k blocks: lane group g holds k = 32 kb + 16 g .. +15 (chunk 2 kb + g);
+            // bytes 0-7 feed the first f16 MFMA, bytes 8-15 the second.
+            uint4 ar[MB], br[NB];
+            auto rd = [&](int kb) {
+                const int c = kb * 2 + g;
 #pragma unroll
-            for (int ks = 0; ks < kBK / 16; ++ks) {
-                v8h af[MB], bf[NB];
+                for (int i = 0; i < MB; ++i)
+                    ar[i] = *reinterpret_cast<const uint4*>(sa + lds_off(wm * MB * 32 + i * 32 + r32, c));
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    br[j] = *reinterpret_cast<const uint4*>(sb + lds_off(wn * NB * 32 + j * 32 + r32, c));
+            };
+            rd(0);
+#pragma unroll
+            for (int kb = 0; kb < kBK / 32; ++kb) {
+                v8h a0[MB], a1[MB], b0[NB], b1[NB];
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
-                    const int row = wm * MB * 32 + i * 32 + r32;
-                    const uint2 raw = *reinterpret_cast<const uint2*>(sa + lds_off(row, ks) + ((g ^ half_swap(row)) << 3));
-                    af[i] = dec8_f16<AF>(raw);
+                    a0[i] = dec8_f16<AF>(make_uint2(ar[i].x, ar[i].y));
+                    a1[i] = dec8_f16<AF>(make_uint2(ar[i].z, ar[i].w));
                 }
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    const int row = wn * NB * 32 + j * 32 + r32;
-                    const uint2 raw = *reinterpret_cast<const uint2*>(sb + lds_off(row, ks) + ((g ^ half_swap(row)) << 3));
-                    bf[j] = dec8_f16<BF>(raw);
+                    b0[j] = dec8_f16<BF>(make_uint2(br[j].x, br[j].y));
+                    b1[j] = dec8_f16<BF>(make_uint2(br[j].z, br[j].w));
                 }
+                if (kb + 1 < kBK / 32) rd(kb + 1);
+                if (more) dma_part(kt + 1, stage ^ 1, kb * NDMA / (kBK / 32), (kb + 1) * NDMA / (kBK / 32));
+                // all first halves, then all second halves: no two adjacent MFMAs
+                // accumulate into the same registers
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
                     for (int j = 0; j < NB; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0[j], a0[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1[j], a1[i], acc[i][j], 0, 0, 0);
             }
         }
-        if (kt + 1 < nk) lstore(stage ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
@@ -316,28 +355,39 @@ k_gemm(GemmParams p) {
     if (p.amax) block_amax_merge(amax, p.amax, red);
 }
 
-template <int MB, int NB, bool FAST>
+template <int WM, int WN, int MB, int NB, bool FAST>
 hipError_t launch_cfg(const GemmParams& base, int afmt, int bfmt, hipStream_t s) {
-    using C = TileCfg<MB, NB>;
+    using C = TileCfg<WM, WN, MB, NB>;
     GemmParams p = base;
     p.tiles_m = (int32_t)((p.m + C::BM - 1) / C::BM);
     p.tiles_n = (int32_t)((p.n + C::BN - 1) / C::BN);
-    const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n), block(kThreads);
-    if (afmt == kE4M3 && bfmt == kE4M3) hipLaunchKernelGGL((k_gemm<MB, NB, kE4M3, kE4M3, FAST>), grid, block, 0, s, p);
-    else if (afmt == kE5M2 && bfmt == kE4M3) hipLaunchKernelGGL((k_gemm<MB, NB, kE5M2, kE4M3, FAST>), grid, block, 0, s, p);
-    else if (afmt == kE4M3) hipLaunchKernelGGL((k_gemm<MB, NB, kE4M3, kE5M2, FAST>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((k_gemm<MB, NB, kE5M2, kE5M2, FAST>), grid, block, 0, s, p);
+    const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n), block(C::THREADS);
+    if (afmt == kE4M3 && bfmt == kE4M3)
+        hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, kE4M3, kE4M3, FAST>), grid, block, 0, s, p);
+    else if (afmt == kE5M2 && bfmt == kE4M3)
+        hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, kE5M2, kE4M3, FAST>), grid, block, 0, s, p);
+    else if (afmt == kE4M3)
+        hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, kE4M3, kE5M2, FAST>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, kE5M2, kE5M2, FAST>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
 template <bool FAST>
 hipError_t launch_path(const GemmParams& p, int afmt, int bfmt, hipStream_t s) {
-    // Tile choice: 256 x 256 when that still gives every CU work, else smaller tiles.
+    // Tile choice: 256 x 256 when that still gives every CU work, else smaller
+    // tiles.  At 256 x 256 the exact path runs 8 waves (2 per SIMD, 128 x 64
+    // each) so one wave's LDS reads and converts overlap the other's MFMAs;
+    // the fast path, which needs half the MFMA time per byte of LDS traffic,
+    // runs 4 waves of 128 x 128.
     const int64_t big = ((p.m + 255) / 256) * ((p.n + 255) / 256);
     const int64_t mid = ((p.m + 127) / 128) * ((p.n + 127) / 128);
-    if (big >= 256) return launch_cfg<4, 4, FAST>(p, afmt, bfmt, s);
-    if (mid >= 256) return launch_cfg<2, 2, FAST>(p, afmt, bfmt, s);
-    return launch_cfg<1, 1, FAST>(p, afmt, bfmt, s);
+    if (big >= 256) {
+        if constexpr (FAST) return launch_cfg<2, 2, 4, 4, FAST>(p, afmt, bfmt, s);
+        else return launch_cfg<2, 4, 4, 2, FAST>(p, afmt, bfmt, s);
+    }
+    if (mid >= 256) return launch_cfg<2, 2, 2, 2, FAST>(p, afmt, bfmt, s);
+    return launch_cfg<2, 2, 1, 1, FAST>(p, afmt, bfmt, s);
 }
 
 }  // namespace
