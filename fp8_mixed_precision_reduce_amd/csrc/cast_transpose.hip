@@ -9,13 +9,17 @@
 // [rows][cols] input.  Load phase: thread t reads 16 consecutive columns of
 // rows (t/8) + 32p, p = 0..3 (all loads issued before any use), merges |x|
 // into its amax, encodes, writes the 16 codes to q with one 16-byte store and
-// to an LDS tile [128][128] with one 16-byte LDS store (8 lanes of a row hit
-// 8 distinct 16-byte bank groups).  Transpose phase: a wave reads 64
-// consecutive LDS columns of one 16-row strip byte by byte (consecutive
-// bytes: no bank conflicts), packs each column's 16 bytes and writes them to
-// q_t with one 16-byte store; each q_t row receives 128 contiguous bytes per
-// tile.  Rows and cols are multiples of 16, so a 16-element chunk is either
-// entirely inside the tensor or entirely outside.
+// to an LDS tile [128][128] with one 16-byte LDS store; the 16-byte chunk of
+// LDS row r is stored at chunk position chunk ^ ((r >> 4) & 7).  Transpose
+// phase: lane l takes the 16-row strip l & 7 of output row (input column)
+// l >> 3, reads that column's 16 bytes one by one (the swizzle spreads the 8
+// strips of a wave over 8 bank groups, so the byte reads are conflict-free),
+// packs them and writes one 16-byte store; 8 consecutive lanes thereby write
+// the 128 contiguous bytes this tile contributes to one q_t row.  Rows and
+// cols are multiples of 16, so a 16-element chunk is either entirely inside
+// the tensor or entirely outside.  At most 2048 workgroups run; each loops
+// over tiles, so the amax merge costs one (usually skipped) atomic per
+// workgroup rather than one per tile.
 #include "common.h"
 
 namespace fp8lin {
@@ -23,6 +27,29 @@ namespace {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
+constexpr int64_t kMaxGrid = 256 * 8;     // workgroups loop over tiles beyond this
+
+// 16 elements from their raw 16-byte words (4 words of f32 or 2 of bf16).
+template <int DT>
+__device__ __forceinline__ void unpack16(const uint4* w, float v[16]) {
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[4 * j + 0] = __uint_as_float(w[j].x); v[4 * j + 1] = __uint_as_float(w[j].y);
+            v[4 * j + 2] = __uint_as_float(w[j].z); v[4 * j + 3] = __uint_as_float(w[j].w);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t u[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[8 * j + 2 * h + 0] = __uint_as_float(u[h] << 16);
+                v[8 * j + 2 * h + 1] = __uint_as_float(u[h] & 0xFFFF0000u);
+            }
+        }
+    }
+}
 
 template <int DT>
 __device__ __forceinline__ void store16(void* base, int64_t idx, const float v[16]) {
@@ -50,36 +77,51 @@ k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t
     __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kTile];
     __shared__ uint32_t red[kThreads / 64];
 
-    const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
-    const int64_t r0 = tr * kTile, c0 = tc * kTile;
     const int t = threadIdx.x;
     const int cc = t & 7;        // 16-column chunk within the tile
     const int rr = t >> 3;       // 0..31
+    const float s = *scale_p;
+    const int64_t ntiles = ((rows + kTile - 1) / kTile) * tiles_c;
+    uint32_t m = 0;
+    for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+    const int64_t tr = tile_id / tiles_c, tc = tile_id % tiles_c;
+    const int64_t r0 = tr * kTile, c0 = tc * kTile;
     const int64_t col = c0 + cc * 16;
     const bool col_ok = col < cols;
-    const float s = *scale_p;
 
-    float v[4][16];
+    // Issue every load of the tile (and of z for the GeLU backward) before
+    // touching any of them, then unpack.
+    constexpr int NV = DT == kF32 ? 4 : 2;              // 16-byte loads per 16 elements
+    uint4 rv[4][NV], rz[DGELU ? 4 : 1][NV];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int64_t row = r0 + rr + 32 * p;
-        if (col_ok && row < rows) {
-            load16<DT>(x, row * cols + col, v[p]);
-        } else {
+        const bool ok = col_ok && row < rows;
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) +
+                                                          (row * cols + col) * (DT == kF32 ? 4 : 2));
 #pragma unroll
-            for (int j = 0; j < 16; ++j) v[p][j] = 0.0f;
-        }
+        for (int j = 0; j < NV; ++j) rv[p][j] = ok ? src[j] : make_uint4(0, 0, 0, 0);
     }
     if constexpr (DGELU) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int64_t row = r0 + rr + 32 * p;
-            float zz[16];
-            if (col_ok && row < rows) load16<DT>(z, row * cols + col, zz);
-            else {
+            const bool ok = col_ok && row < rows;
+            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(z) +
+                                                              (row * cols + col) * (DT == kF32 ? 4 : 2));
 #pragma unroll
-                for (int j = 0; j < 16; ++j) zz[j] = 0.0f;
-            }
+            for (int j = 0; j < NV; ++j) rz[p][j] = ok ? src[j] : make_uint4(0, 0, 0, 0);
+        }
+    }
+    float v[4][16];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) unpack16<DT>(rv[p], v[p]);
+    if constexpr (DGELU) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int64_t row = r0 + rr + 32 * p;
+            float zz[16];
+            unpack16<DT>(rz[p], zz);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const float g = v[p][j] * gelu_grad_f32(zz[j]);
@@ -89,7 +131,6 @@ k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t
         }
     }
 
-    uint32_t m = 0;
     float csum[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) csum[j] = 0.0f;
@@ -104,7 +145,7 @@ k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t
         }
         const uint4 codes = scale_enc16<FMT>(v[p], s);
         if (q && col_ok && row < rows) *reinterpret_cast<uint4*>(q + row * cols + col) = codes;
-        if (qt) *reinterpret_cast<uint4*>(tile + lrow * kTile + cc * 16) = codes;
+        if (qt) *reinterpret_cast<uint4*>(tile + lrow * kTile + ((cc ^ ((lrow >> 4) & 7)) << 4)) = codes;
     }
     __syncthreads();
 
@@ -113,13 +154,14 @@ k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t
     for (int i = 0; i < 4; ++i) {
         if (!qt) break;
         const int idx = t + kThreads * i;
-        const int oc = idx & (kTile - 1);       // output row within the tile (input column)
-        const int rc = idx >> 7;                // 16-row strip 0..7
+        const int rc = idx & 7;                 // 16-row strip 0..7
+        const int oc = idx >> 3;                // output row within the tile (input column)
         const int64_t orow = c0 + oc, ocol = r0 + rc * 16;
+        const int colp = (((oc >> 4) ^ rc) << 4) | (oc & 15);   // swizzled byte column of strip rc
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint8_t* src = tile + (rc * 16 + 4 * j) * kTile + oc;
+            const uint8_t* src = tile + (rc * 16 + 4 * j) * kTile + colp;
             w[j] = (uint32_t)src[0] | ((uint32_t)src[kTile] << 8) | ((uint32_t)src[2 * kTile] << 16) |
                    ((uint32_t)src[3 * kTile] << 24);
         }
@@ -141,6 +183,8 @@ k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t
             if (c0 + t < cols) dbias_ws[tr * cols + c0 + t] = acc;
         }
     }
+    __syncthreads();             // the LDS tile is rewritten by the next tile
+    }
     if (amax_slot) block_amax_merge(m, amax_slot, red);
 }
 
@@ -158,7 +202,8 @@ template <int DT, int FMT>
 hipError_t launch_dt_fmt(const void* x, const void* z, int64_t rows, int64_t cols, const float* scale,
                          uint8_t* q, uint8_t* qt, float* slot, float* dbias_ws, void* dz_out, hipStream_t s) {
     const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
-    const dim3 grid((unsigned)(tiles_r * tiles_c)), block(kThreads);
+    const int64_t ntiles = tiles_r * tiles_c;
+    const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
     const bool dgelu = z != nullptr, dbias = dbias_ws != nullptr;
     if (!dgelu && !dbias)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false>), grid, block, 0, s, x, z, rows, cols,

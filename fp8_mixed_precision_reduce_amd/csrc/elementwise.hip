@@ -22,7 +22,7 @@ constexpr int kThreads = 256;
 int grid_for(int64_t chunks) {
     // Enough workgroups to cover every CU several times, not more than the chunks need.
     const int64_t want = (chunks + 2 * kThreads - 1) / (2 * kThreads);
-    const int64_t cap = 256 * 16;
+    const int64_t cap = 256 * 8;
     return (int)(want < 1 ? 1 : (want > cap ? cap : want));
 }
 
@@ -97,8 +97,7 @@ k_dequant(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ si
     const float si = *sinv_p;
     const int64_t chunks = n >> 4;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < chunks; c += stride) {
-        const uint4 w = reinterpret_cast<const uint4*>(q)[c];
+    auto emit = [&](int64_t c, uint4 w) {
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
         float v[16];
 #pragma unroll
@@ -118,7 +117,15 @@ k_dequant(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ si
                 o[j] = make_uint4(pack_bf16x2(v[8 * j], v[8 * j + 1]), pack_bf16x2(v[8 * j + 2], v[8 * j + 3]),
                                   pack_bf16x2(v[8 * j + 4], v[8 * j + 5]), pack_bf16x2(v[8 * j + 6], v[8 * j + 7]));
         }
+    };
+    int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; c + stride < chunks; c += 2 * stride) {
+        const uint4 w0 = reinterpret_cast<const uint4*>(q)[c];
+        const uint4 w1 = reinterpret_cast<const uint4*>(q)[c + stride];
+        emit(c, w0);
+        emit(c + stride, w1);
     }
+    if (c < chunks) emit(c, reinterpret_cast<const uint4*>(q)[c]);
     for (int64_t i = (chunks << 4) + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
         float v[4];
         dec4<FMT>((uint32_t)q[i], v);
@@ -232,9 +239,7 @@ hipError_t launch_cast(const void* x, int dtype, int64_t n, int fmt, const float
 hipError_t launch_dequant(const uint8_t* q, int fmt, int64_t n, const float* sinv, void* out, int out_dtype,
                           hipStream_t s) {
     if (n == 0) return hipSuccess;
-    const int64_t chunks = (n + 15) >> 4;
-    const int64_t want = (chunks + kThreads - 1) / kThreads;
-    const int g = (int)(want < 1 ? 1 : (want > 256 * 32 ? 256 * 32 : want));
+    const int g = grid_for((n + 15) >> 4);
     timing_before(kKindDequant, s);
     if (fmt == kE4M3 && out_dtype == kF32)
         hipLaunchKernelGGL((k_dequant<kE4M3, kF32>), dim3(g), dim3(kThreads), 0, s, q, n, sinv, out);
