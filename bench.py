@@ -43,38 +43,16 @@ def _exit_multi_gpu(n):
 
 
 class MlpBlock:
-    """Buffers and metas of the MLP block; step() enqueues one fwd+bwd+update."""
+    """The benchmark's MLP block on the seeded inputs (see synth.mlp_inputs)."""
 
     def __init__(self, F, torch, fast_accum=False):
         import synth
-        self.F, self.torch = F, torch
-        dev = "cuda"
-        self.x, self.w1, self.w2, self.dy = synth.mlp_inputs(0, device=dev)
-        bf = dict(dtype=torch.bfloat16, device=dev)
-        self.h = torch.empty(M, FFN, **bf)
-        self.z = torch.empty(M, FFN, **bf)
-        self.y = torch.empty(M, HID, **bf)
-        self.dh = torch.empty(M, FFN, **bf)
-        self.dx = torch.empty(M, HID, **bf)
-        self.dw1 = torch.empty(FFN, HID, dtype=torch.float32, device=dev)
-        self.dw2 = torch.empty(HID, FFN, dtype=torch.float32, device=dev)
-        u8 = dict(dtype=torch.uint8, device=dev)
-        self.gq2, self.gqt2 = torch.empty(M, HID, **u8), torch.empty(HID, M, **u8)
-        self.gq1, self.gqt1 = torch.empty(M, FFN, **u8), torch.empty(FFN, M, **u8)
-        self.s1 = F.Saved(M, FFN, HID, device=dev)
-        self.s2 = F.Saved(M, HID, FFN, device=dev)
-        self.bank = F.MetaBank([F.E4M3, F.E4M3, F.E4M3, F.E4M3, F.E5M2, F.E5M2], HIST, device=dev)
-        self.mx, self.mw1, self.mh, self.mw2, self.mdy, self.mdz = (self.bank.meta(i) for i in range(6))
-        self.recipe = F.Recipe(F.FORMAT_HYBRID, HIST, F.AMAX_MAX, 0, fast_accum)
+        from fp8_mixed_precision_reduce_amd.blocks import Fp8MlpBlock
+        x, w1, w2, dy = synth.mlp_inputs(0, device="cuda")
+        self.block = Fp8MlpBlock(x, w1, w2, dy, history_len=HIST, fast_accum=fast_accum)
 
     def step(self):
-        F, r = self.F, self.recipe
-        F.fp8_linear_fwd(self.x, self.w1, self.h, r, self.mx, self.mw1, self.s1, epilogue=F.EPI_GELU, y_aux=self.z)
-        F.fp8_linear_fwd(self.h, self.w2, self.y, r, self.mh, self.mw2, self.s2)
-        F.fp8_linear_bwd(self.dy, FFN, r, self.mdy, self.s2, self.gq2, self.gqt2, dx=self.dh, dw=self.dw2)
-        F.fp8_linear_bwd(self.dh, HID, r, self.mdz, self.s1, self.gq1, self.gqt1, dx=self.dx, dw=self.dw1,
-                         gelu_z=self.z)
-        self.bank.update(r)
+        self.block.step()
 
     @staticmethod
     def cast_bytes_per_step():
