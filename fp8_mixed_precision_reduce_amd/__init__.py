@@ -7,7 +7,7 @@ C entry point of the same name (include/fp8lin.h) and raises Fp8LinError on a
 non-zero status.  Every step of the computation runs in the library's HIP
 kernels; torch only provides device memory and streams.
 
-The library must be built (python -m fp8_mixed_precision_reduce_amd.build or
+The library must be built (python fp8_mixed_precision_reduce_amd/build.py or
 __graft_entry__.build()); importing this package without it raises
 ImportError -- there is no fallback.
 """
@@ -26,12 +26,13 @@ FORMAT_E4M3, FORMAT_HYBRID = 0, 1
 AMAX_MAX = 0
 EPI_GELU, EPI_ACCUMULATE, EPI_FAST_ACCUM = 1, 2, 4
 KIND_NAMES = ["amax", "cast", "cast_transpose", "dequant", "scale_update", "gemm", "dbias", "other"]
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 FUNCTIONS = [
     "fp8lin_abi_version", "fp8lin_last_error", "fp8lin_status_name", "fp8lin_dbias_workspace_bytes",
     "fp8_amax", "fp8_amax_scale_update", "fp8_cast", "fp8_cast_transpose", "fp8_cast_transpose_dgelu",
-    "fp8_dequant", "fp8_gemm", "fp8_linear_fwd", "fp8_linear_bwd", "fp8lin_timing_enable", "fp8lin_timing_read",
+    "fp8_dequant", "fp8_gemm", "fp8_linear_fwd", "fp8_linear_bwd", "fp8_loss_scale_update",
+    "fp8_loss_scale_apply", "fp8_sgd_step", "fp8lin_timing_enable", "fp8lin_timing_read",
 ]
 
 
@@ -63,7 +64,7 @@ class _SavedC(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run python -m fp8_mixed_precision_reduce_amd.build")
+        raise ImportError(f"{LIB_PATH} is not built; run python fp8_mixed_precision_reduce_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sig = {
@@ -77,12 +78,15 @@ def _load():
         "fp8_cast_transpose": (I32, [P, I32, I64, I64, I32, P, P, P, P, P, P, P]),
         "fp8_cast_transpose_dgelu": (I32, [P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, P]),
         "fp8_dequant": (I32, [P, I32, I64, P, P, I32, P]),
-        "fp8_gemm": (I32, [P, I32, P, I32, I64, I64, I64, P, P, P, I32, I32, P, I32, P, P, P]),
-        "fp8_linear_fwd": (I32, [I64, I64, I64, P, I32, P, I32, P, I32, I32, P, I32, P, P,
+        "fp8_gemm": (I32, [P, I32, P, I32, I64, I64, I64, P, P, P, I32, I32, P, I32, P, P, P, P]),
+        "fp8_linear_fwd": (I32, [I64, I64, I64, P, I32, P, I32, P, I32, I32, P, I32, P, P, P,
                                  ctypes.POINTER(Recipe), ctypes.POINTER(_MetaC), ctypes.POINTER(_MetaC),
                                  ctypes.POINTER(_SavedC), P]),
         "fp8_linear_bwd": (I32, [I64, I64, I64, P, I32, P, P, ctypes.POINTER(Recipe), ctypes.POINTER(_MetaC),
-                                 ctypes.POINTER(_SavedC), P, P, P, I32, P, I32, P, P, P]),
+                                 ctypes.POINTER(_SavedC), P, P, P, I32, P, P, I32, P, P, P]),
+        "fp8_loss_scale_update": (I32, [P, I32, I64, P, I32, ctypes.c_float, ctypes.c_float, P]),
+        "fp8_loss_scale_apply": (I32, [P, I32, I64, P, P, P]),
+        "fp8_sgd_step": (I32, [P, P, I64, ctypes.c_float, P, P]),
         "fp8lin_timing_enable": (I32, [I32]),
         "fp8lin_timing_read": (I32, [P, P, I32]),
     }
@@ -223,33 +227,55 @@ def fp8_dequant(q, fmt, scale_inv, out, stream=None):
     _check(_lib.fp8_dequant(_p(q), fmt, q.numel(), _p(scale_inv), _p(out), _dt(out), _stream(stream)))
 
 
-def fp8_gemm(a, a_fmt, b, b_fmt, sinv_a, sinv_b, d, bias=None, epilogue=0, aux=None, amax_d=None, stream=None):
+def fp8_gemm(a, a_fmt, b, b_fmt, sinv_a, sinv_b, d, bias=None, epilogue=0, aux=None, residual=None, amax_d=None,
+             stream=None):
     m, k = a.shape
     n = b.shape[0]
     bias_dt = _dt(bias) if bias is not None else F32
     _check(_lib.fp8_gemm(_p(a), a_fmt, _p(b), b_fmt, m, n, k, _p(sinv_a), _p(sinv_b), _p(bias), bias_dt, epilogue,
-                         _p(d), _dt(d), _p(aux), _p(amax_d), _stream(stream)))
+                         _p(d), _dt(d), _p(aux), _p(residual), _p(amax_d), _stream(stream)))
 
 
-def fp8_linear_fwd(x, w, y, recipe, mx, mw, saved, bias=None, epilogue=0, y_aux=None, y_amax_slot=None,
-                   stream=None):
+def fp8_linear_fwd(x, w, y, recipe, mx, mw, saved, bias=None, epilogue=0, y_aux=None, residual=None,
+                   y_amax_slot=None, stream=None):
     m, k = x.shape
     n = w.shape[0]
     bias_dt = _dt(bias) if bias is not None else F32
     cx, cw, cs = mx.c(), mw.c(), saved.c()
     _check(_lib.fp8_linear_fwd(m, n, k, _p(x), _dt(x), _p(w), _dt(w), _p(bias), bias_dt, epilogue, _p(y), _dt(y),
-                               _p(y_aux), _p(y_amax_slot), ctypes.byref(recipe), ctypes.byref(cx), ctypes.byref(cw),
-                               ctypes.byref(cs), _stream(stream)))
+                               _p(y_aux), _p(residual), _p(y_amax_slot), ctypes.byref(recipe), ctypes.byref(cx),
+                               ctypes.byref(cw), ctypes.byref(cs), _stream(stream)))
 
 
 def fp8_linear_bwd(dy, k, recipe, mdy, saved, dyq_ws=None, dyq_t_ws=None, dx=None, dw=None, accumulate_dw=False,
-                   dbias=None, dbias_ws=None, gelu_z=None, dz_out=None, stream=None):
+                   dbias=None, dbias_ws=None, gelu_z=None, dz_out=None, dx_residual=None, stream=None):
     m, n = dy.shape
     dx_dt = _dt(dx) if dx is not None else F32
     cm, cs = mdy.c(), saved.c()
     _check(_lib.fp8_linear_bwd(m, n, k, _p(dy), _dt(dy), _p(gelu_z), _p(dz_out), ctypes.byref(recipe),
-                               ctypes.byref(cm), ctypes.byref(cs), _p(dyq_ws), _p(dyq_t_ws), _p(dx), dx_dt, _p(dw),
-                               int(bool(accumulate_dw)), _p(dbias), _p(dbias_ws), _stream(stream)))
+                               ctypes.byref(cm), ctypes.byref(cs), _p(dyq_ws), _p(dyq_t_ws), _p(dx), dx_dt,
+                               _p(dx_residual), _p(dw), int(bool(accumulate_dw)), _p(dbias), _p(dbias_ws),
+                               _stream(stream)))
+
+
+def fp8_loss_scale_update(grad_amaxes, state, stride=1, n=None, growth_interval=5, backoff=0.5, growth=2.0,
+                          stream=None):
+    """found_inf from n gradient amaxes (every `stride`-th float of
+    grad_amaxes), then the dynamic loss-scale state float[4] update."""
+    if n is None:
+        n = (grad_amaxes.numel() + stride - 1) // stride
+    _check(_lib.fp8_loss_scale_update(_p(grad_amaxes), n, stride, _p(state), growth_interval, backoff, growth,
+                                      _stream(stream)))
+
+
+def fp8_loss_scale_apply(g, state, out, stream=None):
+    _check(_lib.fp8_loss_scale_apply(_p(g), _dt(g), g.numel(), _p(state), _p(out), _stream(stream)))
+
+
+def fp8_sgd_step(w, g, lr, state, stream=None):
+    if w.dtype != torch.float32 or g.dtype != torch.float32:
+        raise TypeError("fp8_sgd_step: w and g must be float32")
+    _check(_lib.fp8_sgd_step(_p(w), _p(g), w.numel(), lr, _p(state), _stream(stream)))
 
 
 def dbias_workspace_bytes(rows, cols):

@@ -276,7 +276,8 @@ int32_t fp8_dequant(const uint8_t* q, int32_t fp8_dtype, int64_t n, const float*
 namespace {
 int32_t check_gemm(const char* fn, const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_dtype, int64_t m,
                    int64_t n, int64_t k, const float* sinv_a, const float* sinv_b, const void* bias,
-                   int32_t bias_dtype, int32_t epilogue, void* d, int32_t d_dtype, void* aux, float* amax_d) {
+                   int32_t bias_dtype, int32_t epilogue, void* d, int32_t d_dtype, void* aux, const void* residual,
+                   float* amax_d) {
     if (!is_fp8(a_dtype) || !is_fp8(b_dtype))
         return fail(FP8LIN_ERR_DTYPE, "%s: operand types %d, %d must be E4M3/E5M2", fn, a_dtype, b_dtype);
     if (!is_hp(d_dtype)) return fail(FP8LIN_ERR_DTYPE, "%s: output type %d must be F32 or BF16", fn, d_dtype);
@@ -296,9 +297,17 @@ int32_t check_gemm(const char* fn, const uint8_t* a, int32_t a_dtype, const uint
     if (m * n > 0 && !d) return fail(FP8LIN_ERR_NULL, "%s: null output", fn);
     if (m * n * k > 0 && (!a || !b)) return fail(FP8LIN_ERR_NULL, "%s: null operand", fn);
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(aux, 16) || !aligned(bias, 16) ||
-        !aligned(sinv_a, 4) || !aligned(sinv_b, 4) || !aligned(amax_d, 4))
+        !aligned(residual, 16) || !aligned(sinv_a, 4) || !aligned(sinv_b, 4) || !aligned(amax_d, 4))
         return fail(FP8LIN_ERR_ALIGN, "%s: misaligned pointer", fn);
+    if (residual && (epilogue & FP8LIN_EPI_ACCUMULATE))
+        return fail(FP8LIN_ERR_ARG, "%s: a residual cannot be combined with ACCUMULATE", fn);
     const int64_t db = m * n * elem_size(d_dtype);
+    // the residual may be the output itself (each element is read before it is
+    // written by the same lane) but must not partly overlap it or any other buffer
+    if (residual && residual != d && overlap(residual, db, d, db))
+        return fail(FP8LIN_ERR_ARG, "%s: residual partly overlaps d", fn);
+    if (residual && overlap(residual, db, aux, aux ? db : 0))
+        return fail(FP8LIN_ERR_ARG, "%s: residual overlaps aux", fn);
     const void* ins[3] = {a, b, bias};
     const int64_t ib[3] = {m * k, n * k, bias ? n * elem_size(bias_dtype) : 0};
     for (int i = 0; i < 3; ++i)
@@ -311,12 +320,12 @@ int32_t check_gemm(const char* fn, const uint8_t* a, int32_t a_dtype, const uint
 
 int32_t fp8_gemm(const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_dtype, int64_t m, int64_t n, int64_t k,
                  const float* sinv_a, const float* sinv_b, const void* bias, int32_t bias_dtype, int32_t epilogue,
-                 void* d, int32_t d_dtype, void* aux, float* amax_d, void* stream) {
+                 void* d, int32_t d_dtype, void* aux, const void* residual, float* amax_d, void* stream) {
     const int32_t v = check_gemm("fp8_gemm", a, a_dtype, b, b_dtype, m, n, k, sinv_a, sinv_b, bias, bias_dtype,
-                                 epilogue, d, d_dtype, aux, amax_d);
+                                 epilogue, d, d_dtype, aux, residual, amax_d);
     if (v != FP8LIN_OK) return v;
     return hip_status(launch_gemm(a, a_dtype, b, b_dtype, m, n, k, sinv_a, sinv_b, bias, bias_dtype, epilogue, d,
-                                  d_dtype, aux, amax_d, as_stream(stream)),
+                                  d_dtype, aux, residual, amax_d, as_stream(stream)),
                       "fp8_gemm");
 }
 
@@ -342,7 +351,7 @@ int32_t check_meta(const char* fn, const char* which, const fp8lin_meta* mt) {
 
 int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x_dtype, const void* w,
                        int32_t w_dtype, const void* bias, int32_t bias_dtype, int32_t epilogue, void* y,
-                       int32_t y_dtype, void* y_aux, float* y_amax_slot, const fp8lin_recipe* recipe,
+                       int32_t y_dtype, void* y_aux, const void* residual, float* y_amax_slot, const fp8lin_recipe* recipe,
                        const fp8lin_meta* mx, const fp8lin_meta* mw, const fp8lin_saved* saved, void* stream) {
     const char* fn = "fp8_linear_fwd";
     int32_t v;
@@ -365,7 +374,7 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
                       mw->amax_history, nullptr, nullptr, nullptr, false)))
         return v;
     if ((v = check_gemm(fn, saved->xq, FP8LIN_E4M3, saved->wq, FP8LIN_E4M3, m, n, k, saved->sinv, saved->sinv + 1,
-                        bias, bias_dtype, epilogue | fast, y, y_dtype, y_aux, y_amax_slot)))
+                        bias, bias_dtype, epilogue | fast, y, y_dtype, y_aux, residual, y_amax_slot)))
         return v;
     if (overlap(y, m * n * elem_size(y_dtype), x, m * k * elem_size(x_dtype)) ||
         overlap(y, m * n * elem_size(y_dtype), w, n * k * elem_size(w_dtype)))
@@ -384,14 +393,14 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
     e = launch_copy_scalars(mx->scale_inv, mw->scale_inv, saved->sinv, s);
     if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: save scale_inv");
     e = launch_gemm(saved->xq, FP8LIN_E4M3, saved->wq, FP8LIN_E4M3, m, n, k, saved->sinv, saved->sinv + 1, bias,
-                    bias_dtype, epilogue | fast, y, y_dtype, y_aux, y_amax_slot, s);
+                    bias_dtype, epilogue | fast, y, y_dtype, y_aux, residual, y_amax_slot, s);
     return hip_status(e, "fp8_linear_fwd: gemm");
 }
 
 int32_t fp8_linear_bwd(int64_t m, int64_t n, int64_t k, const void* dy, int32_t dy_dtype, const void* gelu_z,
                        void* dz_out, const fp8lin_recipe* recipe, const fp8lin_meta* mdy, const fp8lin_saved* saved,
-                       uint8_t* dyq_ws, uint8_t* dyq_t_ws, void* dx, int32_t dx_dtype, float* dw,
-                       int32_t accumulate_dw, float* dbias, float* dbias_ws, void* stream) {
+                       uint8_t* dyq_ws, uint8_t* dyq_t_ws, void* dx, int32_t dx_dtype, const void* dx_residual,
+                       float* dw, int32_t accumulate_dw, float* dbias, float* dbias_ws, void* stream) {
     const char* fn = "fp8_linear_bwd";
     int32_t v;
     if ((v = check_recipe(fn, recipe)) || (v = check_meta(fn, "dy", mdy))) return v;
@@ -414,15 +423,19 @@ int32_t fp8_linear_bwd(int64_t m, int64_t n, int64_t k, const void* dy, int32_t 
     if ((v = check_ct(fn, dy, gelu_z, dy_dtype, m, n, gfmt, mdy->scale, qr, qt, mdy->amax_history, dbias, dbias_ws,
                       dz_out, false)))
         return v;
+    if (dx_residual && !dx) return fail(FP8LIN_ERR_ARG, "%s: dx_residual needs dx", fn);
     if (dx && (v = check_gemm(fn, dyq_ws, gfmt, saved->wq_t, FP8LIN_E4M3, m, k, n, mdy->scale_inv, saved->sinv + 1,
-                              nullptr, FP8LIN_F32, fast, dx, dx_dtype, nullptr, nullptr)))
+                              nullptr, FP8LIN_F32, fast, dx, dx_dtype, nullptr, dx_residual, nullptr)))
         return v;
     if (dw && (v = check_gemm(fn, dyq_t_ws, gfmt, saved->xq_t, FP8LIN_E4M3, n, k, m, mdy->scale_inv, saved->sinv,
                               nullptr, FP8LIN_F32, (accumulate_dw ? FP8LIN_EPI_ACCUMULATE : 0) | fast, dw, FP8LIN_F32,
-                              nullptr, nullptr)))
+                              nullptr, nullptr, nullptr)))
         return v;
     if (dx && dw && overlap(dx, m * k * elem_size(dx_dtype), dw, n * k * 4))
         return fail(FP8LIN_ERR_ARG, "%s: dx and dw overlap", fn);
+    if (dx && (overlap(dx, m * k * elem_size(dx_dtype), dy, m * n * elem_size(dy_dtype)) ||
+               overlap(dx, m * k * elem_size(dx_dtype), gelu_z, gelu_z ? m * n * elem_size(dy_dtype) : 0)))
+        return fail(FP8LIN_ERR_ARG, "%s: dx overlaps dy or gelu_z", fn);
 
     hipStream_t s = as_stream(stream);
     hipError_t e = launch_cast_transpose(dy, gelu_z, dy_dtype, m, n, gfmt, mdy->scale, qr, qt, mdy->amax_history,
@@ -430,16 +443,52 @@ int32_t fp8_linear_bwd(int64_t m, int64_t n, int64_t k, const void* dy, int32_t 
     if (e != hipSuccess) return hip_status(e, "fp8_linear_bwd: cast dY");
     if (dx) {
         e = launch_gemm(dyq_ws, gfmt, saved->wq_t, FP8LIN_E4M3, m, k, n, mdy->scale_inv, saved->sinv + 1, nullptr,
-                        FP8LIN_F32, fast, dx, dx_dtype, nullptr, nullptr, s);
+                        FP8LIN_F32, fast, dx, dx_dtype, nullptr, dx_residual, nullptr, s);
         if (e != hipSuccess) return hip_status(e, "fp8_linear_bwd: dgrad");
     }
     if (dw) {
         e = launch_gemm(dyq_t_ws, gfmt, saved->xq_t, FP8LIN_E4M3, n, k, m, mdy->scale_inv, saved->sinv, nullptr,
                         FP8LIN_F32, (accumulate_dw ? FP8LIN_EPI_ACCUMULATE : 0) | fast, dw, FP8LIN_F32, nullptr,
-                        nullptr, s);
+                        nullptr, nullptr, s);
         if (e != hipSuccess) return hip_status(e, "fp8_linear_bwd: wgrad");
     }
     return ok();
+}
+
+// --------------------------------------------------- loss scaling and SGD
+int32_t fp8_loss_scale_update(const float* grad_amaxes, int32_t n, int64_t stride, float* state,
+                              int32_t growth_interval, float backoff, float growth, void* stream) {
+    const char* fn = "fp8_loss_scale_update";
+    if (!grad_amaxes || !state) return fail(FP8LIN_ERR_NULL, "%s: null pointer", fn);
+    if (n < 1 || n > 4096 || stride < 1) return fail(FP8LIN_ERR_SHAPE, "%s: n=%d stride=%lld", fn, n, (long long)stride);
+    if (growth_interval < 1 || !(backoff > 0.0f && backoff < 1.0f) || !(growth > 1.0f))
+        return fail(FP8LIN_ERR_ARG, "%s: need growth_interval >= 1, 0 < backoff < 1 < growth", fn);
+    if (!aligned(grad_amaxes, 4) || !aligned(state, 4)) return fail(FP8LIN_ERR_ALIGN, "%s: misaligned pointer", fn);
+    if (overlap(state, 16, grad_amaxes, ((int64_t)(n - 1) * stride + 1) * 4))
+        return fail(FP8LIN_ERR_ARG, "%s: state overlaps the amaxes", fn);
+    return hip_status(launch_loss_scale_update(grad_amaxes, n, stride, state, growth_interval, backoff, growth,
+                                               as_stream(stream)), fn);
+}
+
+int32_t fp8_loss_scale_apply(const void* g, int32_t dtype, int64_t n, const float* state, void* out, void* stream) {
+    const char* fn = "fp8_loss_scale_apply";
+    if (!is_hp(dtype)) return fail(FP8LIN_ERR_DTYPE, "%s: dtype %d must be F32 or BF16", fn, dtype);
+    if (n < 0 || n > kMaxElems) return fail(FP8LIN_ERR_SHAPE, "%s: n=%lld", fn, (long long)n);
+    if (!state || (n > 0 && (!g || !out))) return fail(FP8LIN_ERR_NULL, "%s: null pointer", fn);
+    if (!aligned(g, 16) || !aligned(out, 16) || !aligned(state, 4)) return fail(FP8LIN_ERR_ALIGN, "%s: misaligned", fn);
+    if (g != out && overlap(g, n * elem_size(dtype), out, n * elem_size(dtype)))
+        return fail(FP8LIN_ERR_ARG, "%s: out partly overlaps g", fn);
+    return hip_status(launch_scale_by(g, dtype, n, state, out, as_stream(stream)), fn);
+}
+
+int32_t fp8_sgd_step(float* w, const float* g, int64_t n, float lr, const float* state, void* stream) {
+    const char* fn = "fp8_sgd_step";
+    if (n < 0 || n > kMaxElems) return fail(FP8LIN_ERR_SHAPE, "%s: n=%lld", fn, (long long)n);
+    if (!state || (n > 0 && (!w || !g))) return fail(FP8LIN_ERR_NULL, "%s: null pointer", fn);
+    if (!aligned(w, 16) || !aligned(g, 16) || !aligned(state, 4)) return fail(FP8LIN_ERR_ALIGN, "%s: misaligned", fn);
+    if (overlap(w, n * 4, g, n * 4) || overlap(w, n * 4, state, 16))
+        return fail(FP8LIN_ERR_ARG, "%s: w overlaps g or the state", fn);
+    return hip_status(launch_sgd(w, g, n, lr, state, as_stream(stream)), fn);
 }
 
 }  // extern "C"

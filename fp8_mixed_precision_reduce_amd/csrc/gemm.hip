@@ -2,8 +2,9 @@
 // epilogue.
 //
 //   y[i][j] = (sum_k dec(A[i][k]) * dec(B[j][k])) * sinv_a * sinv_b + bias[j]
-//   D[i][j] = gelu(y) | y | D[i][j] + y, rounded to fp32 or bf16; optional
-//   pre-GeLU copy and the amax of D as written.
+//   D[i][j] = gelu(y) | y | D[i][j] + y, plus an optional residual R[i][j],
+//   rounded to fp32 or bf16; optional pre-GeLU copy and the amax of D as
+//   written.
 //
 // Pages (titles in include/fp8lin.h): [PT-VI] torch._scaled_mm example (two
 // FP8 operands, the second transposed, their scales, optional bias, output
@@ -72,6 +73,7 @@ struct GemmParams {
     const void* bias;
     void* d;
     void* aux;
+    const void* residual;
     float* amax;
     int32_t tiles_m, tiles_n;
     int32_t bias_dtype, d_dtype, epilogue;
@@ -335,6 +337,16 @@ k_gemm(GemmParams p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) y[e] = gelu_f32(y[e]);
                 }
+                if (p.residual) {
+                    if (out_bf16) {
+                        const uint2 rv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.residual) + off);
+                        y[0] += bf16_to_f32(rv.x & 0xFFFFu); y[1] += bf16_to_f32(rv.x >> 16);
+                        y[2] += bf16_to_f32(rv.y & 0xFFFFu); y[3] += bf16_to_f32(rv.y >> 16);
+                    } else {
+                        const float4 rv = *reinterpret_cast<const float4*>(static_cast<const float*>(p.residual) + off);
+                        y[0] += rv.x; y[1] += rv.y; y[2] += rv.z; y[3] += rv.w;
+                    }
+                }
                 if (out_bf16) {
                     const uint2 o = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.d) + off) = o;
@@ -394,11 +406,11 @@ hipError_t launch_path(const GemmParams& p, int afmt, int bfmt, hipStream_t s) {
 
 hipError_t launch_gemm(const uint8_t* a, int afmt, const uint8_t* b, int bfmt, int64_t m, int64_t n, int64_t k,
                        const float* sinv_a, const float* sinv_b, const void* bias, int bias_dtype, int epilogue,
-                       void* d, int d_dtype, void* aux, float* amax, hipStream_t s) {
+                       void* d, int d_dtype, void* aux, const void* residual, float* amax, hipStream_t s) {
     if (m == 0 || n == 0) return hipSuccess;
     GemmParams p{};
     p.a = a; p.b = b; p.m = m; p.n = n; p.k = k;
-    p.sinv_a = sinv_a; p.sinv_b = sinv_b; p.bias = bias; p.d = d; p.aux = aux; p.amax = amax;
+    p.sinv_a = sinv_a; p.sinv_b = sinv_b; p.bias = bias; p.d = d; p.aux = aux; p.residual = residual; p.amax = amax;
     p.bias_dtype = bias_dtype; p.d_dtype = d_dtype; p.epilogue = epilogue;
     timing_before(kKindGemm, s);
     const hipError_t e = (epilogue & kEpiFastAccum) ? launch_path<true>(p, afmt, bfmt, s)

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 1
+#define FP8LIN_ABI_VERSION 2
 
 /* Status codes returned by every call. */
 enum {
@@ -233,7 +233,8 @@ int32_t fp8_dequant(const uint8_t* q, int32_t fp8_dtype, int64_t n, const float*
 /*
  * fp8_gemm -- the scaled FP8 GEMM with fp32 accumulation and a fused epilogue:
  *   y[i][j] = (sum_k dec(a[i][k]) * dec(b[j][k])) * sinv_a * sinv_b + bias[j]
- *   d[i][j] = gelu(y) | y | d[i][j] + y   (per `epilogue`), rounded to d_dtype
+ *   d[i][j] = gelu(y) | y | d[i][j] + y   (per `epilogue`), then + residual[i][j]
+ *             if a residual is given, rounded to d_dtype
  * [PT-VI] torch._scaled_mm example: two FP8 operands (the second transposed),
  * their scales, an optional bias, an output type, and the output's amax;
  * [MP-KR] "Accumulation into FP32"; [TE-RU] section 3 (inverse scaling after
@@ -245,12 +246,17 @@ int32_t fp8_dequant(const uint8_t* q, int32_t fp8_dtype, int64_t n, const float*
  *   epilogue   0, FP8LIN_EPI_GELU or FP8LIN_EPI_ACCUMULATE, optionally | FP8LIN_EPI_FAST_ACCUM
  *   d          [m][n] of d_dtype (F32 or BF16; ACCUMULATE needs F32)
  *   aux        [m][n] of d_dtype or NULL: y before GeLU (only with GELU)
+ *   residual   [m][n] of d_dtype or NULL: added in fp32 after the activation,
+ *              before the one rounding to d_dtype (a residual connection around
+ *              the layer, [TE-KR] "Transformer Layer 예시").  It may be d
+ *              itself (in-place residual add) but must not otherwise overlap d
+ *              or aux; not combinable with ACCUMULATE.
  *   amax_d     device float or NULL: max-merged amax of d as written
  */
 int32_t fp8_gemm(const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_dtype,
                  int64_t m, int64_t n, int64_t k, const float* sinv_a, const float* sinv_b,
                  const void* bias, int32_t bias_dtype, int32_t epilogue,
-                 void* d, int32_t d_dtype, void* aux, float* amax_d, void* stream);
+                 void* d, int32_t d_dtype, void* aux, const void* residual, float* amax_d, void* stream);
 
 /*
  * fp8_linear_fwd -- forward of Y = X W^T + b on FP8 copies of X and W.
@@ -266,13 +272,14 @@ int32_t fp8_gemm(const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_
  *   x_dtype, w_dtype  F32 or BF16;  bias: [n] of bias_dtype or NULL
  *   epilogue  0 or FP8LIN_EPI_GELU (then y_aux, if not NULL, gets y before GeLU)
  *   y_dtype   F32 or BF16
+ *   residual  [m][n] of y_dtype or NULL, added as in fp8_gemm (may equal y)
  *   mx, mw    HOST structs of device pointers (metas of X and W)
  *   saved     HOST struct of device pointers; xq, wq, sinv required
  */
 int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k,
                        const void* x, int32_t x_dtype, const void* w, int32_t w_dtype,
                        const void* bias, int32_t bias_dtype, int32_t epilogue,
-                       void* y, int32_t y_dtype, void* y_aux, float* y_amax_slot,
+                       void* y, int32_t y_dtype, void* y_aux, const void* residual, float* y_amax_slot,
                        const fp8lin_recipe* recipe, const fp8lin_meta* mx, const fp8lin_meta* mw,
                        const fp8lin_saved* saved, void* stream);
 
@@ -295,7 +302,9 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k,
  *   mdy       HOST struct of device pointers (meta of the gradient)
  *   saved     HOST struct from the forward; wq_t needed for dX, xq_t for dW
  *   dyq_ws    [m][n] bytes (needed when dx != NULL), dyq_t_ws [n][m] bytes (needed when dw != NULL)
- *   dx        [m][k] of dx_dtype (F32 or BF16) or NULL
+ *   dx        [m][k] of dx_dtype (F32 or BF16) or NULL; must not overlap dy or gelu_z
+ *   dx_residual [m][k] of dx_dtype or NULL: added to dX before its rounding
+ *             (the gradient arriving through a residual branch; may equal dx)
  *   dw        [n][k] float or NULL; accumulate_dw != 0 adds into it
  *   dbias     float[n] or NULL; dbias_ws as in fp8_cast_transpose
  */
@@ -303,8 +312,52 @@ int32_t fp8_linear_bwd(int64_t m, int64_t n, int64_t k,
                        const void* dy, int32_t dy_dtype, const void* gelu_z, void* dz_out,
                        const fp8lin_recipe* recipe, const fp8lin_meta* mdy, const fp8lin_saved* saved,
                        uint8_t* dyq_ws, uint8_t* dyq_t_ws,
-                       void* dx, int32_t dx_dtype, float* dw, int32_t accumulate_dw,
-                       float* dbias, float* dbias_ws, void* stream);
+                       void* dx, int32_t dx_dtype, const void* dx_residual,
+                       float* dw, int32_t accumulate_dw, float* dbias, float* dbias_ws, void* stream);
+
+/*
+ * Dynamic loss scaling and the fp32 master-weight step around the FP8 layers.
+ * [MP-KR] "Mixed-Precision Training Iteration" (multiply the loss by S before
+ * back-propagation, multiply the weight gradients by 1/S, update the fp32
+ * master weights) and its dynamic loss-scale procedure (on an Inf/NaN
+ * gradient lower S and skip the update; after N iterations without one raise
+ * S); [MP-KR] "FP32 Master Copy of Weights".
+ * The loss-scale state is a device float[4], 16-byte block owned by the
+ * caller: {S, clean iterations, found_inf of the last step, S that the last
+ * step's gradients carry}.  Initialise it to {S0, 0, 0, S0}.
+ */
+
+/*
+ * fp8_loss_scale_update -- once per step, after backward: found_inf = any of
+ * the n gradient amaxes grad_amaxes[i*stride] is Inf or NaN (these are the
+ * amax slots the backward casts merged into, so overflow is detected without
+ * an extra pass over the gradients); state[3] = S; then
+ *   found_inf: S *= backoff, clean = 0
+ *   else:      clean += 1; if clean >= growth_interval: S *= growth, clean = 0
+ *   grad_amaxes  device float, n entries `stride` floats apart; 1 <= n <= 4096
+ *   state        device float[4], updated in place
+ *   growth_interval >= 1; 0 < backoff < 1 < growth
+ */
+int32_t fp8_loss_scale_update(const float* grad_amaxes, int32_t n, int64_t stride, float* state,
+                              int32_t growth_interval, float backoff, float growth, void* stream);
+
+/*
+ * fp8_loss_scale_apply -- out = round(g * state[0]) elementwise (the loss
+ * gradient entering back-propagation, scaled by the current S).
+ *   g, out   [n] of dtype (F32 or BF16); out may equal g
+ *   state    device float[4]
+ */
+int32_t fp8_loss_scale_apply(const void* g, int32_t dtype, int64_t n, const float* state, void* out,
+                             void* stream);
+
+/*
+ * fp8_sgd_step -- w = fl32(w - fl32(lr * fl32(g * fl32(1 / state[3])))) on
+ * the fp32 master weights, a no-op when state[2] (found_inf) is set.  Run it
+ * after fp8_loss_scale_update of the same step.
+ *   w      device float[n], updated in place;  g  device float[n] (the scaled
+ *          weight gradient);  state  device float[4];  n >= 0
+ */
+int32_t fp8_sgd_step(float* w, const float* g, int64_t n, float lr, const float* state, void* stream);
 
 /*
  * Kernel timing.  fp8lin_timing_enable(capacity) makes the library record a

@@ -79,6 +79,9 @@ def _load():
         "orc_gelu_grad": (D, [D]),
         "orc_gelu_bwd": (None, [P, P, ctypes.c_int, I64, P]),
         "orc_num_threads": (ctypes.c_int, []),
+        "orc_loss_scale_update": (None, [P, I32, I64, P, I32, F, F]),
+        "orc_sgd": (None, [P, P, I64, F, P]),
+        "orc_scale_by": (None, [P, ctypes.c_int, I64, F, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -424,3 +427,37 @@ def mlp_step(x, w1, w2, dy, metas, rows_w=None):
 def mlp_metas(hist_len):
     return {"x": Meta(hist_len, E4M3), "w1": Meta(hist_len, E4M3), "h": Meta(hist_len, E4M3),
             "w2": Meta(hist_len, E4M3), "dy": Meta(hist_len, E5M2), "dz": Meta(hist_len, E5M2)}
+
+
+# ------------------------------------------------- loss scaling and SGD ----
+
+class LossScale:
+    """Dynamic loss-scale state: [S, clean iterations, found_inf, S of the last step]."""
+
+    def __init__(self, s0=65536.0, interval=5, backoff=0.5, growth=2.0):
+        self.state = np.array([s0, 0.0, 0.0, s0], dtype=np.float32)
+        self.interval, self.backoff, self.growth = interval, backoff, growth
+
+    def update(self, grad_amaxes):
+        a = _c(np.asarray(grad_amaxes, dtype=np.float32))
+        _load().orc_loss_scale_update(_ptr(a), a.size, 1, _ptr(self.state), self.interval, float(self.backoff),
+                                      float(self.growth))
+
+    @property
+    def found_inf(self):
+        return bool(self.state[2])
+
+
+def sgd(w, g, lr, loss_scale):
+    """In place on float32 w: w -= lr * g / S (skipped after a found_inf step)."""
+    assert w.dtype == np.float32 and w.flags.c_contiguous
+    g = _c(np.asarray(g, dtype=np.float32))
+    _load().orc_sgd(_ptr(w), _ptr(g), w.size, float(np.float32(lr)), _ptr(loss_scale.state))
+
+
+def scale_by(x, s):
+    """round(x * s) in x's element type (the loss-scaled gradient)."""
+    x = _c(x)
+    out = np.empty(x.shape, dtype=x.dtype)
+    _load().orc_scale_by(_ptr(x), _dtype_code(x), x.size, float(np.float32(s)), _ptr(out))
+    return out

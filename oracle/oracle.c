@@ -505,3 +505,63 @@ void orc_gemm_exact(const uint8_t* a, int afmt, const uint8_t* b, int bfmt,
             lo[i * n + j] = (uint64_t)d;
         }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Loss scaling and the fp32 master-weight update.                           */
+/* [MP-KR] "Mixed-Precision Training Iteration": multiply the loss by S,     */
+/* back-propagate, multiply the weight gradients by 1/S, update the fp32     */
+/* master weights.  [MP-KR] dynamic loss scaling: start with a large S; when */
+/* the weight gradients hold Inf or NaN, lower S and skip the update; after  */
+/* N iterations without Inf/NaN, raise S.  The pages leave the constants     */
+/* open; the caller passes them (reading: S0 = 2^16, x1/2, x2 after N = 5).   */
+/* Unscaling happens on the no-overflow path (the extraction's step list     */
+/* puts it under the overflow branch; the iteration list before it orders    */
+/* unscale -> update).                                                       */
+/*                                                                           */
+/* state: [0] S, [1] clean iterations, [2] found_inf of the last step (0/1), */
+/*        [3] the S the last step's gradients carry.                         */
+/* found_inf is read from the amaxes of the step's gradient tensors: the    */
+/* amax propagates Inf and NaN, so a non-finite amax means a non-finite      */
+/* element.                                                                  */
+/* ------------------------------------------------------------------------ */
+
+void orc_loss_scale_update(const float* amaxes, int32_t n, int64_t stride, float* state,
+                           int32_t interval, float backoff, float growth) {
+    int found = 0;
+    for (int32_t i = 0; i < n; ++i)
+        if (!isfinite(amaxes[(int64_t)i * stride])) found = 1;
+    state[3] = state[0];
+    state[2] = (float)found;
+    if (found) {
+        state[0] = state[0] * backoff;
+        state[1] = 0.0f;
+    } else {
+        state[1] = state[1] + 1.0f;
+        if (state[1] >= (float)interval) {
+            state[0] = state[0] * growth;
+            state[1] = 0.0f;
+        }
+    }
+}
+
+/* w <- fl32(w - fl32(lr * fl32(g * fl32(1/S)))), skipped when found_inf. */
+void orc_sgd(float* w, const float* g, int64_t n, float lr, const float* state) {
+    if (state[2] != 0.0f) return;
+    const float inv = 1.0f / state[3];
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const float u = g[i] * inv;
+        const float d = lr * u;
+        w[i] = w[i] - d;
+    }
+}
+
+/* out = round(x * S): the loss-scaled upstream gradient. */
+void orc_scale_by(const void* x, int dtype, int64_t n, float s, void* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const float v = load_elem(x, dtype, i) * s;
+        if (dtype == ORC_F32) ((float*)out)[i] = v;
+        else ((uint16_t*)out)[i] = orc_bf16_from_f32(v);
+    }
+}

@@ -85,6 +85,12 @@ double   orc_gelu(double z);
 double   orc_gelu_grad(double z);
 void     orc_gelu_bwd(const void* dh, const void* z, int dtype, int64_t n, void* dz);
 
+/* ---- loss scaling and SGD on fp32 masters ---- */
+void     orc_loss_scale_update(const float* amaxes, int32_t n, int64_t stride, float* state,
+                               int32_t interval, float backoff, float growth);
+void     orc_sgd(float* w, const float* g, int64_t n, float lr, const float* state);
+void     orc_scale_by(const void* x, int dtype, int64_t n, float s, void* out);
+
 int      orc_num_threads(void);
 
 #ifdef __cplusplus

@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_names():
-    assert L.fp8lin_abi_version() == 1
+    assert L.fp8lin_abi_version() == 2
     assert L.fp8lin_status_name(0) == b"FP8LIN_OK"
     assert L.fp8lin_status_name(2) == b"FP8LIN_ERR_SHAPE"
     assert L.fp8lin_status_name(99) == b"FP8LIN_UNKNOWN_STATUS"
@@ -85,8 +85,8 @@ def test_dequant_validation():
 
 
 def _gemm(m=64, n=64, k=64, a_dt=F.E4M3, b_dt=F.E4M3, d_dt=F.F32, epi=0, aux=None, bias=None, bias_dt=F.F32,
-          d=P(1 << 30), sa=P(1 << 32), sb=P(1 << 33)):
-    return L.fp8_gemm(A16, a_dt, B16, b_dt, m, n, k, sa, sb, bias, bias_dt, epi, d, d_dt, aux, None, None)
+          d=P(1 << 30), sa=P(1 << 32), sb=P(1 << 33), residual=None):
+    return L.fp8_gemm(A16, a_dt, B16, b_dt, m, n, k, sa, sb, bias, bias_dt, epi, d, d_dt, aux, residual, None, None)
 
 
 def test_gemm_validation():
@@ -102,6 +102,15 @@ def test_gemm_validation():
     assert _err(_gemm(d=P((1 << 20) + 8))) == F.ERR_ALIGN
     assert _err(_gemm(d=P((1 << 20) + 16))) == F.ERR_ARG               # d overlaps A
     assert _gemm(m=0) == F.OK
+
+
+def test_gemm_residual_validation():
+    d = 1 << 30
+    assert _err(_gemm(d=P(d), residual=P(d + 16))) == F.ERR_ARG          # partial overlap with d
+    assert _err(_gemm(d=P(d), residual=P(d + 8))) == F.ERR_ALIGN
+    assert _err(_gemm(epi=F.EPI_ACCUMULATE, residual=P(1 << 34))) == F.ERR_ARG
+    assert _err(_gemm(epi=F.EPI_GELU, aux=P(1 << 34), residual=P((1 << 34) + 64))) == F.ERR_ARG
+    assert _gemm(m=0, residual=P(d)) == F.OK                              # in place (residual == d) is allowed
 
 
 def _recipe(**kw):
@@ -128,24 +137,55 @@ def test_linear_validation():
     meta = F._MetaC(1 << 36, (1 << 36) + 4096, (1 << 36) + 8192)
     saved = F._SavedC(1 << 37, 1 << 38, 1 << 39, 1 << 40, 1 << 41)
     fwd = L.fp8_linear_fwd
-    args = [A16, F.F32, B16, F.F32, None, F.F32, 0, C16, F.F32, None, None, ctypes.byref(r), ctypes.byref(meta),
+    args = [A16, F.F32, B16, F.F32, None, F.F32, 0, C16, F.F32, None, None, None, ctypes.byref(r), ctypes.byref(meta),
             ctypes.byref(meta), ctypes.byref(saved), None]
     assert _err(fwd(64, 64, 60, *args)) == F.ERR_SHAPE
     args_acc = list(args)
     args_acc[6] = F.EPI_ACCUMULATE
     assert _err(fwd(64, 64, 64, *args_acc)) == F.ERR_ARG
     no_saved = list(args)
-    no_saved[14] = None
+    no_saved[15] = None
     assert _err(fwd(64, 64, 64, *no_saved)) == F.ERR_NULL
     bwd = L.fp8_linear_bwd
     saved_no_t = F._SavedC(1 << 37, None, 1 << 39, None, 1 << 41)
     assert _err(bwd(64, 64, 64, A16, F.F32, None, None, ctypes.byref(r), ctypes.byref(meta),
-                    ctypes.byref(saved_no_t), B16, C16, P(1 << 42), F.F32, None, 0, None, None, None)) == F.ERR_NULL
+                    ctypes.byref(saved_no_t), B16, C16, P(1 << 42), F.F32, None, None, 0, None, None, None)) == F.ERR_NULL
     assert _err(bwd(64, 64, 64, A16, F.F32, None, P(1 << 42), ctypes.byref(r), ctypes.byref(meta),
-                    ctypes.byref(saved), B16, C16, None, F.F32, None, 0, None, None, None)) == F.ERR_ARG
+                    ctypes.byref(saved), B16, C16, None, F.F32, None, None, 0, None, None, None)) == F.ERR_ARG
+    # a residual gradient without dx
+    assert _err(bwd(64, 64, 64, A16, F.F32, None, None, ctypes.byref(r), ctypes.byref(meta),
+                    ctypes.byref(saved), B16, C16, None, F.F32, P(1 << 42), P(1 << 43), 0, None, None,
+                    None)) == F.ERR_ARG
+    # dx overlapping dy
+    assert _err(bwd(64, 64, 64, A16, F.F32, None, None, ctypes.byref(r), ctypes.byref(meta),
+                    ctypes.byref(saved), B16, C16, P((1 << 20) + 64), F.F32, None, None, 0, None, None,
+                    None)) == F.ERR_ARG
     bad_fmt = _recipe(format=5)
     assert _err(bwd(64, 64, 64, A16, F.F32, None, None, ctypes.byref(bad_fmt), ctypes.byref(meta),
-                    ctypes.byref(saved), B16, C16, None, F.F32, None, 0, None, None, None)) == F.ERR_ARG
+                    ctypes.byref(saved), B16, C16, None, F.F32, None, None, 0, None, None, None)) == F.ERR_ARG
+
+
+def test_loss_scale_and_sgd_validation():
+    st = P(1 << 34)
+    up = L.fp8_loss_scale_update
+    assert _err(up(A16, 0, 1, st, 5, 0.5, 2.0, None)) == F.ERR_SHAPE
+    assert _err(up(A16, 4, 0, st, 5, 0.5, 2.0, None)) == F.ERR_SHAPE
+    assert _err(up(A16, 4, 1, st, 0, 0.5, 2.0, None)) == F.ERR_ARG
+    assert _err(up(A16, 4, 1, st, 5, 1.0, 2.0, None)) == F.ERR_ARG
+    assert _err(up(A16, 4, 1, st, 5, 0.5, 1.0, None)) == F.ERR_ARG
+    assert _err(up(A16, 4, 1, None, 5, 0.5, 2.0, None)) == F.ERR_NULL
+    assert _err(up(A16, 4, 1, P((1 << 20) + 8), 5, 0.5, 2.0, None)) == F.ERR_ARG   # state inside the amaxes
+    ap = L.fp8_loss_scale_apply
+    assert _err(ap(A16, F.E4M3, 16, st, B16, None)) == F.ERR_DTYPE
+    assert _err(ap(A16, F.F32, 16, None, B16, None)) == F.ERR_NULL
+    assert _err(ap(A16, F.F32, 64, st, P((1 << 20) + 16), None)) == F.ERR_ARG      # partial overlap
+    assert ap(A16, F.F32, 0, st, A16, None) == F.OK
+    sgd = L.fp8_sgd_step
+    assert _err(sgd(A16, B16, -1, 0.1, st, None)) == F.ERR_SHAPE
+    assert _err(sgd(A16, None, 16, 0.1, st, None)) == F.ERR_NULL
+    assert _err(sgd(ODD, B16, 16, 0.1, st, None)) == F.ERR_ALIGN
+    assert _err(sgd(A16, P((1 << 20) + 16), 16, 0.1, st, None)) == F.ERR_ARG       # w overlaps g
+    assert sgd(A16, B16, 0, 0.1, st, None) == F.OK
 
 
 def test_timing_toggle():
