@@ -18,6 +18,13 @@ in HBM).  `roofline` is the GEMM kernel: algorithmic flop per launch over its
 average launch time, measured with HIP events around each launch (recorded by
 the library on the launch stream) during a second pass of the same steps.
 `cpu_baseline` times the CPU oracle on a 1024-token slice of the same step.
+
+`layer_step` reports the FP8 transformer-layer training step beside it: the
+QKV, attention-output, FC1 and FC2 linears (hidden 8192, FFN 28672, 8192
+tokens) forward and backward from fp32 master weights, dynamic loss scaling
+and SGD, 20 iterations with the x100 input spike at iteration 10; 12 GEMMs,
+3.63e13 flop per step.  The attention core is not part of it (its output and
+gradient are seeded stand-in inputs).
 """
 import argparse
 import json
@@ -90,6 +97,64 @@ def kernel_breakdown(block, F, torch, steps):
     return out
 
 
+def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
+    """The transformer-layer step: per-iteration times over the run with the
+    spike, then a per-kind kernel breakdown over a few further steps."""
+    import synth
+    from fp8_mixed_precision_reduce_amd.blocks import Fp8TransformerLayer
+    cfg = synth.LAYER
+    inp = synth.layer_inputs(device="cuda")
+    lay = Fp8TransformerLayer(inp["x"], inp["ctx"], inp["g"], inp["dqkv"], inp["wqkv"], inp["wo"], inp["w1"],
+                              inp["w2"], history_len=cfg["history_len"], fast_accum=fast_accum)
+    for k in ("wqkv", "wo", "w1", "w2"):
+        del inp[k]                                        # copied into the layer's master buffer
+    spiked = synth.layer_spike(inp["x"], cfg["spike_factor"])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iterations + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(iterations):
+        lay.step(spiked if i == cfg["spike_iteration"] else None)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per_it = [ev[i].elapsed_time(ev[i + 1]) for i in range(iterations)]
+    state = lay.ls_state.cpu().tolist()
+    F.timing_enable(64 * breakdown_steps)
+    torch.cuda.synchronize()
+    for _ in range(breakdown_steps):
+        lay.step()
+    torch.cuda.synchronize()
+    rec = F.timing_read(64 * breakdown_steps)
+    F.timing_enable(0)
+    kb = {}
+    for kind, ms in rec:
+        n, tot = kb.get(kind, (0, 0.0))
+        kb[kind] = (n + 1, tot + ms)
+    flop = lay.flops_per_step()
+    n_params = lay.master.numel()
+    later = sorted(per_it[2:])
+    mean_ms = sum(per_it[2:]) / len(per_it[2:])
+    n_sgd, t_sgd = kb.get("sgd", (0, 0.0))
+    sgd_ms = t_sgd / n_sgd if n_sgd else float("nan")
+    out = {
+        "workload": "FP8 transformer layer step: QKV, attention-out, FC1, FC2 linears fwd+bwd, hidden 8192, "
+                    "FFN 28672, tokens 8192, fp32 masters + SGD + dynamic loss scaling, x100 spike at "
+                    "iteration 10, history 1024 (attention core: seeded stand-in inputs)",
+        "iterations": iterations,
+        "ms_per_step_mean_2_to_end": round(mean_ms, 4),
+        "ms_per_step_median": round(later[len(later) // 2], 4),
+        "ms_spike_iteration": round(per_it[cfg["spike_iteration"]], 4),
+        "tflops": round(flop / (mean_ms * 1e-3) / 1e12, 2),
+        "flop_per_step": flop,
+        "loss_scale_after": state[0],
+        "kernels_ms_per_step": {k: round(v[1] / breakdown_steps, 4) for k, v in sorted(kb.items())},
+        "sgd": {"params": n_params, "avg_launch_ms": round(sgd_ms, 4),
+                "achieved_gbs": round(12.0 * n_params / (sgd_ms * 1e-3) / 1e9, 1), "peak_gbs": PEAK_HBM_GBS},
+    }
+    del lay, inp, spiked
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(torch, rows=1024):
     """The CPU oracle on a `rows`-token slice of the same step (full weights)."""
     import numpy as np
@@ -116,6 +181,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fast-accum", action="store_true", help="time the fast-accumulation GEMMs as the main value")
+    ap.add_argument("--no-layer", action="store_true", help="skip the transformer-layer step")
     args = ap.parse_args()
     if args.gpus != 1:
         _exit_multi_gpu(args.gpus)
@@ -143,6 +209,8 @@ def main():
         other.step()
     other_ms = time_steps(other, torch, max(3, args.steps // 2))
     del other
+    torch.cuda.empty_cache()
+    layer = None if args.no_layer else layer_leg(F, torch, fast_accum=args.fast_accum)
 
     value = STEP_FLOP / (ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if args.fast_accum else PEAK_F16_TFLOPS
@@ -185,6 +253,8 @@ def main():
         ("exact_accum" if args.fast_accum else "fast_accum"): {
             "ms_per_step": round(other_ms, 4), "tflops": round(STEP_FLOP / (other_ms * 1e-3) / 1e12, 2)},
     }
+    if layer is not None:
+        line["layer_step"] = layer
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch)
     print(json.dumps(line), flush=True)

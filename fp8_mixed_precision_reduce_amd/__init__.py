@@ -25,7 +25,7 @@ F32, BF16, E4M3, E5M2 = 0, 1, 2, 3
 FORMAT_E4M3, FORMAT_HYBRID = 0, 1
 AMAX_MAX = 0
 EPI_GELU, EPI_ACCUMULATE, EPI_FAST_ACCUM = 1, 2, 4
-KIND_NAMES = ["amax", "cast", "cast_transpose", "dequant", "scale_update", "gemm", "dbias", "other"]
+KIND_NAMES = ["amax", "cast", "cast_transpose", "dequant", "scale_update", "gemm", "dbias", "other", "sgd"]
 ABI_VERSION = 2
 
 FUNCTIONS = [

@@ -13,12 +13,18 @@ every part of it in the library's kernels:
   fp8_linear_bwd(dH; W1, Z)    -> GeLU backward fused into the dZ cast, dX (bf16), dW1 (fp32)
   fp8_amax_scale_update(6 tensors)
 
-Page tags: [TE-KR] "Transformer Engine으로 FP8 사용하기" (coniverse.tistory.com).
+Fp8TransformerLayer: the four FP8 linears of a transformer layer (QKV,
+attention output, FC1, FC2) trained from fp32 master weights with dynamic
+loss scaling and SGD; see its docstring for the wiring.
+
+Page tags: [TE-KR] "Transformer Engine으로 FP8 사용하기" (coniverse.tistory.com);
+[MP-KR] "LLM) Mixed-Precision 개념 및 학습 방법 알아보기" (data-newbie.tistory.com);
+[PT-VI] "Các kiểu dữ liệu FP8 gốc của PyTorch" (hotroai.com).
 """
 import torch
 
 from . import (AMAX_MAX, E4M3, E5M2, EPI_GELU, FORMAT_HYBRID, MetaBank, Recipe, Saved, fp8_linear_bwd,
-               fp8_linear_fwd)
+               fp8_linear_fwd, fp8_loss_scale_apply, fp8_loss_scale_update, fp8_sgd_step)
 
 MLP_TENSORS = ("x", "w1", "h", "w2", "dy", "dz")
 
@@ -73,3 +79,126 @@ class Fp8MlpBlock:
         self.forward()
         self.backward()
         self.update()
+
+
+LAYER_TENSORS = ("x", "wqkv", "ctx", "wo", "y1", "w1", "h", "w2", "g_fc2", "g_fc1", "g_o", "g_qkv")
+LAYER_GRADS = ("g_fc2", "g_fc1", "g_o", "g_qkv")
+LAYER_WEIGHTS = ("wqkv", "wo", "w1", "w2")
+
+
+class Fp8TransformerLayer:
+    """One transformer layer's FP8 linears, trained with fp32 masters.
+
+    Wiring (no normalisation layers, which the pages do not name):
+        QKV = X Wqkv^T                       (its consumer, the bf16 attention
+        Y1  = X + ctx Wo^T                    core, is stood in for by the
+        H   = gelu(Y1 W1^T),  Z kept          inputs ctx and dqkv)
+        Y   = Y1 + H W2^T
+    Loss <Y, G> * S, so dY = bf16(G * S); the attention core's gradient enters
+    the QKV linear as bf16(dqkv * S).  Backward:
+        dH, dW2          = bwd FC2(dY)
+        dY1, dW1         = bwd FC1(dH; gelu'(Z)) + dY          (skip path)
+        dctx, dWo        = bwd O(dY1)
+        dX, dWqkv        = bwd QKV(dqkv * S) + dY1             (skip path)
+    Update, all on the device and in this order ([MP-KR] "Mixed-Precision
+    Training Iteration" and its dynamic loss scaling; [PT-VI] training script
+    for the per-step history update after backward):
+        fp8_loss_scale_update from the four gradient amax slots (Inf/NaN ->
+        found_inf, S halves), fp8_amax_scale_update of the twelve metas, then
+        fp8_sgd_step on all masters at once (skipped on found_inf).
+
+    The masters live in one fp32 buffer and their gradients in another, so the
+    SGD step is one launch over all parameters.  x, ctx, g, dqkv are bf16
+    device tensors of the caller; forward(x_in) may take another input of x's
+    shape (the spiked one).  Residual adds happen in the GEMM epilogues.
+    """
+
+    def __init__(self, x, ctx, g, dqkv, wqkv, wo, w1, w2, history_len=1024, lr=2.0 ** -10, loss_scale=2.0 ** 16,
+                 growth_interval=5, fast_accum=False, keep_dz=False, keep_codes=False):
+        m, hid = x.shape
+        ffn = w1.shape[0]
+        assert wqkv.shape == (3 * hid, hid) and wo.shape == (hid, hid) and w1.shape == (ffn, hid)
+        assert w2.shape == (hid, ffn) and ctx.shape == (m, hid) and g.shape == (m, hid) and dqkv.shape == (m, 3 * hid)
+        dev = x.device
+        self.m, self.hidden, self.ffn = m, hid, ffn
+        self.x, self.ctx, self.g, self.dqkv_in = x, ctx, g, dqkv
+        self.lr, self.growth_interval = lr, growth_interval
+        shapes = {"wqkv": (3 * hid, hid), "wo": (hid, hid), "w1": (ffn, hid), "w2": (hid, ffn)}
+        total = sum(a * b for a, b in shapes.values())
+        self.master = torch.empty(total, dtype=torch.float32, device=dev)
+        self.grad = torch.empty(total, dtype=torch.float32, device=dev)
+        self.w, self.dw, off = {}, {}, 0
+        for name, src in zip(LAYER_WEIGHTS, (wqkv, wo, w1, w2)):
+            n = src.numel()
+            self.w[name] = self.master[off:off + n].view(shapes[name])
+            self.w[name].copy_(src)
+            self.dw[name] = self.grad[off:off + n].view(shapes[name])
+            off += n          # every size is a multiple of 256 elements: the views stay 16-byte aligned
+        act = dict(dtype=x.dtype, device=dev)
+        self.qkv = torch.empty(m, 3 * hid, **act)
+        self.y1 = torch.empty(m, hid, **act)
+        self.z = torch.empty(m, ffn, **act)
+        self.h = torch.empty(m, ffn, **act)
+        self.y = torch.empty(m, hid, **act)
+        self.dy = torch.empty(m, hid, **act)
+        self.dh = torch.empty(m, ffn, **act)
+        self.dz = torch.empty(m, ffn, **act) if keep_dz else None
+        self.dy1 = torch.empty(m, hid, **act)
+        self.dctx = torch.empty(m, hid, **act)
+        self.dqkv = torch.empty(m, 3 * hid, **act)
+        self.dx = torch.empty(m, hid, **act)
+        # gradient-code workspaces: one pair reused by the four backward calls in
+        # turn, or (keep_codes, for inspection) one pair per linear
+        u8 = dict(dtype=torch.uint8, device=dev)
+        cols = {"fc2": hid, "fc1": ffn, "o": hid, "qkv": 3 * hid}
+        if keep_codes:
+            self.gws = {k: (torch.empty(m, c, **u8), torch.empty(c, m, **u8)) for k, c in cols.items()}
+        else:
+            wide = max(cols.values())
+            gq, gqt = torch.empty(m * wide, **u8), torch.empty(m * wide, **u8)
+            self.gws = {k: (gq[:m * c].view(m, c), gqt[:m * c].view(c, m)) for k, c in cols.items()}
+        self.saved = {"qkv": Saved(m, 3 * hid, hid, device=dev), "o": Saved(m, hid, hid, device=dev),
+                      "fc1": Saved(m, ffn, hid, device=dev), "fc2": Saved(m, hid, ffn, device=dev)}
+        self.bank = MetaBank([E5M2 if t.startswith("g_") else E4M3 for t in LAYER_TENSORS], history_len, device=dev)
+        self.meta = {name: self.bank.meta(i) for i, name in enumerate(LAYER_TENSORS)}
+        self.recipe = Recipe(FORMAT_HYBRID, history_len, AMAX_MAX, 0, fast_accum)
+        self.ls_state = torch.tensor([loss_scale, 0.0, 0.0, loss_scale], dtype=torch.float32, device=dev)
+        g0 = LAYER_TENSORS.index(LAYER_GRADS[0])
+        assert LAYER_TENSORS[g0:g0 + len(LAYER_GRADS)] == LAYER_GRADS
+        self._grad_amaxes = self.bank.amax_history[g0:, 0]          # n=4 slots, history_len floats apart
+
+    def forward(self, x=None):
+        x = self.x if x is None else x
+        r, mt, sv, w = self.recipe, self.meta, self.saved, self.w
+        fp8_linear_fwd(x, w["wqkv"], self.qkv, r, mt["x"], mt["wqkv"], sv["qkv"])
+        fp8_linear_fwd(self.ctx, w["wo"], self.y1, r, mt["ctx"], mt["wo"], sv["o"], residual=x)
+        fp8_linear_fwd(self.y1, w["w1"], self.h, r, mt["y1"], mt["w1"], sv["fc1"], epilogue=EPI_GELU, y_aux=self.z)
+        fp8_linear_fwd(self.h, w["w2"], self.y, r, mt["h"], mt["w2"], sv["fc2"], residual=self.y1)
+
+    def backward(self):
+        r, mt, sv, dw = self.recipe, self.meta, self.saved, self.dw
+        hid, ffn = self.hidden, self.ffn
+        fp8_loss_scale_apply(self.g, self.ls_state, self.dy)
+        ws = self.gws
+        fp8_linear_bwd(self.dy, ffn, r, mt["g_fc2"], sv["fc2"], *ws["fc2"], dx=self.dh, dw=dw["w2"])
+        fp8_linear_bwd(self.dh, hid, r, mt["g_fc1"], sv["fc1"], *ws["fc1"], dx=self.dy1, dw=dw["w1"],
+                       gelu_z=self.z, dz_out=self.dz, dx_residual=self.dy)
+        fp8_linear_bwd(self.dy1, hid, r, mt["g_o"], sv["o"], *ws["o"], dx=self.dctx, dw=dw["wo"])
+        fp8_loss_scale_apply(self.dqkv_in, self.ls_state, self.dqkv)
+        fp8_linear_bwd(self.dqkv, hid, r, mt["g_qkv"], sv["qkv"], *ws["qkv"], dx=self.dx, dw=dw["wqkv"],
+                       dx_residual=self.dy1)
+
+    def update(self):
+        fp8_loss_scale_update(self._grad_amaxes, self.ls_state, stride=self.bank.history_len, n=len(LAYER_GRADS),
+                              growth_interval=self.growth_interval)
+        self.bank.update(self.recipe)
+        fp8_sgd_step(self.master, self.grad, self.lr, self.ls_state)
+
+    def step(self, x=None):
+        self.forward(x)
+        self.backward()
+        self.update()
+
+    def flops_per_step(self):
+        m, hid, ffn = self.m, self.hidden, self.ffn
+        return 6 * m * (3 * hid * hid + hid * hid + 2 * ffn * hid)

@@ -13,7 +13,7 @@ enum Dtype : int32_t { kF32 = 0, kBF16 = 1, kE4M3 = 2, kE5M2 = 3 };
 
 // Kinds of kernels, as reported by the event timer.
 enum Kind : int32_t { kKindAmax = 0, kKindCast = 1, kKindCastT = 2, kKindDequant = 3,
-                      kKindScaleUpdate = 4, kKindGemm = 5, kKindDbias = 6, kKindOther = 7 };
+                      kKindScaleUpdate = 4, kKindGemm = 5, kKindDbias = 6, kKindOther = 7, kKindSgd = 8 };
 
 // Host side: record events around a launch when timing is enabled.
 void timing_before(int kind, hipStream_t stream);

@@ -114,7 +114,7 @@ hipError_t launch_loss_scale_update(const float* amaxes, int32_t n, int64_t stri
 
 hipError_t launch_sgd(float* w, const float* g, int64_t n, float lr, const float* state, hipStream_t s) {
     if (n == 0) return hipSuccess;
-    timing_before(kKindOther, s);
+    timing_before(kKindSgd, s);
     hipLaunchKernelGGL(k_sgd, dim3(grid_of((n + 3) >> 2)), dim3(kThreads), 0, s, w, g, n, lr, state);
     timing_after(s);
     return hipGetLastError();

@@ -247,10 +247,12 @@ int32_t fp8_dequant(const uint8_t* q, int32_t fp8_dtype, int64_t n, const float*
  *   d          [m][n] of d_dtype (F32 or BF16; ACCUMULATE needs F32)
  *   aux        [m][n] of d_dtype or NULL: y before GeLU (only with GELU)
  *   residual   [m][n] of d_dtype or NULL: added in fp32 after the activation,
- *              before the one rounding to d_dtype (a residual connection around
- *              the layer, [TE-KR] "Transformer Layer 예시").  It may be d
- *              itself (in-place residual add) but must not otherwise overlap d
- *              or aux; not combinable with ACCUMULATE.
+ *              before the one rounding to d_dtype.  This is the residual
+ *              connection of a transformer block, whose branches end in the
+ *              linear layers that [PT-VI]'s training script swaps for FP8 ones
+ *              (a VisionTransformer); the pages do not spell the wiring out.
+ *              It may be d itself (in-place residual add) but must not
+ *              otherwise overlap d or aux; not combinable with ACCUMULATE.
  *   amax_d     device float or NULL: max-merged amax of d as written
  */
 int32_t fp8_gemm(const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_dtype,
@@ -370,7 +372,7 @@ int32_t fp8_sgd_step(float* w, const float* g, int64_t n, float lr, const float*
 enum {
     FP8LIN_KIND_AMAX = 0, FP8LIN_KIND_CAST = 1, FP8LIN_KIND_CAST_TRANSPOSE = 2,
     FP8LIN_KIND_DEQUANT = 3, FP8LIN_KIND_SCALE_UPDATE = 4, FP8LIN_KIND_GEMM = 5,
-    FP8LIN_KIND_DBIAS = 6, FP8LIN_KIND_OTHER = 7
+    FP8LIN_KIND_DBIAS = 6, FP8LIN_KIND_OTHER = 7, FP8LIN_KIND_SGD = 8
 };
 int32_t fp8lin_timing_enable(int32_t capacity);
 int32_t fp8lin_timing_read(int32_t* kinds, float* ms, int32_t max);

@@ -429,6 +429,78 @@ def mlp_metas(hist_len):
             "w2": Meta(hist_len, E4M3), "dy": Meta(hist_len, E5M2), "dz": Meta(hist_len, E5M2)}
 
 
+# ------------------------------------------- transformer layer step ----
+#
+# The four FP8 linears of a transformer layer (QKV, attention output, FC1,
+# FC2) with the fp32 master weights, dynamic loss scaling and SGD.  The pages
+# do not spell out a layer's wiring; this step reads it as the plainest
+# pre-norm-free block: Y1 = X + O(ctx), Y = Y1 + FC2(gelu(FC1(Y1))), where ctx
+# stands in for the bf16 attention core's output (it is an input here, as is
+# the gradient d(QKV) the attention core would return).  All activations and
+# activation gradients are stored in bf16, the weight gradients in fp32.
+
+LAYER_TENSORS = ("x", "wqkv", "ctx", "wo", "y1", "w1", "h", "w2", "g_fc2", "g_fc1", "g_o", "g_qkv")
+LAYER_GRADS = ("g_fc2", "g_fc1", "g_o", "g_qkv")
+LAYER_WEIGHTS = ("wqkv", "wo", "w1", "w2")
+
+
+def layer_metas(hist_len):
+    return {name: Meta(hist_len, E5M2 if name.startswith("g_") else E4M3) for name in LAYER_TENSORS}
+
+
+def add_residual(y64, r):
+    """fp64 GEMM result plus a residual stored as bf16 bits (or fp32)."""
+    r = np.asarray(r)
+    r64 = bf16_to_f64(r) if r.dtype == np.uint16 else r.astype(np.float64)
+    return y64 + r64
+
+
+def layer_step(x, ctx, g, dqkv, masters, metas, loss_scale, lr):
+    """One training step of the FP8 layer: forward, loss-scaled backward, the
+    found-inf check and loss-scale update ([MP-KR] dynamic loss scaling: an
+    Inf/NaN gradient lowers S and skips the update), the delayed-scaling
+    update of all twelve FP8 tensors ([PT-VI]: once per step after backward,
+    before the optimizer), and SGD on the fp32 masters ([MP-KR] "FP32 Master
+    Copy of Weights": the weight gradient is unscaled by 1/S).
+
+    x, ctx, g [m][h] and dqkv [m][3h] are bf16 bits; masters: dict of float32
+    arrays wqkv [3h][h], wo [h][h], w1 [f][h], w2 [h][f], updated in place.
+    The weights are cast from their fp32 masters straight to E4M3.  The loss is
+    <Y, G> * S, so the gradient entering FC2 is dY = bf16(G * S); the stand-in
+    attention-core gradient enters the QKV linear as bf16(dqkv * S).
+    """
+    S = np.float32(loss_scale.state[0])
+    fq = linear_fwd(x, masters["wqkv"], metas["x"], metas["wqkv"])
+    qkv = bf16_from_f64(fq["y"])
+    fo = linear_fwd(ctx, masters["wo"], metas["ctx"], metas["wo"])
+    y1 = bf16_from_f64(add_residual(fo["y"], x))
+    f1 = linear_fwd(y1, masters["w1"], metas["y1"], metas["w1"], gelu_=True)
+    h, z = bf16_from_f64(f1["y"]), bf16_from_f64(f1["pre"])
+    f2 = linear_fwd(h, masters["w2"], metas["h"], metas["w2"])
+    y = bf16_from_f64(add_residual(f2["y"], y1))
+
+    dy = scale_by(g, S)
+    b2 = linear_bwd(dy, f2, metas["g_fc2"])
+    dh = bf16_from_f64(b2["dx"])
+    dz = gelu_bwd(dh, z)
+    b1 = linear_bwd(dz, f1, metas["g_fc1"])
+    dy1 = bf16_from_f64(add_residual(b1["dx"], dy))          # FC branch + the skip path
+    bo = linear_bwd(dy1, fo, metas["g_o"])
+    dctx = bf16_from_f64(bo["dx"])
+    dq = scale_by(dqkv, S)
+    bq = linear_bwd(dq, fq, metas["g_qkv"])
+    dx = bf16_from_f64(add_residual(bq["dx"], dy1))          # QKV branch + the skip path
+
+    grads = {"wqkv": f32_from_f64(bq["dw"]), "wo": f32_from_f64(bo["dw"]), "w1": f32_from_f64(b1["dw"]),
+             "w2": f32_from_f64(b2["dw"])}
+    loss_scale.update([metas[n].hist[0] for n in LAYER_GRADS])
+    update_metas([metas[n] for n in LAYER_TENSORS])
+    for name in LAYER_WEIGHTS:
+        sgd(masters[name], grads[name], lr, loss_scale)
+    return dict(qkv=qkv, y1=y1, h=h, z=z, y=y, dy=dy, dh=dh, dz=dz, dy1=dy1, dctx=dctx, dqkv=dq, dx=dx,
+                grads=grads, fwd=dict(qkv=fq, o=fo, fc1=f1, fc2=f2), bwd=dict(qkv=bq, o=bo, fc1=b1, fc2=b2))
+
+
 # ------------------------------------------------- loss scaling and SGD ----
 
 class LossScale:

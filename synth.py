@@ -16,6 +16,12 @@ Workloads:
              outlier channels scaled x50 (chosen by a seeded permutation); W1 bf16 14336x4096 and
              W2 bf16 4096x14336 ~ N(0, 0.02); dY bf16 8192x4096 ~ N(0,1)
   quant      bf16 16384x16384; row r has magnitude 2^u_r, u_r ~ U[-20, 10], times N(0,1) values
+  layer      tokens 8192 (seq 4096 x batch 2), hidden 8192, FFN 28672; X bf16 N(0,1); fp32 master
+             weights ~ N(0, 0.02): Wqkv 24576x8192, Wo 8192x8192, W1 28672x8192, W2 8192x28672;
+             upstream gradient G bf16 ~ N(0,1) * 2^-20 (the loss is <Y, G> * S); stand-ins for
+             the bf16 attention core: a context tensor ctx bf16 8192x8192 ~ N(0,1) and a
+             gradient d(QKV) bf16 8192x24576 ~ N(0,1) * 2^-20; the spiked input of iteration 10
+             is bf16(fl32(X) * 100)
 """
 import math
 
@@ -98,3 +104,32 @@ def quant_tensor(device="cpu", rows=16384, cols=16384):
     u = uniform((rows, 1), -20.0, 10.0, seed_of(4, 0, 1), device=device)
     x = normal((rows, cols), 1.0, seed_of(4, 0, 0), device=device)
     return (x * torch.exp2(u)).to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- layer ----
+
+LAYER = dict(m=8192, hidden=8192, ffn=28672, history_len=1024, iterations=20, spike_iteration=10,
+             spike_factor=100.0)
+
+
+def layer_inputs(device="cpu", m=8192, hidden=8192, ffn=28672):
+    """dict of X, ctx, G, dqkv (bf16) and the fp32 masters wqkv, wo, w1, w2.
+
+    The same X, G and stand-ins are used at every iteration; only the master
+    weights (updated by SGD) and the scales change from step to step."""
+    bf = torch.bfloat16
+    return dict(
+        x=normal((m, hidden), 1.0, seed_of(5, 0, 0), bf, device),
+        wqkv=normal((3 * hidden, hidden), 0.02, seed_of(5, 0, 1), device=device),
+        wo=normal((hidden, hidden), 0.02, seed_of(5, 0, 2), device=device),
+        w1=normal((ffn, hidden), 0.02, seed_of(5, 0, 3), device=device),
+        w2=normal((hidden, ffn), 0.02, seed_of(5, 0, 4), device=device),
+        g=normal((m, hidden), 2.0 ** -20, seed_of(5, 0, 5), bf, device),
+        ctx=normal((m, hidden), 1.0, seed_of(5, 0, 6), bf, device),
+        dqkv=normal((m, 3 * hidden), 2.0 ** -20, seed_of(5, 0, 7), bf, device),
+    )
+
+
+def layer_spike(x, factor=100.0):
+    """The spiked layer input: bf16(fl32(x) * factor)."""
+    return (x.float() * factor).to(torch.bfloat16)
