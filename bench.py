@@ -19,6 +19,10 @@ average launch time, measured with HIP events around each launch (recorded by
 the library on the launch stream) during a second pass of the same steps.
 `cpu_baseline` times the CPU oracle on a 1024-token slice of the same step.
 
+`quant` times the standalone quantisation kernels on a 2^28-element bf16
+tensor: amax alone, the dual-format amax+cast+transpose, and dequant, in GB/s
+of algorithmic bytes.
+
 `layer_step` reports the FP8 transformer-layer training step beside it: the
 QKV, attention-output, FC1 and FC2 linears (hidden 8192, FFN 28672, 8192
 tokens) forward and backward from fp32 master weights, dynamic loss scaling
@@ -155,6 +159,65 @@ def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
     return out
 
 
+def quant_leg(F, torch, reps=50, first=10):
+    """Standalone quantisation of the 2^28-element bf16 tensor (16384 x 16384,
+    row magnitudes 2^u, u ~ U[-20, 10]), `reps` repetitions on the same tensor:
+    (i) amax alone, (ii) one dual-format cast-transpose (amax fused, E4M3 and
+    E5M2, both layouts) followed by the scale update of the two metas,
+    (iii) dequant of both code tensors back to bf16.  Per-kernel times from
+    the library's launch events; mean (and median) over repetitions
+    `first`..reps-1."""
+    import synth
+    cfg = synth.QUANT
+    rows, cols, L = cfg["rows"], cfg["cols"], cfg["history_len"]
+    n = rows * cols
+    x = synth.quant_tensor(device="cuda")
+    bank = F.MetaBank([F.E4M3, F.E5M2], L)
+    recipe = F.Recipe(F.FORMAT_HYBRID, L, F.AMAX_MAX, 0)
+    slot = torch.zeros(1, dtype=torch.float32, device="cuda")
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    q4, q4t, q5, q5t = (torch.empty(rows, cols, **u8), torch.empty(cols, rows, **u8), torch.empty(rows, cols, **u8),
+                        torch.empty(cols, rows, **u8))
+    out = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda")
+    F.timing_enable(8 * reps)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        F.fp8_amax(x, slot)
+        F.fp8_cast_transpose_dual(x, bank.scale[0:1], bank.scale[1:2], q4, q4t, q5, q5t, bank.amax_history[0, 0:1],
+                                  bank.amax_history[1, 0:1])
+        bank.update(recipe)
+        F.fp8_dequant(q4, F.E4M3, bank.scale_inv[0:1], out)
+        F.fp8_dequant(q5, F.E5M2, bank.scale_inv[1:2], out)
+    torch.cuda.synchronize()
+    rec = F.timing_read(8 * reps)
+    F.timing_enable(0)
+    per = {}
+    for kind, ms in rec:
+        per.setdefault(kind, []).append(ms)
+    per["dequant"] = [a + b for a, b in zip(per["dequant"][0::2], per["dequant"][1::2])]
+
+    def stat(kind, nbytes):
+        v = per[kind][first:]
+        mean = sum(v) / len(v)
+        med = sorted(v)[len(v) // 2]
+        return {"mean_ms": round(mean, 4), "median_ms": round(med, 4), "bytes": nbytes,
+                "achieved_gbs": round(nbytes / (mean * 1e-3) / 1e9, 1),
+                "frac": round(nbytes / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    res = {
+        "workload": "bf16 16384x16384 (2^28 elements), row magnitudes 2^u, u~U[-20,10]; "
+                    f"{reps} repetitions, mean of {first}..{reps - 1}",
+        "amax": stat("amax", 2 * n),
+        "cast_transpose_dual": stat("cast_transpose", (2 + 4) * n),
+        "scale_update": {"mean_ms": round(sum(per["scale_update"][first:]) / (reps - first), 4)},
+        "dequant_both": stat("dequant", 2 * (1 + 2) * n),
+        "peak_gbs": PEAK_HBM_GBS,
+    }
+    del x, q4, q4t, q5, q5t, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(torch, rows=1024):
     """The CPU oracle on a `rows`-token slice of the same step (full weights)."""
     import numpy as np
@@ -182,6 +245,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fast-accum", action="store_true", help="time the fast-accumulation GEMMs as the main value")
     ap.add_argument("--no-layer", action="store_true", help="skip the transformer-layer step")
+    ap.add_argument("--no-quant", action="store_true", help="skip the standalone quantisation kernels")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="first run a plain elementwise copy (torch.neg) of GIB GiB of fp32 three times, as the "
+                         "known-size reference kernel for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         _exit_multi_gpu(args.gpus)
@@ -191,6 +258,16 @@ def main():
     import torch
 
     import fp8_mixed_precision_reduce_amd as F
+
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     block = MlpBlock(F, torch, fast_accum=args.fast_accum)
     for _ in range(args.warmup):
@@ -211,6 +288,7 @@ def main():
     del other
     torch.cuda.empty_cache()
     layer = None if args.no_layer else layer_leg(F, torch, fast_accum=args.fast_accum)
+    quant = None if args.no_quant else quant_leg(F, torch)
 
     value = STEP_FLOP / (ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if args.fast_accum else PEAK_F16_TFLOPS
@@ -255,6 +333,8 @@ def main():
     }
     if layer is not None:
         line["layer_step"] = layer
+    if quant is not None:
+        line["quant"] = quant
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch)
     print(json.dumps(line), flush=True)

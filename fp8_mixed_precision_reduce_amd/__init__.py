@@ -31,6 +31,7 @@ ABI_VERSION = 2
 FUNCTIONS = [
     "fp8lin_abi_version", "fp8lin_last_error", "fp8lin_status_name", "fp8lin_dbias_workspace_bytes",
     "fp8_amax", "fp8_amax_scale_update", "fp8_cast", "fp8_cast_transpose", "fp8_cast_transpose_dgelu",
+    "fp8_cast_transpose_dual",
     "fp8_dequant", "fp8_gemm", "fp8_linear_fwd", "fp8_linear_bwd", "fp8_loss_scale_update",
     "fp8_loss_scale_apply", "fp8_sgd_step", "fp8lin_timing_enable", "fp8lin_timing_read",
 ]
@@ -77,6 +78,7 @@ def _load():
         "fp8_cast": (I32, [P, I32, I64, I32, P, P, P, P]),
         "fp8_cast_transpose": (I32, [P, I32, I64, I64, I32, P, P, P, P, P, P, P]),
         "fp8_cast_transpose_dgelu": (I32, [P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, P]),
+        "fp8_cast_transpose_dual": (I32, [P, I32, I64, I64, P, P, P, P, P, P, P, P, P]),
         "fp8_dequant": (I32, [P, I32, I64, P, P, I32, P]),
         "fp8_gemm": (I32, [P, I32, P, I32, I64, I64, I64, P, P, P, I32, I32, P, I32, P, P, P, P]),
         "fp8_linear_fwd": (I32, [I64, I64, I64, P, I32, P, I32, P, I32, I32, P, I32, P, P, P,
@@ -221,6 +223,14 @@ def fp8_cast_transpose_dgelu(dh, z, fmt, scale, q, q_t, amax_slot=None, dbias=No
     rows, cols = dh.shape
     _check(_lib.fp8_cast_transpose_dgelu(_p(dh), _p(z), _dt(dh), rows, cols, fmt, _p(scale), _p(q), _p(q_t),
                                          _p(amax_slot), _p(dbias), _p(dbias_ws), _p(dz_out), _stream(stream)))
+
+
+def fp8_cast_transpose_dual(x, scale_e4m3, scale_e5m2, q_e4m3=None, q_e4m3_t=None, q_e5m2=None, q_e5m2_t=None,
+                            amax_slot_e4m3=None, amax_slot_e5m2=None, stream=None):
+    rows, cols = x.shape
+    _check(_lib.fp8_cast_transpose_dual(_p(x), _dt(x), rows, cols, _p(scale_e4m3), _p(q_e4m3), _p(q_e4m3_t),
+                                        _p(amax_slot_e4m3), _p(scale_e5m2), _p(q_e5m2), _p(q_e5m2_t),
+                                        _p(amax_slot_e5m2), _stream(stream)))
 
 
 def fp8_dequant(q, fmt, scale_inv, out, stream=None):

@@ -13,7 +13,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/fp8lin.h"
+#include "fp8lin.h"
 #include "common.h"
 
 namespace fp8lin {
@@ -257,6 +257,30 @@ int32_t fp8_cast_transpose_dgelu(const void* dh, const void* z, int32_t x_dtype,
     return hip_status(launch_cast_transpose(dh, z, x_dtype, rows, cols, fp8_dtype, scale, q, q_t, amax_slot, dbias,
                                             dbias_ws, dz_out, as_stream(stream)),
                       "fp8_cast_transpose_dgelu");
+}
+
+int32_t fp8_cast_transpose_dual(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, const float* scale_e4m3,
+                                uint8_t* q_e4m3, uint8_t* q_e4m3_t, float* amax_slot_e4m3, const float* scale_e5m2,
+                                uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* amax_slot_e5m2, void* stream) {
+    const char* fn = "fp8_cast_transpose_dual";
+    int32_t v;
+    // each format's outputs are checked as one cast-transpose, then the two sets against each other
+    if ((v = check_ct(fn, x, nullptr, x_dtype, rows, cols, FP8LIN_E4M3, scale_e4m3, q_e4m3, q_e4m3_t,
+                      amax_slot_e4m3, nullptr, nullptr, nullptr, false)))
+        return v;
+    if ((v = check_ct(fn, x, nullptr, x_dtype, rows, cols, FP8LIN_E5M2, scale_e5m2, q_e5m2, q_e5m2_t,
+                      amax_slot_e5m2, nullptr, nullptr, nullptr, false)))
+        return v;
+    const int64_t n = rows * cols;
+    if (n > 0 && !q_e4m3 && !q_e4m3_t && !q_e5m2 && !q_e5m2_t) return fail(FP8LIN_ERR_NULL, "%s: no output", fn);
+    const uint8_t* a[2] = {q_e4m3, q_e4m3_t};
+    const uint8_t* b[2] = {q_e5m2, q_e5m2_t};
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j)
+            if (overlap(a[i], n, b[j], n)) return fail(FP8LIN_ERR_ARG, "%s: outputs overlap", fn);
+    return hip_status(launch_cast_transpose_dual(x, x_dtype, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, amax_slot_e4m3,
+                                                 scale_e5m2, q_e5m2, q_e5m2_t, amax_slot_e5m2, as_stream(stream)),
+                      fn);
 }
 
 // ---------------------------------------------------------------- dequant

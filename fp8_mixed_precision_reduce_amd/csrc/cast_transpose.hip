@@ -20,6 +20,10 @@
 // the tensor or entirely outside.  At most 2048 workgroups run; each loops
 // over tiles, so the amax merge costs one (usually skipped) atomic per
 // workgroup rather than one per tile.
+//
+// The dual-format variant encodes every element with two scales, to E4M3 and
+// to E5M2, from one read of the input: four outputs (both formats, both
+// layouts) through two LDS tiles, and one amax for both tensors' metas.
 #include "common.h"
 
 namespace fp8lin {
@@ -68,19 +72,29 @@ __device__ __forceinline__ void store16(void* base, int64_t idx, const float v[1
     }
 }
 
-template <int DT, int FMT, bool DGELU, bool DBIAS>
+// Outputs of the dual-format variant (its second format is always E5M2).
+struct Second {
+    const float* scale;
+    uint8_t* q;
+    uint8_t* qt;
+    float* amax_slot;
+};
+
+template <int DT, int FMT, bool DGELU, bool DBIAS, bool DUAL>
 __global__ void __launch_bounds__(kThreads)
 k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t rows, int64_t cols,
                  int64_t tiles_c, const float* __restrict__ scale_p, uint8_t* __restrict__ q,
                  uint8_t* __restrict__ qt, float* amax_slot, float* __restrict__ dbias_ws,
-                 void* __restrict__ dz_out) {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kTile];
+                 void* __restrict__ dz_out, Second sec) {
+    constexpr int NF = DUAL ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) uint8_t tile[NF * kTile * kTile];
     __shared__ uint32_t red[kThreads / 64];
 
     const int t = threadIdx.x;
     const int cc = t & 7;        // 16-column chunk within the tile
     const int rr = t >> 3;       // 0..31
     const float s = *scale_p;
+    const float s2 = DUAL ? *sec.scale : 0.0f;
     const int64_t ntiles = ((rows + kTile - 1) / kTile) * tiles_c;
     uint32_t m = 0;
     for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
@@ -143,30 +157,42 @@ k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t
             m = max(m, abs_bits(v[p][j]));
             if constexpr (DBIAS) csum[j] += v[p][j];
         }
+        const int lds = lrow * kTile + ((cc ^ ((lrow >> 4) & 7)) << 4);
         const uint4 codes = scale_enc16<FMT>(v[p], s);
         if (q && col_ok && row < rows) *reinterpret_cast<uint4*>(q + row * cols + col) = codes;
-        if (qt) *reinterpret_cast<uint4*>(tile + lrow * kTile + ((cc ^ ((lrow >> 4) & 7)) << 4)) = codes;
+        if (qt) *reinterpret_cast<uint4*>(tile + lds) = codes;
+        if constexpr (DUAL) {
+            const uint4 c2 = scale_enc16<kE5M2>(v[p], s2);
+            if (sec.q && col_ok && row < rows) *reinterpret_cast<uint4*>(sec.q + row * cols + col) = c2;
+            if (sec.qt) *reinterpret_cast<uint4*>(tile + kTile * kTile + lds) = c2;
+        }
     }
     __syncthreads();
 
-    // Transposed write: 128 output rows (input columns) x 8 strips of 16 bytes.
+    // Transposed write: 128 output rows (input columns) x 8 strips of 16 bytes,
+    // per format.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (!qt) break;
-        const int idx = t + kThreads * i;
-        const int rc = idx & 7;                 // 16-row strip 0..7
-        const int oc = idx >> 3;                // output row within the tile (input column)
-        const int64_t orow = c0 + oc, ocol = r0 + rc * 16;
-        const int colp = (((oc >> 4) ^ rc) << 4) | (oc & 15);   // swizzled byte column of strip rc
-        uint32_t w[4];
+    for (int f = 0; f < NF; ++f) {
+        uint8_t* const qtf = f == 0 ? qt : sec.qt;
+        const uint8_t* const tf = tile + f * kTile * kTile;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint8_t* src = tile + (rc * 16 + 4 * j) * kTile + colp;
-            w[j] = (uint32_t)src[0] | ((uint32_t)src[kTile] << 8) | ((uint32_t)src[2 * kTile] << 16) |
-                   ((uint32_t)src[3 * kTile] << 24);
+        for (int i = 0; i < 4; ++i) {
+            if (!qtf) break;
+            const int idx = t + kThreads * i;
+            const int rc = idx & 7;                 // 16-row strip 0..7
+            const int oc = idx >> 3;                // output row within the tile (input column)
+            const int64_t orow = c0 + oc, ocol = r0 + rc * 16;
+            const int colp = (((oc >> 4) ^ rc) << 4) | (oc & 15);   // swizzled byte column of strip rc
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint8_t* src = tf + (rc * 16 + 4 * j) * kTile + colp;
+                w[j] = (uint32_t)src[0] | ((uint32_t)src[kTile] << 8) | ((uint32_t)src[2 * kTile] << 16) |
+                       ((uint32_t)src[3 * kTile] << 24);
+            }
+            if (orow < cols && ocol < rows)
+                *reinterpret_cast<uint4*>(qtf + orow * rows + ocol) = make_uint4(w[0], w[1], w[2], w[3]);
         }
-        if (orow < cols && ocol < rows)
-            *reinterpret_cast<uint4*>(qt + orow * rows + ocol) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 
     if constexpr (DBIAS) {
@@ -186,6 +212,12 @@ k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t
     __syncthreads();             // the LDS tile is rewritten by the next tile
     }
     if (amax_slot) block_amax_merge(m, amax_slot, red);
+    if constexpr (DUAL) {
+        if (sec.amax_slot) {
+            __syncthreads();     // red[] is reused
+            block_amax_merge(m, sec.amax_slot, red);
+        }
+    }
 }
 
 // dbias[c] = sum over row tiles of the partials, in row-tile order.
@@ -205,18 +237,30 @@ hipError_t launch_dt_fmt(const void* x, const void* z, int64_t rows, int64_t col
     const int64_t ntiles = tiles_r * tiles_c;
     const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
     const bool dgelu = z != nullptr, dbias = dbias_ws != nullptr;
+    const Second none{nullptr, nullptr, nullptr, nullptr};
     if (!dgelu && !dbias)
-        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out);
+        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false>), grid, block, 0, s, x, z, rows, cols,
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none);
     else if (!dgelu)
-        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, true>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out);
+        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, true, false>), grid, block, 0, s, x, z, rows, cols,
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none);
     else if (!dbias)
-        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out);
+        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, false, false>), grid, block, 0, s, x, z, rows, cols,
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none);
     else
-        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, true>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out);
+        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, true, false>), grid, block, 0, s, x, z, rows, cols,
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dual_dt(const void* x, int64_t rows, int64_t cols, const float* scale4, uint8_t* q4,
+                          uint8_t* q4t, float* slot4, const Second& sec, hipStream_t s) {
+    const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
+    const int64_t ntiles = tiles_r * tiles_c;
+    const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
+    hipLaunchKernelGGL((k_cast_transpose<DT, kE4M3, false, false, true>), grid, block, 0, s, x, nullptr, rows,
+                       cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec);
     return hipGetLastError();
 }
 
@@ -249,6 +293,19 @@ hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_
                        dbias);
     timing_after(s);
     return hipGetLastError();
+}
+
+hipError_t launch_cast_transpose_dual(const void* x, int dtype, int64_t rows, int64_t cols, const float* scale_e4m3,
+                                      uint8_t* q_e4m3, uint8_t* q_e4m3_t, float* slot_e4m3, const float* scale_e5m2,
+                                      uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* slot_e5m2, hipStream_t s) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const Second sec{scale_e5m2, q_e5m2, q_e5m2_t, slot_e5m2};
+    timing_before(kKindCastT, s);
+    const hipError_t e = dtype == kF32
+        ? launch_dual_dt<kF32>(x, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, slot_e4m3, sec, s)
+        : launch_dual_dt<kBF16>(x, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, slot_e4m3, sec, s);
+    timing_after(s);
+    return e;
 }
 
 }  // namespace fp8lin

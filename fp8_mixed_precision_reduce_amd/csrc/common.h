@@ -34,6 +34,9 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_t rows, int64_t cols,
                                  int fmt, const float* scale, uint8_t* q, uint8_t* qt, float* slot,
                                  float* dbias, float* dbias_ws, void* dz_out, hipStream_t s);
+hipError_t launch_cast_transpose_dual(const void* x, int dtype, int64_t rows, int64_t cols, const float* scale_e4m3,
+                                      uint8_t* q_e4m3, uint8_t* q_e4m3_t, float* slot_e4m3, const float* scale_e5m2,
+                                      uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* slot_e5m2, hipStream_t s);
 int64_t cast_transpose_dbias_ws_bytes(int64_t rows, int64_t cols);
 hipError_t launch_gemm(const uint8_t* a, int afmt, const uint8_t* b, int bfmt, int64_t m, int64_t n,
                        int64_t k, const float* sinv_a, const float* sinv_b, const void* bias,

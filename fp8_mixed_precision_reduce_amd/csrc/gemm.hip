@@ -38,9 +38,12 @@
 // of k per fragment: the exact path splits them into two f16 MFMAs (bytes
 // 0-7 and 8-15; A and B use the same split, so the k order inside an MFMA is
 // only permuted), the fast path reads 32 bytes per 64-k MFMA.  Fragments of
-// the next k block are read before the current block's MFMAs are issued, and
-// the next stage's DMA instructions are spread over the k blocks so that no
-// burst of them stalls the wave's MFMA issue.
+// the next k block are read before the current block's MFMAs are issued.  The
+// two LDS stages are separate arrays and the exact path's k loop is unrolled
+// by two, so the compiler sees that a stage's fragment reads never alias the
+// DMA into the other stage and inserts no wait for that DMA before them; the
+// exact path issues the whole next-stage DMA at the start of a stage (the
+// longest lead), the fast path spreads it over the k blocks.
 // The MFMA takes the B tile as
 // its first operand, so each lane's accumulators run along n: four
 // consecutive outputs of one row, written with one 16-byte (fp32) or 8-byte
@@ -150,7 +153,13 @@ template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST>
 __global__ void __launch_bounds__(64 * WM * WN, (WM * WN * MB * NB >= 64 ? (WM * WN) / 4 : 2))
 k_gemm(GemmParams p) {
     using C = TileCfg<WM, WN, MB, NB>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+    // The two stages are separate arrays, and the k loop is unrolled by two so
+    // that every LDS access names its stage statically: the compiler can then
+    // see that the fragment reads of one stage never alias the DMA into the
+    // other, and does not wait for that DMA before each read (the explicit
+    // wait and barrier at the end of each stage order the two).
+    __shared__ __attribute__((aligned(16))) uint8_t smem0[C::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t smem1[C::STAGE];
     __shared__ uint32_t red[C::WAVES];
 
     int tm, tn;
@@ -175,8 +184,7 @@ k_gemm(GemmParams p) {
     // row = 8 (w + W i) + l / 8, i.e. it loads logical chunk (l % 8) ^ swz(row).
     const int lrow = lane >> 3, lpc = lane & 7;
     // DMA wave-instruction q of a stage: q < A_DMA fills A rows, the rest B rows.
-    auto dma_part = [&](int kt, int stage, int q0, int q1) {
-        uint8_t* sa = smem + stage * C::STAGE;
+    auto dma_part = [&](int kt, uint8_t* sa, int q0, int q1) {
         uint8_t* sb = sa + C::BM * kBK;
         const uint32_t k0 = (uint32_t)kt * kBK;
 #pragma unroll
@@ -203,14 +211,16 @@ k_gemm(GemmParams p) {
 
     const int nk = (int)((K + kBK - 1) / kBK);
     if (nk > 0) {
-        dma_part(0, 0, 0, NDMA);
+        dma_part(0, smem0, 0, NDMA);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
-    for (int kt = 0; kt < nk; ++kt) {
-        const int stage = kt & 1;
-        const bool more = kt + 1 < nk;     // the next stage's DMA is spread over this stage's k blocks
-        const uint8_t* sa = smem + stage * C::STAGE;
+    // One stage: multiply the tile in `cur` while the DMA of stage kt + 1 fills `nxt`.
+    auto stage_step = [&](int kt, const uint8_t* cur, uint8_t* nxt) {
+        // the next stage's DMA: the fast path spreads it over the k blocks, the
+        // exact path (whose reads no longer wait for it) issues it all at once
+        const bool more = kt + 1 < nk;
+        const uint8_t* sa = cur;
         const uint8_t* sb = sa + C::BM * kBK;
         if constexpr (FAST) {
             // 64-k blocks: lane group g holds k = 64 kb + 32 g .. +31 (chunks 4 kb + 2 g, +1).
@@ -243,7 +253,7 @@ k_gemm(GemmParams p) {
                     bf[j] = v8i{(int)blo[j].x, (int)blo[j].y, (int)blo[j].z, (int)blo[j].w,
                                 (int)bhi[j].x, (int)bhi[j].y, (int)bhi[j].z, (int)bhi[j].w};
                 if (kb + 1 < kBK / 64) rd(kb + 1);
-                if (more) dma_part(kt + 1, stage ^ 1, kb * NDMA / (kBK / 64), (kb + 1) * NDMA / (kBK / 64));
+                if (more) dma_part(kt + 1, nxt, kb * NDMA / (kBK / 64), (kb + 1) * NDMA / (kBK / 64));
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -279,7 +289,7 @@ k_gemm(GemmParams p) {
                     b1[j] = dec8_f16<BF>(make_uint2(br[j].z, br[j].w));
                 }
                 if (kb + 1 < kBK / 32) rd(kb + 1);
-                if (more) dma_part(kt + 1, stage ^ 1, kb * NDMA / (kBK / 32), (kb + 1) * NDMA / (kBK / 32));
+                if (more && kb == 0) dma_part(kt + 1, nxt, 0, NDMA);
                 // all first halves, then all second halves: no two adjacent MFMAs
                 // accumulate into the same registers
 #pragma unroll
@@ -296,6 +306,16 @@ k_gemm(GemmParams p) {
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    if constexpr (FAST) {
+        // one body with a run-time stage: the fast tiles hold 256 accumulator
+        // registers, and a second copy of the body would spill
+        for (int kt = 0; kt < nk; ++kt) stage_step(kt, kt & 1 ? smem1 : smem0, kt & 1 ? smem0 : smem1);
+    } else {
+        for (int kt = 0; kt < nk; kt += 2) {
+            stage_step(kt, smem0, smem1);
+            if (kt + 1 < nk) stage_step(kt + 1, smem1, smem0);
+        }
     }
 
     // ---------------------------------------------------------------- epilogue

@@ -220,6 +220,24 @@ int32_t fp8_cast_transpose_dgelu(const void* dh, const void* z, int32_t x_dtype,
                                  void* dz_out, void* stream);
 
 /*
+ * fp8_cast_transpose_dual -- one read of x, cast with two scales to both
+ * formats, each written row-major and transposed: the quantisation of a tensor
+ * whose E4M3 and E5M2 copies are both wanted (e.g. a tensor used in the forward
+ * pass and as a gradient operand).  [TE-KR] "Introduction to FP8" (the two
+ * formats and their roles) and "FP8 자동변환(Autocasting)" (cast with amax);
+ * [PT-VI] (the scaled cast of a tensor to either float8 type).
+ *   x            [rows][cols] of x_dtype (F32 or BF16); rows, cols multiples of 16
+ *   scale_e4m3, scale_e5m2   device floats
+ *   q_e4m3 [rows][cols], q_e4m3_t [cols][rows], q_e5m2, q_e5m2_t: codes, each
+ *                may be NULL (at least one given); no two may overlap
+ *   amax_slot_e4m3, amax_slot_e5m2   device floats or NULL: both get amax(x)
+ */
+int32_t fp8_cast_transpose_dual(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                                const float* scale_e4m3, uint8_t* q_e4m3, uint8_t* q_e4m3_t, float* amax_slot_e4m3,
+                                const float* scale_e5m2, uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* amax_slot_e5m2,
+                                void* stream);
+
+/*
  * fp8_dequant -- out = round_out(fl32(dec_F(q) * scale_inv)) elementwise.
  * [TE-RU] section 3: after the FP8 operation the factor is divided back out;
  * [TE-KR] "정확도(Precision)": the FP8-representable copy of a tensor.

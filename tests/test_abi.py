@@ -77,6 +77,20 @@ def test_cast_transpose_validation():
     assert _err(dg(A16, None, F.BF16, 32, 32, F.E5M2, B16, C16, P(1 << 30), None, None, None, None, None)) == F.ERR_NULL
 
 
+def test_cast_transpose_dual_validation():
+    du = L.fp8_cast_transpose_dual
+    s4, s5 = P(1 << 34), P((1 << 34) + 64)
+    q4, q4t, q5, q5t = P(1 << 36), P(1 << 37), P(1 << 38), P(1 << 39)
+    assert _err(du(A16, F.BF16, 17, 32, s4, q4, q4t, None, s5, q5, q5t, None, None)) == F.ERR_SHAPE
+    assert _err(du(A16, F.E4M3, 32, 32, s4, q4, q4t, None, s5, q5, q5t, None, None)) == F.ERR_DTYPE
+    assert _err(du(A16, F.BF16, 32, 32, s4, None, None, None, s5, None, None, None, None)) == F.ERR_NULL
+    assert _err(du(A16, F.BF16, 32, 32, None, q4, q4t, None, s5, q5, q5t, None, None)) == F.ERR_NULL
+    assert _err(du(A16, F.BF16, 32, 32, s4, q4, q4t, None, s5, P((1 << 36) + 512), q5t, None, None)) == F.ERR_ARG
+    assert _err(du(A16, F.BF16, 32, 32, s4, q4, q4t, None, s5, q5, P((1 << 20) + 64), None, None)) == F.ERR_ARG
+    assert _err(du(A16, F.BF16, 32, 32, s4, q4, ODD, None, s5, q5, q5t, None, None)) == F.ERR_ALIGN
+    assert du(A16, F.BF16, 0, 32, s4, q4, q4t, None, s5, q5, q5t, None, None) == F.OK
+
+
 def test_dequant_validation():
     assert _err(L.fp8_dequant(A16, F.BF16, 16, B16, C16, F.F32, None)) == F.ERR_DTYPE
     assert _err(L.fp8_dequant(A16, F.E4M3, 16, B16, C16, F.E5M2, None)) == F.ERR_DTYPE

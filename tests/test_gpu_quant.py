@@ -10,7 +10,7 @@ import torch
 
 import fp8_mixed_precision_reduce_amd as F
 import synth
-from helpers import assert_bits_equal, np_of
+from helpers import assert_bits_equal, dev, np_of
 
 pytestmark = pytest.mark.gpu
 
@@ -48,3 +48,71 @@ def test_quant_tensor_full_size(oracle):
     # except the tensor's own maximum, nothing is NaN
     codes = np_of(q)
     assert not np.any((codes & 0x7F) == 0x7F)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_cast_transpose_dual_small_ragged(oracle, dtype):
+    """One read, both formats, both layouts: every output equals the
+    single-format oracle cast with that format's scale; the outputs the
+    caller leaves NULL are not written; both amax slots get amax(x)."""
+    rows, cols = 272, 400
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn(rows, cols, generator=g) * torch.exp2(torch.randint(-12, 12, (rows, 1), generator=g))).to(dtype)
+    X = np_of(x)
+    s4, s5 = np.float32(3.5), np.float32(1.0 / 3.0)
+    xd = x.cuda()
+    sd4, sd5 = dev(np.array([s4])), dev(np.array([s5]))
+    outs = [torch.full((rows, cols), 0xA5, dtype=torch.uint8, device="cuda"),
+            torch.full((cols, rows), 0xA5, dtype=torch.uint8, device="cuda"),
+            torch.full((rows, cols), 0xA5, dtype=torch.uint8, device="cuda"),
+            torch.full((cols, rows), 0xA5, dtype=torch.uint8, device="cuda")]
+    slots = torch.zeros(2, dtype=torch.float32, device="cuda")
+    w4, w4t = oracle.cast_transpose(X, 0, s4)
+    w5, w5t = oracle.cast_transpose(X, 1, s5)
+    want = [w4, w4t, w5, w5t]
+    for mask in (0b1111, 0b0101, 0b1010, 0b0001, 0b1000):
+        for o in outs:
+            o.fill_(0xA5)
+        slots.zero_()
+        use = [o if mask >> i & 1 else None for i, o in enumerate(outs)]
+        F.fp8_cast_transpose_dual(xd, sd4, sd5, *use, amax_slot_e4m3=slots[0:1], amax_slot_e5m2=slots[1:2])
+        for i in range(4):
+            got = np_of(outs[i])
+            if mask >> i & 1:
+                assert_bits_equal(got, want[i], f"mask {mask:04b} output {i}")
+            else:
+                assert np.all(got == 0xA5), f"mask {mask:04b}: output {i} written"
+        a = oracle.amax(X)
+        assert_bits_equal(np_of(slots), np.array([a, a], dtype=np.float32), f"mask {mask:04b} amax")
+
+
+def test_cast_transpose_dual_full_size(oracle):
+    """The 2^28-element tensor through the dual-format kernel with the scales a
+    first update of its two metas gives; all four outputs bit-exact."""
+    rows = cols = 16384
+    L = 1024
+    x = synth.quant_tensor(device="cuda")
+    X = np_of(x)
+    bank = F.MetaBank([F.E4M3, F.E5M2], L)
+    recipe = F.Recipe(F.FORMAT_HYBRID, L, F.AMAX_MAX, 0)
+    F.fp8_amax(x, bank.amax_history[0, 0:1])
+    F.fp8_amax(x, bank.amax_history[1, 0:1])
+    bank.update(recipe)
+    om = [oracle.Meta(L, 0), oracle.Meta(L, 1)]
+    for m in om:
+        m.record(X)
+    oracle.update_metas(om)
+    assert_bits_equal(np_of(bank.scale), np.array([om[0].scale, om[1].scale]), "scales")
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    q4, q4t, q5, q5t = (torch.empty(rows, cols, **u8), torch.empty(cols, rows, **u8), torch.empty(rows, cols, **u8),
+                        torch.empty(cols, rows, **u8))
+    F.fp8_cast_transpose_dual(x, bank.scale[0:1], bank.scale[1:2], q4, q4t, q5, q5t, bank.amax_history[0, 0:1],
+                              bank.amax_history[1, 0:1])
+    for fmt, q, qt in ((0, q4, q4t), (1, q5, q5t)):
+        wq, wqt = oracle.cast_transpose(X, fmt, om[fmt].scale)
+        assert_bits_equal(np_of(q), wq, f"fmt {fmt} q")
+        del wq
+        assert_bits_equal(np_of(qt), wqt, f"fmt {fmt} q^T")
+        del wqt
+    a = oracle.amax(X)
+    assert_bits_equal(np_of(bank.amax_history[:, 0]), np.array([a, a], dtype=np.float32), "amax slots")
