@@ -75,7 +75,7 @@ void timing_before(int kind, hipStream_t stream) {
     if (g_timer.capacity == 0) return;
     std::lock_guard<std::mutex> lk(g_timer.mu);
     if (g_timer.used >= g_timer.capacity) return;
-    hipEventRecord(g_timer.ev[2 * g_timer.used], stream);
+    if (hipEventRecord(g_timer.ev[2 * g_timer.used], stream) != hipSuccess) return;   // launch goes untimed
     g_timer.pending_kind = kind;
 }
 
@@ -83,7 +83,10 @@ void timing_after(hipStream_t stream) {
     if (g_timer.capacity == 0) return;
     std::lock_guard<std::mutex> lk(g_timer.mu);
     if (g_timer.pending_kind < 0) return;
-    hipEventRecord(g_timer.ev[2 * g_timer.used + 1], stream);
+    if (hipEventRecord(g_timer.ev[2 * g_timer.used + 1], stream) != hipSuccess) {
+        g_timer.pending_kind = -1;
+        return;
+    }
     g_timer.kinds[g_timer.used] = g_timer.pending_kind;
     g_timer.pending_kind = -1;
     ++g_timer.used;
@@ -119,7 +122,7 @@ int64_t fp8lin_dbias_workspace_bytes(int64_t rows, int64_t cols) {
 
 int32_t fp8lin_timing_enable(int32_t capacity) {
     std::lock_guard<std::mutex> lk(g_timer.mu);
-    for (hipEvent_t e : g_timer.ev) hipEventDestroy(e);
+    for (hipEvent_t e : g_timer.ev) (void)hipEventDestroy(e);
     g_timer.ev.clear();
     g_timer.kinds.clear();
     g_timer.used = 0;
@@ -144,9 +147,10 @@ int32_t fp8lin_timing_read(int32_t* kinds, float* ms, int32_t max) {
     std::lock_guard<std::mutex> lk(g_timer.mu);
     const int32_t n = g_timer.used < max ? g_timer.used : max;
     for (int32_t i = 0; i < n; ++i) {
-        hipEventSynchronize(g_timer.ev[2 * i + 1]);
-        float t = 0.0f;
-        hipEventElapsedTime(&t, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]);
+        float t = -1.0f;                // -1: the events could not be read
+        if (hipEventSynchronize(g_timer.ev[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&t, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]) != hipSuccess)
+            t = -1.0f;
         if (kinds) kinds[i] = g_timer.kinds[i];
         if (ms) ms[i] = t;
     }

@@ -115,6 +115,12 @@ __device__ __forceinline__ void dec4(uint32_t w, float out[4]) {
     out[0] = lo.x; out[1] = lo.y; out[2] = hi.x; out[3] = hi.y;
 }
 
+// Global wave index and wave count of a 1-D launch.
+__device__ __forceinline__ int64_t wave_id() {
+    return (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+}
+__device__ __forceinline__ int64_t wave_count() { return (int64_t)gridDim.x * (blockDim.x >> 6); }
+
 // |x| as an unsigned bit pattern: the amax statistic compares these.
 __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 

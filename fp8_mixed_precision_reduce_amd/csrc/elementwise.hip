@@ -6,12 +6,14 @@
 // section 3 (scale before rounding, inverse scale after the GEMM), [PT-VI]
 // training script (one history/scale update per step after backward).
 //
-// Layout: flat tensors, 16-byte aligned.  A thread owns 16 consecutive
-// elements per iteration (one 16-byte FP8 store; 32 or 64 bytes of input), a
-// grid-stride loop covers the tensor with two chunks in flight per thread, and
-// the element tail (n % 16) is handled one element per thread.  amax is an
-// unsigned max over |x| bit patterns: DPP within the wave, LDS across waves,
-// one atomic per workgroup.
+// Layout: flat tensors, 16-byte aligned.  A lane owns one 16-byte vector per
+// step (8 bf16 or 4 fp32 inputs; for dequant the codes of one 16-byte output
+// vector), the 64 lanes of a wave own 64 consecutive vectors so every memory
+// instruction covers one contiguous KiB, four steps are in flight per lane,
+// and waves stride over the tensor; the element tail that does not fill a
+// vector is handled one element per thread.  amax is an unsigned max over |x|
+// bit patterns: DPP within the wave, LDS across waves, one atomic per
+// workgroup.
 #include "common.h"
 
 namespace fp8lin {
@@ -19,42 +21,91 @@ namespace {
 
 constexpr int kThreads = 256;
 
-int grid_for(int64_t chunks) {
-    // Enough workgroups to cover every CU several times, not more than the chunks need.
-    const int64_t want = (chunks + 2 * kThreads - 1) / (2 * kThreads);
-    const int64_t cap = 256 * 8;
-    return (int)(want < 1 ? 1 : (want > cap ? cap : want));
-}
-
 template <int DT>
 __device__ __forceinline__ float load1(const void* x, int64_t i) {
     if constexpr (DT == kF32) return static_cast<const float*>(x)[i];
     return bf16_to_f32(static_cast<const uint16_t*>(x)[i]);
 }
 
+// Streaming layout: a lane owns one 16-byte vector of the input per step and
+// the 64 lanes of a wave own 64 consecutive vectors (1 KiB), so every load and
+// store instruction covers a contiguous range; kU steps are in flight.
+constexpr int kU = 4;
+
+template <int DT> struct InVec { static constexpr int elems = DT == kF32 ? 4 : 8; };  // elements per 16 B
+
+// Largest |x| bit pattern among the elements of one 16-byte vector.
+template <int DT>
+__device__ __forceinline__ uint32_t absmax_vec(uint4 w) {
+    if constexpr (DT == kF32) {
+        return max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu));
+    } else {
+        const uint32_t hi = max(max(w.x & 0x7FFF0000u, w.y & 0x7FFF0000u), max(w.z & 0x7FFF0000u, w.w & 0x7FFF0000u));
+        const uint32_t lo = max(max((w.x << 16) & 0x7FFF0000u, (w.y << 16) & 0x7FFF0000u),
+                                max((w.z << 16) & 0x7FFF0000u, (w.w << 16) & 0x7FFF0000u));
+        return max(hi, lo);
+    }
+}
+
+// The elements of one 16-byte vector as fp32.
+template <int DT>
+__device__ __forceinline__ void unpack_vec(uint4 w, float v[InVec<DT>::elems]) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    if constexpr (DT == kF32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(u[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(u[j] << 16);
+            v[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+        }
+    }
+}
+
+int grid_vec(int64_t nvec) {
+    const int64_t per_wg = (int64_t)(kThreads / 64) * 64 * kU;
+    const int64_t want = (nvec + per_wg - 1) / per_wg;
+    const int64_t cap = 256 * 8;
+    return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
 template <int DT>
 __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, int64_t n, float* slot) {
     __shared__ uint32_t red[kThreads / 64];
-    const int64_t chunks = n >> 4;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    constexpr int E = InVec<DT>::elems;
+    const uint4* p = static_cast<const uint4*>(x);
+    const int64_t nvec = n / E;
+    const int lane = threadIdx.x & 63;
     uint32_t m = 0;
-    int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (; c + stride < chunks; c += 2 * stride) {
-        float a[16], b[16];
-        load16<DT>(x, c << 4, a);
-        load16<DT>(x, (c + stride) << 4, b);
+    for (int64_t b = wave_id() * (64 * kU); b < nvec; b += wave_count() * (64 * kU)) {
+        uint4 v[kU];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) m = max(m, max(abs_bits(a[j]), abs_bits(b[j])));
-    }
-    if (c < chunks) {
-        float a[16];
-        load16<DT>(x, c << 4, a);
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            v[u] = i < nvec ? p[i] : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) m = max(m, abs_bits(a[j]));
+        for (int u = 0; u < kU; ++u) m = max(m, absmax_vec<DT>(v[u]));
     }
-    for (int64_t i = (chunks << 4) + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+    for (int64_t i = nvec * E + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
         m = max(m, abs_bits(load1<DT>(x, i)));
     block_amax_merge(m, slot, red);
+}
+
+// Codes of the E elements of one vector, written with one store (4 or 8 bytes).
+template <int DT, int FMT>
+__device__ __forceinline__ void cast_vec(uint4 w, float s, uint8_t* q, int64_t i, uint32_t& m) {
+    constexpr int E = InVec<DT>::elems;
+    float v[E];
+    unpack_vec<DT>(w, v);
+    m = max(m, absmax_vec<DT>(w));
+    if constexpr (E == 4) {
+        reinterpret_cast<uint32_t*>(q)[i] = enc4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+    } else {
+        reinterpret_cast<uint2*>(q)[i] = make_uint2(enc4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s),
+                                                    enc4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s));
+    }
 }
 
 template <int DT, int FMT>
@@ -62,28 +113,26 @@ __global__ void __launch_bounds__(kThreads)
 k_cast(const void* __restrict__ x, int64_t n, const float* __restrict__ scale_p, uint8_t* __restrict__ q,
        float* slot) {
     __shared__ uint32_t red[kThreads / 64];
+    constexpr int E = InVec<DT>::elems;
     const float s = *scale_p;
-    const int64_t chunks = n >> 4;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const uint4* p = static_cast<const uint4*>(x);
+    const int64_t nvec = n / E;
+    const int lane = threadIdx.x & 63;
     uint32_t m = 0;
-    int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (; c + stride < chunks; c += 2 * stride) {
-        float a[16], b[16];
-        load16<DT>(x, c << 4, a);
-        load16<DT>(x, (c + stride) << 4, b);
+    for (int64_t b = wave_id() * (64 * kU); b < nvec; b += wave_count() * (64 * kU)) {
+        uint4 v[kU];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) m = max(m, max(abs_bits(a[j]), abs_bits(b[j])));
-        reinterpret_cast<uint4*>(q)[c] = scale_enc16<FMT>(a, s);
-        reinterpret_cast<uint4*>(q)[c + stride] = scale_enc16<FMT>(b, s);
-    }
-    if (c < chunks) {
-        float a[16];
-        load16<DT>(x, c << 4, a);
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            v[u] = i < nvec ? p[i] : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) m = max(m, abs_bits(a[j]));
-        reinterpret_cast<uint4*>(q)[c] = scale_enc16<FMT>(a, s);
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            if (i < nvec) cast_vec<DT, FMT>(v[u], s, q, i, m);
+        }
     }
-    for (int64_t i = (chunks << 4) + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+    for (int64_t i = nvec * E + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
         const float v = load1<DT>(x, i);
         m = max(m, abs_bits(v));
         q[i] = (uint8_t)(enc4<FMT>(v * s, 0.0f, 0.0f, 0.0f) & 0xFFu);
@@ -91,42 +140,42 @@ k_cast(const void* __restrict__ x, int64_t n, const float* __restrict__ scale_p,
     if (slot) block_amax_merge(m, slot, red);
 }
 
+// Dequant: a lane decodes the codes of one 16-byte output vector per step (8
+// codes to bf16, 4 codes to fp32).
 template <int FMT, int OUT>
 __global__ void __launch_bounds__(kThreads)
 k_dequant(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ sinv_p, void* __restrict__ out) {
+    constexpr int E = OUT == kF32 ? 4 : 8;
     const float si = *sinv_p;
-    const int64_t chunks = n >> 4;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    auto emit = [&](int64_t c, uint4 w) {
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-        float v[16];
+    const int64_t nvec = n / E;
+    const int lane = threadIdx.x & 63;
+    uint4* o = static_cast<uint4*>(out);
+    for (int64_t b = wave_id() * (64 * kU); b < nvec; b += wave_count() * (64 * kU)) {
+        uint2 w[kU];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dec4<FMT>(ws[j], v + 4 * j);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = v[j] * si;
-        if constexpr (OUT == kF32) {
-            uint4* o = reinterpret_cast<uint4*>(static_cast<float*>(out) + (c << 4));
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = make_uint4(__float_as_uint(v[4 * j]), __float_as_uint(v[4 * j + 1]),
-                                  __float_as_uint(v[4 * j + 2]), __float_as_uint(v[4 * j + 3]));
-        } else {
-            uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + (c << 4));
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                o[j] = make_uint4(pack_bf16x2(v[8 * j], v[8 * j + 1]), pack_bf16x2(v[8 * j + 2], v[8 * j + 3]),
-                                  pack_bf16x2(v[8 * j + 4], v[8 * j + 5]), pack_bf16x2(v[8 * j + 6], v[8 * j + 7]));
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            if constexpr (E == 8) w[u] = i < nvec ? reinterpret_cast<const uint2*>(q)[i] : make_uint2(0, 0);
+            else w[u] = make_uint2(i < nvec ? reinterpret_cast<const uint32_t*>(q)[i] : 0u, 0u);
         }
-    };
-    int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (; c + stride < chunks; c += 2 * stride) {
-        const uint4 w0 = reinterpret_cast<const uint4*>(q)[c];
-        const uint4 w1 = reinterpret_cast<const uint4*>(q)[c + stride];
-        emit(c, w0);
-        emit(c + stride, w1);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            if (i >= nvec) continue;
+            float v[8];
+            dec4<FMT>(w[u].x, v);
+            if constexpr (E == 8) dec4<FMT>(w[u].y, v + 4);
+#pragma unroll
+            for (int j = 0; j < E; ++j) v[j] = v[j] * si;
+            if constexpr (E == 4)
+                o[i] = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                  __float_as_uint(v[3]));
+            else
+                o[i] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                  pack_bf16x2(v[6], v[7]));
+        }
     }
-    if (c < chunks) emit(c, reinterpret_cast<const uint4*>(q)[c]);
-    for (int64_t i = (chunks << 4) + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+    for (int64_t i = nvec * E + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
         float v[4];
         dec4<FMT>((uint32_t)q[i], v);
         const float r = v[0] * si;
@@ -211,7 +260,7 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
 
 hipError_t launch_amax(const void* x, int dtype, int64_t n, float* slot, hipStream_t s) {
     if (n == 0) return hipSuccess;
-    const int g = grid_for((n + 15) >> 4);
+    const int g = grid_vec(n / (dtype == kF32 ? 4 : 8));
     timing_before(kKindAmax, s);
     if (dtype == kF32) hipLaunchKernelGGL(k_amax<kF32>, dim3(g), dim3(kThreads), 0, s, x, n, slot);
     else hipLaunchKernelGGL(k_amax<kBF16>, dim3(g), dim3(kThreads), 0, s, x, n, slot);
@@ -222,7 +271,7 @@ hipError_t launch_amax(const void* x, int dtype, int64_t n, float* slot, hipStre
 hipError_t launch_cast(const void* x, int dtype, int64_t n, int fmt, const float* scale, uint8_t* q,
                        float* slot, hipStream_t s) {
     if (n == 0) return hipSuccess;
-    const int g = grid_for((n + 15) >> 4);
+    const int g = grid_vec(n / (dtype == kF32 ? 4 : 8));
     timing_before(kKindCast, s);
     if (dtype == kF32 && fmt == kE4M3)
         hipLaunchKernelGGL((k_cast<kF32, kE4M3>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot);
@@ -239,7 +288,7 @@ hipError_t launch_cast(const void* x, int dtype, int64_t n, int fmt, const float
 hipError_t launch_dequant(const uint8_t* q, int fmt, int64_t n, const float* sinv, void* out, int out_dtype,
                           hipStream_t s) {
     if (n == 0) return hipSuccess;
-    const int g = grid_for((n + 15) >> 4);
+    const int g = grid_vec(n / (out_dtype == kF32 ? 4 : 8));
     timing_before(kKindDequant, s);
     if (fmt == kE4M3 && out_dtype == kF32)
         hipLaunchKernelGGL((k_dequant<kE4M3, kF32>), dim3(g), dim3(kThreads), 0, s, q, n, sinv, out);

@@ -62,7 +62,6 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;
-constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kEpiFastAccum = 4;
@@ -263,8 +262,12 @@ k_gemm(GemmParams p) {
             }
         } else {
             // 32-k blocks: lane group g holds k = 32 kb + 16 g .. +15 (chunk 2 kb + g);
-            // bytes 0-7 feed the first f16 MFMA, bytes 8-15 the second.
+            // bytes 0-7 feed the first f16 MFMA ("h1"), bytes 8-15 the second ("h2").
+            // Software pipeline: the h2 converts of block kb run beside its h1
+            // MFMAs, and the h1 converts of block kb + 1 beside its h2 MFMAs, so
+            // a wave keeps the matrix core and the VALU busy at the same time.
             uint4 ar[MB], br[NB];
+            v8h a0[MB], a1[MB], b0[NB], b1[NB];
             auto rd = [&](int kb) {
                 const int c = kb * 2 + g;
 #pragma unroll
@@ -274,34 +277,57 @@ k_gemm(GemmParams p) {
                 for (int j = 0; j < NB; ++j)
                     br[j] = *reinterpret_cast<const uint4*>(sb + lds_off(wn * NB * 32 + j * 32 + r32, c));
             };
+            auto cvt_h1 = [&]() {
+#pragma unroll
+                for (int i = 0; i < MB; ++i) a0[i] = dec8_f16<AF>(make_uint2(ar[i].x, ar[i].y));
+#pragma unroll
+                for (int j = 0; j < NB; ++j) b0[j] = dec8_f16<BF>(make_uint2(br[j].x, br[j].y));
+            };
+            auto cvt_h2 = [&]() {
+#pragma unroll
+                for (int i = 0; i < MB; ++i) a1[i] = dec8_f16<AF>(make_uint2(ar[i].z, ar[i].w));
+#pragma unroll
+                for (int j = 0; j < NB; ++j) b1[j] = dec8_f16<BF>(make_uint2(br[j].z, br[j].w));
+            };
+            constexpr int NMF = MB * NB;              // MFMAs per half block
+            constexpr int NCV = 4 * (MB + NB);        // converts per half block
             rd(0);
+            cvt_h1();
 #pragma unroll
             for (int kb = 0; kb < kBK / 32; ++kb) {
-                v8h a0[MB], a1[MB], b0[NB], b1[NB];
-#pragma unroll
-                for (int i = 0; i < MB; ++i) {
-                    a0[i] = dec8_f16<AF>(make_uint2(ar[i].x, ar[i].y));
-                    a1[i] = dec8_f16<AF>(make_uint2(ar[i].z, ar[i].w));
-                }
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    b0[j] = dec8_f16<BF>(make_uint2(br[j].x, br[j].y));
-                    b1[j] = dec8_f16<BF>(make_uint2(br[j].z, br[j].w));
-                }
-                if (kb + 1 < kBK / 32) rd(kb + 1);
-                if (more && kb == 0) dma_part(kt + 1, nxt, 0, NDMA);
-                // all first halves, then all second halves: no two adjacent MFMAs
-                // accumulate into the same registers
+                cvt_h2();
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
                     for (int j = 0; j < NB; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b0[j], a0[i], acc[i][j], 0, 0, 0);
+                // one MFMA, then a share of the converts, repeated
+#pragma unroll
+                for (int q = 0; q < NMF; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, (NCV + NMF - 1) / NMF, 0);
+                }
+                if (more && kb == 0) dma_part(kt + 1, nxt, 0, NDMA);
+                if (kb + 1 < kBK / 32) {
+                    rd(kb + 1);
+                    cvt_h1();
+                }
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
                     for (int j = 0; j < NB; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b1[j], a1[i], acc[i][j], 0, 0, 0);
+                if (kb + 1 < kBK / 32) {
+                    // the next block's fragment reads first, two MFMAs to cover
+                    // their latency, then MFMAs and its h1 converts interleaved
+                    __builtin_amdgcn_sched_group_barrier(0x100, MB + NB, 1);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+#pragma unroll
+                    for (int q = 2; q < NMF; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(0x002, (NCV + NMF - 3) / (NMF - 2), 1);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                    }
+                }
             }
         }
         __builtin_amdgcn_s_waitcnt(0);

@@ -43,23 +43,43 @@ k_loss_scale_update(const float* __restrict__ amaxes, int32_t n, int64_t stride,
     }
 }
 
+// Streaming layout as in the elementwise kernels: a lane owns one 16-byte
+// vector per step, a wave 64 consecutive vectors, kU steps in flight.
+constexpr int kU = 4;
+
 // w <- w - lr * (g * (1/S)), three roundings, skipped when found_inf.
 __global__ void __launch_bounds__(kThreads)
 k_sgd(float* __restrict__ w, const float* __restrict__ g, int64_t n, float lr, const float* __restrict__ state) {
     if (state[2] != 0.0f) return;
     const float inv = __fdiv_rn(1.0f, state[3]);
     const int64_t n4 = n >> 2;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
-        float4 wv = reinterpret_cast<float4*>(w)[i];
-        const float4 gv = reinterpret_cast<const float4*>(g)[i];
-        wv.x = wv.x - lr * (gv.x * inv);
-        wv.y = wv.y - lr * (gv.y * inv);
-        wv.z = wv.z - lr * (gv.z * inv);
-        wv.w = wv.w - lr * (gv.w * inv);
-        reinterpret_cast<float4*>(w)[i] = wv;
+    float4* w4 = reinterpret_cast<float4*>(w);
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    const int lane = threadIdx.x & 63;
+    for (int64_t b = wave_id() * (64 * kU); b < n4; b += wave_count() * (64 * kU)) {
+        float4 wv[kU], gv[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            if (i < n4) {
+                wv[u] = w4[i];
+                gv[u] = g4[i];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            if (i < n4) {
+                float4 r = wv[u];
+                r.x = r.x - lr * (gv[u].x * inv);
+                r.y = r.y - lr * (gv[u].y * inv);
+                r.z = r.z - lr * (gv[u].z * inv);
+                r.w = r.w - lr * (gv[u].w * inv);
+                w4[i] = r;
+            }
+        }
     }
-    for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+    for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
         w[i] = w[i] - lr * (g[i] * inv);
 }
 
@@ -67,37 +87,48 @@ k_sgd(float* __restrict__ w, const float* __restrict__ g, int64_t n, float lr, c
 template <int DT>
 __global__ void __launch_bounds__(kThreads)
 k_scale_by(const void* __restrict__ x, int64_t n, const float* __restrict__ state, void* __restrict__ out) {
+    constexpr int E = DT == kF32 ? 4 : 8;          // elements per 16-byte vector
     const float s = state[0];
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    if constexpr (DT == kF32) {
-        const int64_t n4 = n >> 2;
-        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
-            float4 v = reinterpret_cast<const float4*>(x)[i];
-            v.x *= s; v.y *= s; v.z *= s; v.w *= s;
-            reinterpret_cast<float4*>(out)[i] = v;
+    const int64_t nv = n / E;
+    const uint4* xv = static_cast<const uint4*>(x);
+    uint4* ov = static_cast<uint4*>(out);
+    const int lane = threadIdx.x & 63;
+    for (int64_t b = wave_id() * (64 * kU); b < nv; b += wave_count() * (64 * kU)) {
+        uint4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            v[u] = i < nv ? xv[i] : make_uint4(0, 0, 0, 0);
         }
-        for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
-            static_cast<float*>(out)[i] = static_cast<const float*>(x)[i] * s;
-    } else {
-        const int64_t n8 = n >> 3;
-        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n8; i += stride) {
-            const uint4 u = reinterpret_cast<const uint4*>(x)[i];
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            if (i >= nv) continue;
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
             uint32_t o[4];
 #pragma unroll
-            for (int h = 0; h < 4; ++h)
-                o[h] = pack_bf16x2(__uint_as_float(w[h] << 16) * s, __uint_as_float(w[h] & 0xFFFF0000u) * s);
-            reinterpret_cast<uint4*>(out)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+            for (int h = 0; h < 4; ++h) {
+                if constexpr (DT == kF32) o[h] = __float_as_uint(__uint_as_float(w[h]) * s);
+                else o[h] = pack_bf16x2(__uint_as_float(w[h] << 16) * s, __uint_as_float(w[h] & 0xFFFF0000u) * s);
+            }
+            ov[i] = make_uint4(o[0], o[1], o[2], o[3]);
         }
-        for (int64_t i = (n8 << 3) + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+    }
+    for (int64_t i = nv * E + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
+        if constexpr (DT == kF32) {
+            static_cast<float*>(out)[i] = static_cast<const float*>(x)[i] * s;
+        } else {
             const float v = bf16_to_f32(static_cast<const uint16_t*>(x)[i]) * s;
             static_cast<uint16_t*>(out)[i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
         }
     }
 }
 
-int grid_of(int64_t work) {
-    const int64_t want = (work + kThreads - 1) / kThreads;
+// Workgroups for `nvec` 16-byte vectors: one step of kU vectors per lane, at
+// most 8 workgroups per CU.
+int grid_of(int64_t nvec) {
+    const int64_t per_wg = (int64_t)kThreads * kU;
+    const int64_t want = (nvec + per_wg - 1) / per_wg;
     return (int)(want < 1 ? 1 : (want > 256 * 8 ? 256 * 8 : want));
 }
 
@@ -115,7 +146,7 @@ hipError_t launch_loss_scale_update(const float* amaxes, int32_t n, int64_t stri
 hipError_t launch_sgd(float* w, const float* g, int64_t n, float lr, const float* state, hipStream_t s) {
     if (n == 0) return hipSuccess;
     timing_before(kKindSgd, s);
-    hipLaunchKernelGGL(k_sgd, dim3(grid_of((n + 3) >> 2)), dim3(kThreads), 0, s, w, g, n, lr, state);
+    hipLaunchKernelGGL(k_sgd, dim3(grid_of(n >> 2)), dim3(kThreads), 0, s, w, g, n, lr, state);
     timing_after(s);
     return hipGetLastError();
 }
@@ -124,9 +155,9 @@ hipError_t launch_scale_by(const void* x, int dtype, int64_t n, const float* sta
     if (n == 0) return hipSuccess;
     timing_before(kKindOther, s);
     if (dtype == kF32)
-        hipLaunchKernelGGL(k_scale_by<kF32>, dim3(grid_of((n + 3) >> 2)), dim3(kThreads), 0, s, x, n, state, out);
+        hipLaunchKernelGGL(k_scale_by<kF32>, dim3(grid_of(n >> 2)), dim3(kThreads), 0, s, x, n, state, out);
     else
-        hipLaunchKernelGGL(k_scale_by<kBF16>, dim3(grid_of((n + 7) >> 3)), dim3(kThreads), 0, s, x, n, state, out);
+        hipLaunchKernelGGL(k_scale_by<kBF16>, dim3(grid_of(n >> 3)), dim3(kThreads), 0, s, x, n, state, out);
     timing_after(s);
     return hipGetLastError();
 }

@@ -384,8 +384,8 @@ int32_t fp8_sgd_step(float* w, const float* g, int64_t n, float lr, const float*
  * pair of HIP events around each of its next `capacity` kernel launches
  * (0 disables and frees the events).  fp8lin_timing_read waits for the
  * recorded events and returns, for up to `max` launches, the kernel kind
- * (FP8LIN_KIND_*) and the elapsed milliseconds; it returns the count and
- * resets the record.  Events are host-side objects; no device memory is used.
+ * (FP8LIN_KIND_*) and the elapsed milliseconds (-1 where the events could not
+ * be read); it returns the count and resets the record.  Events are host-side objects; no device memory is used.
  */
 enum {
     FP8LIN_KIND_AMAX = 0, FP8LIN_KIND_CAST = 1, FP8LIN_KIND_CAST_TRANSPOSE = 2,
