@@ -6,20 +6,27 @@
 // (the second GEMM operand enters transposed).
 //
 // One workgroup (256 threads, 4 waves) owns a 128 x 128 tile of the
-// [rows][cols] input.  Load phase: thread t reads 16 consecutive columns of
-// rows (t/8) + 32p, p = 0..3 (all loads issued before any use), merges |x|
-// into its amax, encodes, writes the 16 codes to q with one 16-byte store and
-// to an LDS tile [128][128] with one 16-byte LDS store; the 16-byte chunk of
-// LDS row r is stored at chunk position chunk ^ ((r >> 4) & 7).  Transpose
-// phase: lane l takes the 16-row strip l & 7 of output row (input column)
-// l >> 3, reads that column's 16 bytes one by one (the swizzle spreads the 8
-// strips of a wave over 8 bank groups, so the byte reads are conflict-free),
-// packs them and writes one 16-byte store; 8 consecutive lanes thereby write
-// the 128 contiguous bytes this tile contributes to one q_t row.  Rows and
-// cols are multiples of 16, so a 16-element chunk is either entirely inside
-// the tensor or entirely outside.  At most 2048 workgroups run; each loops
-// over tiles, so the amax merge costs one (usually skipped) atomic per
-// workgroup rather than one per tile.
+// [rows][cols] input and loops over tiles (at most 2048 workgroups run, so the
+// amax merge costs one, usually skipped, atomic per workgroup).
+//
+// Load phase: the tile is read as 16-byte vectors (8 bf16 or 4 fp32
+// elements); thread t owns vector column t % V of rows t / V + (256 / V) p
+// (V vectors per tile row), so each load instruction of a wave covers whole
+// 256- or 512-byte row segments.  Every load of the tile (and of z for the
+// GeLU backward) is issued before any is used.  Each vector's codes go to q
+// with one 8- or 4-byte store and to an LDS tile [128][128] bytes.
+//
+// Transpose phase: thread t owns input columns 4 cg .. 4 cg + 3 (cg = t / 8)
+// of the 16-row strip s = t % 8: it reads one 4-byte LDS word from each of the
+// strip's 16 rows, transposes the 16 x 4 bytes with byte permutes (4 x 4
+// blocks, 8 permutes each) and writes four 16-byte vectors, one to each of
+// the four q_t rows; the 8 lanes of a column group write the 128 contiguous
+// bytes the tile contributes to a q_t row.  LDS word w of row r is stored at
+// word w ^ (((r >> 5) & 3) << 3), which spreads the four strips a half-wave
+// reads over distinct banks.
+//
+// Rows and cols are multiples of 16, so a 16-row strip or a 4-column group is
+// either entirely inside the tensor or entirely outside.
 //
 // The dual-format variant encodes every element with two scales, to E4M3 and
 // to E5M2, from one read of the input: four outputs (both formats, both
@@ -33,43 +40,61 @@ constexpr int kTile = 128;
 constexpr int kThreads = 256;
 constexpr int64_t kMaxGrid = 256 * 8;     // workgroups loop over tiles beyond this
 
-// 16 elements from their raw 16-byte words (4 words of f32 or 2 of bf16).
+template <int DT> struct CtVec {
+    static constexpr int E = DT == kF32 ? 4 : 8;       // elements per 16-byte vector
+    static constexpr int V = kTile / E;                // vectors per tile row
+    static constexpr int RS = kThreads / V;            // rows between a thread's vectors
+    static constexpr int NP = kTile / RS;              // vectors per thread
+};
+
+// The elements of one 16-byte vector as fp32.
 template <int DT>
-__device__ __forceinline__ void unpack16(const uint4* w, float v[16]) {
+__device__ __forceinline__ void unpack_vec(uint4 w, float v[CtVec<DT>::E]) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
     if constexpr (DT == kF32) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v[4 * j + 0] = __uint_as_float(w[j].x); v[4 * j + 1] = __uint_as_float(w[j].y);
-            v[4 * j + 2] = __uint_as_float(w[j].z); v[4 * j + 3] = __uint_as_float(w[j].w);
-        }
+        for (int j = 0; j < 4; ++j) v[j] = __uint_as_float(u[j]);
     } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t u[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                v[8 * j + 2 * h + 0] = __uint_as_float(u[h] << 16);
-                v[8 * j + 2 * h + 1] = __uint_as_float(u[h] & 0xFFFF0000u);
-            }
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(u[j] << 16);
+            v[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
         }
     }
 }
 
 template <int DT>
-__device__ __forceinline__ void store16(void* base, int64_t idx, const float v[16]) {
-    if constexpr (DT == kF32) {
-        uint4* p = reinterpret_cast<uint4*>(static_cast<float*>(base) + idx);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            p[j] = make_uint4(__float_as_uint(v[4 * j]), __float_as_uint(v[4 * j + 1]),
-                              __float_as_uint(v[4 * j + 2]), __float_as_uint(v[4 * j + 3]));
-    } else {
-        uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            p[j] = make_uint4(pack_bf16x2(v[8 * j], v[8 * j + 1]), pack_bf16x2(v[8 * j + 2], v[8 * j + 3]),
-                              pack_bf16x2(v[8 * j + 4], v[8 * j + 5]), pack_bf16x2(v[8 * j + 6], v[8 * j + 7]));
-    }
+__device__ __forceinline__ uint4 pack_vec(const float v[CtVec<DT>::E]) {
+    if constexpr (DT == kF32)
+        return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+    else
+        return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                          pack_bf16x2(v[6], v[7]));
+}
+
+// Codes of one vector: 4 codes in a word, or 8 codes in two words.
+template <int FMT, int E>
+__device__ __forceinline__ uint2 enc_vec(const float v[E], float s) {
+    const uint32_t lo = enc4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+    if constexpr (E == 4) return make_uint2(lo, 0u);
+    else return make_uint2(lo, enc4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s));
+}
+
+// Byte offset in the LDS tile of the 4-byte word `w` (0..31) of tile row `r`.
+__device__ __forceinline__ int lds_word(int r, int w) { return r * kTile + ((w ^ (((r >> 5) & 3) << 3)) << 2); }
+
+// 4 x 4 byte transpose: a..d are four rows of four bytes; c0..c3 are the four
+// columns (byte i of column j = byte j of row i).
+__device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t& c0,
+                                             uint32_t& c1, uint32_t& c2, uint32_t& c3) {
+    const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+    const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+    const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u);   // c0 d0 c1 d1
+    const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u);   // c2 d2 c3 d3
+    c0 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);             // a0 b0 c0 d0
+    c1 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);             // a1 b1 c1 d1
+    c2 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
+    c3 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
 }
 
 // Outputs of the dual-format variant (its second format is always E5M2).
@@ -86,130 +111,134 @@ k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t
                  int64_t tiles_c, const float* __restrict__ scale_p, uint8_t* __restrict__ q,
                  uint8_t* __restrict__ qt, float* amax_slot, float* __restrict__ dbias_ws,
                  void* __restrict__ dz_out, Second sec) {
+    using C = CtVec<DT>;
+    constexpr int E = C::E, NP = C::NP;
     constexpr int NF = DUAL ? 2 : 1;
     __shared__ __attribute__((aligned(16))) uint8_t tile[NF * kTile * kTile];
     __shared__ uint32_t red[kThreads / 64];
 
     const int t = threadIdx.x;
-    const int cc = t & 7;        // 16-column chunk within the tile
-    const int rr = t >> 3;       // 0..31
+    const int vc = t % C::V;          // vector column in the tile
+    const int r_first = t / C::V;     // first tile row; then every C::RS rows
+    const int cg = t >> 3, strip = t & 7;   // transpose phase
     const float s = *scale_p;
     const float s2 = DUAL ? *sec.scale : 0.0f;
     const int64_t ntiles = ((rows + kTile - 1) / kTile) * tiles_c;
     uint32_t m = 0;
     for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
-    const int64_t tr = tile_id / tiles_c, tc = tile_id % tiles_c;
-    const int64_t r0 = tr * kTile, c0 = tc * kTile;
-    const int64_t col = c0 + cc * 16;
-    const bool col_ok = col < cols;
+        const int64_t tr = tile_id / tiles_c, tc = tile_id % tiles_c;
+        const int64_t r0 = tr * kTile, c0 = tc * kTile;
+        const int64_t col = c0 + vc * E;
+        const bool col_ok = col < cols;
 
-    // Issue every load of the tile (and of z for the GeLU backward) before
-    // touching any of them, then unpack.
-    constexpr int NV = DT == kF32 ? 4 : 2;              // 16-byte loads per 16 elements
-    uint4 rv[4][NV], rz[DGELU ? 4 : 1][NV];
+        uint4 rv[NP], rz[DGELU ? NP : 1];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int64_t row = r0 + rr + 32 * p;
-        const bool ok = col_ok && row < rows;
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) +
-                                                          (row * cols + col) * (DT == kF32 ? 4 : 2));
-#pragma unroll
-        for (int j = 0; j < NV; ++j) rv[p][j] = ok ? src[j] : make_uint4(0, 0, 0, 0);
-    }
-    if constexpr (DGELU) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int64_t row = r0 + rr + 32 * p;
+        for (int p = 0; p < NP; ++p) {
+            const int64_t row = r0 + r_first + C::RS * p;
             const bool ok = col_ok && row < rows;
-            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(z) +
-                                                              (row * cols + col) * (DT == kF32 ? 4 : 2));
-#pragma unroll
-            for (int j = 0; j < NV; ++j) rz[p][j] = ok ? src[j] : make_uint4(0, 0, 0, 0);
+            rv[p] = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) +
+                                                         (row * cols + col) * (DT == kF32 ? 4 : 2))
+                       : make_uint4(0, 0, 0, 0);
         }
-    }
-    float v[4][16];
+        if constexpr (DGELU) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) unpack16<DT>(rv[p], v[p]);
-    if constexpr (DGELU) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int64_t row = r0 + rr + 32 * p;
-            float zz[16];
-            unpack16<DT>(rz[p], zz);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float g = v[p][j] * gelu_grad_f32(zz[j]);
-                v[p][j] = DT == kF32 ? g : round_to_bf16(g);
+            for (int p = 0; p < NP; ++p) {
+                const int64_t row = r0 + r_first + C::RS * p;
+                const bool ok = col_ok && row < rows;
+                rz[p] = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(z) +
+                                                             (row * cols + col) * (DT == kF32 ? 4 : 2))
+                           : make_uint4(0, 0, 0, 0);
             }
-            if (dz_out && col_ok && row < rows) store16<DT>(dz_out, row * cols + col, v[p]);
         }
-    }
 
-    float csum[16];
+        float csum[E];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) csum[j] = 0.0f;
+        for (int j = 0; j < E; ++j) csum[j] = 0.0f;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int lrow = rr + 32 * p;
-        const int64_t row = r0 + lrow;
+        for (int p = 0; p < NP; ++p) {
+            const int lrow = r_first + C::RS * p;
+            const int64_t row = r0 + lrow;
+            const bool ok = col_ok && row < rows;
+            float v[E];
+            unpack_vec<DT>(rv[p], v);
+            if constexpr (DGELU) {
+                float zz[E];
+                unpack_vec<DT>(rz[p], zz);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            m = max(m, abs_bits(v[p][j]));
-            if constexpr (DBIAS) csum[j] += v[p][j];
+                for (int j = 0; j < E; ++j) {
+                    const float g = v[j] * gelu_grad_f32(zz[j]);
+                    v[j] = DT == kF32 ? g : round_to_bf16(g);
+                }
+                if (dz_out && ok)
+                    *reinterpret_cast<uint4*>(static_cast<uint8_t*>(dz_out) + (row * cols + col) * (DT == kF32 ? 4 : 2)) =
+                        pack_vec<DT>(v);
+            }
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                m = max(m, abs_bits(v[j]));
+                if constexpr (DBIAS) csum[j] += v[j];
+            }
+            const int lds = lds_word(lrow, vc * (E / 4));
+            const uint2 codes = enc_vec<FMT, E>(v, s);
+            if constexpr (E == 8) {
+                if (q && ok) *reinterpret_cast<uint2*>(q + row * cols + col) = codes;
+                if (qt) *reinterpret_cast<uint2*>(tile + lds) = codes;
+            } else {
+                if (q && ok) *reinterpret_cast<uint32_t*>(q + row * cols + col) = codes.x;
+                if (qt) *reinterpret_cast<uint32_t*>(tile + lds) = codes.x;
+            }
+            if constexpr (DUAL) {
+                const uint2 c2 = enc_vec<kE5M2, E>(v, s2);
+                if constexpr (E == 8) {
+                    if (sec.q && ok) *reinterpret_cast<uint2*>(sec.q + row * cols + col) = c2;
+                    if (sec.qt) *reinterpret_cast<uint2*>(tile + kTile * kTile + lds) = c2;
+                } else {
+                    if (sec.q && ok) *reinterpret_cast<uint32_t*>(sec.q + row * cols + col) = c2.x;
+                    if (sec.qt) *reinterpret_cast<uint32_t*>(tile + kTile * kTile + lds) = c2.x;
+                }
+            }
         }
-        const int lds = lrow * kTile + ((cc ^ ((lrow >> 4) & 7)) << 4);
-        const uint4 codes = scale_enc16<FMT>(v[p], s);
-        if (q && col_ok && row < rows) *reinterpret_cast<uint4*>(q + row * cols + col) = codes;
-        if (qt) *reinterpret_cast<uint4*>(tile + lds) = codes;
-        if constexpr (DUAL) {
-            const uint4 c2 = scale_enc16<kE5M2>(v[p], s2);
-            if (sec.q && col_ok && row < rows) *reinterpret_cast<uint4*>(sec.q + row * cols + col) = c2;
-            if (sec.qt) *reinterpret_cast<uint4*>(tile + kTile * kTile + lds) = c2;
-        }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // Transposed write: 128 output rows (input columns) x 8 strips of 16 bytes,
-    // per format.
+        // Transposed write: four q_t rows (input columns c0 + 4 cg ..) x one
+        // 16-byte strip (input rows r0 + 16 strip ..) per thread and format.
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-        uint8_t* const qtf = f == 0 ? qt : sec.qt;
-        const uint8_t* const tf = tile + f * kTile * kTile;
+        for (int f = 0; f < NF; ++f) {
+            uint8_t* const qtf = f == 0 ? qt : sec.qt;
+            if (!qtf) continue;
+            const uint8_t* const tf = tile + f * kTile * kTile;
+            uint32_t w[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (!qtf) break;
-            const int idx = t + kThreads * i;
-            const int rc = idx & 7;                 // 16-row strip 0..7
-            const int oc = idx >> 3;                // output row within the tile (input column)
-            const int64_t orow = c0 + oc, ocol = r0 + rc * 16;
-            const int colp = (((oc >> 4) ^ rc) << 4) | (oc & 15);   // swizzled byte column of strip rc
-            uint32_t w[4];
+            for (int i = 0; i < 16; ++i) w[i] = *reinterpret_cast<const uint32_t*>(tf + lds_word(strip * 16 + i, cg));
+            uint32_t o[4][4];       // o[j][k]: word k of the vector for column 4 cg + j
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                transpose4x4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3], o[0][k], o[1][k], o[2][k], o[3][k]);
+            const int64_t ocol = r0 + strip * 16;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint8_t* src = tf + (rc * 16 + 4 * j) * kTile + colp;
-                w[j] = (uint32_t)src[0] | ((uint32_t)src[kTile] << 8) | ((uint32_t)src[2 * kTile] << 16) |
-                       ((uint32_t)src[3 * kTile] << 24);
+                const int64_t orow = c0 + 4 * cg + j;
+                if (orow < cols && ocol < rows)
+                    *reinterpret_cast<uint4*>(qtf + orow * rows + ocol) = make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]);
             }
-            if (orow < cols && ocol < rows)
-                *reinterpret_cast<uint4*>(qtf + orow * rows + ocol) = make_uint4(w[0], w[1], w[2], w[3]);
         }
-    }
 
-    if constexpr (DBIAS) {
-        // Column partial sums of this tile in a fixed order: per thread over its
-        // four rows, then over the 32 row groups.  Reuses the LDS tile as fp32.
-        __syncthreads();
-        float* fs = reinterpret_cast<float*>(tile);      // [32][128] floats = 16 KiB
+        if constexpr (DBIAS) {
+            // Column partial sums of this tile in a fixed order: per thread over
+            // its NP rows, then over the RS threads that share its columns.
+            // Reuses the LDS tile as fp32 [RS][128].
+            __syncthreads();
+            float* fs = reinterpret_cast<float*>(tile);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) fs[rr * kTile + cc * 16 + j] = csum[j];
-        __syncthreads();
-        if (t < kTile) {
-            float acc = 0.0f;
-            for (int g = 0; g < 32; ++g) acc += fs[g * kTile + t];
-            if (c0 + t < cols) dbias_ws[tr * cols + c0 + t] = acc;
+            for (int j = 0; j < E; ++j) fs[r_first * kTile + vc * E + j] = csum[j];
+            __syncthreads();
+            if (t < kTile) {
+                float acc = 0.0f;
+                for (int g = 0; g < C::RS; ++g) acc += fs[g * kTile + t];
+                if (c0 + t < cols) dbias_ws[tr * cols + c0 + t] = acc;
+            }
         }
-    }
-    __syncthreads();             // the LDS tile is rewritten by the next tile
+        __syncthreads();             // the LDS tile is rewritten by the next tile
     }
     if (amax_slot) block_amax_merge(m, amax_slot, red);
     if constexpr (DUAL) {
