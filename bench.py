@@ -73,6 +73,35 @@ class MlpBlock:
                 + M * FFN * (2 + 2 + 2))           # dgelu: read dH and Z, write codes twice
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mlp_step_traffic.md")
+GEMM_SOURCES = ("gemm.hip", "common.h")
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "fp8_mixed_precision_reduce_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch of the MLP step from the committed byte-counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter read for
+    a plain copy of known size), or None when the GEMM sources have changed since
+    the counters were taken (or no summary exists)."""
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    kv = dict(re.findall(r"^(\w+): (\S+)$", text, flags=re.M))
+    if kv.get("gemm_source_sha256") != gemm_source_hash() or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 def time_steps(block, torch, steps):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -319,7 +348,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / peak, 4),
-            "traffic": None,
+            "traffic": gemm_traffic(),
             "kernel": "k_gemm (fp8 GEMM, 256x256 tiles)",
             "per_launch_flop": GEMM_FLOP,
             "avg_launch_ms": round(gemm_ms, 4),
