@@ -25,9 +25,11 @@
 //    are fp32.  This is the same kind of reduced-precision FP8 accumulation
 //    the H100 example on the Transformer Engine page exhibits.
 //
-// Tiling.  Both operands are contiguous along k ("TN").  A workgroup of 4
-// waves (2 x 2) computes a BM x BN tile; each wave owns MB x NB blocks of
-// 32 x 32.  k advances in stages of 128 bytes through a double-buffered LDS
+// Tiling.  Both operands are contiguous along k ("TN").  A workgroup of
+// WM x WN waves computes a BM x BN tile; each wave owns MB x NB blocks of
+// 32 x 32.  The kernel is persistent: one resident wave of workgroups loops
+// over the tiles, so one tile's output stores drain while the next tile's k
+// loop runs.  k advances in stages of 128 bytes through a double-buffered LDS
 // tile.  The next stage is fetched while the current one is multiplied, with
 // buffer loads that write straight into LDS (buffer_load_dwordx4 ... lds: no
 // staging registers, out-of-range rows and the k tail read as zero).  LDS rows
@@ -38,16 +40,18 @@
 // of k per fragment: the exact path splits them into two f16 MFMAs (bytes
 // 0-7 and 8-15; A and B use the same split, so the k order inside an MFMA is
 // only permuted), the fast path reads 32 bytes per 64-k MFMA.  Fragments of
-// the next k block are read before the current block's MFMAs are issued.  The
-// two LDS stages are separate arrays and the exact path's k loop is unrolled
+// the next k block are read before the current block's MFMAs are issued
+// (exact path; the fast path reads each block's fragments just before its
+// MFMAs).  The two LDS stages are separate arrays and the k loop is unrolled
 // by two, so the compiler sees that a stage's fragment reads never alias the
 // DMA into the other stage and inserts no wait for that DMA before them; the
-// exact path issues the whole next-stage DMA at the start of a stage (the
-// longest lead), the fast path spreads it over the k blocks.
+// whole next-stage DMA is issued at the start of a stage (the longest lead).
 // The MFMA takes the B tile as
 // its first operand, so each lane's accumulators run along n: four
-// consecutive outputs of one row, written with one 16-byte (fp32) or 8-byte
-// (bf16) store.  Tiles are rasterised in groups of 8 tile-rows, and the
+// consecutive outputs of one row.  fp32 outputs are written from there with
+// one 16-byte store per lane; bf16 outputs (and the pre-GeLU copy) are first
+// staged in the LDS, which is free after the k loop, and then written by the
+// whole workgroup in 16-byte pieces that cover complete row segments.  Tiles are rasterised in groups of 8 tile-rows, and the
 // workgroup index is remapped so that each XCD (workgroups are dealt
 // round-robin over 8 XCDs) works on a contiguous range of tiles that share
 // operands in its own L2.
@@ -133,9 +137,8 @@ template <> struct MfmaFmt<kE5M2> { static constexpr int value = 1; };
 
 // Logical tile index of this workgroup: undo the round-robin XCD dealing,
 // then raster in groups of kGroupM tile-rows.
-__device__ __forceinline__ void tile_coords(int32_t tiles_m, int32_t tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ void tile_coords(int i, int32_t tiles_m, int32_t tiles_n, int& tm, int& tn) {
     const int nwg = tiles_m * tiles_n;
-    const int i = blockIdx.x;
     const int q = nwg / kXcds, r = nwg % kXcds;
     const int xcd = i % kXcds, local = i / kXcds;
     const int pid = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
@@ -161,15 +164,27 @@ k_gemm(GemmParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t smem1[C::STAGE];
     __shared__ uint32_t red[C::WAVES];
 
-    int tm, tn;
-    tile_coords(p.tiles_m, p.tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     const int64_t M = p.m, N = p.n, K = p.k;
-
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave % WM, wn = wave / WM;
     const int g = lane >> 5, r32 = lane & 31;
+    // Stage DMA: wave-instruction i of wave w fills rows 8 (w + W i) .. +7 (W =
+    // waves per workgroup); lane l lands at physical chunk l % 8 of row
+    // row = 8 (w + W i) + l / 8, i.e. it loads logical chunk (l % 8) ^ swz(row).
+    const int lrow = lane >> 3, lpc = lane & 7;
+    constexpr int NDMA = C::A_DMA + C::B_DMA;
+    const int nk = (int)((K + kBK - 1) / kBK);
+    const int ntiles = p.tiles_m * p.tiles_n;
+    const float sc = (*p.sinv_a) * (*p.sinv_b);
+    uint32_t amax = 0;
+
+    // Persistent: each workgroup takes tiles blockIdx.x, + gridDim.x, ...; the
+    // output stores of one tile drain while the next tile's k loop runs.
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    int tm, tn;
+    tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
 
     // Buffer resources over this tile's rows of A and B.
     const uint32_t rows_a = (uint32_t)min<int64_t>(C::BM, M - m0), rows_b = (uint32_t)min<int64_t>(C::BN, N - n0);
@@ -178,10 +193,6 @@ k_gemm(GemmParams p) {
     const __amdgpu_buffer_rsrc_t rb_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.b + n0 * K), (short)0, (int)(rows_b * (uint32_t)K), 0x00020000);
 
-    // Stage DMA: wave-instruction i of wave w fills rows 8 (w + W i) .. +7 (W =
-    // waves per workgroup); lane l lands at physical chunk l % 8 of row
-    // row = 8 (w + W i) + l / 8, i.e. it loads logical chunk (l % 8) ^ swz(row).
-    const int lrow = lane >> 3, lpc = lane & 7;
     // DMA wave-instruction q of a stage: q < A_DMA fills A rows, the rest B rows.
     auto dma_part = [&](int kt, uint8_t* sa, int q0, int q1) {
         uint8_t* sb = sa + C::BM * kBK;
@@ -198,7 +209,6 @@ k_gemm(GemmParams p) {
                   kb < (uint32_t)K ? off : 0x80000000u);
         }
     };
-    constexpr int NDMA = C::A_DMA + C::B_DMA;
 
     v16f acc[MB][NB];
 #pragma unroll
@@ -208,7 +218,6 @@ k_gemm(GemmParams p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int nk = (int)((K + kBK - 1) / kBK);
     if (nk > 0) {
         dma_part(0, smem0, 0, NDMA);
         __builtin_amdgcn_s_waitcnt(0);
@@ -216,43 +225,35 @@ k_gemm(GemmParams p) {
     }
     // One stage: multiply the tile in `cur` while the DMA of stage kt + 1 fills `nxt`.
     auto stage_step = [&](int kt, const uint8_t* cur, uint8_t* nxt) {
-        // the next stage's DMA: the fast path spreads it over the k blocks, the
-        // exact path (whose reads no longer wait for it) issues it all at once
+        // the next stage's DMA is issued all at once at the start of the stage
+        // (the fragment reads of this stage do not wait for it)
         const bool more = kt + 1 < nk;
         const uint8_t* sa = cur;
         const uint8_t* sb = sa + C::BM * kBK;
         if constexpr (FAST) {
             // 64-k blocks: lane group g holds k = 64 kb + 32 g .. +31 (chunks 4 kb + 2 g, +1).
-            uint4 alo[MB], ahi[MB], blo[NB], bhi[NB];
-            auto rd = [&](int kb) {
+            // The fragments of a block are read right before its MFMAs (no
+            // register prefetch of the next block: the second wave on the SIMD
+            // covers the LDS latency, and the registers are not there to spare).
+#pragma unroll
+            for (int kb = 0; kb < kBK / 64; ++kb) {
                 const int c0 = kb * 4 + g * 2;
+                v8i af[MB], bf[NB];
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
                     const int row = wm * MB * 32 + i * 32 + r32;
-                    alo[i] = *reinterpret_cast<const uint4*>(sa + lds_off(row, c0));
-                    ahi[i] = *reinterpret_cast<const uint4*>(sa + lds_off(row, c0 + 1));
+                    const uint4 lo = *reinterpret_cast<const uint4*>(sa + lds_off(row, c0));
+                    const uint4 hi = *reinterpret_cast<const uint4*>(sa + lds_off(row, c0 + 1));
+                    af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 }
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int row = wn * NB * 32 + j * 32 + r32;
-                    blo[j] = *reinterpret_cast<const uint4*>(sb + lds_off(row, c0));
-                    bhi[j] = *reinterpret_cast<const uint4*>(sb + lds_off(row, c0 + 1));
+                    const uint4 lo = *reinterpret_cast<const uint4*>(sb + lds_off(row, c0));
+                    const uint4 hi = *reinterpret_cast<const uint4*>(sb + lds_off(row, c0 + 1));
+                    bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 }
-            };
-            rd(0);
-#pragma unroll
-            for (int kb = 0; kb < kBK / 64; ++kb) {
-                v8i af[MB], bf[NB];
-#pragma unroll
-                for (int i = 0; i < MB; ++i)
-                    af[i] = v8i{(int)alo[i].x, (int)alo[i].y, (int)alo[i].z, (int)alo[i].w,
-                                (int)ahi[i].x, (int)ahi[i].y, (int)ahi[i].z, (int)ahi[i].w};
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    bf[j] = v8i{(int)blo[j].x, (int)blo[j].y, (int)blo[j].z, (int)blo[j].w,
-                                (int)bhi[j].x, (int)bhi[j].y, (int)bhi[j].z, (int)bhi[j].w};
-                if (kb + 1 < kBK / 64) rd(kb + 1);
-                if (more) dma_part(kt + 1, nxt, kb * NDMA / (kBK / 64), (kb + 1) * NDMA / (kBK / 64));
+                if (more && kb == 0) dma_part(kt + 1, nxt, 0, NDMA);
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -333,72 +334,131 @@ k_gemm(GemmParams p) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
-    if constexpr (FAST) {
-        // one body with a run-time stage: the fast tiles hold 256 accumulator
-        // registers, and a second copy of the body would spill
-        for (int kt = 0; kt < nk; ++kt) stage_step(kt, kt & 1 ? smem1 : smem0, kt & 1 ? smem0 : smem1);
-    } else {
-        for (int kt = 0; kt < nk; kt += 2) {
-            stage_step(kt, smem0, smem1);
-            if (kt + 1 < nk) stage_step(kt + 1, smem1, smem0);
-        }
+    for (int kt = 0; kt < nk; kt += 2) {
+        stage_step(kt, smem0, smem1);
+        if (kt + 1 < nk) stage_step(kt + 1, smem1, smem0);
     }
 
     // ---------------------------------------------------------------- epilogue
-    const float sc = (*p.sinv_a) * (*p.sinv_b);
+    // y = acc * sinv_a * sinv_b + bias, in place.  Lane (r32, g) of block (i, j)
+    // holds row i * 32 + r32 and, for q4 = 0..3, the four columns
+    // j * 32 + 8 q4 + 4 g .. + 3 of its wave's sub-tile.
     const bool gelu = p.epilogue & 1, accum = p.epilogue & 2;
     const bool out_bf16 = p.d_dtype == kBF16;
-    uint32_t amax = 0;
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        const int64_t mrow = m0 + wm * MB * 32 + i * 32 + r32;
+    for (int j = 0; j < NB; ++j) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int64_t ncol = n0 + wn * NB * 32 + j * 32 + 8 * q4 + 4 * g;
-                if (mrow >= M || ncol >= N) continue;
-                float y[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * q4 + e] * sc;
-                if (p.bias) {
-                    if (p.bias_dtype == kF32) {
-                        const float4 bv = *reinterpret_cast<const float4*>(static_cast<const float*>(p.bias) + ncol);
-                        y[0] += bv.x; y[1] += bv.y; y[2] += bv.z; y[3] += bv.w;
-                    } else {
-                        const uint2 bv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.bias) + ncol);
-                        y[0] += bf16_to_f32(bv.x & 0xFFFFu); y[1] += bf16_to_f32(bv.x >> 16);
-                        y[2] += bf16_to_f32(bv.y & 0xFFFFu); y[3] += bf16_to_f32(bv.y >> 16);
-                    }
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int64_t ncol = n0 + wn * NB * 32 + j * 32 + 8 * q4 + 4 * g;
+            float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias && ncol < N) {
+                if (p.bias_dtype == kF32) {
+                    const float4 bv = *reinterpret_cast<const float4*>(static_cast<const float*>(p.bias) + ncol);
+                    b[0] = bv.x; b[1] = bv.y; b[2] = bv.z; b[3] = bv.w;
+                } else {
+                    const uint2 bv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.bias) + ncol);
+                    b[0] = bf16_to_f32(bv.x & 0xFFFFu); b[1] = bf16_to_f32(bv.x >> 16);
+                    b[2] = bf16_to_f32(bv.y & 0xFFFFu); b[3] = bf16_to_f32(bv.y >> 16);
                 }
-                const int64_t off = mrow * N + ncol;
-                if (gelu) {
-                    if (p.aux) {
-                        if (out_bf16)
-                            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.aux) + off) =
-                                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-                        else
-                            *reinterpret_cast<float4*>(static_cast<float*>(p.aux) + off) = make_float4(y[0], y[1], y[2], y[3]);
-                    }
+            }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) y[e] = gelu_f32(y[e]);
-                }
-                if (p.residual) {
-                    if (out_bf16) {
-                        const uint2 rv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.residual) + off);
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][4 * q4 + e] = acc[i][j][4 * q4 + e] * sc + b[e];
+        }
+    }
+
+    if (out_bf16) {
+        // bf16 outputs go through LDS (free after the k loop) so that the global
+        // stores write whole row segments: rows of the wave-row wm go to stage
+        // array wm, BN * 2 bytes per row, 8-byte units XOR-swizzled by row.
+        static_assert(WM == 2 && (C::BM / 2) * C::BN * 2 <= C::STAGE, "bf16 staging must fit one stage array");
+        constexpr int UPR = C::BN / 4;                  // 8-byte units per LDS row
+        auto lds_unit = [&](int lr, int unit) { return lr * (C::BN * 2) + ((unit ^ (((lr & 15) << 1) & (UPR - 1))) << 3); };
+        uint8_t* const half = wm == 0 ? smem0 : smem1;
+        auto stage_store = [&](void* dst) {
+            __syncthreads();
+            constexpr int CPR = C::BN / 8;              // 16-byte chunks per row
+            constexpr int RPP = C::THREADS / CPR;       // rows per pass
+            const int c = t % CPR;
+#pragma unroll
+            for (int pass = 0; pass < C::BM / RPP; ++pass) {
+                const int r = t / CPR + RPP * pass;
+                const int lr = r % (C::BM / 2);
+                const uint8_t* src = (r < C::BM / 2 ? smem0 : smem1) + lds_unit(lr, 2 * c);
+                const uint4 v = *reinterpret_cast<const uint4*>(src);
+                const int64_t row = m0 + r, col = n0 + 8 * c;
+                if (row < M && col < N) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + row * N + col) = v;
+            }
+            __syncthreads();
+        };
+        if (gelu && p.aux) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int lr = i * 32 + r32;
+                        const int unit = (wn * NB * 32 + j * 32 + 8 * q4 + 4 * g) / 4;
+                        *reinterpret_cast<uint2*>(half + lds_unit(lr, unit)) =
+                            make_uint2(pack_bf16x2(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1]),
+                                       pack_bf16x2(acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]));
+                    }
+            stage_store(p.aux);
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const int64_t mrow = m0 + wm * MB * 32 + i * 32 + r32;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int64_t ncol = n0 + wn * NB * 32 + j * 32 + 8 * q4 + 4 * g;
+                    const bool inside = mrow < M && ncol < N;
+                    float y[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = gelu ? gelu_f32(acc[i][j][4 * q4 + e]) : acc[i][j][4 * q4 + e];
+                    if (p.residual && inside) {
+                        const uint2 rv =
+                            *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.residual) + mrow * N + ncol);
                         y[0] += bf16_to_f32(rv.x & 0xFFFFu); y[1] += bf16_to_f32(rv.x >> 16);
                         y[2] += bf16_to_f32(rv.y & 0xFFFFu); y[3] += bf16_to_f32(rv.y >> 16);
-                    } else {
+                    }
+                    const uint2 o = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+                    if (inside)
+                        amax = max(amax, max(max(abs_bits(bf16_to_f32(o.x & 0xFFFFu)), abs_bits(bf16_to_f32(o.x >> 16))),
+                                             max(abs_bits(bf16_to_f32(o.y & 0xFFFFu)), abs_bits(bf16_to_f32(o.y >> 16)))));
+                    const int unit = (wn * NB * 32 + j * 32 + 8 * q4 + 4 * g) / 4;
+                    *reinterpret_cast<uint2*>(half + lds_unit(i * 32 + r32, unit)) = o;
+                }
+            }
+        }
+        stage_store(p.d);
+    } else {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const int64_t mrow = m0 + wm * MB * 32 + i * 32 + r32;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int64_t ncol = n0 + wn * NB * 32 + j * 32 + 8 * q4 + 4 * g;
+                    if (mrow >= M || ncol >= N) continue;
+                    float y[4];
+                    const int64_t off = mrow * N + ncol;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * q4 + e];
+                    if (gelu) {
+                        if (p.aux)
+                            *reinterpret_cast<float4*>(static_cast<float*>(p.aux) + off) = make_float4(y[0], y[1], y[2], y[3]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = gelu_f32(y[e]);
+                    }
+                    if (p.residual) {
                         const float4 rv = *reinterpret_cast<const float4*>(static_cast<const float*>(p.residual) + off);
                         y[0] += rv.x; y[1] += rv.y; y[2] += rv.z; y[3] += rv.w;
                     }
-                }
-                if (out_bf16) {
-                    const uint2 o = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.d) + off) = o;
-                    amax = max(amax, max(max(abs_bits(bf16_to_f32(o.x & 0xFFFFu)), abs_bits(bf16_to_f32(o.x >> 16))),
-                                         max(abs_bits(bf16_to_f32(o.y & 0xFFFFu)), abs_bits(bf16_to_f32(o.y >> 16)))));
-                } else {
                     float4* dp = reinterpret_cast<float4*>(static_cast<float*>(p.d) + off);
                     if (accum) {
                         const float4 old = *dp;
@@ -409,8 +469,44 @@ k_gemm(GemmParams p) {
                 }
             }
         }
+        __syncthreads();     // the next tile's DMA rewrites the LDS
     }
+    }   // tile loop
     if (p.amax) block_amax_merge(amax, p.amax, red);
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <typename Kern>
+int resident_per_cu(Kern kern, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, 0) != hipSuccess || n < 1) n = 1;
+    return n;
+}
+
+template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST>
+hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
+    using C = TileCfg<WM, WN, MB, NB>;
+    static const int per_cu = resident_per_cu(k_gemm<WM, WN, MB, NB, AF, BF, FAST>, C::THREADS);
+    // One resident wave of workgroups, each looping over tiles; a multiple of
+    // 8 so that every workgroup stays on the same XCD's tile range.
+    const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
+    int64_t grid = (int64_t)cu_count() * per_cu;
+    if (grid >= 8) grid -= grid % 8;
+    if (grid > ntiles) grid = ntiles;
+    hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, AF, BF, FAST>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, p);
+    return hipGetLastError();
 }
 
 template <int WM, int WN, int MB, int NB, bool FAST>
@@ -419,31 +515,22 @@ hipError_t launch_cfg(const GemmParams& base, int afmt, int bfmt, hipStream_t s)
     GemmParams p = base;
     p.tiles_m = (int32_t)((p.m + C::BM - 1) / C::BM);
     p.tiles_n = (int32_t)((p.n + C::BN - 1) / C::BN);
-    const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n), block(C::THREADS);
-    if (afmt == kE4M3 && bfmt == kE4M3)
-        hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, kE4M3, kE4M3, FAST>), grid, block, 0, s, p);
-    else if (afmt == kE5M2 && bfmt == kE4M3)
-        hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, kE5M2, kE4M3, FAST>), grid, block, 0, s, p);
-    else if (afmt == kE4M3)
-        hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, kE4M3, kE5M2, FAST>), grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, kE5M2, kE5M2, FAST>), grid, block, 0, s, p);
-    return hipGetLastError();
+    if (afmt == kE4M3 && bfmt == kE4M3) return launch_fmt<WM, WN, MB, NB, kE4M3, kE4M3, FAST>(p, s);
+    if (afmt == kE5M2 && bfmt == kE4M3) return launch_fmt<WM, WN, MB, NB, kE5M2, kE4M3, FAST>(p, s);
+    if (afmt == kE4M3) return launch_fmt<WM, WN, MB, NB, kE4M3, kE5M2, FAST>(p, s);
+    return launch_fmt<WM, WN, MB, NB, kE5M2, kE5M2, FAST>(p, s);
 }
 
 template <bool FAST>
 hipError_t launch_path(const GemmParams& p, int afmt, int bfmt, hipStream_t s) {
     // Tile choice: 256 x 256 when that still gives every CU work, else smaller
-    // tiles.  At 256 x 256 the exact path runs 8 waves (2 per SIMD, 128 x 64
-    // each) so one wave's LDS reads and converts overlap the other's MFMAs;
-    // the fast path, which needs half the MFMA time per byte of LDS traffic,
-    // runs 4 waves of 128 x 128.
+    // tiles.  At 256 x 256 both paths run 8 waves (2 per SIMD, 128 x 64 each)
+    // so one wave's LDS reads and converts overlap the other's MFMAs; 128 x 128
+    // per wave would need 256 accumulator registers, which the persistent
+    // loop's state no longer leaves room for.
     const int64_t big = ((p.m + 255) / 256) * ((p.n + 255) / 256);
     const int64_t mid = ((p.m + 127) / 128) * ((p.n + 127) / 128);
-    if (big >= 256) {
-        if constexpr (FAST) return launch_cfg<2, 2, 4, 4, FAST>(p, afmt, bfmt, s);
-        else return launch_cfg<2, 4, 4, 2, FAST>(p, afmt, bfmt, s);
-    }
+    if (big >= 256) return launch_cfg<2, 4, 4, 2, FAST>(p, afmt, bfmt, s);
     if (mid >= 256) return launch_cfg<2, 2, 2, 2, FAST>(p, afmt, bfmt, s);
     return launch_cfg<2, 2, 1, 1, FAST>(p, afmt, bfmt, s);
 }
