@@ -187,3 +187,39 @@ def test_gemm_fast_accum_within_group_truncation_bound(oracle, pair, shape):
     bound = 2 * _group_bound(ta[a[rows]], tb[b], k) * float(sa) * float(sb) + 1e-6 * np.abs(want) + 1e-30
     err = np.abs(np_of(d)[rows].astype(np.float64) - want)
     assert np.all(err <= bound), float(np.max(err / bound))
+
+
+@pytest.mark.parametrize("in_place", [False, True], ids=["separate", "in_place"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(272, 528, 400), (2048, 1536, 512)], ids=lambda s: "x".join(map(str, s)))
+def test_gemm_residual(oracle, shape, out_dtype, in_place):
+    """d = gelu(y) + residual (and y + residual), added in fp32 before the one
+    rounding to the output type; residual may be d itself (in-place add).
+    Covers a 128- and a 256-tile configuration with ragged tails."""
+    m, n, k = shape
+    rng = np.random.default_rng(m + n + k + (1 if in_place else 0))
+    a = _codes(oracle, rng, (m, k), 0)
+    b = _codes(oracle, rng, (n, k), 0)
+    sa, sb = np.float32(0.05), np.float32(0.7)
+    r = rng.standard_normal((m, n)).astype(np.float32)
+    r_store = r if out_dtype == torch.float32 else oracle.bf16_from_f32(r)
+    for gelu in (False, True):
+        res = dev(r_store)
+        d = res if in_place else torch.empty(m, n, dtype=out_dtype, device="cuda")
+        ax = torch.empty(m, n, dtype=out_dtype, device="cuda") if gelu else None
+        amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+        F.fp8_gemm(dev(a), F.E4M3, dev(b), F.E4M3, _scalar(float(sa)), _scalar(float(sb)), d,
+                   epilogue=F.EPI_GELU if gelu else 0, aux=ax, residual=res, amax_d=amax)
+        rows = np.unique(np.concatenate([np.arange(32), rng.integers(0, m, 64), [m - 1]]))
+        y, pre = oracle.gemm(a, 0, b, 0, sa, sb, gelu=gelu, rows=rows, want_pre=True)
+        want = oracle.add_residual(y, r_store[rows])
+        got = np_of(d)
+        tag = f"{shape} gelu={gelu} in_place={in_place}"
+        if out_dtype == torch.float32:
+            assert_gemm_f32(got[rows], want, tag)
+        else:
+            assert_gemm_bf16(got[rows], want, oracle, tag)
+            if gelu:
+                assert_gemm_bf16(np_of(ax)[rows], pre, oracle, tag + " aux")
+        full = got.astype(np.float64) if out_dtype == torch.float32 else oracle.bf16_to_f64(got)
+        assert_bits_equal(np_of(amax)[0], np.float32(np.max(np.abs(full))), tag + " amax of d as written")
