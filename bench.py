@@ -315,6 +315,13 @@ def main():
         other.step()
     other_ms = time_steps(other, torch, max(3, args.steps // 2))
     del other
+
+    # just-in-time scaling (every cast preceded by its own amax pass), for reference
+    block.block.recipe.just_in_time = 1
+    for _ in range(2):
+        block.step()
+    jit_ms = time_steps(block, torch, max(3, args.steps // 2))
+    block.block.recipe.just_in_time = 0
     torch.cuda.empty_cache()
     layer = None if args.no_layer else layer_leg(F, torch, fast_accum=args.fast_accum)
     quant = None if args.no_quant else quant_leg(F, torch)
@@ -359,6 +366,9 @@ def main():
                          "algorithmic_bytes_per_step": MlpBlock.cast_bytes_per_step()},
         ("exact_accum" if args.fast_accum else "fast_accum"): {
             "ms_per_step": round(other_ms, 4), "tflops": round(STEP_FLOP / (other_ms * 1e-3) / 1e12, 2)},
+        "just_in_time_scaling": {
+            "ms_per_step": round(jit_ms, 4), "tflops": round(STEP_FLOP / (jit_ms * 1e-3) / 1e12, 2),
+            "note": "same step with every tensor scaled from its own current amax (an extra amax pass each)"},
     }
     if layer is not None:
         line["layer_step"] = layer

@@ -26,11 +26,11 @@ FORMAT_E4M3, FORMAT_HYBRID = 0, 1
 AMAX_MAX = 0
 EPI_GELU, EPI_ACCUMULATE, EPI_FAST_ACCUM = 1, 2, 4
 KIND_NAMES = ["amax", "cast", "cast_transpose", "dequant", "scale_update", "gemm", "dbias", "other", "sgd"]
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 FUNCTIONS = [
     "fp8lin_abi_version", "fp8lin_last_error", "fp8lin_status_name", "fp8lin_dbias_workspace_bytes",
-    "fp8_amax", "fp8_amax_scale_update", "fp8_cast", "fp8_cast_transpose", "fp8_cast_transpose_dgelu",
+    "fp8_amax", "fp8_amax_scale_update", "fp8_scale_from_current_amax", "fp8_cast", "fp8_cast_transpose", "fp8_cast_transpose_dgelu",
     "fp8_cast_transpose_dual",
     "fp8_dequant", "fp8_gemm", "fp8_linear_fwd", "fp8_linear_bwd", "fp8_loss_scale_update",
     "fp8_loss_scale_apply", "fp8_sgd_step", "fp8lin_timing_enable", "fp8lin_timing_read",
@@ -45,13 +45,16 @@ class Fp8LinError(RuntimeError):
 
 class Recipe(ctypes.Structure):
     """DelayedScaling recipe: format, amax history length, amax algorithm,
-    margin, and whether the layer GEMMs use the fast (FP8 matrix-core) sums."""
+    margin, whether the layer GEMMs use the fast (FP8 matrix-core) sums, and
+    whether the layer calls scale just in time (from the current amax)."""
     _fields_ = [("format", ctypes.c_int32), ("history_len", ctypes.c_int32),
                 ("amax_compute_algo", ctypes.c_int32), ("margin", ctypes.c_int32),
-                ("fast_accum", ctypes.c_int32)]
+                ("fast_accum", ctypes.c_int32), ("just_in_time", ctypes.c_int32)]
 
-    def __init__(self, format=FORMAT_HYBRID, history_len=16, amax_compute_algo=AMAX_MAX, margin=0, fast_accum=0):
-        super().__init__(format, history_len, amax_compute_algo, margin, int(bool(fast_accum)))
+    def __init__(self, format=FORMAT_HYBRID, history_len=16, amax_compute_algo=AMAX_MAX, margin=0, fast_accum=0,
+                 just_in_time=0):
+        super().__init__(format, history_len, amax_compute_algo, margin, int(bool(fast_accum)),
+                         int(bool(just_in_time)))
 
 
 class _MetaC(ctypes.Structure):
@@ -75,6 +78,7 @@ def _load():
         "fp8lin_dbias_workspace_bytes": (I64, [I64, I64]),
         "fp8_amax": (I32, [P, I32, I64, P, P]),
         "fp8_amax_scale_update": (I32, [P, P, P, P, I32, ctypes.POINTER(Recipe), P]),
+        "fp8_scale_from_current_amax": (I32, [P, P, P, P, I32, ctypes.POINTER(Recipe), P]),
         "fp8_cast": (I32, [P, I32, I64, I32, P, P, P, P]),
         "fp8_cast_transpose": (I32, [P, I32, I64, I64, I32, P, P, P, P, P, P, P]),
         "fp8_cast_transpose_dgelu": (I32, [P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, P]),
@@ -177,6 +181,9 @@ class MetaBank:
     def update(self, recipe, stream=None):
         fp8_amax_scale_update(self.amax_history, self.scale, self.scale_inv, self.formats, recipe, stream)
 
+    def scale_from_current(self, recipe, stream=None):
+        fp8_scale_from_current_amax(self.amax_history, self.scale, self.scale_inv, self.formats, recipe, stream)
+
 
 class Saved:
     """Buffers a forward pass leaves for its backward pass (FP8 copies of X
@@ -206,6 +213,13 @@ def fp8_amax_scale_update(amax_history, scale, scale_inv, formats, recipe, strea
     fm = (ctypes.c_uint8 * len(formats)).from_buffer_copy(bytes(formats))
     _check(_lib.fp8_amax_scale_update(_p(amax_history), _p(scale), _p(scale_inv), ctypes.cast(fm, ctypes.c_void_p),
                                       len(formats), ctypes.byref(recipe), _stream(stream)))
+
+
+def fp8_scale_from_current_amax(amax_history, scale, scale_inv, formats, recipe, stream=None):
+    fm = (ctypes.c_uint8 * len(formats)).from_buffer_copy(bytes(formats))
+    _check(_lib.fp8_scale_from_current_amax(_p(amax_history), _p(scale), _p(scale_inv),
+                                            ctypes.cast(fm, ctypes.c_void_p), len(formats), ctypes.byref(recipe),
+                                            _stream(stream)))
 
 
 def fp8_cast(x, fmt, scale, q, amax_slot=None, stream=None):

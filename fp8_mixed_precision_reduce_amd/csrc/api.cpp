@@ -168,31 +168,48 @@ int32_t fp8_amax(const void* x, int32_t x_dtype, int64_t n, float* amax_slot, vo
 }
 
 // ----------------------------------------------------------- scale update
-int32_t fp8_amax_scale_update(float* amax_history, float* scale, float* scale_inv, const uint8_t* formats,
-                              int32_t n_tensors, const fp8lin_recipe* recipe, void* stream) {
-    if (!amax_history || !scale || !scale_inv || !formats || !recipe)
-        return fail(FP8LIN_ERR_NULL, "fp8_amax_scale_update: null pointer");
+namespace {
+int32_t check_scale_args(const char* fn, float* amax_history, float* scale, float* scale_inv, const uint8_t* formats,
+                         int32_t n_tensors, const fp8lin_recipe* recipe) {
+    if (!amax_history || !scale || !scale_inv || !formats || !recipe) return fail(FP8LIN_ERR_NULL, "%s: null pointer", fn);
     if (n_tensors < 1 || n_tensors > 4096)
-        return fail(FP8LIN_ERR_SHAPE, "fp8_amax_scale_update: n_tensors=%d not in [1, 4096]", n_tensors);
+        return fail(FP8LIN_ERR_SHAPE, "%s: n_tensors=%d not in [1, 4096]", fn, n_tensors);
     if (recipe->history_len < 1 || recipe->history_len > 65536)
-        return fail(FP8LIN_ERR_ARG, "fp8_amax_scale_update: history_len=%d not in [1, 65536]", recipe->history_len);
+        return fail(FP8LIN_ERR_ARG, "%s: history_len=%d not in [1, 65536]", fn, recipe->history_len);
     if (recipe->margin < 0 || recipe->margin > 127)
-        return fail(FP8LIN_ERR_ARG, "fp8_amax_scale_update: margin=%d not in [0, 127]", recipe->margin);
+        return fail(FP8LIN_ERR_ARG, "%s: margin=%d not in [0, 127]", fn, recipe->margin);
     if (recipe->amax_compute_algo != FP8LIN_AMAX_MAX)
-        return fail(FP8LIN_ERR_UNSUPPORTED, "fp8_amax_scale_update: amax_compute_algo %d (only max)",
-                    recipe->amax_compute_algo);
+        return fail(FP8LIN_ERR_UNSUPPORTED, "%s: amax_compute_algo %d (only max)", fn, recipe->amax_compute_algo);
     for (int32_t t = 0; t < n_tensors; ++t)
-        if (!is_fp8(formats[t]))
-            return fail(FP8LIN_ERR_DTYPE, "fp8_amax_scale_update: formats[%d]=%d is not E4M3/E5M2", t, formats[t]);
+        if (!is_fp8(formats[t])) return fail(FP8LIN_ERR_DTYPE, "%s: formats[%d]=%d is not E4M3/E5M2", fn, t, formats[t]);
     if (!aligned(amax_history, 4) || !aligned(scale, 4) || !aligned(scale_inv, 4))
-        return fail(FP8LIN_ERR_ALIGN, "fp8_amax_scale_update: misaligned pointer");
+        return fail(FP8LIN_ERR_ALIGN, "%s: misaligned pointer", fn);
     const int64_t hb = (int64_t)n_tensors * recipe->history_len * 4, sb = (int64_t)n_tensors * 4;
     if (overlap(amax_history, hb, scale, sb) || overlap(amax_history, hb, scale_inv, sb) ||
         overlap(scale, sb, scale_inv, sb))
-        return fail(FP8LIN_ERR_ARG, "fp8_amax_scale_update: history, scale and scale_inv overlap");
+        return fail(FP8LIN_ERR_ARG, "%s: history, scale and scale_inv overlap", fn);
+    return FP8LIN_OK;
+}
+}  // namespace
+
+int32_t fp8_amax_scale_update(float* amax_history, float* scale, float* scale_inv, const uint8_t* formats,
+                              int32_t n_tensors, const fp8lin_recipe* recipe, void* stream) {
+    const char* fn = "fp8_amax_scale_update";
+    const int32_t v = check_scale_args(fn, amax_history, scale, scale_inv, formats, n_tensors, recipe);
+    if (v != FP8LIN_OK) return v;
     return hip_status(launch_scale_update(amax_history, scale, scale_inv, formats, n_tensors, recipe->history_len,
                                           recipe->margin, as_stream(stream)),
-                      "fp8_amax_scale_update");
+                      fn);
+}
+
+int32_t fp8_scale_from_current_amax(float* amax_history, float* scale, float* scale_inv, const uint8_t* formats,
+                                    int32_t n_tensors, const fp8lin_recipe* recipe, void* stream) {
+    const char* fn = "fp8_scale_from_current_amax";
+    const int32_t v = check_scale_args(fn, amax_history, scale, scale_inv, formats, n_tensors, recipe);
+    if (v != FP8LIN_OK) return v;
+    return hip_status(launch_scale_from_current(amax_history, recipe->history_len, scale, scale_inv, formats,
+                                                n_tensors, recipe->margin, as_stream(stream)),
+                      fn);
 }
 
 // ------------------------------------------------------------------- cast
@@ -365,7 +382,21 @@ int32_t check_recipe(const char* fn, const fp8lin_recipe* r) {
         return fail(FP8LIN_ERR_ARG, "%s: recipe format %d", fn, r->format);
     if (r->amax_compute_algo != FP8LIN_AMAX_MAX)
         return fail(FP8LIN_ERR_UNSUPPORTED, "%s: amax_compute_algo %d (only max)", fn, r->amax_compute_algo);
+    if (r->margin < 0 || r->margin > 127) return fail(FP8LIN_ERR_ARG, "%s: margin=%d not in [0, 127]", fn, r->margin);
     return FP8LIN_OK;
+}
+
+// Just-in-time scaling of one tensor: amax(x) into the meta's slot 0 (or, for
+// the GeLU backward, amax of dZ formed on the fly), then its scale from that
+// amax.  The cast that follows needs no amax slot.
+hipError_t jit_scale(const void* x, const void* gelu_z, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt,
+                     const fp8lin_meta* mt, int32_t margin, hipStream_t s) {
+    hipError_t e = gelu_z ? launch_cast_transpose(x, gelu_z, dtype, rows, cols, fmt, mt->scale, nullptr, nullptr,
+                                                  mt->amax_history, nullptr, nullptr, nullptr, s)
+                          : launch_amax(x, dtype, rows * cols, mt->amax_history, s);
+    if (e != hipSuccess) return e;
+    const uint8_t f = (uint8_t)fmt;
+    return launch_scale_from_current(mt->amax_history, 1, mt->scale, mt->scale_inv, &f, 1, margin, s);
 }
 
 int32_t check_meta(const char* fn, const char* which, const fp8lin_meta* mt) {
@@ -410,13 +441,20 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
 
     hipStream_t s = as_stream(stream);
     hipError_t e;
+    const bool jit = recipe->just_in_time != 0;
+    if (jit && (e = jit_scale(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx, recipe->margin, s)) != hipSuccess)
+        return hip_status(e, "fp8_linear_fwd: just-in-time scale of X");
+    float* xslot = jit ? nullptr : mx->amax_history;
     if (saved->xq_t) e = launch_cast_transpose(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx->scale, saved->xq,
-                                               saved->xq_t, mx->amax_history, nullptr, nullptr, nullptr, s);
-    else e = launch_cast(x, x_dtype, m * k, FP8LIN_E4M3, mx->scale, saved->xq, mx->amax_history, s);
+                                               saved->xq_t, xslot, nullptr, nullptr, nullptr, s);
+    else e = launch_cast(x, x_dtype, m * k, FP8LIN_E4M3, mx->scale, saved->xq, xslot, s);
     if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast X");
+    if (jit && (e = jit_scale(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw, recipe->margin, s)) != hipSuccess)
+        return hip_status(e, "fp8_linear_fwd: just-in-time scale of W");
+    float* wslot = jit ? nullptr : mw->amax_history;
     if (saved->wq_t) e = launch_cast_transpose(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw->scale, saved->wq,
-                                               saved->wq_t, mw->amax_history, nullptr, nullptr, nullptr, s);
-    else e = launch_cast(w, w_dtype, n * k, FP8LIN_E4M3, mw->scale, saved->wq, mw->amax_history, s);
+                                               saved->wq_t, wslot, nullptr, nullptr, nullptr, s);
+    else e = launch_cast(w, w_dtype, n * k, FP8LIN_E4M3, mw->scale, saved->wq, wslot, s);
     if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast W");
     e = launch_copy_scalars(mx->scale_inv, mw->scale_inv, saved->sinv, s);
     if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: save scale_inv");
@@ -466,8 +504,12 @@ int32_t fp8_linear_bwd(int64_t m, int64_t n, int64_t k, const void* dy, int32_t 
         return fail(FP8LIN_ERR_ARG, "%s: dx overlaps dy or gelu_z", fn);
 
     hipStream_t s = as_stream(stream);
-    hipError_t e = launch_cast_transpose(dy, gelu_z, dy_dtype, m, n, gfmt, mdy->scale, qr, qt, mdy->amax_history,
-                                         dbias, dbias_ws, dz_out, s);
+    hipError_t e;
+    const bool jit = recipe->just_in_time != 0;
+    if (jit && (e = jit_scale(dy, gelu_z, dy_dtype, m, n, gfmt, mdy, recipe->margin, s)) != hipSuccess)
+        return hip_status(e, "fp8_linear_bwd: just-in-time scale of dY");
+    e = launch_cast_transpose(dy, gelu_z, dy_dtype, m, n, gfmt, mdy->scale, qr, qt, jit ? nullptr : mdy->amax_history,
+                              dbias, dbias_ws, dz_out, s);
     if (e != hipSuccess) return hip_status(e, "fp8_linear_bwd: cast dY");
     if (dx) {
         e = launch_gemm(dyq_ws, gfmt, saved->wq_t, FP8LIN_E4M3, m, k, n, mdy->scale_inv, saved->sinv + 1, nullptr,

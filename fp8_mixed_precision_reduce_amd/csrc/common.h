@@ -29,6 +29,8 @@ hipError_t launch_dequant(const uint8_t* q, int fmt, int64_t n, const float* sin
                           int out_dtype, hipStream_t s);
 hipError_t launch_scale_update(float* hist, float* scale, float* sinv, const uint8_t* fmts,
                                int32_t n, int32_t L, int32_t margin, hipStream_t s);
+hipError_t launch_scale_from_current(const float* hist, int64_t stride, float* scale, float* sinv,
+                                     const uint8_t* fmts, int32_t n, int32_t margin, hipStream_t s);
 hipError_t launch_copy_scalars(const float* a, const float* b, float* dst2, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_t rows, int64_t cols,

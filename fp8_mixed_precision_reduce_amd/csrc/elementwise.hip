@@ -191,6 +191,16 @@ struct FmtBits { uint32_t w[kMaxTensors / 32]; };
 // One workgroup per tensor: max over the finite history entries, the scale
 // rule, then the roll h[i] <- h[i-1], h[0] <- 0 done top-down in chunks of
 // 256 so every read of a chunk precedes the writes that could clobber it.
+// The scale rule: s = fl32(fl32(fp8_max / a) * 2^-margin), FLT_MAX if that
+// overflowed; 0 means "keep the old scale" (a not > 0, or s underflowed).
+__device__ __forceinline__ float scale_rule(float a, float fmax, int32_t margin) {
+    if (!(a > 0.0f)) return 0.0f;
+    float s = __fdiv_rn(fmax, a);
+    s = ldexpf(s, -margin);
+    if (isinf(s)) s = 3.402823466e+38f;
+    return s;
+}
+
 __global__ void __launch_bounds__(kThreads)
 k_scale_update(float* __restrict__ hist, float* __restrict__ scale, float* __restrict__ sinv,
                FmtBits fmts, int32_t L, int32_t margin) {
@@ -209,16 +219,11 @@ k_scale_update(float* __restrict__ hist, float* __restrict__ scale, float* __res
     if (threadIdx.x == 0) {
         float a = red[0];
         for (int w = 1; w < kThreads / 64; ++w) a = fmaxf(a, red[w]);
-        if (a > 0.0f) {
-            const bool e5 = (fmts.w[t >> 5] >> (t & 31)) & 1u;
-            const float fmax = e5 ? 57344.0f : 448.0f;
-            float s = __fdiv_rn(fmax, a);
-            s = ldexpf(s, -margin);
-            if (isinf(s)) s = 3.402823466e+38f;
-            if (s > 0.0f) {
-                scale[t] = s;
-                sinv[t] = __fdiv_rn(1.0f, s);
-            }
+        const bool e5 = (fmts.w[t >> 5] >> (t & 31)) & 1u;
+        const float s = scale_rule(a, e5 ? 57344.0f : 448.0f, margin);
+        if (s > 0.0f) {
+            scale[t] = s;
+            sinv[t] = __fdiv_rn(1.0f, s);
         }
     }
     __syncthreads();
@@ -229,6 +234,23 @@ k_scale_update(float* __restrict__ hist, float* __restrict__ scale, float* __res
         __syncthreads();
         if (i < L) h[i] = prev;
         __syncthreads();
+    }
+}
+
+// Just-in-time scaling: the scale of tensor t from its current amax alone
+// (slot 0 of its history, `stride` floats apart), a non-finite amax keeping
+// the old scale; the history is not rolled.
+__global__ void __launch_bounds__(kThreads)
+k_scale_from_current(const float* __restrict__ hist, int64_t stride, float* __restrict__ scale,
+                     float* __restrict__ sinv, FmtBits fmts, int32_t n, int32_t margin) {
+    const int t = blockIdx.x * kThreads + threadIdx.x;
+    if (t >= n) return;
+    const float a = hist[(int64_t)t * stride];
+    const bool e5 = (fmts.w[t >> 5] >> (t & 31)) & 1u;
+    const float s = isfinite(a) ? scale_rule(a, e5 ? 57344.0f : 448.0f, margin) : 0.0f;
+    if (s > 0.0f) {
+        scale[t] = s;
+        sinv[t] = __fdiv_rn(1.0f, s);
     }
 }
 
@@ -309,6 +331,18 @@ hipError_t launch_scale_update(float* hist, float* scale, float* sinv, const uin
         if (fmts[t] == kE5M2) bits.w[t >> 5] |= 1u << (t & 31);
     timing_before(kKindScaleUpdate, s);
     hipLaunchKernelGGL(k_scale_update, dim3(n), dim3(kThreads), 0, s, hist, scale, sinv, bits, L, margin);
+    timing_after(s);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_from_current(const float* hist, int64_t stride, float* scale, float* sinv,
+                                     const uint8_t* fmts, int32_t n, int32_t margin, hipStream_t s) {
+    FmtBits bits{};
+    for (int32_t t = 0; t < n; ++t)
+        if (fmts[t] == kE5M2) bits.w[t >> 5] |= 1u << (t & 31);
+    timing_before(kKindScaleUpdate, s);
+    hipLaunchKernelGGL(k_scale_from_current, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, s, hist, stride,
+                       scale, sinv, bits, n, margin);
     timing_after(s);
     return hipGetLastError();
 }

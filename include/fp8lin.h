@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 2
+#define FP8LIN_ABI_VERSION 3
 
 /* Status codes returned by every call. */
 enum {
@@ -86,13 +86,22 @@ enum {
 /* Delayed-scaling recipe ([TE-KR] "FP8 사용방안(recipe)", [TE-RU] section 10:
  * DelayedScaling(fp8_format, amax_history_len, amax_compute_algo)).  `margin`
  * divides the scale by 2^margin (0 <= margin <= 127).  `fast_accum` != 0 makes
- * the layer calls run their GEMMs with FP8LIN_EPI_FAST_ACCUM. */
+ * the layer calls run their GEMMs with FP8LIN_EPI_FAST_ACCUM.
+ * `just_in_time` != 0 makes the layer calls scale each tensor they cast from
+ * its current amax instead of the history ([TE-KR] "Scaling factor" strategy,
+ * just-in-time: measure the amax on every use and take the factor from it, at
+ * the cost of an extra pass): amax(x) is merged into slot 0, then
+ * scale = fp8_max / slot0 / 2^margin (fp8_scale_from_current_amax), then the
+ * cast runs with that scale.  Setting it on the first step only gives the
+ * "initial amax" behaviour ([PT-VI] training script: enable_amax_init), so
+ * that step does not cast with the initial scale 1. */
 typedef struct {
     int32_t format;             /* FP8LIN_FORMAT_* */
     int32_t history_len;        /* amax history length L >= 1 */
     int32_t amax_compute_algo;  /* FP8LIN_AMAX_MAX */
     int32_t margin;
     int32_t fast_accum;
+    int32_t just_in_time;
 } fp8lin_recipe;
 
 /* Per-tensor scaling state ([TE-KR] "Scaling factor" strategy: delayed scaling
@@ -167,6 +176,20 @@ int32_t fp8_amax(const void* x, int32_t x_dtype, int64_t n, float* amax_slot, vo
 int32_t fp8_amax_scale_update(float* amax_history, float* scale, float* scale_inv,
                               const uint8_t* formats, int32_t n_tensors,
                               const fp8lin_recipe* recipe, void* stream);
+
+/*
+ * fp8_scale_from_current_amax -- just-in-time scaling of n tensors: for each
+ * tensor t, with a = amax_history[t*L] (slot 0, the current amax):
+ *   if a is finite and > 0: s = fl32(fl32(fp8_max(fmt[t]) / a) * 2^-margin),
+ *   FLT_MAX if that overflowed; if s > 0: scale[t] = s, scale_inv[t] = fl32(1/s)
+ *   (otherwise both are kept).  The history is not rolled.
+ * [TE-KR] "Scaling factor" strategy (just-in-time: the factor from the amax
+ * measured now); [PT-VI] training script (enable_amax_init).  Arguments as in
+ * fp8_amax_scale_update (recipe: history_len, margin).
+ */
+int32_t fp8_scale_from_current_amax(float* amax_history, float* scale, float* scale_inv,
+                                    const uint8_t* formats, int32_t n_tensors,
+                                    const fp8lin_recipe* recipe, void* stream);
 
 /*
  * fp8_cast -- q = enc_F(fl32(x * scale)) elementwise, with amax(x) fused.
@@ -284,7 +307,8 @@ int32_t fp8_gemm(const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_
  * recorded and the factor applied; [TE-KR] "Using FP8 with Transformer
  * Engine" (a Linear(768, 768, bias=True) on a 1024x768 input).
  * Steps (all on `stream`): cast(-transpose) X -> saved->xq (+ xq_t) with
- * mx->scale, amax(X) into mx->amax_history[0]; the same for W with mw;
+ * mx->scale, amax(X) into mx->amax_history[0]; the same for W with mw (with
+ * recipe->just_in_time: amax first, then the scale from it, then the cast);
  * saved->sinv = {*mx->scale_inv, *mw->scale_inv}; then fp8_gemm(xq, wq) with
  * sinv = saved->sinv, bias and epilogue, into y (and y_aux, y_amax_slot).
  * The forward format is E4M3 under both recipe formats.
@@ -309,7 +333,8 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k,
  * E5M2 under HYBRID per "Introduction to FP8"); [MP-KR] "FP32 Master Copy of
  * Weights" (weight gradients feed fp32 masters).
  * Steps: cast-transpose dY (format E5M2 under HYBRID, E4M3 otherwise) with
- * mdy->scale into dyq_ws / dyq_t_ws, amax(dY) into mdy->amax_history[0],
+ * mdy->scale into dyq_ws / dyq_t_ws, amax(dY) into mdy->amax_history[0]
+ * (with recipe->just_in_time: amax first, then the scale from it, then the cast),
  * optional dbias = column sums of dY; then
  *   dX [m][k] = (dYq . Wq)   = fp8_gemm(dyq [m][n], wq_t [k][n]) * sinv_dy * saved->sinv[1]
  *   dW [n][k] = (dYq^T . Xq) = fp8_gemm(dyq_t [n][m], xq_t [k][m]) * sinv_dy * saved->sinv[0]

@@ -368,16 +368,32 @@ def update_metas(metas, margin=0):
         m.scale, m.scale_inv = np.float32(scale[i]), np.float32(sinv[i])
 
 
-def linear_fwd(x, w, mx, mw, bias=None, gelu_=False, rows=None):
+def scale_from_current(meta, margin=0):
+    """Just-in-time scaling ([TE-KR] "Scaling factor" strategy: the factor from
+    the amax measured at this use): the scale rule applied to the current amax
+    alone (slot 0), i.e. the delayed update over a one-entry history, without
+    rolling the tensor's history."""
+    h = meta.hist[0:1].astype(np.float32).reshape(1, 1).copy()
+    sc = np.array([meta.scale], dtype=np.float32)
+    si = np.array([meta.scale_inv], dtype=np.float32)
+    scale_update(h, sc, si, [meta.fmt], margin)
+    meta.scale, meta.scale_inv = np.float32(sc[0]), np.float32(si[0])
+
+
+def linear_fwd(x, w, mx, mw, bias=None, gelu_=False, rows=None, jit=False):
     """Forward of Y = X W^T + b on FP8 copies of X and W.
 
     Records amax(X), amax(W) in slot 0, casts both with their current scales
-    to E4M3 (forward format), runs the FP8 GEMM with fp64 accumulation and
-    returns a dict with the codes, the inverse scales captured for backward
-    and the fp64 result (y before GeLU in 'pre' when gelu_).
+    (with jit: scales taken from those amaxes first) to E4M3 (forward format),
+    runs the FP8 GEMM with fp64 accumulation and returns a dict with the
+    codes, the inverse scales captured for backward and the fp64 result (y
+    before GeLU in 'pre' when gelu_).
     """
     mx.record(x)
     mw.record(w)
+    if jit:
+        scale_from_current(mx)
+        scale_from_current(mw)
     xq, xqt = cast_transpose(x, mx.fmt, mx.scale)
     wq, wqt = cast_transpose(w, mw.fmt, mw.scale)
     b64 = None if bias is None else np.asarray(bias, dtype=np.float32).astype(np.float64)
@@ -386,15 +402,18 @@ def linear_fwd(x, w, mx, mw, bias=None, gelu_=False, rows=None):
                 sinv_w=np.float32(mw.scale_inv), fmt_x=mx.fmt, fmt_w=mw.fmt, y=y, pre=pre)
 
 
-def linear_bwd(dy, saved, mg, rows_dx=None, rows_dw=None):
+def linear_bwd(dy, saved, mg, rows_dx=None, rows_dw=None, jit=False):
     """Backward of the FP8 linear from the forward's saved FP8 copies.
 
-    Records amax(dY), casts dY with its current scale (E5M2 under HYBRID),
+    Records amax(dY), casts dY with its current scale (with jit: the scale
+    taken from that amax first; E5M2 under HYBRID),
     then dX = dYq . Wq (reduction over N, operands dYq [M][N] and Wq^T [K][N])
     and dW = dYq^T . Xq (reduction over M, operands dYq^T [N][M], Xq^T [K][M]).
     dbias = column sums of dY in fp64.
     """
     mg.record(dy)
+    if jit:
+        scale_from_current(mg)
     gq, gqt = cast_transpose(dy, mg.fmt, mg.scale)
     dx = gemm(gq, mg.fmt, saved["wqt"], saved["fmt_w"], mg.scale_inv, saved["sinv_w"], rows=rows_dx)
     dw = gemm(gqt, mg.fmt, saved["xqt"], saved["fmt_x"], mg.scale_inv, saved["sinv_x"], rows=rows_dw)

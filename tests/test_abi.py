@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_names():
-    assert L.fp8lin_abi_version() == 2
+    assert L.fp8lin_abi_version() == 3
     assert L.fp8lin_status_name(0) == b"FP8LIN_OK"
     assert L.fp8lin_status_name(2) == b"FP8LIN_ERR_SHAPE"
     assert L.fp8lin_status_name(99) == b"FP8LIN_UNKNOWN_STATUS"

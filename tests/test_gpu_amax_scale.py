@@ -64,3 +64,29 @@ def test_scale_update_matches_oracle(oracle, L, margin):
         new = rng.uniform(0, 10, n).astype(np.float32)
         hist[:, 0] = new
         dh[:, 0] = dev(new)
+
+
+def test_scale_from_current_amax_matches_oracle(oracle):
+    """fp8_scale_from_current_amax over a bank of 40 tensors whose slot-0
+    amaxes span normal, subnormal, huge, zero, Inf and NaN values (the last
+    three keep the old scale), margins 0 and 3; histories are not rolled."""
+    rng = np.random.default_rng(8)
+    n, L = 40, 8
+    fmts = [int(v) for v in rng.integers(0, 2, n)]
+    hist = (np.abs(rng.standard_normal((n, L))) * np.exp2(rng.uniform(-30, 30, (n, L)))).astype(np.float32)
+    hist[0, 0], hist[1, 0], hist[2, 0], hist[3, 0] = 0.0, np.inf, np.nan, 1e-44
+    hist[4, 0], hist[5, 0] = 3.0e38, 2.0 ** -149
+    for margin in (0, 3):
+        bank = F.MetaBank([F.E4M3 if f == 0 else F.E5M2 for f in fmts], L)
+        bank.amax_history.copy_(torch.from_numpy(hist))
+        bank.scale.fill_(2.0)
+        bank.scale_inv.fill_(0.5)
+        bank.scale_from_current(F.Recipe(F.FORMAT_HYBRID, L, F.AMAX_MAX, margin))
+        for t in range(n):
+            m = oracle.Meta(L, fmts[t])
+            m.hist = hist[t].copy()
+            m.scale, m.scale_inv = np.float32(2.0), np.float32(0.5)
+            oracle.scale_from_current(m, margin)
+            assert_bits_equal(np_of(bank.scale[t]), m.scale, f"margin {margin} scale {t}")
+            assert_bits_equal(np_of(bank.scale_inv[t]), m.scale_inv, f"margin {margin} scale_inv {t}")
+        assert_bits_equal(np_of(bank.amax_history), hist, "history untouched")

@@ -38,7 +38,12 @@ def _sel(a, rows):
     return a if rows is None else a[rows]
 
 
-def _check_fwd(oracle, X, W, mx, mw, saved, y_gpu, rows, tag, residual=None, z_gpu=None):
+def _check_fwd(oracle, X, W, mx, mw, saved, y_gpu, rows, tag, residual=None, z_gpu=None, jit=False):
+    if jit:                               # just-in-time: the scales come from this step's amaxes
+        mx.record(X)
+        mw.record(W)
+        oracle.scale_from_current(mx)
+        oracle.scale_from_current(mw)
     xq, xqt = oracle.cast_transpose(X, E4, mx.scale)
     assert_bits_equal(np_of(saved.xq), xq, tag + " Xq")
     assert_bits_equal(np_of(saved.xq_t), xqt, tag + " Xq^T")
@@ -55,12 +60,16 @@ def _check_fwd(oracle, X, W, mx, mw, saved, y_gpu, rows, tag, residual=None, z_g
     assert_gemm_bf16(_sel(np_of(y_gpu), rows), y_ref, oracle, tag + " Y")
     if z_gpu is not None:
         assert_gemm_bf16(_sel(np_of(z_gpu), rows), pre, oracle, tag + " Z")
-    mx.record(X)
-    mw.record(W)
+    if not jit:
+        mx.record(X)
+        mw.record(W)
     return dict(xqt=xqt, wqt=wqt, sinv_x=mx.scale_inv, sinv_w=mw.scale_inv)
 
 
-def _check_bwd(oracle, G, mg, fwd, ws, dx_gpu, dw_gpu, rows, wrows, tag, residual=None):
+def _check_bwd(oracle, G, mg, fwd, ws, dx_gpu, dw_gpu, rows, wrows, tag, residual=None, jit=False):
+    if jit:
+        mg.record(G)
+        oracle.scale_from_current(mg)
     gq, gqt = oracle.cast_transpose(G, E5, mg.scale)
     assert_bits_equal(np_of(ws[0]), gq, tag + " Gq")
     assert_bits_equal(np_of(ws[1]), gqt, tag + " Gq^T")
@@ -70,40 +79,43 @@ def _check_bwd(oracle, G, mg, fwd, ws, dx_gpu, dw_gpu, rows, wrows, tag, residua
     assert_gemm_bf16(_sel(np_of(dx_gpu), rows), dx_ref, oracle, tag + " dX")
     dw_ref = oracle.gemm(gqt, E5, fwd["xqt"], E4, mg.scale_inv, fwd["sinv_x"], rows=wrows)
     assert_gemm_f32(_sel(np_of(dw_gpu), wrows), dw_ref, tag + " dW")
-    mg.record(G)
+    if not jit:
+        mg.record(G)
 
 
 def _check_step(oracle, lay, om, ols, X, rows, wrows, tag):
     """One step of the layer (already run on the GPU up to the update) checked
-    sub-step by sub-step; then the update is run on both sides and compared."""
+    sub-step by sub-step; then the update is run on both sides and compared.
+    The layer's recipe decides delayed or just-in-time scaling."""
+    jit = bool(lay.recipe.just_in_time)
     mt, sv = om, lay.saved
     W = {n: np_of(lay.w[n]) for n in LAYER_WEIGHTS}
-    f_q = _check_fwd(oracle, X, W["wqkv"], mt["x"], mt["wqkv"], sv["qkv"], lay.qkv, rows, tag + " QKV")
+    f_q = _check_fwd(oracle, X, W["wqkv"], mt["x"], mt["wqkv"], sv["qkv"], lay.qkv, rows, tag + " QKV", jit=jit)
     ctx = np_of(lay.ctx)
-    f_o = _check_fwd(oracle, ctx, W["wo"], mt["ctx"], mt["wo"], sv["o"], lay.y1, rows, tag + " O", residual=X)
+    f_o = _check_fwd(oracle, ctx, W["wo"], mt["ctx"], mt["wo"], sv["o"], lay.y1, rows, tag + " O", residual=X, jit=jit)
     Y1 = np_of(lay.y1)
-    f_1 = _check_fwd(oracle, Y1, W["w1"], mt["y1"], mt["w1"], sv["fc1"], lay.h, rows, tag + " FC1", z_gpu=lay.z)
+    f_1 = _check_fwd(oracle, Y1, W["w1"], mt["y1"], mt["w1"], sv["fc1"], lay.h, rows, tag + " FC1", z_gpu=lay.z, jit=jit)
     f_2 = _check_fwd(oracle, np_of(lay.h), W["w2"], mt["h"], mt["w2"], sv["fc2"], lay.y, rows, tag + " FC2",
-                     residual=Y1)
+                     residual=Y1, jit=jit)
     S = np.float32(ols.state[0])
     assert_bits_equal(np_of(lay.ls_state), ols.state, tag + " loss-scale state before the update")
     dY = np_of(lay.dy)
     assert_bits_equal(dY, oracle.scale_by(np_of(lay.g), S), tag + " dY = G*S")
     _check_bwd(oracle, dY, mt["g_fc2"], f_2, lay.gws["fc2"], lay.dh, lay.dw["w2"], rows, wrows,
-               tag + " bwd FC2")
+               tag + " bwd FC2", jit=jit)
     dH, Z, dZ = np_of(lay.dh), np_of(lay.z), np_of(lay.dz)
     assert _bf16_ulps(dZ, oracle.gelu_bwd(dH, Z)).max() <= 1, tag + " dZ"
     del dH, Z
     _check_bwd(oracle, dZ, mt["g_fc1"], f_1, lay.gws["fc1"], lay.dy1, lay.dw["w1"], rows, wrows,
-               tag + " bwd FC1", residual=dY)
+               tag + " bwd FC1", residual=dY, jit=jit)
     del dZ
     dY1 = np_of(lay.dy1)
     _check_bwd(oracle, dY1, mt["g_o"], f_o, lay.gws["o"], lay.dctx, lay.dw["wo"], rows, wrows,
-               tag + " bwd O")
+               tag + " bwd O", jit=jit)
     dQ = np_of(lay.dqkv)
     assert_bits_equal(dQ, oracle.scale_by(np_of(lay.dqkv_in), S), tag + " dqkv*S")
     _check_bwd(oracle, dQ, mt["g_qkv"], f_q, lay.gws["qkv"], lay.dx, lay.dw["wqkv"], rows, wrows,
-               tag + " bwd QKV", residual=dY1)
+               tag + " bwd QKV", residual=dY1, jit=jit)
     for i, name in enumerate(LAYER_TENSORS):
         assert_bits_equal(np_of(lay.bank.amax_history[i, 0]), om[name].hist[0], f"{tag} amax {name}")
     # update: loss scale from the four gradient amaxes, the twelve metas, SGD
@@ -218,3 +230,35 @@ def test_layer_full_size_sampled(oracle):
     torch.cuda.synchronize()
     # the spike's amax sits in the history and keeps X's scale low afterwards
     assert om["x"].hist[2] == oracle.amax(np_of(spiked))
+
+
+def test_layer_spike_just_in_time_versus_delayed(oracle):
+    """The x100 spike under delayed scaling (the scale from the clean steps'
+    history saturates most of X) and, from the same state, under just-in-time
+    scaling (only the largest element reaches the top code).  Both steps are
+    checked against the oracle; the quantisation error of X is compared."""
+    inp = _small_inputs()
+    spiked = synth.layer_spike(inp["x"])
+    S = np_of(spiked)
+    res = {}
+    for jit in (False, True):
+        lay = _layer(inp, 16)
+        om, ols = oracle.layer_metas(16), oracle.LossScale(2.0 ** 16, interval=5)
+        for step in range(3):
+            lay.forward()
+            lay.backward()
+            torch.cuda.synchronize()
+            _check_step(oracle, lay, om, ols, np_of(inp["x"]), None, None, f"jit={jit} step {step}")
+        lay.recipe.just_in_time = int(jit)
+        lay.forward(spiked)
+        lay.backward()
+        torch.cuda.synchronize()
+        _check_step(oracle, lay, om, ols, S, None, None, f"jit={jit} spike step")
+        codes = np_of(lay.saved["qkv"].xq)
+        deq = oracle.bf16_to_f64(oracle.dequant(codes, E4, np.float32(np_of(lay.saved["qkv"].sinv)[0]), 1))
+        xs = oracle.bf16_to_f64(S)
+        res[jit] = (int(np.count_nonzero((codes & 0x7F) == 0x7E)), np.linalg.norm(deq - xs) / np.linalg.norm(xs))
+    print(f"spike step: delayed saturated {res[False][0]} codes, error {res[False][1]:.3e}; "
+          f"just-in-time saturated {res[True][0]}, error {res[True][1]:.3e}", flush=True)
+    assert res[False][0] > 0.5 * S.size and res[True][0] <= 2
+    assert res[True][1] < 0.1 * res[False][1]
