@@ -168,11 +168,11 @@ k_dequant(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ si
 #pragma unroll
             for (int j = 0; j < E; ++j) v[j] = v[j] * si;
             if constexpr (E == 4)
-                o[i] = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                                  __float_as_uint(v[3]));
+                store_nt(o + i, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                           __float_as_uint(v[3])));
             else
-                o[i] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                                  pack_bf16x2(v[6], v[7]));
+                store_nt(o + i, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                           pack_bf16x2(v[6], v[7])));
         }
     }
     for (int64_t i = nvec * E + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
