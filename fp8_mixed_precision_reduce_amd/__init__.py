@@ -26,7 +26,7 @@ FORMAT_E4M3, FORMAT_HYBRID = 0, 1
 AMAX_MAX = 0
 EPI_GELU, EPI_ACCUMULATE, EPI_FAST_ACCUM = 1, 2, 4
 KIND_NAMES = ["amax", "cast", "cast_transpose", "dequant", "scale_update", "gemm", "dbias", "other", "sgd"]
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 FUNCTIONS = [
     "fp8lin_abi_version", "fp8lin_last_error", "fp8lin_status_name", "fp8lin_dbias_workspace_bytes",
@@ -61,6 +61,28 @@ class _MetaC(ctypes.Structure):
     _fields_ = [("amax_history", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("scale_inv", ctypes.c_void_p)]
 
 
+class _QOutC(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_void_p), ("q", ctypes.c_void_p), ("q_t", ctypes.c_void_p),
+                ("fp8_dtype", ctypes.c_int32)]
+
+
+class QOut:
+    """An FP8 copy of a GEMM output, cast in the epilogue: the scale (device
+    float tensor) of the tensor the output becomes, its codes q [m][n] and
+    transposed codes q_t [n][m] (either may be None) and the format."""
+
+    def __init__(self, scale, q=None, q_t=None, fmt=E4M3):
+        self.scale, self.q, self.q_t, self.fmt = scale, q, q_t, fmt
+
+    def c(self):
+        return _QOutC(self.scale.data_ptr(), self.q.data_ptr() if self.q is not None else None,
+                      self.q_t.data_ptr() if self.q_t is not None else None, self.fmt)
+
+
+def _qref(q_out):
+    return ctypes.byref(q_out.c()) if q_out is not None else None
+
+
 class _SavedC(ctypes.Structure):
     _fields_ = [("xq", ctypes.c_void_p), ("xq_t", ctypes.c_void_p), ("wq", ctypes.c_void_p),
                 ("wq_t", ctypes.c_void_p), ("sinv", ctypes.c_void_p)]
@@ -84,8 +106,8 @@ def _load():
         "fp8_cast_transpose_dgelu": (I32, [P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, P]),
         "fp8_cast_transpose_dual": (I32, [P, I32, I64, I64, P, P, P, P, P, P, P, P, P]),
         "fp8_dequant": (I32, [P, I32, I64, P, P, I32, P]),
-        "fp8_gemm": (I32, [P, I32, P, I32, I64, I64, I64, P, P, P, I32, I32, P, I32, P, P, P, P]),
-        "fp8_linear_fwd": (I32, [I64, I64, I64, P, I32, P, I32, P, I32, I32, P, I32, P, P, P,
+        "fp8_gemm": (I32, [P, I32, P, I32, I64, I64, I64, P, P, P, I32, I32, P, I32, P, P, P, P, P]),
+        "fp8_linear_fwd": (I32, [I64, I64, I64, P, I32, P, I32, P, I32, I32, P, I32, P, P, P, P,
                                  ctypes.POINTER(Recipe), ctypes.POINTER(_MetaC), ctypes.POINTER(_MetaC),
                                  ctypes.POINTER(_SavedC), P]),
         "fp8_linear_bwd": (I32, [I64, I64, I64, P, I32, P, P, ctypes.POINTER(Recipe), ctypes.POINTER(_MetaC),
@@ -252,23 +274,29 @@ def fp8_dequant(q, fmt, scale_inv, out, stream=None):
 
 
 def fp8_gemm(a, a_fmt, b, b_fmt, sinv_a, sinv_b, d, bias=None, epilogue=0, aux=None, residual=None, amax_d=None,
-             stream=None):
+             q_out=None, stream=None):
+    """d may be None when q_out is given (its values are still rounded to bf16)."""
     m, k = a.shape
     n = b.shape[0]
     bias_dt = _dt(bias) if bias is not None else F32
+    d_dt = _dt(d) if d is not None else BF16
     _check(_lib.fp8_gemm(_p(a), a_fmt, _p(b), b_fmt, m, n, k, _p(sinv_a), _p(sinv_b), _p(bias), bias_dt, epilogue,
-                         _p(d), _dt(d), _p(aux), _p(residual), _p(amax_d), _stream(stream)))
+                         _p(d), d_dt, _p(aux), _p(residual), _p(amax_d), _qref(q_out), _stream(stream)))
 
 
 def fp8_linear_fwd(x, w, y, recipe, mx, mw, saved, bias=None, epilogue=0, y_aux=None, residual=None,
-                   y_amax_slot=None, stream=None):
-    m, k = x.shape
+                   y_amax_slot=None, y_q=None, stream=None):
+    """x None: X's codes are already in saved (written by the producer's y_q).
+    y None: only the FP8 copy y_q is written (y_dtype bf16)."""
+    m, k = saved.xq.shape if x is None else x.shape
     n = w.shape[0]
     bias_dt = _dt(bias) if bias is not None else F32
+    x_dt = _dt(x) if x is not None else BF16
+    y_dt = _dt(y) if y is not None else BF16
     cx, cw, cs = mx.c(), mw.c(), saved.c()
-    _check(_lib.fp8_linear_fwd(m, n, k, _p(x), _dt(x), _p(w), _dt(w), _p(bias), bias_dt, epilogue, _p(y), _dt(y),
-                               _p(y_aux), _p(residual), _p(y_amax_slot), ctypes.byref(recipe), ctypes.byref(cx),
-                               ctypes.byref(cw), ctypes.byref(cs), _stream(stream)))
+    _check(_lib.fp8_linear_fwd(m, n, k, _p(x), x_dt, _p(w), _dt(w), _p(bias), bias_dt, epilogue, _p(y), y_dt,
+                               _p(y_aux), _p(residual), _p(y_amax_slot), _qref(y_q), ctypes.byref(recipe),
+                               ctypes.byref(cx), ctypes.byref(cw), ctypes.byref(cs), _stream(stream)))
 
 
 def fp8_linear_bwd(dy, k, recipe, mdy, saved, dyq_ws=None, dyq_t_ws=None, dx=None, dw=None, accumulate_dw=False,

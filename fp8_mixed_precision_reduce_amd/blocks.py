@@ -9,6 +9,10 @@ every part of it in the library's kernels:
 
   fp8_linear_fwd(X, W1, GELU)  -> H = gelu(Z) (bf16), Z kept for backward
   fp8_linear_fwd(H, W2)        -> Y (bf16)
+  (fuse_casts=True: H leaves FC1's epilogue already cast to E4M3 -- codes and
+  transposed codes straight into FC2's saved operands, amax(H) into H's history
+  -- and FC2 skips its input cast.  Measured on MI355X the fused epilogue costs
+  the GEMM about what the separate cast costs, so it is off by default.)
   fp8_linear_bwd(dY; W2)       -> dH (bf16), dW2 (fp32)
   fp8_linear_bwd(dH; W1, Z)    -> GeLU backward fused into the dZ cast, dX (bf16), dW1 (fp32)
   fp8_amax_scale_update(6 tensors)
@@ -23,7 +27,7 @@ Page tags: [TE-KR] "Transformer Engine으로 FP8 사용하기" (coniverse.tistor
 """
 import torch
 
-from . import (AMAX_MAX, E4M3, E5M2, EPI_GELU, FORMAT_HYBRID, MetaBank, Recipe, Saved, fp8_linear_bwd,
+from . import (AMAX_MAX, E4M3, E5M2, EPI_GELU, FORMAT_HYBRID, MetaBank, QOut, Recipe, Saved, fp8_linear_bwd,
                fp8_linear_fwd, fp8_loss_scale_apply, fp8_loss_scale_update, fp8_sgd_step)
 
 MLP_TENSORS = ("x", "w1", "h", "w2", "dy", "dz")
@@ -34,9 +38,11 @@ class Fp8MlpBlock:
 
     x [m][hidden], w1 [ffn][hidden], w2 [hidden][ffn], dy [m][hidden]: bf16 (or
     fp32) device tensors owned by the caller.  keep_dz=True also writes the
-    rounded GeLU-backward gradient dZ (for inspection)."""
+    rounded GeLU-backward gradient dZ, keep_h=True the bf16 H (for inspection;
+    with fuse_casts=False H is always written)."""
 
-    def __init__(self, x, w1, w2, dy, history_len=1024, fast_accum=False, keep_dz=False):
+    def __init__(self, x, w1, w2, dy, history_len=1024, fast_accum=False, keep_dz=False, fuse_casts=False,
+                 keep_h=False):
         m, hidden = x.shape
         ffn = w1.shape[0]
         assert w1.shape == (ffn, hidden) and w2.shape == (hidden, ffn) and dy.shape == (m, hidden)
@@ -44,7 +50,8 @@ class Fp8MlpBlock:
         self.m, self.hidden, self.ffn = m, hidden, ffn
         self.x, self.w1, self.w2, self.dy = x, w1, w2, dy
         act = dict(dtype=x.dtype, device=dev)
-        self.h = torch.empty(m, ffn, **act)
+        self.fuse_casts = fuse_casts and x.dtype == torch.bfloat16
+        self.h = torch.empty(m, ffn, **act) if (keep_h or not self.fuse_casts) else None
         self.z = torch.empty(m, ffn, **act)
         self.y = torch.empty(m, hidden, **act)
         self.dh = torch.empty(m, ffn, **act)
@@ -63,8 +70,14 @@ class Fp8MlpBlock:
 
     def forward(self):
         r, mt = self.recipe, self.meta
-        fp8_linear_fwd(self.x, self.w1, self.h, r, mt["x"], mt["w1"], self.saved1, epilogue=EPI_GELU, y_aux=self.z)
-        fp8_linear_fwd(self.h, self.w2, self.y, r, mt["h"], mt["w2"], self.saved2)
+        if self.fuse_casts and not r.just_in_time:
+            hq = QOut(mt["h"].scale, self.saved2.xq, self.saved2.xq_t, E4M3)
+            fp8_linear_fwd(self.x, self.w1, self.h, r, mt["x"], mt["w1"], self.saved1, epilogue=EPI_GELU,
+                           y_aux=self.z, y_q=hq, y_amax_slot=mt["h"].amax_history[0:1])
+            fp8_linear_fwd(None, self.w2, self.y, r, mt["h"], mt["w2"], self.saved2)
+        else:
+            fp8_linear_fwd(self.x, self.w1, self.h, r, mt["x"], mt["w1"], self.saved1, epilogue=EPI_GELU, y_aux=self.z)
+            fp8_linear_fwd(self.h, self.w2, self.y, r, mt["h"], mt["w2"], self.saved2)
 
     def backward(self):
         r, mt = self.recipe, self.meta
@@ -110,11 +123,16 @@ class Fp8TransformerLayer:
     The masters live in one fp32 buffer and their gradients in another, so the
     SGD step is one launch over all parameters.  x, ctx, g, dqkv are bf16
     device tensors of the caller; forward(x_in) may take another input of x's
-    shape (the spiked one).  Residual adds happen in the GEMM epilogues.
+    shape (the spiked one).  Residual adds happen in the GEMM epilogues; with
+    fuse_casts (delayed scaling only; off by default, see the module notes) Y1
+    and H are also cast to E4M3 there, straight into the next linear's saved
+    operands, so FC1 and FC2 skip their input casts (keep_h=True still writes
+    the bf16 H).
     """
 
     def __init__(self, x, ctx, g, dqkv, wqkv, wo, w1, w2, history_len=1024, lr=2.0 ** -10, loss_scale=2.0 ** 16,
-                 growth_interval=5, fast_accum=False, keep_dz=False, keep_codes=False):
+                 growth_interval=5, fast_accum=False, keep_dz=False, keep_codes=False, fuse_casts=False,
+                 keep_h=False):
         m, hid = x.shape
         ffn = w1.shape[0]
         assert wqkv.shape == (3 * hid, hid) and wo.shape == (hid, hid) and w1.shape == (ffn, hid)
@@ -135,10 +153,11 @@ class Fp8TransformerLayer:
             self.dw[name] = self.grad[off:off + n].view(shapes[name])
             off += n          # every size is a multiple of 256 elements: the views stay 16-byte aligned
         act = dict(dtype=x.dtype, device=dev)
+        self.fuse_casts = fuse_casts and x.dtype == torch.bfloat16
         self.qkv = torch.empty(m, 3 * hid, **act)
         self.y1 = torch.empty(m, hid, **act)
         self.z = torch.empty(m, ffn, **act)
-        self.h = torch.empty(m, ffn, **act)
+        self.h = torch.empty(m, ffn, **act) if (keep_h or not self.fuse_casts) else None
         self.y = torch.empty(m, hid, **act)
         self.dy = torch.empty(m, hid, **act)
         self.dh = torch.empty(m, ffn, **act)
@@ -171,9 +190,20 @@ class Fp8TransformerLayer:
         x = self.x if x is None else x
         r, mt, sv, w = self.recipe, self.meta, self.saved, self.w
         fp8_linear_fwd(x, w["wqkv"], self.qkv, r, mt["x"], mt["wqkv"], sv["qkv"])
-        fp8_linear_fwd(self.ctx, w["wo"], self.y1, r, mt["ctx"], mt["wo"], sv["o"], residual=x)
-        fp8_linear_fwd(self.y1, w["w1"], self.h, r, mt["y1"], mt["w1"], sv["fc1"], epilogue=EPI_GELU, y_aux=self.z)
-        fp8_linear_fwd(self.h, w["w2"], self.y, r, mt["h"], mt["w2"], sv["fc2"], residual=self.y1)
+        if self.fuse_casts and not r.just_in_time:
+            # Y1 and H leave their GEMMs already cast to E4M3 for the next linear
+            y1q = QOut(mt["y1"].scale, sv["fc1"].xq, sv["fc1"].xq_t, E4M3)
+            fp8_linear_fwd(self.ctx, w["wo"], self.y1, r, mt["ctx"], mt["wo"], sv["o"], residual=x, y_q=y1q,
+                           y_amax_slot=mt["y1"].amax_history[0:1])
+            hq = QOut(mt["h"].scale, sv["fc2"].xq, sv["fc2"].xq_t, E4M3)
+            fp8_linear_fwd(None, w["w1"], self.h, r, mt["y1"], mt["w1"], sv["fc1"], epilogue=EPI_GELU, y_aux=self.z,
+                           y_q=hq, y_amax_slot=mt["h"].amax_history[0:1])
+            fp8_linear_fwd(None, w["w2"], self.y, r, mt["h"], mt["w2"], sv["fc2"], residual=self.y1)
+        else:
+            fp8_linear_fwd(self.ctx, w["wo"], self.y1, r, mt["ctx"], mt["wo"], sv["o"], residual=x)
+            fp8_linear_fwd(self.y1, w["w1"], self.h, r, mt["y1"], mt["w1"], sv["fc1"], epilogue=EPI_GELU,
+                           y_aux=self.z)
+            fp8_linear_fwd(self.h, w["w2"], self.y, r, mt["h"], mt["w2"], sv["fc2"], residual=self.y1)
 
     def backward(self):
         r, mt, sv, dw = self.recipe, self.meta, self.saved, self.dw

@@ -322,7 +322,7 @@ namespace {
 int32_t check_gemm(const char* fn, const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_dtype, int64_t m,
                    int64_t n, int64_t k, const float* sinv_a, const float* sinv_b, const void* bias,
                    int32_t bias_dtype, int32_t epilogue, void* d, int32_t d_dtype, void* aux, const void* residual,
-                   float* amax_d) {
+                   float* amax_d, const fp8lin_qout* q_out = nullptr) {
     if (!is_fp8(a_dtype) || !is_fp8(b_dtype))
         return fail(FP8LIN_ERR_DTYPE, "%s: operand types %d, %d must be E4M3/E5M2", fn, a_dtype, b_dtype);
     if (!is_hp(d_dtype)) return fail(FP8LIN_ERR_DTYPE, "%s: output type %d must be F32 or BF16", fn, d_dtype);
@@ -339,7 +339,27 @@ int32_t check_gemm(const char* fn, const uint8_t* a, int32_t a_dtype, const uint
         return fail(FP8LIN_ERR_DTYPE, "%s: ACCUMULATE needs an F32 output", fn);
     if (aux && !(epilogue & FP8LIN_EPI_GELU)) return fail(FP8LIN_ERR_ARG, "%s: aux is only written with GELU", fn);
     if (!sinv_a || !sinv_b) return fail(FP8LIN_ERR_NULL, "%s: null scale pointer", fn);
-    if (m * n > 0 && !d) return fail(FP8LIN_ERR_NULL, "%s: null output", fn);
+    if (q_out) {
+        if (d_dtype != FP8LIN_BF16) return fail(FP8LIN_ERR_UNSUPPORTED, "%s: an FP8 copy of the output needs BF16", fn);
+        if (a_dtype != FP8LIN_E4M3 || b_dtype != FP8LIN_E4M3)
+            return fail(FP8LIN_ERR_UNSUPPORTED, "%s: an FP8 copy of the output needs E4M3 x E4M3 operands", fn);
+        if (!is_fp8(q_out->fp8_dtype)) return fail(FP8LIN_ERR_DTYPE, "%s: q_out fp8_dtype %d", fn, q_out->fp8_dtype);
+        if (!q_out->scale) return fail(FP8LIN_ERR_NULL, "%s: q_out has no scale", fn);
+        if (m * n > 0 && !q_out->q && !q_out->q_t) return fail(FP8LIN_ERR_NULL, "%s: q_out has no output", fn);
+        if (!aligned(q_out->scale, 4) || !aligned(q_out->q, 16) || !aligned(q_out->q_t, 16))
+            return fail(FP8LIN_ERR_ALIGN, "%s: q_out misaligned", fn);
+        const int64_t db = m * n * 2;
+        const void* others[7] = {a, b, bias, d, aux, residual, q_out->q_t};
+        const int64_t ob[7] = {m * k, n * k, bias ? n * elem_size(bias_dtype) : 0, d ? db : 0, aux ? db : 0,
+                               residual ? db : 0, q_out->q_t ? m * n : 0};
+        for (int i = 0; i < 7; ++i) {
+            if (q_out->q && overlap(q_out->q, m * n, others[i], ob[i]))
+                return fail(FP8LIN_ERR_ARG, "%s: q_out->q overlaps another buffer", fn);
+            if (i < 6 && q_out->q_t && overlap(q_out->q_t, m * n, others[i], ob[i]))
+                return fail(FP8LIN_ERR_ARG, "%s: q_out->q_t overlaps another buffer", fn);
+        }
+    }
+    if (m * n > 0 && !d && !q_out) return fail(FP8LIN_ERR_NULL, "%s: null output", fn);
     if (m * n * k > 0 && (!a || !b)) return fail(FP8LIN_ERR_NULL, "%s: null operand", fn);
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 16) || !aligned(aux, 16) || !aligned(bias, 16) ||
         !aligned(residual, 16) || !aligned(sinv_a, 4) || !aligned(sinv_b, 4) || !aligned(amax_d, 4))
@@ -365,12 +385,15 @@ int32_t check_gemm(const char* fn, const uint8_t* a, int32_t a_dtype, const uint
 
 int32_t fp8_gemm(const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_dtype, int64_t m, int64_t n, int64_t k,
                  const float* sinv_a, const float* sinv_b, const void* bias, int32_t bias_dtype, int32_t epilogue,
-                 void* d, int32_t d_dtype, void* aux, const void* residual, float* amax_d, void* stream) {
+                 void* d, int32_t d_dtype, void* aux, const void* residual, float* amax_d, const fp8lin_qout* q_out,
+                 void* stream) {
     const int32_t v = check_gemm("fp8_gemm", a, a_dtype, b, b_dtype, m, n, k, sinv_a, sinv_b, bias, bias_dtype,
-                                 epilogue, d, d_dtype, aux, residual, amax_d);
+                                 epilogue, d, d_dtype, aux, residual, amax_d, q_out);
     if (v != FP8LIN_OK) return v;
     return hip_status(launch_gemm(a, a_dtype, b, b_dtype, m, n, k, sinv_a, sinv_b, bias, bias_dtype, epilogue, d,
-                                  d_dtype, aux, residual, amax_d, as_stream(stream)),
+                                  d_dtype, aux, residual, amax_d, q_out ? q_out->scale : nullptr,
+                                  q_out ? q_out->q : nullptr, q_out ? q_out->q_t : nullptr,
+                                  q_out ? q_out->fp8_dtype : 0, as_stream(stream)),
                       "fp8_gemm");
 }
 
@@ -410,8 +433,9 @@ int32_t check_meta(const char* fn, const char* which, const fp8lin_meta* mt) {
 
 int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x_dtype, const void* w,
                        int32_t w_dtype, const void* bias, int32_t bias_dtype, int32_t epilogue, void* y,
-                       int32_t y_dtype, void* y_aux, const void* residual, float* y_amax_slot, const fp8lin_recipe* recipe,
-                       const fp8lin_meta* mx, const fp8lin_meta* mw, const fp8lin_saved* saved, void* stream) {
+                       int32_t y_dtype, void* y_aux, const void* residual, float* y_amax_slot, const fp8lin_qout* y_q,
+                       const fp8lin_recipe* recipe, const fp8lin_meta* mx, const fp8lin_meta* mw,
+                       const fp8lin_saved* saved, void* stream) {
     const char* fn = "fp8_linear_fwd";
     int32_t v;
     if ((v = check_recipe(fn, recipe)) || (v = check_meta(fn, "x", mx)) || (v = check_meta(fn, "w", mw))) return v;
@@ -422,33 +446,47 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
     if (m < 0 || n < 0 || k < 0 || m % 16 || n % 16 || k % 16)
         return fail(FP8LIN_ERR_SHAPE, "%s: m=%lld n=%lld k=%lld must be >= 0 multiples of 16", fn, (long long)m,
                     (long long)n, (long long)k);
-    if (m * k > 0 && !x) return fail(FP8LIN_ERR_NULL, "%s: null x", fn);
+    const bool x_quantised = x == nullptr;      // X's codes are already in saved (cast by the producer)
+    if (x_quantised && recipe->just_in_time)
+        return fail(FP8LIN_ERR_ARG, "%s: a pre-quantised X cannot be scaled just in time", fn);
     if (n * k > 0 && !w) return fail(FP8LIN_ERR_NULL, "%s: null w", fn);
     if (!aligned(saved->sinv, 4)) return fail(FP8LIN_ERR_ALIGN, "%s: saved->sinv misaligned", fn);
     // Validate every sub-call before launching any of them.
-    if ((v = check_ct(fn, x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx->scale, saved->xq, saved->xq_t,
-                      mx->amax_history, nullptr, nullptr, nullptr, false)))
+    if (!x_quantised && (v = check_ct(fn, x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx->scale, saved->xq, saved->xq_t,
+                                      mx->amax_history, nullptr, nullptr, nullptr, false)))
         return v;
+    if (x_quantised && (!aligned(saved->xq, 16) || !aligned(saved->xq_t, 16)))
+        return fail(FP8LIN_ERR_ALIGN, "%s: saved codes misaligned", fn);
     if ((v = check_ct(fn, w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw->scale, saved->wq, saved->wq_t,
                       mw->amax_history, nullptr, nullptr, nullptr, false)))
         return v;
     if ((v = check_gemm(fn, saved->xq, FP8LIN_E4M3, saved->wq, FP8LIN_E4M3, m, n, k, saved->sinv, saved->sinv + 1,
-                        bias, bias_dtype, epilogue | fast, y, y_dtype, y_aux, residual, y_amax_slot)))
+                        bias, bias_dtype, epilogue | fast, y, y_dtype, y_aux, residual, y_amax_slot, y_q)))
         return v;
     if (overlap(y, m * n * elem_size(y_dtype), x, m * k * elem_size(x_dtype)) ||
         overlap(y, m * n * elem_size(y_dtype), w, n * k * elem_size(w_dtype)))
         return fail(FP8LIN_ERR_ARG, "%s: y overlaps an input", fn);
+    if (y_q) {
+        const void* mine[4] = {saved->xq, saved->xq_t, saved->wq, saved->wq_t};
+        const int64_t mb[4] = {m * k, saved->xq_t ? m * k : 0, n * k, saved->wq_t ? n * k : 0};
+        for (int i = 0; i < 4; ++i)
+            if (overlap(y_q->q, y_q->q ? m * n : 0, mine[i], mb[i]) ||
+                overlap(y_q->q_t, y_q->q_t ? m * n : 0, mine[i], mb[i]))
+                return fail(FP8LIN_ERR_ARG, "%s: y_q overlaps this layer's saved codes", fn);
+    }
 
     hipStream_t s = as_stream(stream);
     hipError_t e;
     const bool jit = recipe->just_in_time != 0;
-    if (jit && (e = jit_scale(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx, recipe->margin, s)) != hipSuccess)
-        return hip_status(e, "fp8_linear_fwd: just-in-time scale of X");
-    float* xslot = jit ? nullptr : mx->amax_history;
-    if (saved->xq_t) e = launch_cast_transpose(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx->scale, saved->xq,
-                                               saved->xq_t, xslot, nullptr, nullptr, nullptr, s);
-    else e = launch_cast(x, x_dtype, m * k, FP8LIN_E4M3, mx->scale, saved->xq, xslot, s);
-    if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast X");
+    if (!x_quantised) {
+        if (jit && (e = jit_scale(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx, recipe->margin, s)) != hipSuccess)
+            return hip_status(e, "fp8_linear_fwd: just-in-time scale of X");
+        float* xslot = jit ? nullptr : mx->amax_history;
+        if (saved->xq_t) e = launch_cast_transpose(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx->scale, saved->xq,
+                                                   saved->xq_t, xslot, nullptr, nullptr, nullptr, s);
+        else e = launch_cast(x, x_dtype, m * k, FP8LIN_E4M3, mx->scale, saved->xq, xslot, s);
+        if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast X");
+    }
     if (jit && (e = jit_scale(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw, recipe->margin, s)) != hipSuccess)
         return hip_status(e, "fp8_linear_fwd: just-in-time scale of W");
     float* wslot = jit ? nullptr : mw->amax_history;
@@ -459,7 +497,8 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
     e = launch_copy_scalars(mx->scale_inv, mw->scale_inv, saved->sinv, s);
     if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: save scale_inv");
     e = launch_gemm(saved->xq, FP8LIN_E4M3, saved->wq, FP8LIN_E4M3, m, n, k, saved->sinv, saved->sinv + 1, bias,
-                    bias_dtype, epilogue | fast, y, y_dtype, y_aux, residual, y_amax_slot, s);
+                    bias_dtype, epilogue | fast, y, y_dtype, y_aux, residual, y_amax_slot, y_q ? y_q->scale : nullptr,
+                    y_q ? y_q->q : nullptr, y_q ? y_q->q_t : nullptr, y_q ? y_q->fp8_dtype : 0, s);
     return hip_status(e, "fp8_linear_fwd: gemm");
 }
 
@@ -513,13 +552,13 @@ int32_t fp8_linear_bwd(int64_t m, int64_t n, int64_t k, const void* dy, int32_t 
     if (e != hipSuccess) return hip_status(e, "fp8_linear_bwd: cast dY");
     if (dx) {
         e = launch_gemm(dyq_ws, gfmt, saved->wq_t, FP8LIN_E4M3, m, k, n, mdy->scale_inv, saved->sinv + 1, nullptr,
-                        FP8LIN_F32, fast, dx, dx_dtype, nullptr, dx_residual, nullptr, s);
+                        FP8LIN_F32, fast, dx, dx_dtype, nullptr, dx_residual, nullptr, nullptr, nullptr, nullptr, 0, s);
         if (e != hipSuccess) return hip_status(e, "fp8_linear_bwd: dgrad");
     }
     if (dw) {
         e = launch_gemm(dyq_t_ws, gfmt, saved->xq_t, FP8LIN_E4M3, n, k, m, mdy->scale_inv, saved->sinv, nullptr,
                         FP8LIN_F32, (accumulate_dw ? FP8LIN_EPI_ACCUMULATE : 0) | fast, dw, FP8LIN_F32, nullptr,
-                        nullptr, nullptr, s);
+                        nullptr, nullptr, nullptr, nullptr, nullptr, 0, s);
         if (e != hipSuccess) return hip_status(e, "fp8_linear_bwd: wgrad");
     }
     return ok();

@@ -43,7 +43,7 @@ int64_t cast_transpose_dbias_ws_bytes(int64_t rows, int64_t cols);
 hipError_t launch_gemm(const uint8_t* a, int afmt, const uint8_t* b, int bfmt, int64_t m, int64_t n,
                        int64_t k, const float* sinv_a, const float* sinv_b, const void* bias,
                        int bias_dtype, int epilogue, void* d, int d_dtype, void* aux, const void* residual,
-                       float* amax, hipStream_t s);
+                       float* amax, const float* q_scale, uint8_t* q, uint8_t* qt, int q_fmt, hipStream_t s);
 hipError_t launch_loss_scale_update(const float* amaxes, int32_t n, int64_t stride, float* state,
                                     int32_t interval, float backoff, float growth, hipStream_t s);
 hipError_t launch_sgd(float* w, const float* g, int64_t n, float lr, const float* state, hipStream_t s);

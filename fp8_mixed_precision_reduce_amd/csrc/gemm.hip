@@ -81,6 +81,10 @@ struct GemmParams {
     void* aux;
     const void* residual;
     float* amax;
+    const float* q_scale;      // FP8 copy of the output (bf16 outputs only): scale, codes, transposed codes
+    uint8_t* q;
+    uint8_t* qt;
+    int32_t q_fmt;
     int32_t tiles_m, tiles_n;
     int32_t bias_dtype, d_dtype, epilogue;
 };
@@ -130,6 +134,20 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_bas
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, off, 0, 0, 0);
 }
 
+// 4 x 4 byte transpose: a..d are four rows of four bytes; c0..c3 are the four
+// columns (byte i of column j = byte j of row i).
+__device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t& c0,
+                                             uint32_t& c1, uint32_t& c2, uint32_t& c3) {
+    const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+    const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+    const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u);   // c0 d0 c1 d1
+    const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u);   // c2 d2 c3 d3
+    c0 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);             // a0 b0 c0 d0
+    c1 = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);
+    c2 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
+    c3 = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
+}
+
 // MFMA format selector of an FP8 operand.
 template <int FMT> struct MfmaFmt;
 template <> struct MfmaFmt<kE4M3> { static constexpr int value = 0; };
@@ -151,7 +169,7 @@ __device__ __forceinline__ void tile_coords(int i, int32_t tiles_m, int32_t tile
     tn = rem / gsize;
 }
 
-template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST>
+template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST, bool QOUT>
 __global__ void __launch_bounds__(64 * WM * WN, (WM * WN * MB * NB >= 64 ? (WM * WN) / 4 : 2))
 k_gemm(GemmParams p) {
     using C = TileCfg<WM, WN, MB, NB>;
@@ -434,7 +452,78 @@ k_gemm(GemmParams p) {
                 }
             }
         }
-        stage_store(p.d);
+        if constexpr (!QOUT) {
+            stage_store(p.d);
+        } else {
+            // The output as written (bf16) is also cast to FP8 with the scale of the
+            // tensor it becomes: codes = enc(fl32(bf16 value * scale)), the same
+            // arithmetic as a separate cast of d.  Row-major codes are stored
+            // straight from the staged values; for the transposed codes each
+            // segment of SEG rows goes through a byte tile in an LDS region of its
+            // own (16 KiB; 4-byte words XOR-swizzled by an even function of the
+            // row, so 8-byte pairs stay together) and 4 x 4 byte transposes, as in
+            // the cast-transpose kernel.
+            constexpr int CPR = C::BN / 8;              // 16-byte bf16 chunks (8 values) per row
+            constexpr int RPP = C::THREADS / CPR;       // rows per pass
+            constexpr int HALF = C::BM / 2;
+            constexpr int SEG = (16384 / C::BN) < HALF ? (16384 / C::BN) : HALF;
+            constexpr int NPASS = SEG / RPP;            // passes per segment
+            constexpr int WPR = C::BN / 4;              // 4-byte words per code row
+            static_assert(SEG % RPP == 0 && SEG % 16 == 0 && HALF % SEG == 0, "code segment layout");
+            __shared__ __attribute__((aligned(16))) uint8_t codes[SEG * C::BN];
+            auto code_word = [&](int r, int w) { return r * C::BN + ((w ^ (((r >> 4) << 1) & (WPR - 1))) << 2); };
+            const float qs = *p.q_scale;
+            const int c = t % CPR;
+            __syncthreads();
+#pragma unroll
+            for (int sg = 0; sg < C::BM / SEG; ++sg) {
+#pragma unroll
+                for (int pass = 0; pass < NPASS; ++pass) {
+                    const int lr = t / CPR + RPP * pass;        // row within the segment
+                    const int r = sg * SEG + lr;
+                    const uint4 v = *reinterpret_cast<const uint4*>((r < HALF ? smem0 : smem1) + lds_unit(r % HALF, 2 * c));
+                    const int64_t row = m0 + r, col = n0 + 8 * c;
+                    const bool inside = row < M && col < N;
+                    if (p.d && inside) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.d) + row * N + col) = v;
+                    const float f[8] = {bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
+                                        bf16_to_f32(v.y >> 16),     bf16_to_f32(v.z & 0xFFFFu), bf16_to_f32(v.z >> 16),
+                                        bf16_to_f32(v.w & 0xFFFFu), bf16_to_f32(v.w >> 16)};
+                    const uint2 q8 = p.q_fmt == kE4M3
+                        ? make_uint2(enc4<kE4M3>(f[0] * qs, f[1] * qs, f[2] * qs, f[3] * qs),
+                                     enc4<kE4M3>(f[4] * qs, f[5] * qs, f[6] * qs, f[7] * qs))
+                        : make_uint2(enc4<kE5M2>(f[0] * qs, f[1] * qs, f[2] * qs, f[3] * qs),
+                                     enc4<kE5M2>(f[4] * qs, f[5] * qs, f[6] * qs, f[7] * qs));
+                    if (p.q && inside) *reinterpret_cast<uint2*>(p.q + row * N + col) = q8;
+                    if (p.qt) *reinterpret_cast<uint2*>(codes + code_word(lr, 2 * c)) = q8;
+                }
+                if (p.qt) {
+                    __syncthreads();
+                    constexpr int STRIPS = SEG / 16;
+                    for (int u = t; u < WPR * STRIPS; u += C::THREADS) {
+                        const int cg = u / STRIPS, strip = u % STRIPS;
+                        uint32_t w[16];
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            w[i] = *reinterpret_cast<const uint32_t*>(codes + code_word(strip * 16 + i, cg));
+                        uint32_t o4[4][4];
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk)
+                            transpose4x4(w[4 * kk], w[4 * kk + 1], w[4 * kk + 2], w[4 * kk + 3], o4[0][kk], o4[1][kk],
+                                         o4[2][kk], o4[3][kk]);
+                        const int64_t ocol = m0 + sg * SEG + strip * 16;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int64_t orow = n0 + 4 * cg + j;
+                            if (orow < N && ocol < M)
+                                *reinterpret_cast<uint4*>(p.qt + orow * M + ocol) =
+                                    make_uint4(o4[j][0], o4[j][1], o4[j][2], o4[j][3]);
+                        }
+                    }
+                    __syncthreads();       // the code tile is rewritten by the next segment
+                }
+            }
+            __syncthreads();               // the staged values are read; the next tile may DMA
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
@@ -495,17 +584,17 @@ int resident_per_cu(Kern kern, int threads) {
     return n;
 }
 
-template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST>
+template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST, bool QOUT = false>
 hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
     using C = TileCfg<WM, WN, MB, NB>;
-    static const int per_cu = resident_per_cu(k_gemm<WM, WN, MB, NB, AF, BF, FAST>, C::THREADS);
+    static const int per_cu = resident_per_cu(k_gemm<WM, WN, MB, NB, AF, BF, FAST, QOUT>, C::THREADS);
     // One resident wave of workgroups, each looping over tiles; a multiple of
     // 8 so that every workgroup stays on the same XCD's tile range.
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     int64_t grid = (int64_t)cu_count() * per_cu;
     if (grid >= 8) grid -= grid % 8;
     if (grid > ntiles) grid = ntiles;
-    hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, AF, BF, FAST>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, p);
+    hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, AF, BF, FAST, QOUT>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, p);
     return hipGetLastError();
 }
 
@@ -515,6 +604,8 @@ hipError_t launch_cfg(const GemmParams& base, int afmt, int bfmt, hipStream_t s)
     GemmParams p = base;
     p.tiles_m = (int32_t)((p.m + C::BM - 1) / C::BM);
     p.tiles_n = (int32_t)((p.n + C::BN - 1) / C::BN);
+    // the FP8 copy of the output is built for the forward GEMMs (E4M3 x E4M3) only
+    if (p.q_scale) return launch_fmt<WM, WN, MB, NB, kE4M3, kE4M3, FAST, true>(p, s);
     if (afmt == kE4M3 && bfmt == kE4M3) return launch_fmt<WM, WN, MB, NB, kE4M3, kE4M3, FAST>(p, s);
     if (afmt == kE5M2 && bfmt == kE4M3) return launch_fmt<WM, WN, MB, NB, kE5M2, kE4M3, FAST>(p, s);
     if (afmt == kE4M3) return launch_fmt<WM, WN, MB, NB, kE4M3, kE5M2, FAST>(p, s);
@@ -539,11 +630,13 @@ hipError_t launch_path(const GemmParams& p, int afmt, int bfmt, hipStream_t s) {
 
 hipError_t launch_gemm(const uint8_t* a, int afmt, const uint8_t* b, int bfmt, int64_t m, int64_t n, int64_t k,
                        const float* sinv_a, const float* sinv_b, const void* bias, int bias_dtype, int epilogue,
-                       void* d, int d_dtype, void* aux, const void* residual, float* amax, hipStream_t s) {
+                       void* d, int d_dtype, void* aux, const void* residual, float* amax, const float* q_scale,
+                       uint8_t* q, uint8_t* qt, int q_fmt, hipStream_t s) {
     if (m == 0 || n == 0) return hipSuccess;
     GemmParams p{};
     p.a = a; p.b = b; p.m = m; p.n = n; p.k = k;
     p.sinv_a = sinv_a; p.sinv_b = sinv_b; p.bias = bias; p.d = d; p.aux = aux; p.residual = residual; p.amax = amax;
+    p.q_scale = q_scale; p.q = q; p.qt = qt; p.q_fmt = q_fmt;
     p.bias_dtype = bias_dtype; p.d_dtype = d_dtype; p.epilogue = epilogue;
     timing_before(kKindGemm, s);
     const hipError_t e = (epilogue & kEpiFastAccum) ? launch_path<true>(p, afmt, bfmt, s)

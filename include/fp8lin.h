@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 3
+#define FP8LIN_ABI_VERSION 4
 
 /* Status codes returned by every call. */
 enum {
@@ -127,6 +127,26 @@ typedef struct {
     uint8_t* wq_t;
     float* sinv;
 } fp8lin_saved;
+
+/* An FP8 copy of a GEMM's output, cast in the GEMM epilogue.  With delayed
+ * scaling the factor of a tensor is known before the tensor exists ([TE-KR]
+ * "Scaling factor" strategy: delayed scaling takes it from earlier
+ * iterations), so the layer that produces the tensor can emit it in FP8
+ * directly, with its amax ([PT-VI] torch._scaled_mm example: the scaled GEMM
+ * returns its output and the output's amax), and the next layer skips its
+ * input cast.  Device pointers:
+ *   scale      the output tensor's current scale
+ *   q [m][n], q_t [n][m]   codes, row-major and transposed; either may be NULL
+ *   fp8_dtype  FP8LIN_E4M3 or FP8LIN_E5M2
+ * The codes are exactly those fp8_cast_transpose would produce from the output
+ * as rounded to its type: enc(fl32(bf16(y) * scale)).  bf16 outputs of
+ * E4M3 x E4M3 GEMMs (the forward pass) only. */
+typedef struct {
+    const float* scale;
+    uint8_t* q;
+    uint8_t* q_t;
+    int32_t fp8_dtype;
+} fp8lin_qout;
 
 /* ------------------------------------------------------------------------ */
 
@@ -295,11 +315,16 @@ int32_t fp8_dequant(const uint8_t* q, int32_t fp8_dtype, int64_t n, const float*
  *              It may be d itself (in-place residual add) but must not
  *              otherwise overlap d or aux; not combinable with ACCUMULATE.
  *   amax_d     device float or NULL: max-merged amax of d as written
+ *   q_out      HOST struct or NULL: also write the FP8 codes of d (see
+ *              fp8lin_qout; needs d_dtype BF16).  With q_out, d may be NULL
+ *              (the values are still rounded to bf16 before the cast, and
+ *              amax_d is still of those values).
  */
 int32_t fp8_gemm(const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_dtype,
                  int64_t m, int64_t n, int64_t k, const float* sinv_a, const float* sinv_b,
                  const void* bias, int32_t bias_dtype, int32_t epilogue,
-                 void* d, int32_t d_dtype, void* aux, const void* residual, float* amax_d, void* stream);
+                 void* d, int32_t d_dtype, void* aux, const void* residual, float* amax_d,
+                 const fp8lin_qout* q_out, void* stream);
 
 /*
  * fp8_linear_fwd -- forward of Y = X W^T + b on FP8 copies of X and W.
@@ -317,15 +342,23 @@ int32_t fp8_gemm(const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_
  *   epilogue  0 or FP8LIN_EPI_GELU (then y_aux, if not NULL, gets y before GeLU)
  *   y_dtype   F32 or BF16
  *   residual  [m][n] of y_dtype or NULL, added as in fp8_gemm (may equal y)
+ *   y_q       HOST struct or NULL: the FP8 copy of Y for the next layer, cast
+ *             in the epilogue (fp8_gemm's q_out; y may then be NULL); pass the
+ *             next tensor's meta scale, its saved codes, and its amax slot as
+ *             y_amax_slot
  *   mx, mw    HOST structs of device pointers (metas of X and W)
  *   saved     HOST struct of device pointers; xq, wq, sinv required
+ * x may be NULL: X's codes are then already in saved->xq (and saved->xq_t),
+ * cast with mx->scale by the producer's y_q; the call copies *mx->scale_inv
+ * into saved->sinv[0] and records no amax of X (the producer did).  Not with
+ * recipe->just_in_time.
  */
 int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k,
                        const void* x, int32_t x_dtype, const void* w, int32_t w_dtype,
                        const void* bias, int32_t bias_dtype, int32_t epilogue,
                        void* y, int32_t y_dtype, void* y_aux, const void* residual, float* y_amax_slot,
-                       const fp8lin_recipe* recipe, const fp8lin_meta* mx, const fp8lin_meta* mw,
-                       const fp8lin_saved* saved, void* stream);
+                       const fp8lin_qout* y_q, const fp8lin_recipe* recipe, const fp8lin_meta* mx,
+                       const fp8lin_meta* mw, const fp8lin_saved* saved, void* stream);
 
 /*
  * fp8_linear_bwd -- backward of the FP8 linear from the forward's saved state.

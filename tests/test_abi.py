@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_names():
-    assert L.fp8lin_abi_version() == 3
+    assert L.fp8lin_abi_version() == 4
     assert L.fp8lin_status_name(0) == b"FP8LIN_OK"
     assert L.fp8lin_status_name(2) == b"FP8LIN_ERR_SHAPE"
     assert L.fp8lin_status_name(99) == b"FP8LIN_UNKNOWN_STATUS"
@@ -99,8 +99,9 @@ def test_dequant_validation():
 
 
 def _gemm(m=64, n=64, k=64, a_dt=F.E4M3, b_dt=F.E4M3, d_dt=F.F32, epi=0, aux=None, bias=None, bias_dt=F.F32,
-          d=P(1 << 30), sa=P(1 << 32), sb=P(1 << 33), residual=None):
-    return L.fp8_gemm(A16, a_dt, B16, b_dt, m, n, k, sa, sb, bias, bias_dt, epi, d, d_dt, aux, residual, None, None)
+          d=P(1 << 30), sa=P(1 << 32), sb=P(1 << 33), residual=None, q_out=None):
+    return L.fp8_gemm(A16, a_dt, B16, b_dt, m, n, k, sa, sb, bias, bias_dt, epi, d, d_dt, aux, residual, None, q_out,
+                      None)
 
 
 def test_gemm_validation():
@@ -151,14 +152,14 @@ def test_linear_validation():
     meta = F._MetaC(1 << 36, (1 << 36) + 4096, (1 << 36) + 8192)
     saved = F._SavedC(1 << 37, 1 << 38, 1 << 39, 1 << 40, 1 << 41)
     fwd = L.fp8_linear_fwd
-    args = [A16, F.F32, B16, F.F32, None, F.F32, 0, C16, F.F32, None, None, None, ctypes.byref(r), ctypes.byref(meta),
+    args = [A16, F.F32, B16, F.F32, None, F.F32, 0, C16, F.F32, None, None, None, None, ctypes.byref(r), ctypes.byref(meta),
             ctypes.byref(meta), ctypes.byref(saved), None]
     assert _err(fwd(64, 64, 60, *args)) == F.ERR_SHAPE
     args_acc = list(args)
     args_acc[6] = F.EPI_ACCUMULATE
     assert _err(fwd(64, 64, 64, *args_acc)) == F.ERR_ARG
     no_saved = list(args)
-    no_saved[15] = None
+    no_saved[16] = None
     assert _err(fwd(64, 64, 64, *no_saved)) == F.ERR_NULL
     bwd = L.fp8_linear_bwd
     saved_no_t = F._SavedC(1 << 37, None, 1 << 39, None, 1 << 41)
@@ -177,6 +178,30 @@ def test_linear_validation():
     bad_fmt = _recipe(format=5)
     assert _err(bwd(64, 64, 64, A16, F.F32, None, None, ctypes.byref(bad_fmt), ctypes.byref(meta),
                     ctypes.byref(saved), B16, C16, None, F.F32, None, None, 0, None, None, None)) == F.ERR_ARG
+
+
+def test_gemm_q_out_validation():
+    qs = P(1 << 35)
+    def q(scale=qs, qq=P(1 << 36), qt=P(1 << 37), fmt=F.E4M3):
+        return ctypes.byref(F._QOutC(scale, qq, qt, fmt))
+    assert _err(_gemm(d_dt=F.F32, q_out=q())) == F.ERR_UNSUPPORTED              # bf16 outputs only
+    assert _err(_gemm(d_dt=F.BF16, q_out=q(fmt=F.BF16))) == F.ERR_DTYPE
+    assert _err(_gemm(d_dt=F.BF16, q_out=q(scale=None))) == F.ERR_NULL
+    assert _err(_gemm(d_dt=F.BF16, q_out=q(qq=None, qt=None))) == F.ERR_NULL
+    assert _err(_gemm(d_dt=F.BF16, q_out=q(qq=P((1 << 36) + 8)))) == F.ERR_ALIGN
+    assert _err(_gemm(d_dt=F.BF16, q_out=q(qq=P(1 << 30)))) == F.ERR_ARG          # codes overlap d
+    assert _err(_gemm(d_dt=F.BF16, q_out=q(qt=P(1 << 36)))) == F.ERR_ARG          # q and q_t overlap
+    assert _err(_gemm(d_dt=F.BF16, d=None)) == F.ERR_NULL                         # no output at all
+    assert _gemm(m=0, d_dt=F.BF16, d=None, q_out=q()) == F.OK
+
+
+def test_linear_prequantised_x_validation():
+    r = F.Recipe(just_in_time=1)
+    meta = F._MetaC(1 << 36, (1 << 36) + 4096, (1 << 36) + 8192)
+    saved = F._SavedC(1 << 37, 1 << 38, 1 << 39, 1 << 40, 1 << 41)
+    fwd = L.fp8_linear_fwd
+    assert _err(fwd(64, 64, 64, None, F.BF16, B16, F.F32, None, F.F32, 0, C16, F.F32, None, None, None, None,
+                    ctypes.byref(r), ctypes.byref(meta), ctypes.byref(meta), ctypes.byref(saved), None)) == F.ERR_ARG
 
 
 def test_loss_scale_and_sgd_validation():

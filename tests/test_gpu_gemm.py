@@ -223,3 +223,44 @@ def test_gemm_residual(oracle, shape, out_dtype, in_place):
                 assert_gemm_bf16(np_of(ax)[rows], pre, oracle, tag + " aux")
         full = got.astype(np.float64) if out_dtype == torch.float32 else oracle.bf16_to_f64(got)
         assert_bits_equal(np_of(amax)[0], np.float32(np.max(np.abs(full))), tag + " amax of d as written")
+
+
+@pytest.mark.parametrize("fmt", [(F.E4M3, 0), (F.E5M2, 1)], ids=["e4m3", "e5m2"])
+@pytest.mark.parametrize("shape", [(80, 48, 400), (272, 528, 400), (2048, 1536, 512), (1040, 4096, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gemm_fp8_output(oracle, shape, fmt):
+    """The epilogue's FP8 copy of a bf16 output (GeLU and residual on): the
+    codes and transposed codes equal the oracle's cast-transpose of the bf16
+    output as written, with the given scale; without d the same codes come
+    out and the amax is unchanged.  Covers the 64, 128 and 256 tile
+    configurations with ragged tails."""
+    lf, of = fmt
+    m, n, k = shape
+    rng = np.random.default_rng(m + 5 * n + k + lf)
+    a = _codes(oracle, rng, (m, k), 0)
+    b = _codes(oracle, rng, (n, k), 0)
+    sa, sb = np.float32(0.05), np.float32(0.7)
+    r = oracle.bf16_from_f32(rng.standard_normal((m, n)).astype(np.float32))
+    qs = np.float32(37.5 if lf == F.E4M3 else 3000.0)
+    outs = []
+    for with_d in (True, False):
+        d = torch.empty(m, n, dtype=torch.bfloat16, device="cuda") if with_d else None
+        ax = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+        q = torch.full((m, n), 0xA5, dtype=torch.uint8, device="cuda")
+        qt = torch.full((n, m), 0xA5, dtype=torch.uint8, device="cuda")
+        amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+        F.fp8_gemm(dev(a), F.E4M3, dev(b), F.E4M3, _scalar(float(sa)), _scalar(float(sb)), d, epilogue=F.EPI_GELU,
+                   aux=ax, residual=dev(r), amax_d=amax, q_out=F.QOut(_scalar(float(qs)), q, qt, lf))
+        outs.append((np_of(d) if with_d else None, np_of(q), np_of(qt), np_of(amax)[0]))
+    D, q1, qt1, a1 = outs[0]
+    wq, wqt = oracle.cast_transpose(D, of, qs)
+    assert_bits_equal(q1, wq, "codes")
+    assert_bits_equal(qt1, wqt, "transposed codes")
+    assert_bits_equal(a1, oracle.amax(D), "amax of d as written")
+    _, q2, qt2, a2 = outs[1]
+    assert_bits_equal(q2, q1, "codes without d")
+    assert_bits_equal(qt2, qt1, "transposed codes without d")
+    assert_bits_equal(a2, a1, "amax without d")
+    rows = np.unique(np.concatenate([np.arange(16), rng.integers(0, m, 32), [m - 1]]))
+    y = oracle.gemm(a, 0, b, 0, sa, sb, gelu=True, rows=rows)
+    assert_gemm_bf16(D[rows], oracle.add_residual(y, r[rows]), oracle, "d")

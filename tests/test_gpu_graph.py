@@ -44,7 +44,7 @@ def test_mlp_block_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         junk = torch.randn(1 << 20, device="cuda").sum()     # unrelated eager work between replays
         tag = f"replay {rep}"
-        for name in ("h", "z", "y", "dh", "dx", "dw1", "dw2", "dyq", "dzq"):
+        for name in ("z", "y", "dh", "dx", "dw1", "dw2", "dyq", "dzq"):
             assert_bits_equal(np_of(getattr(graphed, name)), np_of(getattr(eager, name)), f"{tag} {name}")
         for what in ("amax_history", "scale", "scale_inv"):
             assert_bits_equal(np_of(getattr(graphed.bank, what)), np_of(getattr(eager.bank, what)), f"{tag} {what}")
@@ -66,7 +66,7 @@ def test_layer_step_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         tag = f"replay {rep}"
-        for name in ("qkv", "y1", "h", "y", "dx", "dctx", "grad", "master", "ls_state"):
+        for name in ("qkv", "y1", "z", "y", "dx", "dctx", "grad", "master", "ls_state"):
             assert_bits_equal(np_of(getattr(graphed, name)), np_of(getattr(eager, name)), f"{tag} {name}")
         for what in ("amax_history", "scale", "scale_inv"):
             assert_bits_equal(np_of(getattr(graphed.bank, what)), np_of(getattr(eager.bank, what)), f"{tag} {what}")

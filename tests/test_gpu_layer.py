@@ -136,7 +136,7 @@ def _check_step(oracle, lay, om, ols, X, rows, wrows, tag):
 
 def _layer(inp, history_len, **kw):
     return Fp8TransformerLayer(inp["x"], inp["ctx"], inp["g"], inp["dqkv"], inp["wqkv"], inp["wo"], inp["w1"],
-                               inp["w2"], history_len=history_len, lr=LR, keep_dz=True, keep_codes=True, **kw)
+                               inp["w2"], history_len=history_len, lr=LR, keep_dz=True, keep_codes=True, keep_h=True, **kw)
 
 
 def _oracle_state_from(oracle, lay):
@@ -173,6 +173,20 @@ def test_layer_small_ragged_with_spike(oracle):
         _check_step(oracle, lay, om, ols, np_of(x_in), None, None, f"step {step}")
     assert ols.state[0] == 2.0 ** 17                       # grown after five clean steps
     assert om["x"].hist[3] == oracle.amax(np_of(spiked))    # the spike's amax, rolled by three updates
+
+
+def test_layer_small_fused_casts(oracle):
+    """The layer with Y1 and H cast to E4M3 in their GEMMs' epilogues (FC1 and
+    FC2 take pre-quantised inputs): every code, amax and output as in the
+    separate-cast path, 3 steps."""
+    inp = _small_inputs()
+    lay = _layer(inp, 16, fuse_casts=True)
+    om, ols = oracle.layer_metas(16), oracle.LossScale(2.0 ** 16, interval=5)
+    for step in range(3):
+        lay.forward()
+        lay.backward()
+        torch.cuda.synchronize()
+        _check_step(oracle, lay, om, ols, np_of(inp["x"]), None, None, f"fused step {step}")
 
 
 def test_layer_inf_gradient_skips_sgd(oracle):

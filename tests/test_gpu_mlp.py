@@ -95,17 +95,19 @@ def _run_steps(oracle, blk, steps, rows, wrows):
             assert_bits_equal(np_of(blk.bank.scale_inv[i]), om[name].scale_inv, f"{tag} scale_inv {name}")
 
 
-def test_mlp_block_small_ragged_all_outputs(oracle):
+@pytest.mark.parametrize("fused", [False, True], ids=["separate_casts", "fused_h_cast"])
+def test_mlp_block_small_ragged_all_outputs(oracle, fused):
     m, hidden, ffn = 272, 208, 464
     x, w1, w2, dy = synth.mlp_inputs(0, device="cpu", m=m, hidden=hidden, ffn=ffn)
-    blk = Fp8MlpBlock(x.cuda(), w1.cuda(), w2.cuda(), dy.cuda(), history_len=16, keep_dz=True)
+    blk = Fp8MlpBlock(x.cuda(), w1.cuda(), w2.cuda(), dy.cuda(), history_len=16, keep_dz=True, keep_h=True,
+                      fuse_casts=fused)
     _run_steps(oracle, blk, steps=4, rows=None, wrows=None)
 
 
 def test_mlp_block_full_size_sampled(oracle):
     """8192 tokens x hidden 4096 x FFN 14336 (the benchmark's block), 2 steps."""
     x, w1, w2, dy = synth.mlp_inputs(0, device="cuda")
-    blk = Fp8MlpBlock(x, w1, w2, dy, history_len=1024, keep_dz=True)
+    blk = Fp8MlpBlock(x, w1, w2, dy, history_len=1024, keep_dz=True, keep_h=True)
     rng = np.random.default_rng(7)
     rows = np.sort(rng.choice(8192, 12, replace=False))
     wrows = np.sort(rng.choice(4096, 4, replace=False))
