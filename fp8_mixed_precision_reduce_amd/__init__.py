@@ -25,8 +25,9 @@ F32, BF16, E4M3, E5M2 = 0, 1, 2, 3
 FORMAT_E4M3, FORMAT_HYBRID = 0, 1
 AMAX_MAX = 0
 EPI_GELU, EPI_ACCUMULATE, EPI_FAST_ACCUM = 1, 2, 4
-KIND_NAMES = ["amax", "cast", "cast_transpose", "dequant", "scale_update", "gemm", "dbias", "other", "sgd"]
-ABI_VERSION = 4
+KIND_NAMES = ["amax", "cast", "cast_transpose", "dequant", "scale_update", "gemm", "dbias", "other", "sgd",
+              "attention"]
+ABI_VERSION = 5
 
 FUNCTIONS = [
     "fp8lin_abi_version", "fp8lin_last_error", "fp8lin_status_name", "fp8lin_dbias_workspace_bytes",
@@ -34,6 +35,7 @@ FUNCTIONS = [
     "fp8_cast_transpose_dual",
     "fp8_dequant", "fp8_gemm", "fp8_linear_fwd", "fp8_linear_bwd", "fp8_loss_scale_update",
     "fp8_loss_scale_apply", "fp8_sgd_step", "fp8lin_timing_enable", "fp8lin_timing_read",
+    "bf16_attention_workspace_bytes", "bf16_attention_fwd", "bf16_attention_bwd",
 ]
 
 
@@ -116,6 +118,9 @@ def _load():
         "fp8_loss_scale_apply": (I32, [P, I32, I64, P, P, P]),
         "fp8_sgd_step": (I32, [P, P, I64, ctypes.c_float, P, P]),
         "fp8lin_timing_enable": (I32, [I32]),
+        "bf16_attention_workspace_bytes": (I64, [I64, I64, I64, I64, I32]),
+        "bf16_attention_fwd": (I32, [P, I64, I64, I64, I64, P, P, P, P]),
+        "bf16_attention_bwd": (I32, [P, P, P, P, I64, I64, I64, I64, P, P, P]),
         "fp8lin_timing_read": (I32, [P, P, I32]),
     }
     for name, (res, args) in sig.items():
@@ -344,3 +349,37 @@ def timing_read(max_records=1 << 16):
     ms = (ctypes.c_float * max_records)()
     n = _lib.fp8lin_timing_read(ctypes.cast(kinds, ctypes.c_void_p), ctypes.cast(ms, ctypes.c_void_p), max_records)
     return [(KIND_NAMES[kinds[i]], ms[i]) for i in range(n)]
+
+
+# ------------------------------------------------------------- attention core
+
+def attention_workspace_bytes(batch, seq, heads, head_dim=128, backward=False):
+    """Bytes of device workspace bf16_attention_fwd (backward=False) or
+    bf16_attention_bwd needs; -1 for an unsupported shape."""
+    return _lib.bf16_attention_workspace_bytes(batch, seq, heads, head_dim, int(bool(backward)))
+
+
+def _attn_shape(qkv, batch, heads):
+    if qkv.dtype != torch.bfloat16 or qkv.dim() != 2:
+        raise TypeError("attention: qkv must be a 2-D bfloat16 tensor [batch*seq, 3*heads*head_dim]")
+    tokens, cols = qkv.shape
+    if tokens % batch or cols % (3 * heads):
+        raise ValueError(f"attention: qkv shape {tuple(qkv.shape)} does not split into batch={batch}, heads={heads}")
+    return tokens // batch, cols // (3 * heads)
+
+
+def bf16_attention_fwd(qkv, batch, heads, ctx, lse, workspace, stream=None):
+    """ctx [batch*seq, heads*D] bf16 = softmax(Q K^T / sqrt(D)) V per (batch,
+    head) from qkv [batch*seq, 3*heads*D] ([Q | K | V], head-major); lse
+    float32 [batch, heads, seq] (base-2 log-sum-exp, kept for the backward);
+    workspace: a uint8 device tensor of attention_workspace_bytes(...) bytes."""
+    seq, d = _attn_shape(qkv, batch, heads)
+    _check(_lib.bf16_attention_fwd(_p(qkv), batch, seq, heads, d, _p(ctx), _p(lse), _p(workspace), _stream(stream)))
+
+
+def bf16_attention_bwd(qkv, ctx, lse, dctx, batch, heads, dqkv, workspace, stream=None):
+    """dqkv [batch*seq, 3*heads*D] bf16 = the gradient of <ctx, dctx> with
+    respect to qkv (all three parts written), from the forward's qkv, ctx, lse."""
+    seq, d = _attn_shape(qkv, batch, heads)
+    _check(_lib.bf16_attention_bwd(_p(qkv), _p(ctx), _p(lse), _p(dctx), batch, seq, heads, d, _p(dqkv),
+                                   _p(workspace), _stream(stream)))

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfp8lin.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["elementwise.hip", "cast_transpose.hip", "gemm.hip", "training.hip", "api.cpp"]
+SOURCES = ["elementwise.hip", "cast_transpose.hip", "gemm.hip", "training.hip", "attention.hip", "api.cpp"]
 
 
 def hipcc():

@@ -600,4 +600,73 @@ int32_t fp8_sgd_step(float* w, const float* g, int64_t n, float lr, const float*
     return hip_status(launch_sgd(w, g, n, lr, state, as_stream(stream)), fn);
 }
 
+
+// ------------------------------------------------------------ attention core
+namespace {
+// Validates the shape; on success sets the element counts of one head-split
+// tensor (batch*seq*heads*128) and returns FP8LIN_OK.
+int32_t check_attn_shape(const char* fn, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, int64_t* n) {
+    if (head_dim != 128) return fail(FP8LIN_ERR_UNSUPPORTED, "%s: head_dim=%lld (only 128)", fn, (long long)head_dim);
+    if (batch < 1 || heads < 1 || seq < 256 || seq % 256 != 0)
+        return fail(FP8LIN_ERR_SHAPE, "%s: batch=%lld heads=%lld seq=%lld (seq a multiple of 256)", fn,
+                    (long long)batch, (long long)heads, (long long)seq);
+    if (batch > (1 << 20) || heads > (1 << 20) || seq > (1 << 24) || batch * seq * heads * 128 >= (int64_t(1) << 31))
+        return fail(FP8LIN_ERR_SHAPE, "%s: batch*seq*heads*head_dim must be < 2^31", fn);
+    *n = batch * seq * heads * 128;
+    return FP8LIN_OK;
+}
+}  // namespace
+
+int64_t bf16_attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, int32_t backward) {
+    int64_t n = 0;
+    if (check_attn_shape("bf16_attention_workspace_bytes", batch, seq, heads, head_dim, &n) != FP8LIN_OK) return -1;
+    return backward ? 3 * n * 2 + batch * heads * seq * 4 : n * 2;
+}
+
+int32_t bf16_attention_fwd(const void* qkv, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void* ctx,
+                           float* lse, void* workspace, void* stream) {
+    const char* fn = "bf16_attention_fwd";
+    int64_t n = 0;
+    const int32_t st = check_attn_shape(fn, batch, seq, heads, head_dim, &n);
+    if (st != FP8LIN_OK) return st;
+    if (!qkv || !ctx || !lse || !workspace) return fail(FP8LIN_ERR_NULL, "%s: null pointer", fn);
+    if (!aligned(qkv, 16) || !aligned(ctx, 16) || !aligned(lse, 16) || !aligned(workspace, 16))
+        return fail(FP8LIN_ERR_ALIGN, "%s: misaligned pointer", fn);
+    const int64_t lb = batch * heads * seq * 4;
+    const void* bufs[4] = {qkv, ctx, lse, workspace};
+    const int64_t bytes[4] = {3 * n * 2, n * 2, lb, n * 2};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(bufs[i], bytes[i], bufs[j], bytes[j])) return fail(FP8LIN_ERR_ARG, "%s: buffers overlap", fn);
+    const uint16_t* q = static_cast<const uint16_t*>(qkv);
+    return hip_status(launch_attention_fwd(q, batch, seq, heads, static_cast<uint16_t*>(ctx), lse,
+                                           static_cast<uint16_t*>(workspace), as_stream(stream)), fn);
+}
+
+int32_t bf16_attention_bwd(const void* qkv, const void* ctx, const float* lse, const void* dctx, int64_t batch,
+                           int64_t seq, int64_t heads, int64_t head_dim, void* dqkv, void* workspace, void* stream) {
+    const char* fn = "bf16_attention_bwd";
+    int64_t n = 0;
+    const int32_t st = check_attn_shape(fn, batch, seq, heads, head_dim, &n);
+    if (st != FP8LIN_OK) return st;
+    if (!qkv || !ctx || !lse || !dctx || !dqkv || !workspace) return fail(FP8LIN_ERR_NULL, "%s: null pointer", fn);
+    if (!aligned(qkv, 16) || !aligned(ctx, 16) || !aligned(lse, 16) || !aligned(dctx, 16) || !aligned(dqkv, 16) ||
+        !aligned(workspace, 16))
+        return fail(FP8LIN_ERR_ALIGN, "%s: misaligned pointer", fn);
+    const int64_t lb = batch * heads * seq * 4;
+    const int64_t wsb = 3 * n * 2 + lb;
+    const void* ins[4] = {qkv, ctx, lse, dctx};
+    const int64_t inb[4] = {3 * n * 2, n * 2, lb, n * 2};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(dqkv, 3 * n * 2, ins[i], inb[i]) || overlap(workspace, wsb, ins[i], inb[i]))
+            return fail(FP8LIN_ERR_ARG, "%s: an output or the workspace overlaps an input", fn);
+    if (overlap(dqkv, 3 * n * 2, workspace, wsb)) return fail(FP8LIN_ERR_ARG, "%s: dqkv overlaps the workspace", fn);
+    uint16_t* ws = static_cast<uint16_t*>(workspace);
+    return hip_status(launch_attention_bwd(static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(ctx), lse,
+                                           static_cast<const uint16_t*>(dctx), batch, seq, heads,
+                                           static_cast<uint16_t*>(dqkv), ws, ws + n, ws + 2 * n,
+                                           reinterpret_cast<float*>(ws + 3 * n), as_stream(stream)),
+                      fn);
+}
+
 }  // extern "C"

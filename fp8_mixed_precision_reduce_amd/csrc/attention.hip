@@ -1,0 +1,569 @@
+// bf16 scaled dot-product attention (no mask) between the fused QKV
+// projection and the output projection of the transformer layer: forward and
+// backward on the v_mfma_f32_32x32x16_bf16 matrix cores.
+//
+// Per batch b and head h (head width D = 128):
+//   S = Q K^T / sqrt(D),  P = softmax(S) over the keys,  O = P V;
+//   backward for dO: dV = P^T dO, dP = dO V^T, dS = P (dP - rowsum(dO * O)),
+//   dQ = dS K / sqrt(D), dK = dS^T Q / sqrt(D).
+// The pages run this core in bf16 between the FP8 linears ([PT-VI], the
+// vision-transformer workload); they do not write it out, so this is the
+// textbook form.  Q, K, V are the [Q | K | V] column parts of the projection
+// output [B*S][3*H*D] (head h owns columns h*D .. h*D+D-1 of each part); O and
+// dO are [B*S][H*D]; dQ, dK, dV are written to the matching parts of
+// dqkv [B*S][3*H*D].
+//
+// Numerics: products of bf16 values are exact in the MFMA and summed in fp32;
+// the softmax runs in fp32 in the base-2 domain (x * log2(e) / sqrt(D), then
+// v_exp_f32); P and dS are rounded to bf16 (RNE) as operands of the second
+// products; the normaliser sums the fp32 P.  The forward saves
+// lse2 = m + log2(l) per query (log2 domain) so that the backward recomputes
+// P = exp2(S log2(e)/sqrt(D) - lse2) without a second pass.
+//
+// MFMA operand layout used throughout (32x32x16, 8 bf16 per lane): the first
+// operand gives row i = lane % 32, the second column j = lane % 32, and lane
+// group g = lane / 32 gives 8 values of the contraction index, the same 8 for
+// both operands; accumulator register r of lane l holds
+// D[8 (r / 4) + 4 g + r % 4][l % 32].  When a score tile feeds the next product
+// (P V, P^T dO, dS K, dS^T Q) its accumulators must hold 8 consecutive keys
+// (or queries) per lane group: the row operand of the score product therefore
+// reads row sigma(i) for MFMA row i, with sigma swapping bits 2 and 3, so
+// register r of group g holds index 16 (r / 8) + 8 g + r % 8.
+//
+// V (forward), Q, K and dO (backward) are also needed with the token index
+// contiguous; a transpose kernel writes those copies ([H*D][B*S]) into the
+// caller's workspace first.
+#include "common.h"
+
+namespace fp8lin {
+namespace {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef float v8f __attribute__((ext_vector_type(8)));
+
+constexpr int kD = 128;            // head width
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int sigma(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+__device__ __forceinline__ v8bf lds16(const uint8_t* p) { return __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(p)); }
+__device__ __forceinline__ v8bf as_bf(uint4 u) { return __builtin_bit_cast(v8bf, v4u{u.x, u.y, u.z, u.w}); }
+__device__ __forceinline__ v4u ldg16(const void* p) { return *reinterpret_cast<const v4u*>(p); }
+__device__ __forceinline__ void sts16(uint8_t* p, v4u v) { *reinterpret_cast<v4u*>(p) = v; }
+
+// Eight fp32 accumulators (registers r0 .. r0+7) to eight bf16, RNE.
+__device__ __forceinline__ v8bf pack8(const v16f& a, int r0) {
+    v8f v = {a[r0], a[r0 + 1], a[r0 + 2], a[r0 + 3], a[r0 + 4], a[r0 + 5], a[r0 + 6], a[r0 + 7]};
+    return __builtin_convertvector(v, v8bf);
+}
+
+__device__ __forceinline__ v16f mfma(v8bf a, v8bf b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row-major tiles of 256-byte rows (a head's D = 128 bf16): the 16-byte chunk
+// index is XOR-swizzled by the row's low 4 bits, so 16 rows with distinct low
+// bits (the sigma-permuted rows of a quarter wave) hit 16 distinct bank groups.
+__device__ __forceinline__ int off256(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+// 128-byte rows (64 tokens): chunk swizzled by (row >> 1) & 7 (two rows span the 64 banks).
+__device__ __forceinline__ int off128(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// 64-byte rows (32 tokens): chunk swizzled by (row >> 2) & 3 (four rows span the 64 banks).
+__device__ __forceinline__ int off64(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+// Logical block index: undo the round-robin dealing of workgroups over the 8
+// XCDs, so consecutive logical blocks (the same batch and head, which share
+// K and V or Q and dO) run on one XCD and share its L2.
+__device__ __forceinline__ int xcd_block(int i, int n) {
+    const int q = n / kXcds, r = n % kXcds;
+    const int xcd = i % kXcds, local = i / kXcds;
+    return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+struct AttnShape {
+    int32_t batch, seq, heads;
+    float c2;              // log2(e) / sqrt(D)
+    float scale;           // 1 / sqrt(D)
+};
+
+// ------------------------------------------------------------------ forward
+// Workgroup: 8 waves, 256 queries of one (b, h), 32 per wave.  Key blocks of
+// 64 go through a double-buffered LDS tile: K [64][256 B] and V^T [128][128 B].
+constexpr int kFwdQ = 256, kFwdK = 64, kFwdThreads = 512;
+constexpr int kFwdBuf = 64 * 256 + 128 * 128;
+
+__global__ void __launch_bounds__(kFwdThreads, 1)
+k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, uint16_t* __restrict__ ctx,
+           float* __restrict__ lse, AttnShape sh) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kFwdBuf];
+    const int S = sh.seq, H = sh.heads;
+    const int64_t BS = (int64_t)sh.batch * S, HD = (int64_t)H * kD, ld = 3 * HD;
+    const int qblocks = S / kFwdQ;
+    const int id = xcd_block(blockIdx.x, gridDim.x);
+    const int qb = id % qblocks, h = (id / qblocks) % H, b = id / (qblocks * H);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+    const int64_t tok0 = (int64_t)b * S;
+    const int q = qb * kFwdQ + w * 32 + l32;          // this lane's query
+
+    // Q fragments (second operand of S^T = K Q^T): lane's query, d = 16 st + 8 g ..
+    v8bf qf[8];
+    {
+        const uint16_t* qrow = qkv + (tok0 + q) * ld + (int64_t)h * kD;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) qf[st] = as_bf(*reinterpret_cast<const uint4*>(qrow + 16 * st + 8 * g));
+    }
+    // Tile loads: thread t moves 16-byte chunks t and t + 512 of K and of V^T.
+    const uint16_t* kbase = qkv + tok0 * ld + HD + (int64_t)h * kD;
+    const uint16_t* vbase = vt + (int64_t)h * kD * BS + tok0;
+    v4u st0, st1, st2, st3;
+    const int c1 = t + kFwdThreads;
+    auto load = [&](int k0) __attribute__((always_inline)) {
+        st0 = ldg16(kbase + (int64_t)(k0 + (t >> 4)) * ld + (t & 15) * 8);
+        st1 = ldg16(kbase + (int64_t)(k0 + (c1 >> 4)) * ld + (c1 & 15) * 8);
+        st2 = ldg16(vbase + (int64_t)(t >> 3) * BS + k0 + (t & 7) * 8);
+        st3 = ldg16(vbase + (int64_t)(c1 >> 3) * BS + k0 + (c1 & 7) * 8);
+    };
+    auto store = [&](uint8_t* buf) __attribute__((always_inline)) {
+        sts16(buf + off256(t >> 4, t & 15), st0);
+        sts16(buf + off256(c1 >> 4, c1 & 15), st1);
+        sts16(buf + 64 * 256 + off128(t >> 3, t & 7), st2);
+        sts16(buf + 64 * 256 + off128(c1 >> 3, c1 & 7), st3);
+    };
+
+    v16f o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
+    float m2 = -__builtin_inff(), lsum = 0.0f;
+
+    const int nblk = S / kFwdK;
+    load(0);
+    store(smem);
+    __syncthreads();
+    for (int j = 0; j < nblk; ++j) {
+        const uint8_t* buf = smem + (j & 1) * kFwdBuf;
+        if (j + 1 < nblk) load((j + 1) * kFwdK);
+        // S^T tiles: keys 32 kt + sigma(i) of the block against the lane's query.
+        v16f s[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[kt][e] = 0.0f;
+            const int row = 32 * kt + sigma(l32);
+#pragma unroll
+            for (int st = 0; st < 8; ++st) s[kt] = mfma(lds16(buf + off256(row, 2 * st + g)), qf[st], s[kt]);
+        }
+        // Online softmax in the base-2 domain; the two lane groups of a query
+        // share its running maximum.
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                s[kt][e] *= sh.c2;
+                mx = fmaxf(mx, s[kt][e]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m2, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+        m2 = mnew;
+        float ps = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                s[kt][e] = __builtin_amdgcn_exp2f(s[kt][e] - mnew);
+                ps += s[kt][e];
+            }
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+        // O^T += V^T P: keys 16 ks + 8 g + slot, registers 8 (ks & 1) + slot of tile ks / 2.
+        v8bf pb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) pb[ks] = pack8(s[ks >> 1], 8 * (ks & 1));
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                o[dt] = mfma(lds16(buf + 64 * 256 + off128(32 * dt + l32, 2 * ks + g)), pb[ks], o[dt]);
+        if (j + 1 < nblk) store(smem + ((j + 1) & 1) * kFwdBuf);
+        __syncthreads();
+    }
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float inv = 1.0f / ltot;
+    uint16_t* orow = ctx + (tok0 + q) * HD + (int64_t)h * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int d = 32 * dt + 8 * r4 + 4 * g;
+            *reinterpret_cast<uint2*>(orow + d) =
+                make_uint2(pack_bf16x2(o[dt][4 * r4] * inv, o[dt][4 * r4 + 1] * inv),
+                           pack_bf16x2(o[dt][4 * r4 + 2] * inv, o[dt][4 * r4 + 3] * inv));
+        }
+    if (g == 0) lse[((int64_t)b * H + h) * S + q] = m2 + __builtin_amdgcn_logf(ltot);
+}
+
+// ------------------------------------------------------------ transposes
+// out[c][r] = in[r * ld + c] for a rows x cols bf16 view (both multiples of
+// 64): 64 x 64 tiles through LDS, 16-byte loads and stores.
+__global__ void __launch_bounds__(256)
+k_transpose_bf16(const uint16_t* __restrict__ in, int64_t ld, int64_t rows, int64_t cols, uint16_t* __restrict__ out) {
+    __shared__ uint16_t tile[64][64 + 2];
+    const int64_t tiles_c = cols / 64;
+    const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * 64, c0 = (int64_t)(blockIdx.x % tiles_c) * 64;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int c = t + 256 * u, row = c >> 3, cc = (c & 7) * 8;
+        const uint4 v = *reinterpret_cast<const uint4*>(in + (r0 + row) * ld + c0 + cc);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            tile[row][cc + 2 * e] = (uint16_t)(w4[e] & 0xFFFFu);
+            tile[row][cc + 2 * e + 1] = (uint16_t)(w4[e] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int c = t + 256 * u, orow = c >> 3, rr = (c & 7) * 8;
+        uint32_t w4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w4[e] = (uint32_t)tile[rr + 2 * e][orow] | ((uint32_t)tile[rr + 2 * e + 1][orow] << 16);
+        *reinterpret_cast<uint4*>(out + (c0 + orow) * rows + r0 + rr) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+}
+
+// Dq[b][h][s] = sum_d dO * O (fp32): 16 lanes per (token, head), 8 d each,
+// then a fixed xor-shuffle tree.
+__global__ void __launch_bounds__(256)
+k_attn_rowdot(const uint16_t* __restrict__ dctx, const uint16_t* __restrict__ ctx, float* __restrict__ dq_rows,
+              AttnShape sh) {
+    const int64_t HD = (int64_t)sh.heads * kD;
+    const int64_t unit = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;       // (token, head)
+    const int sub = threadIdx.x & 15;
+    const int64_t n = (int64_t)sh.batch * sh.seq * sh.heads;
+    if (unit >= n) return;
+    const int64_t tok = unit / sh.heads;
+    const int h = (int)(unit % sh.heads);
+    const int64_t off = tok * HD + (int64_t)h * kD + sub * 8;
+    const uint4 a = *reinterpret_cast<const uint4*>(dctx + off);
+    const uint4 c = *reinterpret_cast<const uint4*>(ctx + off);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        acc += bf16_to_f32(aw[e] & 0xFFFFu) * bf16_to_f32(cw[e] & 0xFFFFu);
+        acc += bf16_to_f32(aw[e] >> 16) * bf16_to_f32(cw[e] >> 16);
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+    if (sub == 0) {
+        const int64_t b = tok / sh.seq, s = tok % sh.seq;
+        dq_rows[(b * sh.heads + h) * sh.seq + s] = acc;
+    }
+}
+
+// ------------------------------------------------------------ dK and dV
+// Workgroup: 8 waves, 256 keys of one (b, h), 32 per wave (each lane one key;
+// its K fragments in registers, the workgroup's V rows in LDS for the whole
+// kernel).  Query blocks of 32 go through a double-buffered LDS tile: Q and dO
+// [32][256 B], Q^T and dO^T [128][64 B], lse2 and Dq [32].
+constexpr int kKvKeys = 256, kKvQ = 32, kKvThreads = 512;
+constexpr int kKvQt = 32 * 256, kKvBuf = 2 * 32 * 256 + 2 * 128 * 64 + 2 * 32 * 4;
+
+__global__ void __launch_bounds__(kKvThreads, 1)
+k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx, const uint16_t* __restrict__ qt,
+              const uint16_t* __restrict__ dot, const float* __restrict__ lse, const float* __restrict__ dq_rows,
+              uint16_t* __restrict__ dqkv, AttnShape sh) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kKvBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t vtile[kKvKeys * 256];
+    const int S = sh.seq, H = sh.heads;
+    const int64_t BS = (int64_t)sh.batch * S, HD = (int64_t)H * kD, ld = 3 * HD;
+    const int kblocks = S / kKvKeys;
+    const int id = xcd_block(blockIdx.x, gridDim.x);
+    const int kb = id % kblocks, h = (id / kblocks) % H, b = id / (kblocks * H);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+    const int64_t tok0 = (int64_t)b * S;
+    const int key = kb * kKvKeys + w * 32 + l32;
+
+    v8bf kf[8];
+    {
+        const uint16_t* krow = qkv + (tok0 + key) * ld + HD + (int64_t)h * kD;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) kf[st] = as_bf(*reinterpret_cast<const uint4*>(krow + 16 * st + 8 * g));
+        // the workgroup's 256 V rows: 4096 chunks of 16 bytes, 8 per thread
+        const uint16_t* vrows = qkv + (tok0 + kb * kKvKeys) * ld + 2 * HD + (int64_t)h * kD;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int c = t + u * kKvThreads;
+            sts16(vtile + off256(c >> 4, c & 15), ldg16(vrows + (int64_t)(c >> 4) * ld + (c & 15) * 8));
+        }
+    }
+    const int vrow = w * 32 + l32;
+    const uint16_t* qbase = qkv + tok0 * ld + (int64_t)h * kD;
+    const uint16_t* dobase = dctx + tok0 * HD + (int64_t)h * kD;
+    const uint16_t* qtbase = qt + (int64_t)h * kD * BS + tok0;
+    const uint16_t* dotbase = dot + (int64_t)h * kD * BS + tok0;
+    const float* lbase = lse + ((int64_t)b * H + h) * S;
+    const float* dbase = dq_rows + ((int64_t)b * H + h) * S;
+    // 16-byte chunks: 512 of Q (32 rows x 16), 512 of dO, 512 of Q^T (128 rows x 4),
+    // 512 of dO^T; thread t takes chunk t of each; threads 0..15 also lse2 and Dq.
+    v4u st0, st1, st2, st3, sv = {0u, 0u, 0u, 0u};
+    auto load = [&](int q0) __attribute__((always_inline)) {
+        st0 = ldg16(qbase + (int64_t)(q0 + (t >> 4)) * ld + (t & 15) * 8);
+        st1 = ldg16(dobase + (int64_t)(q0 + (t >> 4)) * HD + (t & 15) * 8);
+        st2 = ldg16(qtbase + (int64_t)(t >> 2) * BS + q0 + (t & 3) * 8);
+        st3 = ldg16(dotbase + (int64_t)(t >> 2) * BS + q0 + (t & 3) * 8);
+        if (t < 16) sv = ldg16(t < 8 ? lbase + q0 + 4 * t : dbase + q0 + 4 * (t - 8));
+    };
+    auto store = [&](uint8_t* buf) __attribute__((always_inline)) {
+        sts16(buf + off256(t >> 4, t & 15), st0);
+        sts16(buf + kKvQt + off256(t >> 4, t & 15), st1);
+        sts16(buf + 2 * kKvQt + off64(t >> 2, t & 3), st2);
+        sts16(buf + 2 * kKvQt + 128 * 64 + off64(t >> 2, t & 3), st3);
+        if (t < 16) sts16(buf + 2 * kKvQt + 2 * 128 * 64 + 16 * t, sv);
+    };
+
+    v16f dk[4], dv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { dk[i][e] = 0.0f; dv[i][e] = 0.0f; }
+
+    const int nblk = S / kKvQ;
+    load(0);
+    store(smem);
+    __syncthreads();
+    for (int j = 0; j < nblk; ++j) {
+        const uint8_t* buf = smem + (j & 1) * kKvBuf;
+        const uint8_t* sq = buf;
+        const uint8_t* sdo = buf + kKvQt;
+        const uint8_t* sqt = buf + 2 * kKvQt;
+        const uint8_t* sdot = sqt + 128 * 64;
+        const float* sl = reinterpret_cast<const float*>(sqt + 2 * 128 * 64);
+        if (j + 1 < nblk) load((j + 1) * kKvQ);
+        // S and dP tiles, rows = queries sigma(i) of the block, column = the lane's key.
+        v16f s, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { s[e] = 0.0f; dp[e] = 0.0f; }
+        const int row = sigma(l32);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            s = mfma(lds16(sq + off256(row, 2 * st + g)), kf[st], s);
+            dp = mfma(lds16(sdo + off256(row, 2 * st + g)), lds16(vtile + off256(vrow, 2 * st + g)), dp);
+        }
+        // register r holds query 16 (r / 8) + 8 g + r % 8 of the block: P and
+        // dS for registers 8 hb .. 8 hb + 7 from 8 consecutive lse2 and Dq values
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const float4 la = *reinterpret_cast<const float4*>(sl + 16 * hb + 8 * g);
+            const float4 lc = *reinterpret_cast<const float4*>(sl + 16 * hb + 8 * g + 4);
+            const float4 da = *reinterpret_cast<const float4*>(sl + 32 + 16 * hb + 8 * g);
+            const float4 dc = *reinterpret_cast<const float4*>(sl + 32 + 16 * hb + 8 * g + 4);
+            const float lq[8] = {la.x, la.y, la.z, la.w, lc.x, lc.y, lc.z, lc.w};
+            const float dq[8] = {da.x, da.y, da.z, da.w, dc.x, dc.y, dc.z, dc.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = __builtin_amdgcn_exp2f(s[8 * hb + e] * sh.c2 - lq[e]);
+                s[8 * hb + e] = p;
+                dp[8 * hb + e] = p * (dp[8 * hb + e] - dq[e]);
+            }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS: queries 16 ks + 8 g + slot = registers 8 ks + slot.
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const v8bf pb = pack8(s, 8 * ks), sb = pack8(dp, 8 * ks);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                dv[dt] = mfma(lds16(sdot + off64(32 * dt + l32, 2 * ks + g)), pb, dv[dt]);
+                dk[dt] = mfma(lds16(sqt + off64(32 * dt + l32, 2 * ks + g)), sb, dk[dt]);
+            }
+        }
+        if (j + 1 < nblk) store(smem + ((j + 1) & 1) * kKvBuf);
+        __syncthreads();
+    }
+    // register r of tile dt holds d = 32 dt + 8 (r / 4) + 4 g + r % 4 of the lane's key
+    uint16_t* krow = dqkv + (tok0 + key) * ld + HD + (int64_t)h * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int d = 32 * dt + 8 * r4 + 4 * g;
+            const float c = sh.scale;
+            *reinterpret_cast<uint2*>(krow + d) =
+                make_uint2(pack_bf16x2(dk[dt][4 * r4] * c, dk[dt][4 * r4 + 1] * c),
+                           pack_bf16x2(dk[dt][4 * r4 + 2] * c, dk[dt][4 * r4 + 3] * c));
+            *reinterpret_cast<uint2*>(krow + HD + d) =
+                make_uint2(pack_bf16x2(dv[dt][4 * r4], dv[dt][4 * r4 + 1]),
+                           pack_bf16x2(dv[dt][4 * r4 + 2], dv[dt][4 * r4 + 3]));
+        }
+}
+
+// ------------------------------------------------------------------- dQ
+// Workgroup: 8 waves, 256 queries of one (b, h), 32 per wave (Q and dO
+// fragments in registers).  Key blocks of 32: K and V [32][256 B], K^T [128][64 B].
+constexpr int kQQ = 256, kQK = 32, kQThreads = 512;
+constexpr int kQKt = 32 * 256, kQBuf = 2 * 32 * 256 + 128 * 64;
+
+__global__ void __launch_bounds__(kQThreads, 1)
+k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx, const uint16_t* __restrict__ kt,
+             const float* __restrict__ lse, const float* __restrict__ dq_rows, uint16_t* __restrict__ dqkv,
+             AttnShape sh) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kQBuf];
+    const int S = sh.seq, H = sh.heads;
+    const int64_t BS = (int64_t)sh.batch * S, HD = (int64_t)H * kD, ld = 3 * HD;
+    const int qblocks = S / kQQ;
+    const int id = xcd_block(blockIdx.x, gridDim.x);
+    const int qb = id % qblocks, h = (id / qblocks) % H, b = id / (qblocks * H);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+    const int64_t tok0 = (int64_t)b * S;
+    const int q = qb * kQQ + w * 32 + l32;
+
+    v8bf qf[8], df[8];
+    {
+        const uint16_t* qrow = qkv + (tok0 + q) * ld + (int64_t)h * kD;
+        const uint16_t* drow = dctx + (tok0 + q) * HD + (int64_t)h * kD;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            qf[st] = as_bf(*reinterpret_cast<const uint4*>(qrow + 16 * st + 8 * g));
+            df[st] = as_bf(*reinterpret_cast<const uint4*>(drow + 16 * st + 8 * g));
+        }
+    }
+    const float lq = lse[((int64_t)b * H + h) * S + q];
+    const float dd = dq_rows[((int64_t)b * H + h) * S + q];
+    const uint16_t* kbase = qkv + tok0 * ld + HD + (int64_t)h * kD;
+    const uint16_t* ktbase = kt + (int64_t)h * kD * BS + tok0;
+    // 16-byte chunks: 512 of K (32 rows x 16), 512 of V, 512 of K^T (128 rows x 4).
+    v4u st0, st1, st2;
+    auto load = [&](int k0) __attribute__((always_inline)) {
+        st0 = ldg16(kbase + (int64_t)(k0 + (t >> 4)) * ld + (t & 15) * 8);
+        st1 = ldg16(kbase + HD + (int64_t)(k0 + (t >> 4)) * ld + (t & 15) * 8);
+        st2 = ldg16(ktbase + (int64_t)(t >> 2) * BS + k0 + (t & 3) * 8);
+    };
+    auto store = [&](uint8_t* buf) __attribute__((always_inline)) {
+        sts16(buf + off256(t >> 4, t & 15), st0);
+        sts16(buf + kQKt + off256(t >> 4, t & 15), st1);
+        sts16(buf + 2 * kQKt + off64(t >> 2, t & 3), st2);
+    };
+
+    v16f acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+
+    const int nblk = S / kQK;
+    load(0);
+    store(smem);
+    __syncthreads();
+    for (int j = 0; j < nblk; ++j) {
+        const uint8_t* buf = smem + (j & 1) * kQBuf;
+        if (j + 1 < nblk) load((j + 1) * kQK);
+        v16f s, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { s[e] = 0.0f; dp[e] = 0.0f; }
+        const int row = sigma(l32);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            s = mfma(lds16(buf + off256(row, 2 * st + g)), qf[st], s);
+            dp = mfma(lds16(buf + kQKt + off256(row, 2 * st + g)), df[st], dp);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dp[e] = __builtin_amdgcn_exp2f(s[e] * sh.c2 - lq) * (dp[e] - dd);
+        // dQ^T += K^T dS: keys 16 ks + 8 g + slot = registers 8 ks + slot
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const v8bf sb = pack8(dp, 8 * ks);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+                acc[dt] = mfma(lds16(buf + 2 * kQKt + off64(32 * dt + l32, 2 * ks + g)), sb, acc[dt]);
+        }
+        if (j + 1 < nblk) store(smem + ((j + 1) & 1) * kQBuf);
+        __syncthreads();
+    }
+    uint16_t* qrow = dqkv + (tok0 + q) * ld + (int64_t)h * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int d = 32 * dt + 8 * r4 + 4 * g;
+            const float c = sh.scale;
+            *reinterpret_cast<uint2*>(qrow + d) =
+                make_uint2(pack_bf16x2(acc[dt][4 * r4] * c, acc[dt][4 * r4 + 1] * c),
+                           pack_bf16x2(acc[dt][4 * r4 + 2] * c, acc[dt][4 * r4 + 3] * c));
+        }
+}
+
+AttnShape make_shape(int64_t batch, int64_t seq, int64_t heads) {
+    AttnShape sh;
+    sh.batch = (int32_t)batch; sh.seq = (int32_t)seq; sh.heads = (int32_t)heads;
+    sh.scale = (float)(1.0 / 11.313708498984761);                 // 1 / sqrt(128)
+    sh.c2 = (float)(1.4426950408889634 / 11.313708498984761);     // log2(e) / sqrt(128)
+    return sh;
+}
+
+hipError_t transpose(const uint16_t* in, int64_t ld, int64_t rows, int64_t cols, uint16_t* out, hipStream_t s) {
+    const int64_t tiles = (rows / 64) * (cols / 64);
+    hipLaunchKernelGGL(k_transpose_bf16, dim3((unsigned)tiles), dim3(256), 0, s, in, ld, rows, cols, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Shapes are validated by the caller: seq a multiple of 256, head width 128,
+// batch * seq * heads * 128 elements within the int32 index range of a tile.
+hipError_t launch_attention_fwd(const uint16_t* qkv, int64_t batch, int64_t seq, int64_t heads, uint16_t* ctx,
+                                float* lse, uint16_t* vt_ws, hipStream_t s) {
+    const AttnShape sh = make_shape(batch, seq, heads);
+    const int64_t BS = batch * seq, HD = heads * kD;
+    timing_before(kKindOther, s);
+    hipError_t e = transpose(qkv + 2 * HD, 3 * HD, BS, HD, vt_ws, s);
+    timing_after(s);
+    if (e != hipSuccess) return e;
+    timing_before(kKindAttn, s);
+    const int64_t blocks = batch * heads * (seq / kFwdQ);
+    hipLaunchKernelGGL(k_attn_fwd, dim3((unsigned)blocks), dim3(kFwdThreads), 0, s, qkv, vt_ws, ctx, lse, sh);
+    e = hipGetLastError();
+    timing_after(s);
+    return e;
+}
+
+hipError_t launch_attention_bwd(const uint16_t* qkv, const uint16_t* ctx, const float* lse, const uint16_t* dctx,
+                                int64_t batch, int64_t seq, int64_t heads, uint16_t* dqkv, uint16_t* qt_ws,
+                                uint16_t* kt_ws, uint16_t* dot_ws, float* rows_ws, hipStream_t s) {
+    const AttnShape sh = make_shape(batch, seq, heads);
+    const int64_t BS = batch * seq, HD = heads * kD;
+    timing_before(kKindOther, s);
+    hipError_t e = transpose(qkv, 3 * HD, BS, HD, qt_ws, s);
+    if (e == hipSuccess) e = transpose(qkv + HD, 3 * HD, BS, HD, kt_ws, s);
+    if (e == hipSuccess) e = transpose(dctx, HD, BS, HD, dot_ws, s);
+    if (e == hipSuccess) {
+        const int64_t units = BS * heads;
+        hipLaunchKernelGGL(k_attn_rowdot, dim3((unsigned)((units * 16 + 255) / 256)), dim3(256), 0, s, dctx, ctx,
+                           rows_ws, sh);
+        e = hipGetLastError();
+    }
+    timing_after(s);
+    if (e != hipSuccess) return e;
+    timing_before(kKindAttn, s);
+    hipLaunchKernelGGL(k_attn_bwd_kv, dim3((unsigned)(batch * heads * (seq / kKvKeys))), dim3(kKvThreads), 0, s, qkv,
+                       dctx, qt_ws, dot_ws, lse, rows_ws, dqkv, sh);
+    e = hipGetLastError();
+    timing_after(s);
+    if (e != hipSuccess) return e;
+    timing_before(kKindAttn, s);
+    hipLaunchKernelGGL(k_attn_bwd_q, dim3((unsigned)(batch * heads * (seq / kQQ))), dim3(kQThreads), 0, s, qkv, dctx,
+                       kt_ws, lse, rows_ws, dqkv, sh);
+    e = hipGetLastError();
+    timing_after(s);
+    return e;
+}
+
+}  // namespace fp8lin

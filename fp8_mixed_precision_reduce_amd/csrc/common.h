@@ -13,7 +13,8 @@ enum Dtype : int32_t { kF32 = 0, kBF16 = 1, kE4M3 = 2, kE5M2 = 3 };
 
 // Kinds of kernels, as reported by the event timer.
 enum Kind : int32_t { kKindAmax = 0, kKindCast = 1, kKindCastT = 2, kKindDequant = 3,
-                      kKindScaleUpdate = 4, kKindGemm = 5, kKindDbias = 6, kKindOther = 7, kKindSgd = 8 };
+                      kKindScaleUpdate = 4, kKindGemm = 5, kKindDbias = 6, kKindOther = 7, kKindSgd = 8,
+                      kKindAttn = 9 };
 
 // Host side: record events around a launch when timing is enabled.
 void timing_before(int kind, hipStream_t stream);
@@ -48,6 +49,11 @@ hipError_t launch_loss_scale_update(const float* amaxes, int32_t n, int64_t stri
                                     int32_t interval, float backoff, float growth, hipStream_t s);
 hipError_t launch_sgd(float* w, const float* g, int64_t n, float lr, const float* state, hipStream_t s);
 hipError_t launch_scale_by(const void* x, int dtype, int64_t n, const float* state, void* out, hipStream_t s);
+hipError_t launch_attention_fwd(const uint16_t* qkv, int64_t batch, int64_t seq, int64_t heads, uint16_t* ctx,
+                                float* lse, uint16_t* vt_ws, hipStream_t s);
+hipError_t launch_attention_bwd(const uint16_t* qkv, const uint16_t* ctx, const float* lse, const uint16_t* dctx,
+                                int64_t batch, int64_t seq, int64_t heads, uint16_t* dqkv, uint16_t* qt_ws,
+                                uint16_t* kt_ws, uint16_t* dot_ws, float* rows_ws, hipStream_t s);
 
 #ifdef __HIPCC__
 // ------------------------------------------------------------ device helpers

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 4
+#define FP8LIN_ABI_VERSION 5
 
 /* Status codes returned by every call. */
 enum {
@@ -438,6 +438,52 @@ int32_t fp8_loss_scale_apply(const void* g, int32_t dtype, int64_t n, const floa
 int32_t fp8_sgd_step(float* w, const float* g, int64_t n, float lr, const float* state, void* stream);
 
 /*
+ * bf16 attention core between the fused QKV projection and the output
+ * projection of a transformer layer ([PT-VI], its vision-transformer
+ * workload: multi-head attention in bf16 between FP8 linears; the pages do not
+ * write the core out, so this is textbook scaled dot-product attention with no
+ * mask).  Per batch b and head h, with D = head_dim:
+ *   S = Q K^T / sqrt(D), P = softmax(S) over the keys, O = P V;
+ *   backward for dO: dV = P^T dO, dP = dO V^T, dS = P (dP - rowsum(dO * O)),
+ *   dQ = dS K / sqrt(D), dK = dS^T Q / sqrt(D).
+ * Layouts (bf16, row-major):
+ *   qkv   [batch*seq][3*heads*D]: columns [Q | K | V], head h at columns
+ *         h*D .. h*D+D-1 of each part (token index b*seq + s)
+ *   ctx   [batch*seq][heads*D]: O, same head layout (the output projection's input)
+ *   lse   device float[batch][heads][seq]: m + log2(l) of each query's
+ *         softmax in the base-2 domain (scores times log2(e)/sqrt(D)), saved
+ *         by the forward for the backward
+ * Numerics: bf16 products exact, fp32 sums; softmax in fp32; P and dS rounded
+ * to bf16 as operands of the second products; outputs rounded to bf16 (RNE).
+ * Inf/NaN inputs give unspecified (non-finite) outputs.
+ * Supported: head_dim == 128 (else FP8LIN_ERR_UNSUPPORTED), seq a multiple of
+ * 256, batch*seq*heads*128 < 2^31.
+ * Workspaces (caller-owned device memory, 16-byte aligned, contents not
+ * preserved): bf16_attention_workspace_bytes(batch, seq, heads, head_dim,
+ * backward) bytes: the forward holds V^T, the backward Q^T, K^T, dO^T and
+ * rowsum(dO * O).
+ */
+int64_t bf16_attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
+                                       int32_t backward);
+
+/*
+ * bf16_attention_fwd -- ctx = attention(qkv), lse saved for the backward.
+ *   qkv in; ctx, lse out (must not overlap qkv, each other or the workspace).
+ */
+int32_t bf16_attention_fwd(const void* qkv, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
+                           void* ctx, float* lse, void* workspace, void* stream);
+
+/*
+ * bf16_attention_bwd -- dqkv = gradient of <ctx, dctx> with respect to qkv,
+ * from the forward's qkv, ctx and lse.  All three parts of dqkv are written
+ * (overwritten, not accumulated).
+ *   qkv, ctx, lse, dctx in; dqkv out (must not overlap the inputs or the workspace).
+ */
+int32_t bf16_attention_bwd(const void* qkv, const void* ctx, const float* lse, const void* dctx, int64_t batch,
+                           int64_t seq, int64_t heads, int64_t head_dim, void* dqkv, void* workspace,
+                           void* stream);
+
+/*
  * Kernel timing.  fp8lin_timing_enable(capacity) makes the library record a
  * pair of HIP events around each of its next `capacity` kernel launches
  * (0 disables and frees the events).  fp8lin_timing_read waits for the
@@ -448,7 +494,7 @@ int32_t fp8_sgd_step(float* w, const float* g, int64_t n, float lr, const float*
 enum {
     FP8LIN_KIND_AMAX = 0, FP8LIN_KIND_CAST = 1, FP8LIN_KIND_CAST_TRANSPOSE = 2,
     FP8LIN_KIND_DEQUANT = 3, FP8LIN_KIND_SCALE_UPDATE = 4, FP8LIN_KIND_GEMM = 5,
-    FP8LIN_KIND_DBIAS = 6, FP8LIN_KIND_OTHER = 7, FP8LIN_KIND_SGD = 8
+    FP8LIN_KIND_DBIAS = 6, FP8LIN_KIND_OTHER = 7, FP8LIN_KIND_SGD = 8, FP8LIN_KIND_ATTENTION = 9
 };
 int32_t fp8lin_timing_enable(int32_t capacity);
 int32_t fp8lin_timing_read(int32_t* kinds, float* ms, int32_t max);

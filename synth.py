@@ -22,6 +22,9 @@ Workloads:
              the bf16 attention core: a context tensor ctx bf16 8192x8192 ~ N(0,1) and a
              gradient d(QKV) bf16 8192x24576 ~ N(0,1) * 2^-20; the spiked input of iteration 10
              is bf16(fl32(X) * 100)
+  attention  the bf16 attention core of the layer (64 heads of width 128 over seq 4096 x batch 2):
+             its input qkv bf16 [batch*seq][3*heads*128] ~ N(0, std^2) and an incoming gradient
+             dctx bf16 [batch*seq][heads*128] ~ N(0,1) (smaller shapes for the parity cases)
 """
 import math
 
@@ -133,3 +136,13 @@ def layer_inputs(device="cpu", m=8192, hidden=8192, ffn=28672):
 def layer_spike(x, factor=100.0):
     """The spiked layer input: bf16(fl32(x) * factor)."""
     return (x.float() * factor).to(torch.bfloat16)
+
+
+def attention_inputs(batch, seq, heads, std=1.0, seed=None, device="cpu", head_dim=128):
+    """qkv [batch*seq][3*heads*head_dim] bf16 ~ N(0, std^2) and dctx
+    [batch*seq][heads*head_dim] bf16 ~ N(0,1)."""
+    seed = seed_of(5, 0, 20) if seed is None else seed
+    m, hd = batch * seq, heads * head_dim
+    qkv = normal((m, 3 * hd), std, seed, dtype=torch.bfloat16, device=device)
+    dctx = normal((m, hd), 1.0, seed + 1, dtype=torch.bfloat16, device=device)
+    return qkv, dctx

@@ -22,7 +22,7 @@ ODD = P((1 << 20) + 4)    # 4-byte aligned, not 16-byte aligned
 def _header_functions():
     text = open(os.path.join(ROOT, "include", "fp8lin.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fp8\w*)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?((?:fp8|bf16)\w*)\s*\(", text, flags=re.M)))
 
 
 def test_exports_every_declared_function():
@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_names():
-    assert L.fp8lin_abi_version() == 4
+    assert L.fp8lin_abi_version() == 5
     assert L.fp8lin_status_name(0) == b"FP8LIN_OK"
     assert L.fp8lin_status_name(2) == b"FP8LIN_ERR_SHAPE"
     assert L.fp8lin_status_name(99) == b"FP8LIN_UNKNOWN_STATUS"
@@ -230,3 +230,29 @@ def test_loss_scale_and_sgd_validation():
 def test_timing_toggle():
     assert L.fp8lin_timing_enable(-1) == F.ERR_ARG
     assert L.fp8lin_timing_enable(0) == F.OK
+
+
+def test_attention_validation():
+    I64 = ctypes.c_int64
+    ws_bytes = L.bf16_attention_workspace_bytes
+    ws_bytes.restype = I64
+    ws_bytes.argtypes = [I64, I64, I64, I64, ctypes.c_int32]
+    assert ws_bytes(2, 4096, 64, 128, 0) == 2 * 4096 * 64 * 128 * 2
+    assert ws_bytes(2, 4096, 64, 128, 1) == 3 * 2 * 4096 * 64 * 128 * 2 + 2 * 64 * 4096 * 4
+    assert ws_bytes(2, 4096, 64, 64, 0) == -1 and ws_bytes(1, 100, 2, 128, 1) == -1
+    fwd, bwd = L.bf16_attention_fwd, L.bf16_attention_bwd
+    fwd.argtypes = [P, I64, I64, I64, I64, P, P, P, P]
+    bwd.argtypes = [P, P, P, P, I64, I64, I64, I64, P, P, P]
+    big = [P(1 << 36), P(1 << 37), P(1 << 38), P(1 << 39), P(1 << 40), P(1 << 41)]
+    assert fwd(big[0], 1, 256, 2, 64, big[1], big[2], big[3], None) == F.ERR_UNSUPPORTED
+    assert fwd(big[0], 1, 100, 2, 128, big[1], big[2], big[3], None) == F.ERR_SHAPE
+    assert fwd(big[0], 0, 256, 2, 128, big[1], big[2], big[3], None) == F.ERR_SHAPE
+    assert fwd(big[0], 1 << 12, 4096, 256, 128, big[1], big[2], big[3], None) == F.ERR_SHAPE
+    assert fwd(None, 1, 256, 2, 128, big[1], big[2], big[3], None) == F.ERR_NULL
+    assert fwd(big[0], 1, 256, 2, 128, ODD, big[2], big[3], None) == F.ERR_ALIGN
+    assert fwd(big[0], 1, 256, 2, 128, big[0], big[2], big[3], None) == F.ERR_ARG          # ctx on qkv
+    assert fwd(big[0], 1, 256, 2, 128, big[1], big[2], big[1], None) == F.ERR_ARG          # workspace on ctx
+    assert bwd(big[0], big[1], big[2], big[3], 1, 256, 2, 128, big[0], big[5], None) == F.ERR_ARG   # dqkv on qkv
+    assert bwd(big[0], big[1], big[2], big[3], 1, 256, 2, 128, big[4], big[3], None) == F.ERR_ARG   # ws on dctx
+    assert bwd(big[0], big[1], None, big[3], 1, 256, 2, 128, big[4], big[5], None) == F.ERR_NULL
+    assert bwd(big[0], big[1], big[2], big[3], 1, 512, 2, 96, big[4], big[5], None) == F.ERR_UNSUPPORTED
