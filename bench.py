@@ -137,9 +137,10 @@ def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
     from fp8_mixed_precision_reduce_amd.blocks import Fp8TransformerLayer
     cfg = synth.LAYER
     inp = synth.layer_inputs(device="cuda")
-    lay = Fp8TransformerLayer(inp["x"], inp["ctx"], inp["g"], inp["dqkv"], inp["wqkv"], inp["wo"], inp["w1"],
-                              inp["w2"], history_len=cfg["history_len"], fast_accum=fast_accum)
-    for k in ("wqkv", "wo", "w1", "w2"):
+    lay = Fp8TransformerLayer(inp["x"], None, inp["g"], None, inp["wqkv"], inp["wo"], inp["w1"], inp["w2"],
+                              history_len=cfg["history_len"], fast_accum=fast_accum, heads=cfg["heads"],
+                              batch=cfg["batch"])
+    for k in ("wqkv", "wo", "w1", "w2", "ctx", "dqkv"):
         del inp[k]                                        # copied into the layer's master buffer
     spiked = synth.layer_spike(inp["x"], cfg["spike_factor"])
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(iterations + 1)]
@@ -151,12 +152,12 @@ def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
     torch.cuda.synchronize()
     per_it = [ev[i].elapsed_time(ev[i + 1]) for i in range(iterations)]
     state = lay.ls_state.cpu().tolist()
-    F.timing_enable(64 * breakdown_steps)
+    F.timing_enable(96 * breakdown_steps)
     torch.cuda.synchronize()
     for _ in range(breakdown_steps):
         lay.step()
     torch.cuda.synchronize()
-    rec = F.timing_read(64 * breakdown_steps)
+    rec = F.timing_read(96 * breakdown_steps)
     F.timing_enable(0)
     kb = {}
     for kind, ms in rec:
@@ -169,9 +170,10 @@ def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
     n_sgd, t_sgd = kb.get("sgd", (0, 0.0))
     sgd_ms = t_sgd / n_sgd if n_sgd else float("nan")
     out = {
-        "workload": "FP8 transformer layer step: QKV, attention-out, FC1, FC2 linears fwd+bwd, hidden 8192, "
-                    "FFN 28672, tokens 8192, fp32 masters + SGD + dynamic loss scaling, x100 spike at "
-                    "iteration 10, history 1024 (attention core: seeded stand-in inputs)",
+        "workload": "FP8 transformer layer step: QKV, attention-out, FC1, FC2 linears fwd+bwd around the bf16 "
+                    "attention core (64 heads of 128, seq 4096 x batch 2, no mask), hidden 8192, FFN 28672, "
+                    "tokens 8192, fp32 masters + SGD + dynamic loss scaling, x100 spike at iteration 10, "
+                    "history 1024",
         "iterations": iterations,
         "ms_per_step_mean_2_to_end": round(mean_ms, 4),
         "ms_per_step_median": round(later[len(later) // 2], 4),
@@ -180,6 +182,12 @@ def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
         "flop_per_step": flop,
         "loss_scale_after": state[0],
         "kernels_ms_per_step": {k: round(v[1] / breakdown_steps, 4) for k, v in sorted(kb.items())},
+        "attention": {"flop_per_step": lay.attention_flops(),
+                      "ms_per_step": round(kb.get("attention", (0, 0.0))[1] / breakdown_steps, 4),
+                      "tflops": round(lay.attention_flops() / (kb.get("attention", (0, 1e30))[1] / breakdown_steps
+                                                                * 1e-3) / 1e12, 1),
+                      "note": "forward (QK^T, PV) and backward (dP, dV, dQ, dK) products over the attention "
+                              "kernels' event time; the transposes into the workspaces are under 'other'"},
         "sgd": {"params": n_params, "avg_launch_ms": round(sgd_ms, 4),
                 "achieved_gbs": round(12.0 * n_params / (sgd_ms * 1e-3) / 1e9, 1), "peak_gbs": PEAK_HBM_GBS},
     }

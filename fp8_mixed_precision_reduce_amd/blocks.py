@@ -18,8 +18,9 @@ every part of it in the library's kernels:
   fp8_amax_scale_update(6 tensors)
 
 Fp8TransformerLayer: the four FP8 linears of a transformer layer (QKV,
-attention output, FC1, FC2) trained from fp32 master weights with dynamic
-loss scaling and SGD; see its docstring for the wiring.
+attention output, FC1, FC2) around the bf16 attention core, trained from fp32
+master weights with dynamic loss scaling and SGD; see its docstring for the
+wiring.
 
 Page tags: [TE-KR] "Transformer Engine으로 FP8 사용하기" (coniverse.tistory.com);
 [MP-KR] "LLM) Mixed-Precision 개념 및 학습 방법 알아보기" (data-newbie.tistory.com);
@@ -27,8 +28,9 @@ Page tags: [TE-KR] "Transformer Engine으로 FP8 사용하기" (coniverse.tistor
 """
 import torch
 
-from . import (AMAX_MAX, E4M3, E5M2, EPI_GELU, FORMAT_HYBRID, MetaBank, QOut, Recipe, Saved, fp8_linear_bwd,
-               fp8_linear_fwd, fp8_loss_scale_apply, fp8_loss_scale_update, fp8_sgd_step)
+from . import (AMAX_MAX, E4M3, E5M2, EPI_GELU, FORMAT_HYBRID, MetaBank, QOut, Recipe, Saved, attention_workspace_bytes,
+               bf16_attention_bwd, bf16_attention_fwd, fp8_linear_bwd, fp8_linear_fwd, fp8_loss_scale_apply,
+               fp8_loss_scale_update, fp8_sgd_step)
 
 MLP_TENSORS = ("x", "w1", "h", "w2", "dy", "dz")
 
@@ -100,19 +102,26 @@ LAYER_WEIGHTS = ("wqkv", "wo", "w1", "w2")
 
 
 class Fp8TransformerLayer:
-    """One transformer layer's FP8 linears, trained with fp32 masters.
+    """One transformer layer's FP8 linears around its bf16 attention core,
+    trained with fp32 masters.
 
     Wiring (no normalisation layers, which the pages do not name):
-        QKV = X Wqkv^T                       (its consumer, the bf16 attention
-        Y1  = X + ctx Wo^T                    core, is stood in for by the
-        H   = gelu(Y1 W1^T),  Z kept          inputs ctx and dqkv)
+        QKV = X Wqkv^T
+        ctx = attention(QKV)                  bf16 scaled dot-product attention,
+                                              `heads` heads of width hidden/heads
+                                              over `batch` sequences of m/batch tokens
+        Y1  = X + ctx Wo^T
+        H   = gelu(Y1 W1^T),  Z kept
         Y   = Y1 + H W2^T
-    Loss <Y, G> * S, so dY = bf16(G * S); the attention core's gradient enters
-    the QKV linear as bf16(dqkv * S).  Backward:
+    Loss <Y, G> * S, so dY = bf16(G * S).  Backward:
         dH, dW2          = bwd FC2(dY)
         dY1, dW1         = bwd FC1(dH; gelu'(Z)) + dY          (skip path)
         dctx, dWo        = bwd O(dY1)
-        dX, dWqkv        = bwd QKV(dqkv * S) + dY1             (skip path)
+        dqkv             = bwd attention(dctx)
+        dX, dWqkv        = bwd QKV(dqkv) + dY1                 (skip path)
+    With heads=None the attention core is stood in for by the caller's
+    tensors: ctx is the O linear's input and the QKV linear's gradient is
+    bf16(dqkv * S) (the QKV output is computed and left unused).
     Update, all on the device and in this order ([MP-KR] "Mixed-Precision
     Training Iteration" and its dynamic loss scaling; [PT-VI] training script
     for the per-step history update after backward):
@@ -121,22 +130,26 @@ class Fp8TransformerLayer:
         fp8_sgd_step on all masters at once (skipped on found_inf).
 
     The masters live in one fp32 buffer and their gradients in another, so the
-    SGD step is one launch over all parameters.  x, ctx, g, dqkv are bf16
-    device tensors of the caller; forward(x_in) may take another input of x's
-    shape (the spiked one).  Residual adds happen in the GEMM epilogues; with
-    fuse_casts (delayed scaling only; off by default, see the module notes) Y1
-    and H are also cast to E4M3 there, straight into the next linear's saved
-    operands, so FC1 and FC2 skip their input casts (keep_h=True still writes
-    the bf16 H).
+    SGD step is one launch over all parameters.  x, g (and the stand-ins ctx,
+    dqkv) are bf16 device tensors of the caller; forward(x_in) may take another
+    input of x's shape (the spiked one).  Residual adds happen in the GEMM
+    epilogues; with fuse_casts (delayed scaling only; off by default, see the
+    module notes) Y1 and H are also cast to E4M3 there, straight into the next
+    linear's saved operands, so FC1 and FC2 skip their input casts (keep_h=True
+    still writes the bf16 H).
     """
 
     def __init__(self, x, ctx, g, dqkv, wqkv, wo, w1, w2, history_len=1024, lr=2.0 ** -10, loss_scale=2.0 ** 16,
                  growth_interval=5, fast_accum=False, keep_dz=False, keep_codes=False, fuse_casts=False,
-                 keep_h=False):
+                 keep_h=False, heads=None, batch=1):
         m, hid = x.shape
         ffn = w1.shape[0]
         assert wqkv.shape == (3 * hid, hid) and wo.shape == (hid, hid) and w1.shape == (ffn, hid)
-        assert w2.shape == (hid, ffn) and ctx.shape == (m, hid) and g.shape == (m, hid) and dqkv.shape == (m, 3 * hid)
+        assert w2.shape == (hid, ffn) and g.shape == (m, hid)
+        if heads is None:
+            assert ctx is not None and dqkv is not None and ctx.shape == (m, hid) and dqkv.shape == (m, 3 * hid)
+        else:
+            assert hid % heads == 0 and m % batch == 0 and x.dtype == torch.bfloat16
         dev = x.device
         self.m, self.hidden, self.ffn = m, hid, ffn
         self.x, self.ctx, self.g, self.dqkv_in = x, ctx, g, dqkv
@@ -165,6 +178,16 @@ class Fp8TransformerLayer:
         self.dy1 = torch.empty(m, hid, **act)
         self.dctx = torch.empty(m, hid, **act)
         self.dqkv = torch.empty(m, 3 * hid, **act)
+        self.heads, self.batch = heads, batch
+        if heads is not None:
+            seq = m // batch
+            wsb = attention_workspace_bytes(batch, seq, heads, hid // heads, backward=True)
+            if wsb < 0:
+                raise ValueError(f"attention core: unsupported shape batch={batch} seq={seq} heads={heads} "
+                                 f"head width {hid // heads}")
+            self.ctx = torch.empty(m, hid, **act)
+            self.lse = torch.empty(batch, heads, seq, dtype=torch.float32, device=dev)
+            self.attn_ws = torch.empty(wsb, dtype=torch.uint8, device=dev)     # holds the forward's too
         self.dx = torch.empty(m, hid, **act)
         # gradient-code workspaces: one pair reused by the four backward calls in
         # turn, or (keep_codes, for inspection) one pair per linear
@@ -190,6 +213,8 @@ class Fp8TransformerLayer:
         x = self.x if x is None else x
         r, mt, sv, w = self.recipe, self.meta, self.saved, self.w
         fp8_linear_fwd(x, w["wqkv"], self.qkv, r, mt["x"], mt["wqkv"], sv["qkv"])
+        if self.heads is not None:
+            bf16_attention_fwd(self.qkv, self.batch, self.heads, self.ctx, self.lse, self.attn_ws)
         if self.fuse_casts and not r.just_in_time:
             # Y1 and H leave their GEMMs already cast to E4M3 for the next linear
             y1q = QOut(mt["y1"].scale, sv["fc1"].xq, sv["fc1"].xq_t, E4M3)
@@ -214,7 +239,11 @@ class Fp8TransformerLayer:
         fp8_linear_bwd(self.dh, hid, r, mt["g_fc1"], sv["fc1"], *ws["fc1"], dx=self.dy1, dw=dw["w1"],
                        gelu_z=self.z, dz_out=self.dz, dx_residual=self.dy)
         fp8_linear_bwd(self.dy1, hid, r, mt["g_o"], sv["o"], *ws["o"], dx=self.dctx, dw=dw["wo"])
-        fp8_loss_scale_apply(self.dqkv_in, self.ls_state, self.dqkv)
+        if self.heads is not None:
+            bf16_attention_bwd(self.qkv, self.ctx, self.lse, self.dctx, self.batch, self.heads, self.dqkv,
+                               self.attn_ws)
+        else:
+            fp8_loss_scale_apply(self.dqkv_in, self.ls_state, self.dqkv)
         fp8_linear_bwd(self.dqkv, hid, r, mt["g_qkv"], sv["qkv"], *ws["qkv"], dx=self.dx, dw=dw["wqkv"],
                        dx_residual=self.dy1)
 
@@ -230,5 +259,19 @@ class Fp8TransformerLayer:
         self.update()
 
     def flops_per_step(self):
+        """Algorithmic flops of one step: the twelve FP8 GEMMs (2 m n k each)
+        and, with the attention core, its forward products Q K^T and P V and
+        backward products dP, dV, dQ, dK (2 S^2 D each per sequence and head;
+        the backward's recomputation of S is not counted)."""
         m, hid, ffn = self.m, self.hidden, self.ffn
-        return 6 * m * (3 * hid * hid + hid * hid + 2 * ffn * hid)
+        linears = 6 * m * (3 * hid * hid + hid * hid + 2 * ffn * hid)
+        if self.heads is None:
+            return linears
+        seq = m // self.batch
+        return linears + 12 * self.batch * self.heads * seq * seq * (hid // self.heads)
+
+    def attention_flops(self):
+        if self.heads is None:
+            return 0
+        seq = self.m // self.batch
+        return 12 * self.batch * self.heads * seq * seq * (self.hidden // self.heads)

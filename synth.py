@@ -18,10 +18,10 @@ Workloads:
   quant      bf16 16384x16384; row r has magnitude 2^u_r, u_r ~ U[-20, 10], times N(0,1) values
   layer      tokens 8192 (seq 4096 x batch 2), hidden 8192, FFN 28672; X bf16 N(0,1); fp32 master
              weights ~ N(0, 0.02): Wqkv 24576x8192, Wo 8192x8192, W1 28672x8192, W2 8192x28672;
-             upstream gradient G bf16 ~ N(0,1) * 2^-20 (the loss is <Y, G> * S); stand-ins for
-             the bf16 attention core: a context tensor ctx bf16 8192x8192 ~ N(0,1) and a
-             gradient d(QKV) bf16 8192x24576 ~ N(0,1) * 2^-20; the spiked input of iteration 10
-             is bf16(fl32(X) * 100)
+             upstream gradient G bf16 ~ N(0,1) * 2^-20 (the loss is <Y, G> * S); 64 attention
+             heads of width 128; the spiked input of iteration 10 is bf16(fl32(X) * 100).  For
+             the layer run without its attention core: stand-ins ctx bf16 8192x8192 ~ N(0,1) and
+             d(QKV) bf16 8192x24576 ~ N(0,1) * 2^-20
   attention  the bf16 attention core of the layer (64 heads of width 128 over seq 4096 x batch 2):
              its input qkv bf16 [batch*seq][3*heads*128] ~ N(0, std^2) and an incoming gradient
              dctx bf16 [batch*seq][heads*128] ~ N(0,1) (smaller shapes for the parity cases)
@@ -112,7 +112,7 @@ def quant_tensor(device="cpu", rows=16384, cols=16384):
 # ---------------------------------------------------------------- layer ----
 
 LAYER = dict(m=8192, hidden=8192, ffn=28672, history_len=1024, iterations=20, spike_iteration=10,
-             spike_factor=100.0)
+             spike_factor=100.0, heads=64, batch=2)
 
 
 def layer_inputs(device="cpu", m=8192, hidden=8192, ffn=28672):

@@ -11,6 +11,9 @@ Comparison rules (the tolerances are stated here, once):
   of the bf16 output is <= 2^-8 (bf16's unit roundoff is 2^-9).
 * Non-finite reference elements (an Inf added in by a residual) must be
   reproduced exactly; the norms and the RMS are taken over the finite ones.
+* bf16 attention outputs and gradients: |gpu - oracle| <= 2^-8 (T + |oracle|)
+  per element, T the oracle's sum of absolute terms (derivation in
+  tests/test_gpu_attention.py).
 """
 import numpy as np
 import torch
@@ -99,3 +102,14 @@ def assert_gemm_bf16(got_bits, want64, oracle, what=""):
     if den > 0:
         err = np.linalg.norm(bf16_bits_to_f64(got_bits) - want64) / den
         assert err <= 2.0 ** -8, f"{what}: bf16 normwise error {err:.3e}"
+
+
+def assert_within_terms(got_bits, want, terms, what=""):
+    """bf16 results against fp64 references: |err| <= 2^-8 (T + |want|)."""
+    got = bf16_bits_to_f64(got_bits)
+    bound = 2.0 ** -8 * (terms + np.abs(want)) + 1e-30
+    err = np.abs(got - want)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} beyond the bound, worst ratio "
+                           f"{float(np.nanmax(err / bound)):.3g} at {np.argwhere(bad)[:4].tolist()}")
+    return float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))

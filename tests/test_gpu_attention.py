@@ -23,7 +23,7 @@ import torch
 import fp8_mixed_precision_reduce_amd as F
 import synth
 from oracle import attention as A
-from helpers import np_of, bf16_bits_to_f64
+from helpers import assert_within_terms as _assert_within, bf16_bits_to_f64, np_of
 
 pytestmark = pytest.mark.gpu
 LN2 = float(np.log(2.0))
@@ -45,16 +45,6 @@ def _run_bwd(qkv, ctx, lse, dctx, batch, heads):
     ws = torch.empty(F.attention_workspace_bytes(batch, seq, heads, backward=True), dtype=torch.uint8, device="cuda")
     F.bf16_attention_bwd(qkv, ctx, lse, dctx, batch, heads, dqkv, ws)
     return dqkv
-
-
-def _assert_within(got_bits, want, terms, what):
-    got = bf16_bits_to_f64(got_bits)
-    bound = 2.0 ** -8 * (terms + np.abs(want)) + 1e-30
-    err = np.abs(got - want)
-    bad = ~(err <= bound)
-    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} beyond the bound, worst ratio "
-                           f"{float(np.nanmax(err / bound)):.3g} at {np.argwhere(bad)[:4].tolist()}")
-    return float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
 
 
 @pytest.mark.parametrize("batch,seq,heads,std", [(1, 256, 2, 1.0), (2, 512, 3, 1.0), (1, 768, 2, 3.0)],

@@ -51,13 +51,18 @@ def test_mlp_block_step_graph_replays_match_eager():
         del junk
 
 
-def test_layer_step_graph_replays_match_eager():
-    inp = synth.layer_inputs(device="cpu", m=272, hidden=208, ffn=464)
+@pytest.mark.parametrize("attention", [False, True], ids=["stand_in", "attention_core"])
+def test_layer_step_graph_replays_match_eager(attention):
+    """The whole layer step captured once and replayed (with the attention
+    core: 2 sequences of 256 tokens, two heads of 128)."""
+    shape = dict(m=512, hidden=256, ffn=464) if attention else dict(m=272, hidden=208, ffn=464)
+    inp = synth.layer_inputs(device="cpu", **shape)
+    kw = dict(heads=2, batch=2) if attention else {}
 
     def make():
         d = {k: v.cuda() for k, v in inp.items()}
         return Fp8TransformerLayer(d["x"], d["ctx"], d["g"], d["dqkv"], d["wqkv"], d["wo"], d["w1"], d["w2"],
-                                   history_len=16, lr=2.0 ** -10)
+                                   history_len=16, lr=2.0 ** -10, **kw)
     eager, graphed = make(), make()
     g = _capture(graphed.step)
     eager.step()
@@ -66,7 +71,7 @@ def test_layer_step_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         tag = f"replay {rep}"
-        for name in ("qkv", "y1", "z", "y", "dx", "dctx", "grad", "master", "ls_state"):
+        for name in ("qkv", "ctx", "y1", "z", "y", "dx", "dctx", "dqkv", "grad", "master", "ls_state"):
             assert_bits_equal(np_of(getattr(graphed, name)), np_of(getattr(eager, name)), f"{tag} {name}")
         for what in ("amax_history", "scale", "scale_inv"):
             assert_bits_equal(np_of(getattr(graphed.bank, what)), np_of(getattr(eager.bank, what)), f"{tag} {what}")

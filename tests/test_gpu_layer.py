@@ -12,9 +12,14 @@ into the next cast.  Per step:
 * GEMM tolerances (tests/helpers.py): QKV, Y1 (with the residual X), Z, H,
   Y (with the residual Y1), dH, dY1 (with the residual dY), dctx, dX (with
   the residual dY1) in bf16; the four weight gradients in fp32;
-* dZ = bf16(dH * gelu'(Z)) within one bf16 ulp.
-The full-size cases run the layer at hidden 8192, FFN 28672, 8192 tokens in
-the benchmark's launch configuration and check sampled output rows.
+* dZ = bf16(dH * gelu'(Z)) within one bf16 ulp;
+* with the attention core: ctx from the GPU's QKV and dqkv from the GPU's QKV,
+  ctx and dctx against the attention oracle within 2^-8 (T + |x|)
+  (tests/helpers.py), all heads at the small size, sampled heads and rows at
+  full size.
+The full-size cases run the layer at hidden 8192, FFN 28672, 8192 tokens (64
+heads over seq 4096 x batch 2) in the benchmark's launch configuration and
+check sampled output rows.
 """
 import numpy as np
 import pytest
@@ -22,7 +27,8 @@ import torch
 
 import synth
 from fp8_mixed_precision_reduce_amd.blocks import LAYER_GRADS, LAYER_TENSORS, LAYER_WEIGHTS, Fp8TransformerLayer
-from helpers import assert_bits_equal, assert_gemm_bf16, assert_gemm_f32, np_of
+from helpers import assert_bits_equal, assert_gemm_bf16, assert_gemm_f32, assert_within_terms, bf16_bits_to_f64, np_of
+from oracle import attention as attn_oracle
 
 pytestmark = pytest.mark.gpu
 E4, E5 = 0, 1
@@ -83,6 +89,35 @@ def _check_bwd(oracle, G, mg, fwd, ws, dx_gpu, dw_gpu, rows, wrows, tag, residua
         mg.record(G)
 
 
+def _check_attention(lay, ctx, dqkv, tag, heads_sample=((0, 0), (1, 37)), nrows=32):
+    """The attention core on the GPU's own QKV: every head when the layer is
+    small, else the forward on sampled query rows of the sampled heads and the
+    whole backward of the first of them."""
+    qkv, dctx = np_of(lay.qkv), np_of(lay.dctx)
+    batch, heads, hd = lay.batch, lay.heads, lay.hidden
+    seq = lay.m // batch
+    if seq * heads <= 4096:
+        o, _, a = attn_oracle.attention_fwd(qkv, batch, seq, heads)
+        assert_within_terms(ctx, o, a, tag + " attention ctx")
+        d, t = attn_oracle.attention_bwd(qkv, ctx, dctx, batch, seq, heads)
+        assert_within_terms(dqkv, d, t, tag + " attention dqkv")
+        return
+    rng = np.random.default_rng(23)
+    for i, (b, h) in enumerate(heads_sample):
+        toks = slice(b * seq, (b + 1) * seq)
+        hcols = h * (hd // heads) + np.arange(hd // heads)             # the head's columns of ctx, dctx
+        cols = [p * hd + hcols for p in range(3)]                       # ... and of Q, K, V in qkv
+        q, k, v = (x[0, 0] for x in attn_oracle.split_heads(qkv[toks][:, np.concatenate(cols)], 1, seq, 1))
+        rows = np.sort(rng.choice(seq, nrows, replace=False))
+        o, _, a = attn_oracle.head_fwd(q, k, v, rows=rows)
+        assert_within_terms(ctx[toks][rows][:, hcols], o, a, f"{tag} attention ctx b{b} h{h}")
+        if i == 0:
+            g = attn_oracle.head_bwd(q, k, v, bf16_bits_to_f64(ctx[toks][:, hcols]),
+                                     bf16_bits_to_f64(dctx[toks][:, hcols]))
+            for p, name in enumerate(("dq", "dk", "dv")):
+                assert_within_terms(dqkv[toks][:, cols[p]], g[name], g["t" + name[1]], f"{tag} attention {name}")
+
+
 def _check_step(oracle, lay, om, ols, X, rows, wrows, tag):
     """One step of the layer (already run on the GPU up to the update) checked
     sub-step by sub-step; then the update is run on both sides and compared.
@@ -113,7 +148,10 @@ def _check_step(oracle, lay, om, ols, X, rows, wrows, tag):
     _check_bwd(oracle, dY1, mt["g_o"], f_o, lay.gws["o"], lay.dctx, lay.dw["wo"], rows, wrows,
                tag + " bwd O", jit=jit)
     dQ = np_of(lay.dqkv)
-    assert_bits_equal(dQ, oracle.scale_by(np_of(lay.dqkv_in), S), tag + " dqkv*S")
+    if lay.heads is None:
+        assert_bits_equal(dQ, oracle.scale_by(np_of(lay.dqkv_in), S), tag + " dqkv*S")
+    else:
+        _check_attention(lay, ctx, dQ, tag)
     _check_bwd(oracle, dQ, mt["g_qkv"], f_q, lay.gws["qkv"], lay.dx, lay.dw["wqkv"], rows, wrows,
                tag + " bwd QKV", residual=dY1, jit=jit)
     for i, name in enumerate(LAYER_TENSORS):
@@ -137,6 +175,23 @@ def _check_step(oracle, lay, om, ols, X, rows, wrows, tag):
 def _layer(inp, history_len, **kw):
     return Fp8TransformerLayer(inp["x"], inp["ctx"], inp["g"], inp["dqkv"], inp["wqkv"], inp["wo"], inp["w1"],
                                inp["w2"], history_len=history_len, lr=LR, keep_dz=True, keep_codes=True, keep_h=True, **kw)
+
+
+def test_layer_small_attention_with_spike(oracle):
+    """The layer with its bf16 attention core: 2 sequences of 256 tokens, two
+    heads of 128 (hidden 256), FFN 464 (ragged), history 16; steps 0..4 with the
+    x100 spike at step 2."""
+    inp = {k: v.cuda() for k, v in synth.layer_inputs(device="cpu", m=512, hidden=256, ffn=464).items()}
+    lay = _layer(inp, 16, heads=2, batch=2)
+    om, ols = oracle.layer_metas(16), oracle.LossScale(2.0 ** 16, interval=5)
+    spiked = synth.layer_spike(inp["x"])
+    for step in range(5):
+        x_in = spiked if step == 2 else inp["x"]
+        lay.forward(x_in)
+        lay.backward()
+        torch.cuda.synchronize()
+        _check_step(oracle, lay, om, ols, np_of(x_in), None, None, f"attention step {step}")
+    assert om["x"].hist[3] == oracle.amax(np_of(spiked))    # the spike's amax, rolled by three updates
 
 
 def _oracle_state_from(oracle, lay):
@@ -217,12 +272,13 @@ def test_layer_inf_gradient_skips_sgd(oracle):
 
 @pytest.mark.timeout(900)
 def test_layer_full_size_sampled(oracle):
-    """Hidden 8192, FFN 28672, 8192 tokens, history 1024: steps 0 and 1 checked,
-    steps 2..9 run unchecked, then the spike step 10 and step 11 checked from
-    the GPU's state (metas, loss scale, masters) at that point."""
+    """Hidden 8192, FFN 28672, 8192 tokens (64 heads over seq 4096 x batch 2),
+    history 1024: steps 0 and 1 checked, steps 2..9 run unchecked, then the
+    spike step 10 and step 11 checked from the GPU's state (metas, loss scale,
+    masters) at that point."""
     cfg = synth.LAYER
     inp = synth.layer_inputs(device="cuda")
-    lay = _layer(inp, cfg["history_len"])
+    lay = _layer(inp, cfg["history_len"], heads=cfg["heads"], batch=cfg["batch"])
     rng = np.random.default_rng(17)
     rows = np.sort(rng.choice(cfg["m"], 8, replace=False))
     wrows = np.sort(rng.choice(cfg["hidden"], 4, replace=False))
