@@ -59,6 +59,28 @@ __device__ __forceinline__ v8bf pack8(const v16f& a, int r0) {
     return __builtin_convertvector(v, v8bf);
 }
 
+// Lane l and lane l ^ 32 (the two lane groups of an MFMA column) combined
+// with one v_permlane32_swap; both lanes get the same value (low half first).
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Wave priority around the matrix-core phases: the wave that reaches its
+// products first keeps the matrix cores while the other wave of the SIMD runs
+// its softmax, so the two drift into opposite phases.
+#ifndef ATTN_PRIO
+#define ATTN_PRIO 1
+#endif
+__device__ __forceinline__ void prio_mfma() { if (ATTN_PRIO) __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void prio_valu() { if (ATTN_PRIO) __builtin_amdgcn_s_setprio(0); }
+
+constexpr float kLazy = 8.0f;   // log2 headroom of the forward's reference maximum
+
 __device__ __forceinline__ v16f mfma(v8bf a, v8bf b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -88,23 +110,30 @@ struct AttnShape {
 };
 
 // ------------------------------------------------------------------ forward
-// Workgroup: 8 waves, 256 queries of one (b, h), 32 per wave.  Key blocks of
-// 64 go through a double-buffered LDS tile: K [64][256 B] and V^T [128][128 B].
-constexpr int kFwdQ = 256, kFwdK = 64, kFwdThreads = 512;
+// Workgroup: WAVES waves, 32 queries each, of one (b, h).  Key blocks of 64 go
+// through three LDS buffers (K [64][256 B] and V^T [128][128 B] each), loaded
+// two blocks ahead through registers.
+constexpr int kFwdK = 64;
+#ifndef FWD_WAVES
+#define FWD_WAVES 8
+#endif
+constexpr int kFwdWaves = FWD_WAVES;
 constexpr int kFwdBuf = 64 * 256 + 128 * 128;
 
-__global__ void __launch_bounds__(kFwdThreads, 1)
+template <int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, 8 / WAVES)
 k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, uint16_t* __restrict__ ctx,
            float* __restrict__ lse, AttnShape sh) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kFwdBuf];
+    constexpr int THREADS = 64 * WAVES, BQ = 32 * WAVES, NCH = 1024 / THREADS;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[3 * kFwdBuf];
     const int S = sh.seq, H = sh.heads;
     const int64_t BS = (int64_t)sh.batch * S, HD = (int64_t)H * kD, ld = 3 * HD;
-    const int qblocks = S / kFwdQ;
+    const int qblocks = S / BQ;
     const int id = xcd_block(blockIdx.x, gridDim.x);
     const int qb = id % qblocks, h = (id / qblocks) % H, b = id / (qblocks * H);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
     const int64_t tok0 = (int64_t)b * S;
-    const int q = qb * kFwdQ + w * 32 + l32;          // this lane's query
+    const int q = qb * BQ + w * 32 + l32;          // this lane's query
 
     // Q fragments (second operand of S^T = K Q^T): lane's query, d = 16 st + 8 g ..
     v8bf qf[8];
@@ -113,22 +142,26 @@ k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, ui
 #pragma unroll
         for (int st = 0; st < 8; ++st) qf[st] = as_bf(*reinterpret_cast<const uint4*>(qrow + 16 * st + 8 * g));
     }
-    // Tile loads: thread t moves 16-byte chunks t and t + 512 of K and of V^T.
+    // Tile loads: thread t moves 16-byte chunks t + THREADS u of K (1024 chunks)
+    // and of V^T (1024 chunks).
     const uint16_t* kbase = qkv + tok0 * ld + HD + (int64_t)h * kD;
     const uint16_t* vbase = vt + (int64_t)h * kD * BS + tok0;
-    v4u st0, st1, st2, st3;
-    const int c1 = t + kFwdThreads;
+    v4u stk[NCH], stv[NCH];
     auto load = [&](int k0) __attribute__((always_inline)) {
-        st0 = ldg16(kbase + (int64_t)(k0 + (t >> 4)) * ld + (t & 15) * 8);
-        st1 = ldg16(kbase + (int64_t)(k0 + (c1 >> 4)) * ld + (c1 & 15) * 8);
-        st2 = ldg16(vbase + (int64_t)(t >> 3) * BS + k0 + (t & 7) * 8);
-        st3 = ldg16(vbase + (int64_t)(c1 >> 3) * BS + k0 + (c1 & 7) * 8);
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            const int c = t + u * THREADS;
+            stk[u] = ldg16(kbase + (int64_t)(k0 + (c >> 4)) * ld + (c & 15) * 8);
+            stv[u] = ldg16(vbase + (int64_t)(c >> 3) * BS + k0 + (c & 7) * 8);
+        }
     };
     auto store = [&](uint8_t* buf) __attribute__((always_inline)) {
-        sts16(buf + off256(t >> 4, t & 15), st0);
-        sts16(buf + off256(c1 >> 4, c1 & 15), st1);
-        sts16(buf + 64 * 256 + off128(t >> 3, t & 7), st2);
-        sts16(buf + 64 * 256 + off128(c1 >> 3, c1 & 7), st3);
+#pragma unroll
+        for (int u = 0; u < NCH; ++u) {
+            const int c = t + u * THREADS;
+            sts16(buf + off256(c >> 4, c & 15), stk[u]);
+            sts16(buf + 64 * 256 + off128(c >> 3, c & 7), stv[u]);
+        }
     };
 
     v16f o[4];
@@ -138,63 +171,96 @@ k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, ui
         for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
     float m2 = -__builtin_inff(), lsum = 0.0f;
 
+    // Software pipeline over key blocks (three LDS buffers, blocks two ahead
+    // in flight): iteration j issues the score products of block j + 1 beside
+    // the exponentials of block j, then block j's P V products.  Block j's
+    // maximum (and the rare rescale) is taken first, outside that interleave.
     const int nblk = S / kFwdK;
+    const int row = sigma(l32);
     load(0);
     store(smem);
+    load(kFwdK);
+    store(smem + kFwdBuf);
     __syncthreads();
+    v16f sc[2], sn[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { sc[0][e] = 0.0f; sc[1][e] = 0.0f; }
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        sc[0] = mfma(lds16(smem + off256(row, 2 * st + g)), qf[st], sc[0]);
+        sc[1] = mfma(lds16(smem + off256(32 + row, 2 * st + g)), qf[st], sc[1]);
+    }
+    int bj = 0;                       // buffer of block j (j mod 3)
     for (int j = 0; j < nblk; ++j) {
-        const uint8_t* buf = smem + (j & 1) * kFwdBuf;
-        if (j + 1 < nblk) load((j + 1) * kFwdK);
-        // S^T tiles: keys 32 kt + sigma(i) of the block against the lane's query.
-        v16f s[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[kt][e] = 0.0f;
-            const int row = 32 * kt + sigma(l32);
-#pragma unroll
-            for (int st = 0; st < 8; ++st) s[kt] = mfma(lds16(buf + off256(row, 2 * st + g)), qf[st], s[kt]);
-        }
-        // Online softmax in the base-2 domain; the two lane groups of a query
-        // share its running maximum.
+        const int bn = bj == 2 ? 0 : bj + 1, b2 = bn == 2 ? 0 : bn + 1;
+        const uint8_t* vb = smem + bj * kFwdBuf + 64 * 256;     // V^T of block j
+        const uint8_t* kn = smem + bn * kFwdBuf;                // K of block j + 1 (stale past the end: unused)
+        if (j + 2 < nblk) load((j + 2) * kFwdK);
+        // block j's maximum; the reference maximum m2 moves only when the block
+        // exceeds it by more than kLazy (then every P of the block is <= 2^kLazy,
+        // harmless in fp32 and bf16), and O and l are rescaled with it -- exact in
+        // the algebra, since both carry the same factor.  max(s * c2) = max(s) * c2
+        // (c2 > 0, rounding is monotonic), so the scale goes on the maximum.
         float mx = -__builtin_inff();
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int e = 0; e < 16; e += 2)
+            mx = fmaxf(mx, fmaxf(fmaxf(sc[0][e], sc[0][e + 1]), fmaxf(sc[1][e], sc[1][e + 1])));
+        mx = pair_max(mx) * sh.c2;
+        if (__any(mx > m2 + kLazy)) {
+            const float mnew = mx > m2 + kLazy ? mx : m2;
+            const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+            m2 = mnew;
+            lsum *= alpha;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                s[kt][e] *= sh.c2;
-                mx = fmaxf(mx, s[kt][e]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m2, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-        m2 = mnew;
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+        }
+        // block j + 1's scores (MFMA) interleaved with block j's P (VALU): step st
+        // runs the two score products of d-slice st and the exponentials of
+        // registers 2 st, 2 st + 1 of both tiles.
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { sn[0][e] = 0.0f; sn[1][e] = 0.0f; }
         float ps = 0.0f;
+        v8bf ka = lds16(kn + off256(row, g)), kb = lds16(kn + off256(32 + row, g));
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                s[kt][e] = __builtin_amdgcn_exp2f(s[kt][e] - mnew);
-                ps += s[kt][e];
+        for (int st = 0; st < 8; ++st) {
+            v8bf na = ka, nb = kb;
+            if (st < 7) {
+                na = lds16(kn + off256(row, 2 * st + 2 + g));
+                nb = lds16(kn + off256(32 + row, 2 * st + 2 + g));
             }
-        lsum = lsum * alpha + ps;
+            sn[0] = mfma(ka, qf[st], sn[0]);
+            sn[1] = mfma(kb, qf[st], sn[1]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-        // O^T += V^T P: keys 16 ks + 8 g + slot, registers 8 (ks & 1) + slot of tile ks / 2.
+                for (int e = 2 * st; e < 2 * st + 2; ++e) {
+                    sc[kt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][e], sh.c2, -m2));
+                    ps += sc[kt][e];
+                }
+            if (st < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // next fragments
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                // two products
+            __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);               // exponentials (VALU and TRANS)
+            ka = na;
+            kb = nb;
+        }
+        lsum += ps;
+        // O^T += V^T P: keys 16 ks + 8 g + slot = registers 8 (ks & 1) + slot of tile ks / 2
         v8bf pb[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) pb[ks] = pack8(s[ks >> 1], 8 * (ks & 1));
+        for (int ks = 0; ks < 4; ++ks) pb[ks] = pack8(sc[ks >> 1], 8 * (ks & 1));
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                o[dt] = mfma(lds16(buf + 64 * 256 + off128(32 * dt + l32, 2 * ks + g)), pb[ks], o[dt]);
-        if (j + 1 < nblk) store(smem + ((j + 1) & 1) * kFwdBuf);
+            for (int dt = 0; dt < 4; ++dt) o[dt] = mfma(lds16(vb + off128(32 * dt + l32, 2 * ks + g)), pb[ks], o[dt]);
+        if (j + 2 < nblk) store(smem + b2 * kFwdBuf);
         __syncthreads();
+        sc[0] = sn[0];
+        sc[1] = sn[1];
+        bj = bn;
     }
-    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float ltot = pair_sum(lsum);
     const float inv = 1.0f / ltot;
     uint16_t* orow = ctx + (tok0 + q) * HD + (int64_t)h * kD;
 #pragma unroll
@@ -371,7 +437,7 @@ k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dct
             const float dq[8] = {da.x, da.y, da.z, da.w, dc.x, dc.y, dc.z, dc.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(s[8 * hb + e] * sh.c2 - lq[e]);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * hb + e], sh.c2, -lq[e]));
                 s[8 * hb + e] = p;
                 dp[8 * hb + e] = p * (dp[8 * hb + e] - dq[e]);
             }
@@ -476,7 +542,7 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
             dp = mfma(lds16(buf + kQKt + off256(row, 2 * st + g)), df[st], dp);
         }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dp[e] = __builtin_amdgcn_exp2f(s[e] * sh.c2 - lq) * (dp[e] - dd);
+        for (int e = 0; e < 16; ++e) dp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sh.c2, -lq)) * (dp[e] - dd);
         // dQ^T += K^T dS: keys 16 ks + 8 g + slot = registers 8 ks + slot
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -528,8 +594,9 @@ hipError_t launch_attention_fwd(const uint16_t* qkv, int64_t batch, int64_t seq,
     timing_after(s);
     if (e != hipSuccess) return e;
     timing_before(kKindAttn, s);
-    const int64_t blocks = batch * heads * (seq / kFwdQ);
-    hipLaunchKernelGGL(k_attn_fwd, dim3((unsigned)blocks), dim3(kFwdThreads), 0, s, qkv, vt_ws, ctx, lse, sh);
+    constexpr int waves = kFwdWaves;
+    const int64_t blocks = batch * heads * (seq / (32 * waves));
+    hipLaunchKernelGGL(k_attn_fwd<waves>, dim3((unsigned)blocks), dim3(64 * waves), 0, s, qkv, vt_ws, ctx, lse, sh);
     e = hipGetLastError();
     timing_after(s);
     return e;
