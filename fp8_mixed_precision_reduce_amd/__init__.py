@@ -211,6 +211,21 @@ class MetaBank:
     def scale_from_current(self, recipe, stream=None):
         fp8_scale_from_current_amax(self.amax_history, self.scale, self.scale_inv, self.formats, recipe, stream)
 
+    def state_dict(self):
+        """Host copies of the delayed-scaling state (histories, scales, inverse
+        scales): the operator state that a checkpoint keeps."""
+        return {"amax_history": self.amax_history.cpu().clone(), "scale": self.scale.cpu().clone(),
+                "scale_inv": self.scale_inv.cpu().clone(), "formats": torch.tensor(list(self.formats), dtype=torch.uint8)}
+
+    def load_state_dict(self, state):
+        """Restores a state_dict in place (the metas handed out stay valid)."""
+        if bytes(state["formats"].tolist()) != self.formats or tuple(state["amax_history"].shape) != tuple(
+                self.amax_history.shape):
+            raise ValueError("MetaBank.load_state_dict: formats or history shape differ")
+        self.amax_history.copy_(state["amax_history"])
+        self.scale.copy_(state["scale"])
+        self.scale_inv.copy_(state["scale_inv"])
+
 
 class Saved:
     """Buffers a forward pass leaves for its backward pass (FP8 copies of X

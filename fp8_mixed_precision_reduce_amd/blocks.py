@@ -95,6 +95,14 @@ class Fp8MlpBlock:
         self.backward()
         self.update()
 
+    def state_dict(self):
+        """The block's training state: the delayed-scaling metas (its weights
+        are the caller's and are not updated here)."""
+        return {"bank": self.bank.state_dict()}
+
+    def load_state_dict(self, state):
+        self.bank.load_state_dict(state["bank"])
+
 
 LAYER_TENSORS = ("x", "wqkv", "ctx", "wo", "y1", "w1", "h", "w2", "g_fc2", "g_fc1", "g_o", "g_qkv")
 LAYER_GRADS = ("g_fc2", "g_fc1", "g_o", "g_qkv")
@@ -257,6 +265,23 @@ class Fp8TransformerLayer:
         self.forward(x)
         self.backward()
         self.update()
+
+    def state_dict(self):
+        """Everything a training run carries from step to step: the fp32
+        masters, the delayed-scaling metas of the twelve tensors and the
+        loss-scale state (host copies; plain tensors, so torch.save /
+        torch.load(weights_only=True) round-trip them)."""
+        return {"master": self.master.cpu().clone(), "bank": self.bank.state_dict(),
+                "ls_state": self.ls_state.cpu().clone()}
+
+    def load_state_dict(self, state):
+        """Restores a state_dict in place; the next step continues exactly as
+        the saved run would have."""
+        if state["master"].shape != self.master.shape:
+            raise ValueError("Fp8TransformerLayer.load_state_dict: master size differs")
+        self.master.copy_(state["master"])
+        self.bank.load_state_dict(state["bank"])
+        self.ls_state.copy_(state["ls_state"])
 
     def flops_per_step(self):
         """Algorithmic flops of one step: the twelve FP8 GEMMs (2 m n k each)
