@@ -112,7 +112,7 @@ struct AttnShape {
 // ------------------------------------------------------------------ forward
 // Workgroup: WAVES waves, 32 queries each, of one (b, h).  Key blocks of 64 go
 // through three LDS buffers (K [64][256 B] and V^T [128][128 B] each), loaded
-// two blocks ahead through registers.
+// one block ahead through registers.
 constexpr int kFwdK = 64;
 #ifndef FWD_WAVES
 #define FWD_WAVES 8
@@ -171,31 +171,42 @@ k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, ui
         for (int e = 0; e < 16; ++e) o[i][e] = 0.0f;
     float m2 = -__builtin_inff(), lsum = 0.0f;
 
-    // Software pipeline over key blocks (three LDS buffers, blocks two ahead
-    // in flight): iteration j issues the score products of block j + 1 beside
-    // the exponentials of block j, then block j's P V products.  Block j's
-    // maximum (and the rare rescale) is taken first, outside that interleave.
+    // Neighbouring waves run in opposite phases: the odd ("late") waves
+    // multiply P V one block behind their scores, so that while one wave runs
+    // its softmax (VALU) its neighbour can run products (MFMA) on the matrix
+    // core they share.  (Pairing w with w ^ 1 measured 5 % faster than no
+    // shift; pairing w with w + 4 gained nothing.)  Three LDS buffers keep
+    // block j - 1's V^T for the late waves while block j is used and block
+    // j + 1 is staged.
     const int nblk = S / kFwdK;
     const int row = sigma(l32);
+    const bool late = (w & 1) != 0;
     load(0);
     store(smem);
-    load(kFwdK);
-    store(smem + kFwdBuf);
     __syncthreads();
-    v16f sc[2], sn[2];
+    v8bf pl[4];                        // the late waves' P of the previous block
+    auto pv = [&](const uint8_t* vb, const v8bf* pb) __attribute__((always_inline)) {
+        // O^T += V^T P: keys 16 ks + 8 g + slot = registers 8 (ks & 1) + slot of tile ks / 2
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { sc[0][e] = 0.0f; sc[1][e] = 0.0f; }
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-        sc[0] = mfma(lds16(smem + off256(row, 2 * st + g)), qf[st], sc[0]);
-        sc[1] = mfma(lds16(smem + off256(32 + row, 2 * st + g)), qf[st], sc[1]);
-    }
-    int bj = 0;                       // buffer of block j (j mod 3)
+            for (int dt = 0; dt < 4; ++dt) o[dt] = mfma(lds16(vb + off128(32 * dt + l32, 2 * ks + g)), pb[ks], o[dt]);
+    };
+    int bj = 0, bp = 2;                // buffers of blocks j and j - 1 (mod 3)
     for (int j = 0; j < nblk; ++j) {
-        const int bn = bj == 2 ? 0 : bj + 1, b2 = bn == 2 ? 0 : bn + 1;
-        const uint8_t* vb = smem + bj * kFwdBuf + 64 * 256;     // V^T of block j
-        const uint8_t* kn = smem + bn * kFwdBuf;                // K of block j + 1 (stale past the end: unused)
-        if (j + 2 < nblk) load((j + 2) * kFwdK);
+        const int bn = bj == 2 ? 0 : bj + 1;
+        const uint8_t* buf = smem + bj * kFwdBuf;
+        if (j + 1 < nblk) load((j + 1) * kFwdK);
+        if (late && j > 0) pv(smem + bp * kFwdBuf + 64 * 256, pl);
+        // S^T tiles: keys kt * 32 + sigma(i) of the block against the lane's query.
+        v16f sc[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { sc[0][e] = 0.0f; sc[1][e] = 0.0f; }
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            sc[0] = mfma(lds16(buf + off256(row, 2 * st + g)), qf[st], sc[0]);
+            sc[1] = mfma(lds16(buf + off256(32 + row, 2 * st + g)), qf[st], sc[1]);
+        }
         // block j's maximum; the reference maximum m2 moves only when the block
         // exceeds it by more than kLazy (then every P of the block is <= 2^kLazy,
         // harmless in fp32 and bf16), and O and l are rescaled with it -- exact in
@@ -216,50 +227,30 @@ k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, ui
 #pragma unroll
                 for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
         }
-        // block j + 1's scores (MFMA) interleaved with block j's P (VALU): step st
-        // runs the two score products of d-slice st and the exponentials of
-        // registers 2 st, 2 st + 1 of both tiles.
-#pragma unroll
-        for (int e = 0; e < 16; ++e) { sn[0][e] = 0.0f; sn[1][e] = 0.0f; }
         float ps = 0.0f;
-        v8bf ka = lds16(kn + off256(row, g)), kb = lds16(kn + off256(32 + row, g));
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            v8bf na = ka, nb = kb;
-            if (st < 7) {
-                na = lds16(kn + off256(row, 2 * st + 2 + g));
-                nb = lds16(kn + off256(32 + row, 2 * st + 2 + g));
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                sc[kt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][e], sh.c2, -m2));
+                ps += sc[kt][e];
             }
-            sn[0] = mfma(ka, qf[st], sn[0]);
-            sn[1] = mfma(kb, qf[st], sn[1]);
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int e = 2 * st; e < 2 * st + 2; ++e) {
-                    sc[kt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][e], sh.c2, -m2));
-                    ps += sc[kt][e];
-                }
-            if (st < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // next fragments
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                // two products
-            __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);               // exponentials (VALU and TRANS)
-            ka = na;
-            kb = nb;
-        }
         lsum += ps;
-        // O^T += V^T P: keys 16 ks + 8 g + slot = registers 8 (ks & 1) + slot of tile ks / 2
         v8bf pb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) pb[ks] = pack8(sc[ks >> 1], 8 * (ks & 1));
+        if (late) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[dt] = mfma(lds16(vb + off128(32 * dt + l32, 2 * ks + g)), pb[ks], o[dt]);
-        if (j + 2 < nblk) store(smem + b2 * kFwdBuf);
+            for (int ks = 0; ks < 4; ++ks) pl[ks] = pb[ks];
+        } else {
+            pv(buf + 64 * 256, pb);
+        }
+        if (j + 1 < nblk) store(smem + bn * kFwdBuf);
         __syncthreads();
-        sc[0] = sn[0];
-        sc[1] = sn[1];
+        bp = bj;
         bj = bn;
     }
+    if (late) pv(smem + bp * kFwdBuf + 64 * 256, pl);
     const float ltot = pair_sum(lsum);
     const float inv = 1.0f / ltot;
     uint16_t* orow = ctx + (tok0 + q) * HD + (int64_t)h * kD;
