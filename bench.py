@@ -196,6 +196,65 @@ def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
     return out
 
 
+def linear768_leg(F, torch, iters=200):
+    """The 768-wide linear (1024 x 768 x 768, fp32 in and out, history 16): one
+    forward step (amax + cast of X and W, FP8 GEMM with bias, scale update) and
+    one forward + backward step in HYBRID (adds the E5M2 cast-transpose of dY,
+    dgrad and wgrad), each timed launched one call at a time (eager) and
+    replayed from a captured HIP graph.  At 1.2 GFLOP per GEMM these steps are
+    bound by launch latency, not by the matrix cores or HBM, so they are
+    reported in microseconds per step."""
+    import synth
+    m, n, k = 1024, 768, 768
+    w, b = (t.cuda() for t in synth.linear768_weights())
+    x, dy = synth.linear768_x(0).cuda(), synth.linear768_dy(0).cuda()
+    recipe = F.Recipe(F.FORMAT_HYBRID, 16, F.AMAX_MAX, 0)
+    bank = F.MetaBank([F.E4M3, F.E4M3, F.E5M2], 16, device="cuda")
+    saved = F.Saved(m, n, k, device="cuda")
+    y = torch.empty(m, n, device="cuda")
+    dx, dw = torch.empty(m, k, device="cuda"), torch.empty(n, k, device="cuda")
+    gq, gqt = torch.empty(m, n, dtype=torch.uint8, device="cuda"), torch.empty(n, m, dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        F.fp8_linear_fwd(x, w, y, recipe, bank.meta(0), bank.meta(1), saved, bias=b)
+        bank.update(recipe)
+
+    def fwd_bwd():
+        F.fp8_linear_fwd(x, w, y, recipe, bank.meta(0), bank.meta(1), saved, bias=b)
+        F.fp8_linear_bwd(dy, k, recipe, bank.meta(2), saved, gq, gqt, dx, dw)
+        bank.update(recipe)
+
+    def timed(fn):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(iters):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / iters
+
+    out = {"workload": "linear 1024x768x768 fp32 in/out, E4M3 (forward) / HYBRID (forward+backward), "
+                       "history 16, launch-latency bound", "iterations": iters}
+    for name, fn in (("forward", fwd), ("forward_backward", fwd_bwd)):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        eager = timed(fn)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graph = timed(g.replay)
+        out[name] = {"us_per_step_eager": round(eager, 2), "us_per_step_graph": round(graph, 2)}
+        del g
+    return out
+
+
 def quant_leg(F, torch, reps=50, first=10):
     """Standalone quantisation of the 2^28-element bf16 tensor (16384 x 16384,
     row magnitudes 2^u, u ~ U[-20, 10]), `reps` repetitions on the same tensor:
@@ -331,6 +390,7 @@ def main():
     jit_ms = time_steps(block, torch, max(3, args.steps // 2))
     block.block.recipe.just_in_time = 0
     torch.cuda.empty_cache()
+    lin768 = linear768_leg(F, torch)
     layer = None if args.no_layer else layer_leg(F, torch, fast_accum=args.fast_accum)
     quant = None if args.no_quant else quant_leg(F, torch)
 
@@ -378,6 +438,7 @@ def main():
             "ms_per_step": round(jit_ms, 4), "tflops": round(STEP_FLOP / (jit_ms * 1e-3) / 1e12, 2),
             "note": "same step with every tensor scaled from its own current amax (an extra amax pass each)"},
     }
+    line["linear768"] = lin768
     if layer is not None:
         line["layer_step"] = layer
     if quant is not None:
