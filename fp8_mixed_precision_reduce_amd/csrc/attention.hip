@@ -70,15 +70,6 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Wave priority around the matrix-core phases: the wave that reaches its
-// products first keeps the matrix cores while the other wave of the SIMD runs
-// its softmax, so the two drift into opposite phases.
-#ifndef ATTN_PRIO
-#define ATTN_PRIO 1
-#endif
-__device__ __forceinline__ void prio_mfma() { if (ATTN_PRIO) __builtin_amdgcn_s_setprio(1); }
-__device__ __forceinline__ void prio_valu() { if (ATTN_PRIO) __builtin_amdgcn_s_setprio(0); }
-
 constexpr float kLazy = 8.0f;   // log2 headroom of the forward's reference maximum
 
 __device__ __forceinline__ v16f mfma(v8bf a, v8bf b, v16f c) {
@@ -114,10 +105,7 @@ struct AttnShape {
 // through three LDS buffers (K [64][256 B] and V^T [128][128 B] each), loaded
 // one block ahead through registers.
 constexpr int kFwdK = 64;
-#ifndef FWD_WAVES
-#define FWD_WAVES 8
-#endif
-constexpr int kFwdWaves = FWD_WAVES;
+constexpr int kFwdWaves = 8;
 constexpr int kFwdBuf = 64 * 256 + 128 * 128;
 
 template <int WAVES>
