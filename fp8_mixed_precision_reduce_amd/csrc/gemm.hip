@@ -612,6 +612,16 @@ hipError_t launch_cfg(const GemmParams& base, int afmt, int bfmt, hipStream_t s)
     return launch_fmt<WM, WN, MB, NB, kE5M2, kE5M2, FAST>(p, s);
 }
 
+// Workgroups of one resident wave of the 256 x 256 configuration.
+template <bool FAST>
+int64_t big_grid() {
+    using C = TileCfg<2, 4, 4, 2>;
+    static const int per_cu = resident_per_cu(k_gemm<2, 4, 4, 2, kE4M3, kE4M3, FAST, false>, C::THREADS);
+    int64_t grid = (int64_t)cu_count() * per_cu;
+    if (grid >= 8) grid -= grid % 8;
+    return grid;
+}
+
 template <bool FAST>
 hipError_t launch_path(const GemmParams& p, int afmt, int bfmt, hipStream_t s) {
     // Tile choice: 256 x 256 when that still gives every CU work, else smaller
@@ -619,9 +629,39 @@ hipError_t launch_path(const GemmParams& p, int afmt, int bfmt, hipStream_t s) {
     // so one wave's LDS reads and converts overlap the other's MFMAs; 128 x 128
     // per wave would need 256 accumulator registers, which the persistent
     // loop's state no longer leaves room for.
-    const int64_t big = ((p.m + 255) / 256) * ((p.n + 255) / 256);
+    const int64_t tm = (p.m + 255) / 256, tn = (p.n + 255) / 256;
+    const int64_t big = tm * tn;
     const int64_t mid = ((p.m + 127) / 128) * ((p.n + 127) / 128);
-    if (big >= 256) return launch_cfg<2, 4, 4, 2, FAST>(p, afmt, bfmt, s);
+    if (big >= 256) {
+        // A last round at most half full (e.g. 896 tiles on 256 workgroups)
+        // leaves CUs idle: the tile rows of the full rounds run on 256 x 256
+        // tiles, the remaining rows (at most 8 tile rows) on 128 x 128 tiles,
+        // four times as many, in a second launch.  Every output element is
+        // computed exactly as in one launch (same k order); the output amax is
+        // merged by both.  Not for the FP8-output epilogue (its transposed
+        // codes are indexed by the full M).
+        const int64_t grid = big_grid<FAST>();
+        const int64_t rem = big % grid;
+        if (rem != 0 && rem <= grid / 2 && !p.q_scale) {
+            int64_t tm1 = tm - 1;
+            while (tm1 > 0 && (tm1 * tn) % grid != 0) --tm1;
+            if (tm1 > 0 && tm - tm1 <= 8) {
+                const int64_t r0 = tm1 * 256;
+                const int64_t esz = p.d_dtype == kF32 ? 4 : 2;
+                GemmParams top = p, rest = p;
+                top.m = r0;
+                rest.m = p.m - r0;
+                rest.a = p.a + r0 * p.k;
+                rest.d = static_cast<uint8_t*>(p.d) + r0 * p.n * esz;
+                if (p.aux) rest.aux = static_cast<uint8_t*>(p.aux) + r0 * p.n * esz;
+                if (p.residual) rest.residual = static_cast<const uint8_t*>(p.residual) + r0 * p.n * esz;
+                const hipError_t e = launch_cfg<2, 4, 4, 2, FAST>(top, afmt, bfmt, s);
+                if (e != hipSuccess) return e;
+                return launch_cfg<2, 2, 2, 2, FAST>(rest, afmt, bfmt, s);
+            }
+        }
+        return launch_cfg<2, 4, 4, 2, FAST>(p, afmt, bfmt, s);
+    }
     if (mid >= 256) return launch_cfg<2, 2, 2, 2, FAST>(p, afmt, bfmt, s);
     return launch_cfg<2, 2, 1, 1, FAST>(p, afmt, bfmt, s);
 }

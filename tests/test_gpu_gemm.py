@@ -264,3 +264,32 @@ def test_gemm_fp8_output(oracle, shape, fmt):
     rows = np.unique(np.concatenate([np.arange(16), rng.integers(0, m, 32), [m - 1]]))
     y = oracle.gemm(a, 0, b, 0, sa, sb, gelu=True, rows=rows)
     assert_gemm_bf16(D[rows], oracle.add_residual(y, r[rows]), oracle, "d")
+
+
+@pytest.mark.parametrize("mode", ["f32_accumulate", "bf16_gelu_aux"])
+def test_gemm_partial_last_round_split(oracle, mode):
+    """14336 x 4096 outputs: 896 tiles of 256 x 256 on a 256-workgroup grid
+    leave a half-empty last round, so the library runs the first 12288 rows on
+    256 x 256 tiles and the last 2048 on 128 x 128 tiles (two launches).  Rows
+    on both sides of the split, the output amax over the whole output, and the
+    accumulate / GeLU / pre-GeLU-copy epilogues are checked."""
+    m, n, k = 14336, 4096, 256
+    rng = np.random.default_rng(14336)
+    a = _codes(oracle, rng, (m, k), 1)
+    b = _codes(oracle, rng, (n, k), 0)
+    sa, sb = np.float32(0.5), np.float32(0.25)
+    rows = np.unique(np.concatenate([rng.integers(0, 12288, 24), rng.integers(12288, m, 24), [12287, 12288, m - 1]]))
+    if mode == "f32_accumulate":
+        d0 = torch.from_numpy(rng.standard_normal((m, n)).astype(np.float32)).cuda()
+        d, _, amax = _run(a, F.E5M2, b, F.E4M3, float(sa), float(sb), d0=d0, epilogue=F.EPI_ACCUMULATE)
+        want = oracle.gemm(a, 1, b, 0, sa, sb, rows=rows) + np_of(d0)[rows].astype(np.float64)
+        got = np_of(d)
+        assert_gemm_f32(got[rows], want, "split f32 accumulate")
+    else:
+        d, ax, amax = _run(a, F.E5M2, b, F.E4M3, float(sa), float(sb), out_dtype=torch.bfloat16,
+                           epilogue=F.EPI_GELU, aux=True)
+        want, pre = oracle.gemm(a, 1, b, 0, sa, sb, gelu=True, rows=rows, want_pre=True)
+        assert_gemm_bf16(np_of(d)[rows], want, oracle, "split bf16 gelu")
+        assert_gemm_bf16(np_of(ax)[rows], pre, oracle, "split pre-GeLU copy")
+        got = oracle.bf16_to_f64(np_of(d))
+    assert_bits_equal(np_of(amax)[0], np.float32(np.max(np.abs(got))), "output amax over both launches")
