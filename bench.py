@@ -355,6 +355,11 @@ def main():
 
     import fp8_mixed_precision_reduce_amd as F
 
+    t0 = time.perf_counter()
+
+    def progress(what):
+        print(f"bench: {what} done ({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+
     if args.copy_calibration > 0:
         n = int(args.copy_calibration * (1 << 30)) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -370,6 +375,7 @@ def main():
         block.step()
     ms = time_steps(block, torch, args.steps)
     kb = kernel_breakdown(block, F, torch, args.steps)
+    progress("MLP block step")
     n_g, t_g = kb.get("gemm", (1, float("nan")))
     gemm_ms = t_g / n_g
     gemm_tflops = GEMM_FLOP / (gemm_ms * 1e-3) / 1e12
@@ -390,9 +396,15 @@ def main():
     jit_ms = time_steps(block, torch, max(3, args.steps // 2))
     block.block.recipe.just_in_time = 0
     torch.cuda.empty_cache()
+    progress("other accumulation mode and just-in-time scaling")
     lin768 = linear768_leg(F, torch)
+    progress("768-wide linear")
     layer = None if args.no_layer else layer_leg(F, torch, fast_accum=args.fast_accum)
+    if layer is not None:
+        progress("transformer-layer step")
     quant = None if args.no_quant else quant_leg(F, torch)
+    if quant is not None:
+        progress("quantisation kernels")
 
     value = STEP_FLOP / (ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if args.fast_accum else PEAK_F16_TFLOPS
@@ -445,6 +457,7 @@ def main():
         line["quant"] = quant
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch)
+        progress("oracle on the host")
     print(json.dumps(line), flush=True)
 
 
