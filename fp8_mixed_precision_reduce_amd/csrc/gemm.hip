@@ -49,9 +49,12 @@
 // The MFMA takes the B tile as
 // its first operand, so each lane's accumulators run along n: four
 // consecutive outputs of one row.  fp32 outputs are written from there with
-// one 16-byte store per lane; bf16 outputs (and the pre-GeLU copy) are first
-// staged in the LDS, which is free after the k loop, and then written by the
-// whole workgroup in 16-byte pieces that cover complete row segments.  Tiles are rasterised in groups of 8 tile-rows, and the
+// one 16-byte store per lane, except where the output's row stride is a
+// multiple of 32 KiB; those, and bf16 outputs (and the pre-GeLU copy), are
+// first staged in the LDS, which is free after the k loop, and then written by
+// the whole workgroup in 16-byte pieces that cover complete row segments.  A
+// launch may cover a column range of a wider output (its row stride is then
+// the full width).  Tiles are rasterised in groups of 8 tile-rows, and the
 // workgroup index is remapped so that each XCD (workgroups are dealt
 // round-robin over 8 XCDs) works on a contiguous range of tiles that share
 // operands in its own L2.
@@ -69,11 +72,13 @@ constexpr int kBK = 128;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kEpiFastAccum = 4;
+constexpr int kOutDirect = 0, kOutF32Staged = 1;     // epilogue kinds (kernel template)
 
 struct GemmParams {
     const uint8_t* a;
     const uint8_t* b;
     int64_t m, n, k;
+    int64_t ldd;               // row stride (elements) of d, aux and residual; n unless a launch covers a column range
     const float* sinv_a;
     const float* sinv_b;
     const void* bias;
@@ -169,7 +174,7 @@ __device__ __forceinline__ void tile_coords(int i, int32_t tiles_m, int32_t tile
     tn = rem / gsize;
 }
 
-template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST, bool QOUT>
+template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST, bool QOUT, int OUT>
 __global__ void __launch_bounds__(64 * WM * WN, (WM * WN * MB * NB >= 64 ? (WM * WN) / 4 : 2))
 k_gemm(GemmParams p) {
     using C = TileCfg<WM, WN, MB, NB>;
@@ -182,7 +187,7 @@ k_gemm(GemmParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t smem1[C::STAGE];
     __shared__ uint32_t red[C::WAVES];
 
-    const int64_t M = p.m, N = p.n, K = p.k;
+    const int64_t M = p.m, N = p.n, K = p.k, LDD = p.ldd;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave % WM, wn = wave / WM;
@@ -362,7 +367,6 @@ k_gemm(GemmParams p) {
     // holds row i * 32 + r32 and, for q4 = 0..3, the four columns
     // j * 32 + 8 q4 + 4 g .. + 3 of its wave's sub-tile.
     const bool gelu = p.epilogue & 1, accum = p.epilogue & 2;
-    const bool out_bf16 = p.d_dtype == kBF16;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
 #pragma unroll
@@ -386,7 +390,7 @@ k_gemm(GemmParams p) {
         }
     }
 
-    if (out_bf16) {
+    if (OUT == kOutDirect && p.d_dtype == kBF16) {     // (OUT folds at compile time)
         // bf16 outputs go through LDS (free after the k loop) so that the global
         // stores write whole row segments: rows of the wave-row wm go to stage
         // array wm, BN * 2 bytes per row, 8-byte units XOR-swizzled by row.
@@ -406,7 +410,7 @@ k_gemm(GemmParams p) {
                 const uint8_t* src = (r < C::BM / 2 ? smem0 : smem1) + lds_unit(lr, 2 * c);
                 const uint4 v = *reinterpret_cast<const uint4*>(src);
                 const int64_t row = m0 + r, col = n0 + 8 * c;
-                if (row < M && col < N) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + row * N + col) = v;
+                if (row < M && col < N) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + row * LDD + col) = v;
             }
             __syncthreads();
         };
@@ -439,7 +443,7 @@ k_gemm(GemmParams p) {
                     for (int e = 0; e < 4; ++e) y[e] = gelu ? gelu_f32(acc[i][j][4 * q4 + e]) : acc[i][j][4 * q4 + e];
                     if (p.residual && inside) {
                         const uint2 rv =
-                            *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.residual) + mrow * N + ncol);
+                            *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.residual) + mrow * LDD + ncol);
                         y[0] += bf16_to_f32(rv.x & 0xFFFFu); y[1] += bf16_to_f32(rv.x >> 16);
                         y[2] += bf16_to_f32(rv.y & 0xFFFFu); y[3] += bf16_to_f32(rv.y >> 16);
                     }
@@ -484,7 +488,7 @@ k_gemm(GemmParams p) {
                     const uint4 v = *reinterpret_cast<const uint4*>((r < HALF ? smem0 : smem1) + lds_unit(r % HALF, 2 * c));
                     const int64_t row = m0 + r, col = n0 + 8 * c;
                     const bool inside = row < M && col < N;
-                    if (p.d && inside) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.d) + row * N + col) = v;
+                    if (p.d && inside) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.d) + row * LDD + col) = v;
                     const float f[8] = {bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
                                         bf16_to_f32(v.y >> 16),     bf16_to_f32(v.z & 0xFFFFu), bf16_to_f32(v.z >> 16),
                                         bf16_to_f32(v.w & 0xFFFFu), bf16_to_f32(v.w >> 16)};
@@ -524,7 +528,66 @@ k_gemm(GemmParams p) {
             }
             __syncthreads();               // the staged values are read; the next tile may DMA
         }
+    } else if (OUT == kOutF32Staged) {
+        // fp32 outputs whose row stride is a multiple of 32 KiB go through LDS
+        // as well: written from registers, each wave store puts 32 bytes into
+        // each of 32 rows one stride apart, which such strides map onto one
+        // memory channel (measured 9-11% slower on 8192- and 16384-column
+        // outputs; 4096- and 12288-column outputs are not affected and keep
+        // the register path).  One wave-row (BM / 2 rows) per pass, its rows
+        // split over the two stage arrays, 1 KiB per row for BN = 256,
+        // 16-byte units XOR-swizzled by the row's low 4 bits; then the whole
+        // workgroup applies the residual and the accumulate in the same order
+        // as the register path and writes complete row segments.  Never
+        // launched with GeLU.
+        static_assert(WM == 2 && (C::BM / 4) * C::BN * 4 <= C::STAGE && C::BN >= 64, "fp32 staging layout");
+        constexpr int UPR = C::BN / 4;                  // 16-byte units (4 floats) per row
+        constexpr int QR = C::BM / 4;                   // rows per stage array in one pass
+        constexpr int RPP = C::THREADS / UPR;           // rows per store step
+        auto f32_unit = [&](int lr, int unit) {
+            return (lr < QR ? smem0 : smem1) + (lr % QR) * (C::BN * 4) + ((unit ^ (lr & 15)) << 4);
+        };
+        const int c = t % UPR;
+#pragma unroll
+        for (int pass = 0; pass < WM; ++pass) {
+            __syncthreads();
+            if (wm == pass) {
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4)
+                            *reinterpret_cast<float4*>(f32_unit(i * 32 + r32, (wn * NB * 32 + j * 32 + 8 * q4 + 4 * g) / 4)) =
+                                make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
+                                            acc[i][j][4 * q4 + 3]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int st = 0; st < (C::BM / 2) / RPP; ++st) {
+                const int lr = t / UPR + RPP * st;
+                const int64_t mrow = m0 + pass * (C::BM / 2) + lr, ncol = n0 + 4 * c;
+                if (mrow >= M || ncol >= N) continue;
+                const float4 v = *reinterpret_cast<const float4*>(f32_unit(lr, c));
+                float y[4] = {v.x, v.y, v.z, v.w};
+                const int64_t off = mrow * LDD + ncol;
+                if (p.residual) {
+                    const float4 rv = *reinterpret_cast<const float4*>(static_cast<const float*>(p.residual) + off);
+                    y[0] += rv.x; y[1] += rv.y; y[2] += rv.z; y[3] += rv.w;
+                }
+                float4* dp = reinterpret_cast<float4*>(static_cast<float*>(p.d) + off);
+                if (accum) {
+                    const float4 old = *dp;
+                    y[0] = old.x + y[0]; y[1] = old.y + y[1]; y[2] = old.z + y[2]; y[3] = old.w + y[3];
+                }
+                *dp = make_float4(y[0], y[1], y[2], y[3]);
+                amax = max(amax, max(max(abs_bits(y[0]), abs_bits(y[1])), max(abs_bits(y[2]), abs_bits(y[3]))));
+            }
+        }
+        __syncthreads();     // the next tile's DMA rewrites the LDS
     } else {
+        // fp32 outputs from registers: lane (r32, g) writes four consecutive
+        // columns of its row per 32 x 32 block.
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
             const int64_t mrow = m0 + wm * MB * 32 + i * 32 + r32;
@@ -535,7 +598,7 @@ k_gemm(GemmParams p) {
                     const int64_t ncol = n0 + wn * NB * 32 + j * 32 + 8 * q4 + 4 * g;
                     if (mrow >= M || ncol >= N) continue;
                     float y[4];
-                    const int64_t off = mrow * N + ncol;
+                    const int64_t off = mrow * LDD + ncol;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * q4 + e];
                     if (gelu) {
@@ -584,18 +647,34 @@ int resident_per_cu(Kern kern, int threads) {
     return n;
 }
 
-template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST, bool QOUT = false>
-hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
+template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST, bool QOUT, int OUT>
+hipError_t launch_out(const GemmParams& p, hipStream_t s) {
     using C = TileCfg<WM, WN, MB, NB>;
-    static const int per_cu = resident_per_cu(k_gemm<WM, WN, MB, NB, AF, BF, FAST, QOUT>, C::THREADS);
+    static const int per_cu = resident_per_cu(k_gemm<WM, WN, MB, NB, AF, BF, FAST, QOUT, OUT>, C::THREADS);
     // One resident wave of workgroups, each looping over tiles; a multiple of
     // 8 so that every workgroup stays on the same XCD's tile range.
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     int64_t grid = (int64_t)cu_count() * per_cu;
     if (grid >= 8) grid -= grid % 8;
     if (grid > ntiles) grid = ntiles;
-    hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, AF, BF, FAST, QOUT>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, p);
+    hipLaunchKernelGGL((k_gemm<WM, WN, MB, NB, AF, BF, FAST, QOUT, OUT>), dim3((unsigned)grid), dim3(C::THREADS), 0, s,
+                       p);
     return hipGetLastError();
+}
+
+// The staged fp32 epilogue is an instance of its own: with it in the same
+// kernel as the bf16 and register fp32 epilogues, the register allocation of
+// the whole kernel changed (37 spilled registers instead of 14 on the exact
+// path) and bf16-output GEMMs measured 2-5% slower.
+template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST, bool QOUT = false>
+hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
+    if constexpr (QOUT) {
+        return launch_out<WM, WN, MB, NB, AF, BF, FAST, true, kOutDirect>(p, s);     // bf16 outputs only
+    } else {
+        if (p.d_dtype == kF32 && !(p.epilogue & 1) && (p.ldd * 4) % 32768 == 0)
+            return launch_out<WM, WN, MB, NB, AF, BF, FAST, false, kOutF32Staged>(p, s);
+        return launch_out<WM, WN, MB, NB, AF, BF, FAST, false, kOutDirect>(p, s);
+    }
 }
 
 template <int WM, int WN, int MB, int NB, bool FAST>
@@ -616,7 +695,7 @@ hipError_t launch_cfg(const GemmParams& base, int afmt, int bfmt, hipStream_t s)
 template <bool FAST>
 int64_t big_grid() {
     using C = TileCfg<2, 4, 4, 2>;
-    static const int per_cu = resident_per_cu(k_gemm<2, 4, 4, 2, kE4M3, kE4M3, FAST, false>, C::THREADS);
+    static const int per_cu = resident_per_cu(k_gemm<2, 4, 4, 2, kE4M3, kE4M3, FAST, false, kOutDirect>, C::THREADS);
     int64_t grid = (int64_t)cu_count() * per_cu;
     if (grid >= 8) grid -= grid % 8;
     return grid;
@@ -638,26 +717,47 @@ hipError_t launch_path(const GemmParams& p, int afmt, int bfmt, hipStream_t s) {
         // tiles, the remaining rows (at most 8 tile rows) on 128 x 128 tiles,
         // four times as many, in a second launch.  Every output element is
         // computed exactly as in one launch (same k order); the output amax is
-        // merged by both.  Not for the FP8-output epilogue (its transposed
-        // codes are indexed by the full M).
+        // merged by both.  Not for the FP8-output epilogue (its codes are
+        // indexed by the full M and N).
         const int64_t grid = big_grid<FAST>();
         const int64_t rem = big % grid;
         if (rem != 0 && rem <= grid / 2 && !p.q_scale) {
+            const int64_t esz = p.d_dtype == kF32 ? 4 : 2;
             int64_t tm1 = tm - 1;
             while (tm1 > 0 && (tm1 * tn) % grid != 0) --tm1;
             if (tm1 > 0 && tm - tm1 <= 8) {
                 const int64_t r0 = tm1 * 256;
-                const int64_t esz = p.d_dtype == kF32 ? 4 : 2;
                 GemmParams top = p, rest = p;
                 top.m = r0;
                 rest.m = p.m - r0;
                 rest.a = p.a + r0 * p.k;
-                rest.d = static_cast<uint8_t*>(p.d) + r0 * p.n * esz;
-                if (p.aux) rest.aux = static_cast<uint8_t*>(p.aux) + r0 * p.n * esz;
-                if (p.residual) rest.residual = static_cast<const uint8_t*>(p.residual) + r0 * p.n * esz;
+                rest.d = static_cast<uint8_t*>(p.d) + r0 * p.ldd * esz;
+                if (p.aux) rest.aux = static_cast<uint8_t*>(p.aux) + r0 * p.ldd * esz;
+                if (p.residual) rest.residual = static_cast<const uint8_t*>(p.residual) + r0 * p.ldd * esz;
                 const hipError_t e = launch_cfg<2, 4, 4, 2, FAST>(top, afmt, bfmt, s);
                 if (e != hipSuccess) return e;
                 return launch_cfg<2, 2, 2, 2, FAST>(rest, afmt, bfmt, s);
+            }
+            // A wide output (e.g. 4096 x 14336) splits by columns instead: the
+            // first tile columns on 256 x 256 tiles, the last (at most 8) on
+            // 128 x 128 tiles, both writing into the full-width output through
+            // its row stride.
+            int64_t tn1 = tn - 1;
+            while (tn1 > 0 && (tm * tn1) % grid != 0) --tn1;
+            if (tn1 > 0 && tn - tn1 <= 8) {
+                const int64_t c0 = tn1 * 256;
+                const int64_t bsz = p.bias_dtype == kF32 ? 4 : 2;
+                GemmParams left = p, right = p;
+                left.n = c0;
+                right.n = p.n - c0;
+                right.b = p.b + c0 * p.k;
+                if (p.bias) right.bias = static_cast<const uint8_t*>(p.bias) + c0 * bsz;
+                right.d = static_cast<uint8_t*>(p.d) + c0 * esz;
+                if (p.aux) right.aux = static_cast<uint8_t*>(p.aux) + c0 * esz;
+                if (p.residual) right.residual = static_cast<const uint8_t*>(p.residual) + c0 * esz;
+                const hipError_t e = launch_cfg<2, 4, 4, 2, FAST>(left, afmt, bfmt, s);
+                if (e != hipSuccess) return e;
+                return launch_cfg<2, 2, 2, 2, FAST>(right, afmt, bfmt, s);
             }
         }
         return launch_cfg<2, 4, 4, 2, FAST>(p, afmt, bfmt, s);
@@ -674,7 +774,7 @@ hipError_t launch_gemm(const uint8_t* a, int afmt, const uint8_t* b, int bfmt, i
                        uint8_t* q, uint8_t* qt, int q_fmt, hipStream_t s) {
     if (m == 0 || n == 0) return hipSuccess;
     GemmParams p{};
-    p.a = a; p.b = b; p.m = m; p.n = n; p.k = k;
+    p.a = a; p.b = b; p.m = m; p.n = n; p.k = k; p.ldd = n;
     p.sinv_a = sinv_a; p.sinv_b = sinv_b; p.bias = bias; p.d = d; p.aux = aux; p.residual = residual; p.amax = amax;
     p.q_scale = q_scale; p.q = q; p.qt = qt; p.q_fmt = q_fmt;
     p.bias_dtype = bias_dtype; p.d_dtype = d_dtype; p.epilogue = epilogue;

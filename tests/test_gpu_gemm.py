@@ -109,13 +109,14 @@ def test_gemm_deterministic(oracle):
     assert torch.equal(d1.view(torch.int32), d2.view(torch.int32)) and torch.equal(m1, m2)
 
 
-@pytest.mark.parametrize("which", ["fc1", "fc2_dgrad", "fc1_wgrad"])
+@pytest.mark.parametrize("which", ["fc1", "fc2_dgrad", "fc1_wgrad", "fc2_wgrad"])
 def test_gemm_full_size_mlp_shapes_sampled(oracle, which):
     """The MLP block's GEMM shapes at full size, in the launch configuration the
     benchmark times; the oracle recomputes 24 sampled rows."""
     m, n, k, af, oaf = {"fc1": (8192, 14336, 4096, F.E4M3, 0),
                         "fc2_dgrad": (8192, 14336, 4096, F.E5M2, 1),
-                        "fc1_wgrad": (14336, 4096, 8192, F.E5M2, 1)}[which]
+                        "fc1_wgrad": (14336, 4096, 8192, F.E5M2, 1),
+                        "fc2_wgrad": (4096, 14336, 8192, F.E5M2, 1)}[which]
     g = torch.Generator(device="cuda")
     g.manual_seed(m + n + k)
     a32 = torch.randn(m, k, device="cuda", generator=g)
@@ -266,30 +267,79 @@ def test_gemm_fp8_output(oracle, shape, fmt):
     assert_gemm_bf16(D[rows], oracle.add_residual(y, r[rows]), oracle, "d")
 
 
+@pytest.mark.parametrize("shape", [(272, 8192, 128), (1040, 8192, 256), (2064, 16384, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gemm_f32_row_stride_of_32k_multiple(oracle, shape):
+    """fp32 outputs whose rows are a multiple of 32 KiB apart (8192 or 16384
+    columns) take the LDS-staged epilogue; the three shapes run it on 64-,
+    128- and 256-tile configurations with a ragged M.  Bias, residual and
+    accumulate are applied in the register path's order, so the results are
+    checked against the oracle and the amax against the output as written;
+    a GeLU epilogue on the same shape (register path) is checked too."""
+    m, n, k = shape
+    rng = np.random.default_rng(m + n + k)
+    a = _codes(oracle, rng, (m, k), 1)
+    b = _codes(oracle, rng, (n, k), 0)
+    sa, sb = np.float32(0.125), np.float32(0.75)
+    bias = rng.standard_normal(n).astype(np.float32)
+    r = rng.standard_normal((m, n)).astype(np.float32)
+    d0 = rng.standard_normal((m, n)).astype(np.float32)
+    rows = np.unique(np.concatenate([np.arange(8), rng.integers(0, m, 40), [m - 1]]))
+    # bias + residual
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    d = torch.empty(m, n, dtype=torch.float32, device="cuda")
+    F.fp8_gemm(dev(a), F.E5M2, dev(b), F.E4M3, _scalar(float(sa)), _scalar(float(sb)), d, bias=dev(bias),
+               residual=dev(r), amax_d=amax)
+    y = oracle.gemm(a, 1, b, 0, sa, sb, bias.astype(np.float64), rows=rows)
+    got = np_of(d)
+    assert_gemm_f32(got[rows], oracle.add_residual(y, r[rows]), f"{shape} bias+residual")
+    assert_bits_equal(np_of(amax)[0], np.float32(np.max(np.abs(got))), f"{shape} amax")
+    # accumulate into d
+    dacc = dev(d0)
+    F.fp8_gemm(dev(a), F.E5M2, dev(b), F.E4M3, _scalar(float(sa)), _scalar(float(sb)), dacc,
+               epilogue=F.EPI_ACCUMULATE)
+    want = oracle.gemm(a, 1, b, 0, sa, sb, rows=rows) + d0[rows].astype(np.float64)
+    assert_gemm_f32(np_of(dacc)[rows], want, f"{shape} accumulate")
+    # GeLU with its fp32 pre-GeLU copy
+    dg = torch.empty(m, n, dtype=torch.float32, device="cuda")
+    ax = torch.empty(m, n, dtype=torch.float32, device="cuda")
+    F.fp8_gemm(dev(a), F.E5M2, dev(b), F.E4M3, _scalar(float(sa)), _scalar(float(sb)), dg, bias=dev(bias),
+               epilogue=F.EPI_GELU, aux=ax)
+    yg, pre = oracle.gemm(a, 1, b, 0, sa, sb, bias.astype(np.float64), gelu=True, rows=rows, want_pre=True)
+    assert_gemm_f32(np_of(dg)[rows], yg, f"{shape} gelu")
+    assert_gemm_f32(np_of(ax)[rows], pre, f"{shape} pre-gelu copy")
+
+
 @pytest.mark.parametrize("mode", ["f32_accumulate", "bf16_gelu_aux"])
-def test_gemm_partial_last_round_split(oracle, mode):
-    """14336 x 4096 outputs: 896 tiles of 256 x 256 on a 256-workgroup grid
-    leave a half-empty last round, so the library runs the first 12288 rows on
-    256 x 256 tiles and the last 2048 on 128 x 128 tiles (two launches).  Rows
-    on both sides of the split, the output amax over the whole output, and the
-    accumulate / GeLU / pre-GeLU-copy epilogues are checked."""
-    m, n, k = 14336, 4096, 256
-    rng = np.random.default_rng(14336)
+@pytest.mark.parametrize("orient", ["tall", "wide"])
+def test_gemm_partial_last_round_split(oracle, mode, orient):
+    """14336 x 4096 and 4096 x 14336 outputs: 896 tiles of 256 x 256 on a
+    256-workgroup grid leave a half-empty last round, so the library runs the
+    first 12288 rows (tall) or columns (wide) on 256 x 256 tiles and the rest
+    on 128 x 128 tiles (two launches; the wide case writes through the output's
+    row stride).  Outputs on both sides of the split, the output amax over the
+    whole output, the bias, and the accumulate / GeLU / pre-GeLU-copy
+    epilogues are checked."""
+    m, n, k = (14336, 4096, 256) if orient == "tall" else (4096, 14336, 256)
+    rng = np.random.default_rng(m + 2 * n)
     a = _codes(oracle, rng, (m, k), 1)
     b = _codes(oracle, rng, (n, k), 0)
     sa, sb = np.float32(0.5), np.float32(0.25)
-    rows = np.unique(np.concatenate([rng.integers(0, 12288, 24), rng.integers(12288, m, 24), [12287, 12288, m - 1]]))
+    rows = np.unique(np.concatenate([rng.integers(0, min(m, 12288), 24), rng.integers(min(m, 12288) - 256, m, 24),
+                                     [0, m - 1] + ([12287, 12288] if m > 12288 else [])]))
+    bias = rng.standard_normal(n).astype(np.float32)
     if mode == "f32_accumulate":
         d0 = torch.from_numpy(rng.standard_normal((m, n)).astype(np.float32)).cuda()
-        d, _, amax = _run(a, F.E5M2, b, F.E4M3, float(sa), float(sb), d0=d0, epilogue=F.EPI_ACCUMULATE)
-        want = oracle.gemm(a, 1, b, 0, sa, sb, rows=rows) + np_of(d0)[rows].astype(np.float64)
+        d, _, amax = _run(a, F.E5M2, b, F.E4M3, float(sa), float(sb), d0=d0, bias=dev(bias),
+                          epilogue=F.EPI_ACCUMULATE)
+        want = oracle.gemm(a, 1, b, 0, sa, sb, bias.astype(np.float64), rows=rows) + np_of(d0)[rows].astype(np.float64)
         got = np_of(d)
-        assert_gemm_f32(got[rows], want, "split f32 accumulate")
+        assert_gemm_f32(got[rows], want, f"split ({orient}) f32 accumulate")
     else:
-        d, ax, amax = _run(a, F.E5M2, b, F.E4M3, float(sa), float(sb), out_dtype=torch.bfloat16,
+        d, ax, amax = _run(a, F.E5M2, b, F.E4M3, float(sa), float(sb), out_dtype=torch.bfloat16, bias=dev(bias),
                            epilogue=F.EPI_GELU, aux=True)
-        want, pre = oracle.gemm(a, 1, b, 0, sa, sb, gelu=True, rows=rows, want_pre=True)
-        assert_gemm_bf16(np_of(d)[rows], want, oracle, "split bf16 gelu")
-        assert_gemm_bf16(np_of(ax)[rows], pre, oracle, "split pre-GeLU copy")
+        want, pre = oracle.gemm(a, 1, b, 0, sa, sb, bias.astype(np.float64), gelu=True, rows=rows, want_pre=True)
+        assert_gemm_bf16(np_of(d)[rows], want, oracle, f"split ({orient}) bf16 gelu")
+        assert_gemm_bf16(np_of(ax)[rows], pre, oracle, f"split ({orient}) pre-GeLU copy")
         got = oracle.bf16_to_f64(np_of(d))
     assert_bits_equal(np_of(amax)[0], np.float32(np.max(np.abs(got))), "output amax over both launches")
