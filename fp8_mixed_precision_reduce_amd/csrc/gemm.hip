@@ -367,6 +367,7 @@ k_gemm(GemmParams p) {
     // holds row i * 32 + r32 and, for q4 = 0..3, the four columns
     // j * 32 + 8 q4 + 4 g .. + 3 of its wave's sub-tile.
     const bool gelu = p.epilogue & 1, accum = p.epilogue & 2;
+    const bool want_amax = p.amax != nullptr;      // the output amax costs VALU work per element
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
 #pragma unroll
@@ -448,7 +449,7 @@ k_gemm(GemmParams p) {
                         y[2] += bf16_to_f32(rv.y & 0xFFFFu); y[3] += bf16_to_f32(rv.y >> 16);
                     }
                     const uint2 o = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-                    if (inside)
+                    if (want_amax && inside)
                         amax = max(amax, max(max(abs_bits(bf16_to_f32(o.x & 0xFFFFu)), abs_bits(bf16_to_f32(o.x >> 16))),
                                              max(abs_bits(bf16_to_f32(o.y & 0xFFFFu)), abs_bits(bf16_to_f32(o.y >> 16)))));
                     const int unit = (wn * NB * 32 + j * 32 + 8 * q4 + 4 * g) / 4;
@@ -581,7 +582,8 @@ k_gemm(GemmParams p) {
                     y[0] = old.x + y[0]; y[1] = old.y + y[1]; y[2] = old.z + y[2]; y[3] = old.w + y[3];
                 }
                 *dp = make_float4(y[0], y[1], y[2], y[3]);
-                amax = max(amax, max(max(abs_bits(y[0]), abs_bits(y[1])), max(abs_bits(y[2]), abs_bits(y[3]))));
+                if (want_amax)
+                    amax = max(amax, max(max(abs_bits(y[0]), abs_bits(y[1])), max(abs_bits(y[2]), abs_bits(y[3]))));
             }
         }
         __syncthreads();     // the next tile's DMA rewrites the LDS
@@ -617,7 +619,8 @@ k_gemm(GemmParams p) {
                         y[0] = old.x + y[0]; y[1] = old.y + y[1]; y[2] = old.z + y[2]; y[3] = old.w + y[3];
                     }
                     *dp = make_float4(y[0], y[1], y[2], y[3]);
-                    amax = max(amax, max(max(abs_bits(y[0]), abs_bits(y[1])), max(abs_bits(y[2]), abs_bits(y[3]))));
+                    if (want_amax)
+                        amax = max(amax, max(max(abs_bits(y[0]), abs_bits(y[1])), max(abs_bits(y[2]), abs_bits(y[3]))));
                 }
             }
         }
