@@ -7,6 +7,7 @@
 // device memory, or lets a C++ exception escape.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -65,14 +66,14 @@ struct Timer {
     std::vector<hipEvent_t> ev;     // 2 per record
     std::vector<int32_t> kinds;
     int32_t used = 0;
-    int32_t capacity = 0;
+    std::atomic<int32_t> capacity{0};   // read without the lock on every launch (0: timing off)
     int32_t pending_kind = -1;
 };
 Timer g_timer;
 }  // namespace
 
 void timing_before(int kind, hipStream_t stream) {
-    if (g_timer.capacity == 0) return;
+    if (g_timer.capacity.load(std::memory_order_relaxed) == 0) return;
     std::lock_guard<std::mutex> lk(g_timer.mu);
     if (g_timer.used >= g_timer.capacity) return;
     if (hipEventRecord(g_timer.ev[2 * g_timer.used], stream) != hipSuccess) return;   // launch goes untimed
@@ -80,7 +81,7 @@ void timing_before(int kind, hipStream_t stream) {
 }
 
 void timing_after(hipStream_t stream) {
-    if (g_timer.capacity == 0) return;
+    if (g_timer.capacity.load(std::memory_order_relaxed) == 0) return;
     std::lock_guard<std::mutex> lk(g_timer.mu);
     if (g_timer.pending_kind < 0) return;
     if (hipEventRecord(g_timer.ev[2 * g_timer.used + 1], stream) != hipSuccess) {
@@ -132,10 +133,12 @@ int32_t fp8lin_timing_enable(int32_t capacity) {
     if (capacity == 0) return ok();
     g_timer.ev.resize(2 * (size_t)capacity);
     g_timer.kinds.assign(capacity, 0);
-    for (auto& e : g_timer.ev) {
-        const hipError_t r = hipEventCreate(&e);
+    for (size_t i = 0; i < g_timer.ev.size(); ++i) {
+        const hipError_t r = hipEventCreate(&g_timer.ev[i]);
         if (r != hipSuccess) {
+            for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(g_timer.ev[j]);
             g_timer.ev.clear();
+            g_timer.kinds.clear();
             return hip_status(r, "hipEventCreate");
         }
     }

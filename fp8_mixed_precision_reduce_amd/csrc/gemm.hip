@@ -58,6 +58,8 @@
 // workgroup index is remapped so that each XCD (workgroups are dealt
 // round-robin over 8 XCDs) works on a contiguous range of tiles that share
 // operands in its own L2.
+#include <atomic>
+
 #include "common.h"
 
 namespace fp8lin {
@@ -630,17 +632,18 @@ k_gemm(GemmParams p) {
     if (p.amax) block_amax_merge(amax, p.amax, red);
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; callers on several
+// host threads may race to fill an entry, with the same value).
 int cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 template <typename Kern>
