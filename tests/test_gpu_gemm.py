@@ -26,6 +26,11 @@ def _codes(oracle, rng, shape, fmt, spread=4.0):
     return oracle.cast(x, fmt, 1.0)
 
 
+def _torch_codes(x, fmt):
+    """FP8 codes of x (in range) from PyTorch's float8 conversion, as uint8."""
+    return x.to(torch.float8_e4m3fn if fmt == F.E4M3 else torch.float8_e5m2).view(torch.uint8)
+
+
 def _run(a, af, b, bf, sa, sb, out_dtype=torch.float32, bias=None, epilogue=0, aux=False, d0=None):
     m, n = a.shape[0], b.shape[0]
     d = d0.clone() if d0 is not None else torch.empty(m, n, dtype=out_dtype, device="cuda")
@@ -119,13 +124,9 @@ def test_gemm_full_size_mlp_shapes_sampled(oracle, which):
                         "fc2_wgrad": (4096, 14336, 8192, F.E5M2, 1)}[which]
     g = torch.Generator(device="cuda")
     g.manual_seed(m + n + k)
-    a32 = torch.randn(m, k, device="cuda", generator=g)
-    b32 = torch.randn(n, k, device="cuda", generator=g) * 0.02
-    a = torch.empty(m, k, dtype=torch.uint8, device="cuda")
-    b = torch.empty(n, k, dtype=torch.uint8, device="cuda")
-    F.fp8_cast(a32, af, _scalar(8.0), a)
-    F.fp8_cast(b32, F.E4M3, _scalar(2000.0), b)
-    del a32, b32
+    # operand codes from PyTorch's own float8 conversions (not this library's cast)
+    a = _torch_codes(torch.randn(m, k, device="cuda", generator=g) * 8.0, af)
+    b = _torch_codes(torch.randn(n, k, device="cuda", generator=g) * 40.0, F.E4M3)
     d = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
     F.fp8_gemm(a, af, b, F.E4M3, _scalar(0.125), _scalar(1 / 2000.0), d)
     rows = np.random.default_rng(0).choice(m, 24, replace=False)

@@ -112,3 +112,74 @@ def test_mlp_block_full_size_sampled(oracle):
     rows = np.sort(rng.choice(8192, 12, replace=False))
     wrows = np.sort(rng.choice(4096, 4, replace=False))
     _run_steps(oracle, blk, steps=2, rows=rows, wrows=wrows)
+
+
+def test_mlp_block_end_to_end_from_inputs_alone(oracle):
+    """The oracle runs the whole block from the seeded inputs alone, 4 steps,
+    with no GPU value entering it (the stepwise tests above feed each sub-step
+    the GPU's own inputs).  Everything that depends only on the inputs and
+    their histories is bit-exact: the codes of X, W1, W2 and dY and their
+    amaxes, histories and scales.  The chained tensors may differ where a
+    one-ulp bf16 difference upstream crosses an FP8 rounding boundary: H and
+    Z stay within one bf16 ulp (their inputs are exact), a differing H or dZ
+    code is an adjacent code and at most 1% of them differ, and Y, dH, dX,
+    dW1, dW2 agree to 1e-2 normwise, far below the FP8 quantisation step
+    (2^-4 relative for E4M3)."""
+    m, hidden, ffn, L = 272, 208, 464, 16
+    x, w1, w2, dy = synth.mlp_inputs(0, device="cpu", m=m, hidden=hidden, ffn=ffn)
+    blk = Fp8MlpBlock(x.cuda(), w1.cuda(), w2.cuda(), dy.cuda(), history_len=L, keep_dz=True, keep_h=True)
+    X, W1, W2, DY = (np_of(t) for t in (x, w1, w2, dy))
+    metas = oracle.mlp_metas(L)
+    idx = {name: i for i, name in enumerate(MLP_TENSORS)}
+
+    def ranks(fmt):
+        # position of each code's value among the format's distinct finite values (+0 and -0 share one)
+        vals = np.array([oracle.decode(c, fmt) for c in range(256)])
+        finite = np.unique(vals[np.isfinite(vals)])
+        return np.array([np.searchsorted(finite, v) if np.isfinite(v) else -10 for v in vals])
+
+    rank = {E4: ranks(E4), E5: ranks(E5)}
+
+    def code_diff(got, want, fmt, tag):
+        d = got != want
+        if d.any():
+            step = np.abs(rank[fmt][got[d]] - rank[fmt][want[d]])
+            assert np.all(step <= 1), tag + ": a differing code is not a neighbouring value"
+        assert d.mean() <= 0.01, f"{tag}: {d.mean():.4f} of the codes differ"
+
+    def normwise(got64, want64, tag):
+        err = np.linalg.norm(got64 - want64) / np.linalg.norm(want64)
+        assert err <= 1e-2, f"{tag}: normwise error {err:.2e}"
+
+    for step in range(4):
+        tag = f"step {step}"
+        blk.forward()
+        blk.backward()
+        torch.cuda.synchronize()
+        hist_before = np_of(blk.bank.amax_history[:, 0])
+        ref = oracle.mlp_step(X, W1, W2, DY, metas)
+        blk.update()
+        torch.cuda.synchronize()
+        # input-only quantities: bit-exact
+        assert_bits_equal(np_of(blk.saved1.xq), ref["fw1"]["xq"], tag + " Xq")
+        assert_bits_equal(np_of(blk.saved1.wq), ref["fw1"]["wq"], tag + " W1q")
+        assert_bits_equal(np_of(blk.saved2.wq), ref["fw2"]["wq"], tag + " W2q")
+        assert_bits_equal(np_of(blk.dyq), ref["bw2"]["gq"], tag + " dYq")
+        for name in ("x", "w1", "w2", "dy"):
+            i = idx[name]
+            assert_bits_equal(hist_before[i], np.float32(metas[name].hist[1]), f"{tag} amax {name}")
+            assert_bits_equal(np_of(blk.bank.amax_history[i]), metas[name].hist, f"{tag} history {name}")
+            assert_bits_equal(np_of(blk.bank.scale[i]), metas[name].scale, f"{tag} scale {name}")
+        # chained quantities
+        assert _bf16_ulps(np_of(blk.h), ref["h"]).max() <= 1, tag + " H"
+        assert _bf16_ulps(np_of(blk.z), ref["z"]).max() <= 1, tag + " Z"
+        code_diff(np_of(blk.saved2.xq), ref["fw2"]["xq"], E4, tag + " Hq")
+        code_diff(np_of(blk.dzq), ref["bw1"]["gq"], E5, tag + " dZq")
+        for name in ("y", "dh", "dx"):
+            normwise(oracle.bf16_to_f64(np_of(getattr(blk, name))), oracle.bf16_to_f64(ref[name]), f"{tag} {name}")
+        normwise(np_of(blk.dw1).astype(np.float64), ref["dw1"], tag + " dW1")
+        normwise(np_of(blk.dw2).astype(np.float64), ref["dw2"], tag + " dW2")
+        for name in ("h", "dz"):
+            i = idx[name]
+            got, want = np_of(blk.bank.scale[i]).astype(np.float64), np.float64(metas[name].scale)
+            assert abs(got - want) <= 2.0 ** -7 * want, f"{tag} scale {name}: {got} vs {want}"
