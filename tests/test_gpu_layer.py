@@ -332,3 +332,56 @@ def test_layer_spike_just_in_time_versus_delayed(oracle):
           f"just-in-time saturated {res[True][0]}, error {res[True][1]:.3e}", flush=True)
     assert res[False][0] > 0.5 * S.size and res[True][0] <= 2
     assert res[True][1] < 0.1 * res[False][1]
+
+
+def test_layer_end_to_end_from_inputs_alone(oracle):
+    """The oracle runs the layer step (attention stand-in) from the seeded inputs
+    and initial masters alone, 4 steps with the x100 spike at step 2, with no
+    GPU value entering it.  Bit-exact: the codes of X and ctx, the
+    loss-scaled gradients bf16(G*S) and bf16(dqkv*S) and their codes, the
+    weight codes of the first step, and the loss-scale state.  The rest may
+    differ where a one-ulp difference upstream crosses an FP8 rounding
+    boundary: every activation and gradient agrees to 1e-2 normwise (the FP8
+    step is 2^-4 relative for E4M3), each step's change of the fp32 masters
+    too, and every scale to one bf16 ulp of its amax."""
+    inp = _small_inputs()
+    lay = _layer(inp, 16)
+    metas, ls = oracle.layer_metas(16), oracle.LossScale(2.0 ** 16, interval=5)
+    masters = {n: np_of(lay.w[n]).copy() for n in LAYER_WEIGHTS}
+    ctx, g, dqkv = np_of(inp["ctx"]), np_of(inp["g"]), np_of(inp["dqkv"])
+    spiked = synth.layer_spike(inp["x"])
+
+    def normwise(got64, want64, tag):
+        den = np.linalg.norm(want64)
+        err = np.linalg.norm(got64 - want64) / den if den > 0 else np.linalg.norm(got64)
+        assert err <= 1e-2, f"{tag}: normwise error {err:.2e}"
+
+    for step in range(4):
+        tag = f"step {step}"
+        x_in = spiked if step == 2 else inp["x"]
+        before = {n: np_of(lay.w[n]).astype(np.float64) for n in LAYER_WEIGHTS}
+        ref_before = {n: masters[n].astype(np.float64) for n in LAYER_WEIGHTS}
+        lay.forward(x_in)
+        lay.backward()
+        torch.cuda.synchronize()
+        ref = oracle.layer_step(np_of(x_in), ctx, g, dqkv, masters, metas, ls, LR)
+        assert_bits_equal(np_of(lay.saved["qkv"].xq), ref["fwd"]["qkv"]["xq"], tag + " Xq")
+        assert_bits_equal(np_of(lay.saved["o"].xq), ref["fwd"]["o"]["xq"], tag + " ctx codes")
+        assert_bits_equal(np_of(lay.dy), ref["dy"], tag + " dY = G*S")
+        assert_bits_equal(np_of(lay.dqkv), ref["dqkv"], tag + " dqkv*S")
+        assert_bits_equal(np_of(lay.gws["fc2"][0]), ref["bwd"]["fc2"]["gq"], tag + " dY codes")
+        assert_bits_equal(np_of(lay.gws["qkv"][0]), ref["bwd"]["qkv"]["gq"], tag + " dqkv codes")
+        if step == 0:
+            for name in ("qkv", "o", "fc1", "fc2"):
+                assert_bits_equal(np_of(lay.saved[name].wq), ref["fwd"][name]["wq"], f"{tag} {name} weight codes")
+        for name in ("qkv", "y1", "h", "z", "y", "dh", "dz", "dy1", "dctx", "dx"):
+            normwise(oracle.bf16_to_f64(np_of(getattr(lay, name))), oracle.bf16_to_f64(ref[name]), f"{tag} {name}")
+        lay.update()
+        torch.cuda.synchronize()
+        assert_bits_equal(np_of(lay.ls_state), ls.state, tag + " loss-scale state")
+        for n in LAYER_WEIGHTS:
+            normwise(np_of(lay.w[n]).astype(np.float64) - before[n], masters[n].astype(np.float64) - ref_before[n],
+                     f"{tag} SGD change of {n}")
+        for i, name in enumerate(LAYER_TENSORS):
+            got, want = np.float64(np_of(lay.bank.scale[i])), np.float64(metas[name].scale)
+            assert abs(got - want) <= 2.0 ** -7 * want, f"{tag} scale {name}: {got} vs {want}"
