@@ -493,12 +493,17 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
     if (jit && (e = jit_scale(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw, recipe->margin, s)) != hipSuccess)
         return hip_status(e, "fp8_linear_fwd: just-in-time scale of W");
     float* wslot = jit ? nullptr : mw->amax_history;
+    // the W cast also snapshots the two inverse scales into saved->sinv (an
+    // empty W launches no cast, so a one-thread copy does it)
+    const SinvSnap snap{mx->scale_inv, mw->scale_inv, saved->sinv};
     if (saved->wq_t) e = launch_cast_transpose(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw->scale, saved->wq,
-                                               saved->wq_t, wslot, nullptr, nullptr, nullptr, s);
-    else e = launch_cast(w, w_dtype, n * k, FP8LIN_E4M3, mw->scale, saved->wq, wslot, s);
+                                               saved->wq_t, wslot, nullptr, nullptr, nullptr, s, snap);
+    else e = launch_cast(w, w_dtype, n * k, FP8LIN_E4M3, mw->scale, saved->wq, wslot, s, snap);
     if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast W");
-    e = launch_copy_scalars(mx->scale_inv, mw->scale_inv, saved->sinv, s);
-    if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: save scale_inv");
+    if (n * k == 0) {
+        e = launch_copy_scalars(mx->scale_inv, mw->scale_inv, saved->sinv, s);
+        if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: save scale_inv");
+    }
     e = launch_gemm(saved->xq, FP8LIN_E4M3, saved->wq, FP8LIN_E4M3, m, n, k, saved->sinv, saved->sinv + 1, bias,
                     bias_dtype, epilogue | fast, y, y_dtype, y_aux, residual, y_amax_slot, y_q ? y_q->scale : nullptr,
                     y_q ? y_q->q : nullptr, y_q ? y_q->q_t : nullptr, y_q ? y_q->fp8_dtype : 0, s);

@@ -110,12 +110,13 @@ __global__ void __launch_bounds__(kThreads)
 k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t rows, int64_t cols,
                  int64_t tiles_c, const float* __restrict__ scale_p, uint8_t* __restrict__ q,
                  uint8_t* __restrict__ qt, float* amax_slot, float* __restrict__ dbias_ws,
-                 void* __restrict__ dz_out, Second sec) {
+                 void* __restrict__ dz_out, Second sec, SinvSnap snap) {
     using C = CtVec<DT>;
     constexpr int E = C::E, NP = C::NP;
     constexpr int NF = DUAL ? 2 : 1;
     __shared__ __attribute__((aligned(16))) uint8_t tile[NF * kTile * kTile];
     __shared__ uint32_t red[kThreads / 64];
+    take_snapshot(snap);
 
     const int t = threadIdx.x;
     const int vc = t % C::V;          // vector column in the tile
@@ -261,7 +262,8 @@ k_dbias_reduce(const float* __restrict__ ws, int64_t tiles_r, int64_t cols, floa
 
 template <int DT, int FMT>
 hipError_t launch_dt_fmt(const void* x, const void* z, int64_t rows, int64_t cols, const float* scale,
-                         uint8_t* q, uint8_t* qt, float* slot, float* dbias_ws, void* dz_out, hipStream_t s) {
+                         uint8_t* q, uint8_t* qt, float* slot, float* dbias_ws, void* dz_out, hipStream_t s,
+                         SinvSnap snap) {
     const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
     const int64_t ntiles = tiles_r * tiles_c;
     const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
@@ -269,16 +271,16 @@ hipError_t launch_dt_fmt(const void* x, const void* z, int64_t rows, int64_t col
     const Second none{nullptr, nullptr, nullptr, nullptr};
     if (!dgelu && !dbias)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap);
     else if (!dgelu)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, true, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap);
     else if (!dbias)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, false, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap);
     else
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, true, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap);
     return hipGetLastError();
 }
 
@@ -289,7 +291,7 @@ hipError_t launch_dual_dt(const void* x, int64_t rows, int64_t cols, const float
     const int64_t ntiles = tiles_r * tiles_c;
     const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
     hipLaunchKernelGGL((k_cast_transpose<DT, kE4M3, false, false, true>), grid, block, 0, s, x, nullptr, rows,
-                       cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec);
+                       cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec, SinvSnap{});
     return hipGetLastError();
 }
 
@@ -302,7 +304,7 @@ int64_t cast_transpose_dbias_ws_bytes(int64_t rows, int64_t cols) {
 
 hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_t rows, int64_t cols, int fmt,
                                  const float* scale, uint8_t* q, uint8_t* qt, float* slot, float* dbias,
-                                 float* dbias_ws, void* dz_out, hipStream_t s) {
+                                 float* dbias_ws, void* dz_out, hipStream_t s, SinvSnap snap) {
     if (rows == 0 || cols == 0) {
         if (dbias && cols > 0) return launch_zero_f32(dbias, cols, s);
         return hipSuccess;
@@ -310,10 +312,14 @@ hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_
     float* ws = dbias ? dbias_ws : nullptr;
     hipError_t e;
     timing_before(kKindCastT, s);
-    if (dtype == kF32 && fmt == kE4M3) e = launch_dt_fmt<kF32, kE4M3>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s);
-    else if (dtype == kF32) e = launch_dt_fmt<kF32, kE5M2>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s);
-    else if (fmt == kE4M3) e = launch_dt_fmt<kBF16, kE4M3>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s);
-    else e = launch_dt_fmt<kBF16, kE5M2>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s);
+    if (dtype == kF32 && fmt == kE4M3)
+        e = launch_dt_fmt<kF32, kE4M3>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap);
+    else if (dtype == kF32)
+        e = launch_dt_fmt<kF32, kE5M2>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap);
+    else if (fmt == kE4M3)
+        e = launch_dt_fmt<kBF16, kE4M3>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap);
+    else
+        e = launch_dt_fmt<kBF16, kE5M2>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap);
     timing_after(s);
     if (e != hipSuccess || !dbias) return e;
     const int64_t tiles_r = (rows + kTile - 1) / kTile;

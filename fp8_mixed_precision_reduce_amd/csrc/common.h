@@ -20,12 +20,29 @@ enum Kind : int32_t { kKindAmax = 0, kKindCast = 1, kKindCastT = 2, kKindDequant
 void timing_before(int kind, hipStream_t stream);
 void timing_after(hipStream_t stream);
 
+// A cast kernel can also take the forward's snapshot of the two inverse scales
+// (the backward uses the values the forward multiplied with): workgroup 0,
+// thread 0 copies *a and *b to dst[0], dst[1].  dst == nullptr: no snapshot.
+struct SinvSnap {
+    const float* a;
+    const float* b;
+    float* dst;
+};
+#ifdef __HIPCC__
+__device__ __forceinline__ void take_snapshot(const SinvSnap& snap) {
+    if (snap.dst && blockIdx.x == 0 && threadIdx.x == 0) {
+        snap.dst[0] = *snap.a;
+        snap.dst[1] = *snap.b;
+    }
+}
+#endif
+
 // ------------------------------------------------------------------ launchers
 // Each returns the hipError_t of its launch.  Arguments are validated by the
 // C entry points before these are called.
 hipError_t launch_amax(const void* x, int dtype, int64_t n, float* slot, hipStream_t s);
 hipError_t launch_cast(const void* x, int dtype, int64_t n, int fmt, const float* scale,
-                       uint8_t* q, float* slot, hipStream_t s);
+                       uint8_t* q, float* slot, hipStream_t s, SinvSnap snap = {});
 hipError_t launch_dequant(const uint8_t* q, int fmt, int64_t n, const float* sinv, void* out,
                           int out_dtype, hipStream_t s);
 hipError_t launch_scale_update(float* hist, float* scale, float* sinv, const uint8_t* fmts,
@@ -36,7 +53,7 @@ hipError_t launch_copy_scalars(const float* a, const float* b, float* dst2, hipS
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_t rows, int64_t cols,
                                  int fmt, const float* scale, uint8_t* q, uint8_t* qt, float* slot,
-                                 float* dbias, float* dbias_ws, void* dz_out, hipStream_t s);
+                                 float* dbias, float* dbias_ws, void* dz_out, hipStream_t s, SinvSnap snap = {});
 hipError_t launch_cast_transpose_dual(const void* x, int dtype, int64_t rows, int64_t cols, const float* scale_e4m3,
                                       uint8_t* q_e4m3, uint8_t* q_e4m3_t, float* slot_e4m3, const float* scale_e5m2,
                                       uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* slot_e5m2, hipStream_t s);

@@ -111,8 +111,9 @@ __device__ __forceinline__ void cast_vec(uint4 w, float s, uint8_t* q, int64_t i
 template <int DT, int FMT>
 __global__ void __launch_bounds__(kThreads)
 k_cast(const void* __restrict__ x, int64_t n, const float* __restrict__ scale_p, uint8_t* __restrict__ q,
-       float* slot) {
+       float* slot, SinvSnap snap) {
     __shared__ uint32_t red[kThreads / 64];
+    take_snapshot(snap);
     constexpr int E = InVec<DT>::elems;
     const float s = *scale_p;
     const uint4* p = static_cast<const uint4*>(x);
@@ -291,18 +292,18 @@ hipError_t launch_amax(const void* x, int dtype, int64_t n, float* slot, hipStre
 }
 
 hipError_t launch_cast(const void* x, int dtype, int64_t n, int fmt, const float* scale, uint8_t* q,
-                       float* slot, hipStream_t s) {
+                       float* slot, hipStream_t s, SinvSnap snap) {
     if (n == 0) return hipSuccess;
     const int g = grid_vec(n / (dtype == kF32 ? 4 : 8));
     timing_before(kKindCast, s);
     if (dtype == kF32 && fmt == kE4M3)
-        hipLaunchKernelGGL((k_cast<kF32, kE4M3>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot);
+        hipLaunchKernelGGL((k_cast<kF32, kE4M3>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap);
     else if (dtype == kF32)
-        hipLaunchKernelGGL((k_cast<kF32, kE5M2>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot);
+        hipLaunchKernelGGL((k_cast<kF32, kE5M2>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap);
     else if (fmt == kE4M3)
-        hipLaunchKernelGGL((k_cast<kBF16, kE4M3>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot);
+        hipLaunchKernelGGL((k_cast<kBF16, kE4M3>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap);
     else
-        hipLaunchKernelGGL((k_cast<kBF16, kE5M2>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot);
+        hipLaunchKernelGGL((k_cast<kBF16, kE5M2>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap);
     timing_after(s);
     return hipGetLastError();
 }
