@@ -224,17 +224,23 @@ def linear768_leg(F, torch, iters=200):
         F.fp8_linear_bwd(dy, k, recipe, bank.meta(2), saved, gq, gqt, dx, dw)
         bank.update(recipe)
 
-    def timed(fn):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record()
-        for _ in range(iters):
-            fn()
-        ev[1].record()
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) * 1e3 / iters
+    def timed(fn, batches=5):
+        # median over batches of iters / batches steps: a one-off stall (a clock
+        # change, the first replay's upload) does not move the figure
+        per = []
+        for _ in range(batches):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            for _ in range(iters // batches):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            per.append(ev[0].elapsed_time(ev[1]) * 1e3 / (iters // batches))
+        return sorted(per)[batches // 2]
 
     out = {"workload": "linear 1024x768x768 fp32 in/out, E4M3 (forward) / HYBRID (forward+backward), "
-                       "history 16, launch-latency bound", "iterations": iters}
+                       "history 16, launch-latency bound", "iterations": iters,
+           "statistic": "median over 5 batches of iterations / 5 steps"}
     for name, fn in (("forward", fwd), ("forward_backward", fwd_bwd)):
         for _ in range(5):
             fn()
@@ -249,6 +255,9 @@ def linear768_leg(F, torch, iters=200):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
         graph = timed(g.replay)
         out[name] = {"us_per_step_eager": round(eager, 2), "us_per_step_graph": round(graph, 2)}
         del g

@@ -481,6 +481,25 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
     hipStream_t s = as_stream(stream);
     hipError_t e;
     const bool jit = recipe->just_in_time != 0;
+    // the W cast also snapshots the two inverse scales into saved->sinv (an
+    // empty W launches no cast, so a one-thread copy does it)
+    const SinvSnap snap{mx->scale_inv, mw->scale_inv, saved->sinv};
+    if (!x_quantised && saved->xq_t && saved->wq_t && x_dtype == w_dtype && m * k > 0 && n * k > 0) {
+        // X and W in one launch (same kernel variant, independent tensors)
+        if (jit && (e = jit_scale(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx, recipe->margin, s)) != hipSuccess)
+            return hip_status(e, "fp8_linear_fwd: just-in-time scale of X");
+        if (jit && (e = jit_scale(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw, recipe->margin, s)) != hipSuccess)
+            return hip_status(e, "fp8_linear_fwd: just-in-time scale of W");
+        e = launch_cast_transpose_pair(x, w, x_dtype, m, k, n, k, FP8LIN_E4M3, mx->scale, saved->xq, saved->xq_t,
+                                       jit ? nullptr : mx->amax_history, mw->scale, saved->wq, saved->wq_t,
+                                       jit ? nullptr : mw->amax_history, s, snap);
+        if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast X and W");
+        return hip_status(launch_gemm(saved->xq, FP8LIN_E4M3, saved->wq, FP8LIN_E4M3, m, n, k, saved->sinv,
+                                      saved->sinv + 1, bias, bias_dtype, epilogue | fast, y, y_dtype, y_aux, residual,
+                                      y_amax_slot, y_q ? y_q->scale : nullptr, y_q ? y_q->q : nullptr,
+                                      y_q ? y_q->q_t : nullptr, y_q ? y_q->fp8_dtype : 0, s),
+                          "fp8_linear_fwd: gemm");
+    }
     if (!x_quantised) {
         if (jit && (e = jit_scale(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx, recipe->margin, s)) != hipSuccess)
             return hip_status(e, "fp8_linear_fwd: just-in-time scale of X");
@@ -493,9 +512,6 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
     if (jit && (e = jit_scale(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw, recipe->margin, s)) != hipSuccess)
         return hip_status(e, "fp8_linear_fwd: just-in-time scale of W");
     float* wslot = jit ? nullptr : mw->amax_history;
-    // the W cast also snapshots the two inverse scales into saved->sinv (an
-    // empty W launches no cast, so a one-thread copy does it)
-    const SinvSnap snap{mx->scale_inv, mw->scale_inv, saved->sinv};
     if (saved->wq_t) e = launch_cast_transpose(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw->scale, saved->wq,
                                                saved->wq_t, wslot, nullptr, nullptr, nullptr, s, snap);
     else e = launch_cast(w, w_dtype, n * k, FP8LIN_E4M3, mw->scale, saved->wq, wslot, s, snap);

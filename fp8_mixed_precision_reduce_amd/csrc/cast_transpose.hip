@@ -105,12 +105,25 @@ struct Second {
     float* amax_slot;
 };
 
-template <int DT, int FMT, bool DGELU, bool DBIAS, bool DUAL>
+// A second tensor of the same element type and format, cast by the same
+// launch (the pair variant): the workgroups' tile indices past the first
+// tensor's tiles address this one.
+struct CtJob {
+    const void* x;
+    int64_t rows, cols, tiles_c;
+    const float* scale;
+    uint8_t* q;
+    uint8_t* qt;
+    float* amax_slot;
+};
+
+template <int DT, int FMT, bool DGELU, bool DBIAS, bool DUAL, bool PAIR = false>
 __global__ void __launch_bounds__(kThreads)
-k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t rows, int64_t cols,
-                 int64_t tiles_c, const float* __restrict__ scale_p, uint8_t* __restrict__ q,
-                 uint8_t* __restrict__ qt, float* amax_slot, float* __restrict__ dbias_ws,
-                 void* __restrict__ dz_out, Second sec, SinvSnap snap) {
+k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64_t rows_a, int64_t cols_a,
+                 int64_t tiles_ca, const float* __restrict__ scale_p, uint8_t* __restrict__ q_a,
+                 uint8_t* __restrict__ qt_a, float* amax_slot, float* __restrict__ dbias_ws,
+                 void* __restrict__ dz_out, Second sec, SinvSnap snap, CtJob job_b) {
+    static_assert(!PAIR || (!DGELU && !DBIAS && !DUAL), "the pair variant is a plain cast-transpose");
     using C = CtVec<DT>;
     constexpr int E = C::E, NP = C::NP;
     constexpr int NF = DUAL ? 2 : 1;
@@ -122,12 +135,23 @@ k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t
     const int vc = t % C::V;          // vector column in the tile
     const int r_first = t / C::V;     // first tile row; then every C::RS rows
     const int cg = t >> 3, strip = t & 7;   // transpose phase
-    const float s = *scale_p;
+    const float s_a = *scale_p;
+    const float s_b = PAIR ? *job_b.scale : 0.0f;
     const float s2 = DUAL ? *sec.scale : 0.0f;
-    const int64_t ntiles = ((rows + kTile - 1) / kTile) * tiles_c;
-    uint32_t m = 0;
+    const int64_t ntiles_a = ((rows_a + kTile - 1) / kTile) * tiles_ca;
+    const int64_t ntiles = ntiles_a + (PAIR ? ((job_b.rows + kTile - 1) / kTile) * job_b.tiles_c : 0);
+    uint32_t m_a = 0, m_b = 0;
     for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
-        const int64_t tr = tile_id / tiles_c, tc = tile_id % tiles_c;
+        const bool second = PAIR && tile_id >= ntiles_a;        // uniform per workgroup
+        const void* const x = second ? job_b.x : x_a;
+        const int64_t rows = second ? job_b.rows : rows_a, cols = second ? job_b.cols : cols_a;
+        const int64_t tiles_c = second ? job_b.tiles_c : tiles_ca;
+        const float s = second ? s_b : s_a;
+        uint8_t* const q = second ? job_b.q : q_a;
+        uint8_t* const qt = second ? job_b.qt : qt_a;
+        const int64_t local_id = second ? tile_id - ntiles_a : tile_id;
+        uint32_t m = 0;
+        const int64_t tr = local_id / tiles_c, tc = local_id % tiles_c;
         const int64_t r0 = tr * kTile, c0 = tc * kTile;
         const int64_t col = c0 + vc * E;
         const bool col_ok = col < cols;
@@ -240,12 +264,20 @@ k_cast_transpose(const void* __restrict__ x, const void* __restrict__ z, int64_t
             }
         }
         __syncthreads();             // the LDS tile is rewritten by the next tile
+        if (second) m_b = max(m_b, m);
+        else m_a = max(m_a, m);
     }
-    if (amax_slot) block_amax_merge(m, amax_slot, red);
+    if (amax_slot) block_amax_merge(m_a, amax_slot, red);
     if constexpr (DUAL) {
         if (sec.amax_slot) {
             __syncthreads();     // red[] is reused
-            block_amax_merge(m, sec.amax_slot, red);
+            block_amax_merge(m_a, sec.amax_slot, red);
+        }
+    }
+    if constexpr (PAIR) {
+        if (job_b.amax_slot) {
+            __syncthreads();
+            block_amax_merge(m_b, job_b.amax_slot, red);
         }
     }
 }
@@ -271,16 +303,16 @@ hipError_t launch_dt_fmt(const void* x, const void* z, int64_t rows, int64_t col
     const Second none{nullptr, nullptr, nullptr, nullptr};
     if (!dgelu && !dbias)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{});
     else if (!dgelu)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, true, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{});
     else if (!dbias)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, false, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{});
     else
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, true, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{});
     return hipGetLastError();
 }
 
@@ -291,7 +323,19 @@ hipError_t launch_dual_dt(const void* x, int64_t rows, int64_t cols, const float
     const int64_t ntiles = tiles_r * tiles_c;
     const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
     hipLaunchKernelGGL((k_cast_transpose<DT, kE4M3, false, false, true>), grid, block, 0, s, x, nullptr, rows,
-                       cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec, SinvSnap{});
+                       cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec, SinvSnap{}, CtJob{});
+    return hipGetLastError();
+}
+
+template <int DT, int FMT>
+hipError_t launch_pair_dt_fmt(const void* xa, int64_t rows, int64_t cols, const float* scale, uint8_t* q, uint8_t* qt,
+                              float* slot, const CtJob& b, hipStream_t s, SinvSnap snap) {
+    const int64_t tiles_c = (cols + kTile - 1) / kTile;
+    const int64_t ntiles = ((rows + kTile - 1) / kTile) * tiles_c + ((b.rows + kTile - 1) / kTile) * b.tiles_c;
+    const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
+    const Second none{nullptr, nullptr, nullptr, nullptr};
+    hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false, true>), grid, block, 0, s, xa, nullptr, rows,
+                       cols, tiles_c, scale, q, qt, slot, nullptr, nullptr, none, snap, b);
     return hipGetLastError();
 }
 
@@ -339,6 +383,25 @@ hipError_t launch_cast_transpose_dual(const void* x, int dtype, int64_t rows, in
     const hipError_t e = dtype == kF32
         ? launch_dual_dt<kF32>(x, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, slot_e4m3, sec, s)
         : launch_dual_dt<kBF16>(x, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, slot_e4m3, sec, s);
+    timing_after(s);
+    return e;
+}
+
+hipError_t launch_cast_transpose_pair(const void* xa, const void* xb, int dtype, int64_t rows_a, int64_t cols_a,
+                                      int64_t rows_b, int64_t cols_b, int fmt, const float* scale_a, uint8_t* q_a,
+                                      uint8_t* qt_a, float* slot_a, const float* scale_b, uint8_t* q_b, uint8_t* qt_b,
+                                      float* slot_b, hipStream_t s, SinvSnap snap) {
+    const CtJob b{xb, rows_b, cols_b, (cols_b + kTile - 1) / kTile, scale_b, q_b, qt_b, slot_b};
+    hipError_t e;
+    timing_before(kKindCastT, s);
+    if (dtype == kF32 && fmt == kE4M3)
+        e = launch_pair_dt_fmt<kF32, kE4M3>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap);
+    else if (dtype == kF32)
+        e = launch_pair_dt_fmt<kF32, kE5M2>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap);
+    else if (fmt == kE4M3)
+        e = launch_pair_dt_fmt<kBF16, kE4M3>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap);
+    else
+        e = launch_pair_dt_fmt<kBF16, kE5M2>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap);
     timing_after(s);
     return e;
 }

@@ -54,6 +54,11 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_t rows, int64_t cols,
                                  int fmt, const float* scale, uint8_t* q, uint8_t* qt, float* slot,
                                  float* dbias, float* dbias_ws, void* dz_out, hipStream_t s, SinvSnap snap = {});
+// Two non-empty tensors of one element type cast to one format in one launch.
+hipError_t launch_cast_transpose_pair(const void* xa, const void* xb, int dtype, int64_t rows_a, int64_t cols_a,
+                                      int64_t rows_b, int64_t cols_b, int fmt, const float* scale_a, uint8_t* q_a,
+                                      uint8_t* qt_a, float* slot_a, const float* scale_b, uint8_t* q_b, uint8_t* qt_b,
+                                      float* slot_b, hipStream_t s, SinvSnap snap);
 hipError_t launch_cast_transpose_dual(const void* x, int dtype, int64_t rows, int64_t cols, const float* scale_e4m3,
                                       uint8_t* q_e4m3, uint8_t* q_e4m3_t, float* slot_e4m3, const float* scale_e5m2,
                                       uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* slot_e5m2, hipStream_t s);
