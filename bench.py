@@ -102,15 +102,21 @@ def gemm_traffic():
     return float(kv["traffic_bytes_per_launch"])
 
 
-def time_steps(block, torch, steps):
+def time_steps(block, torch, steps, median=False):
+    """Mean ms per step over `steps` steps (events at every step boundary);
+    with median=True also the median step."""
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         block.step()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    mean = ev[0].elapsed_time(ev[steps]) / steps
+    if not median:
+        return mean
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return mean, per[steps // 2]
 
 
 def kernel_breakdown(block, F, torch, steps):
@@ -382,7 +388,7 @@ def main():
     block = MlpBlock(F, torch, fast_accum=args.fast_accum)
     for _ in range(args.warmup):
         block.step()
-    ms = time_steps(block, torch, args.steps)
+    ms, ms_median = time_steps(block, torch, args.steps, median=True)
     kb = kernel_breakdown(block, F, torch, args.steps)
     progress("MLP block step")
     n_g, t_g = kb.get("gemm", (1, float("nan")))
@@ -425,6 +431,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(ms_median, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
