@@ -251,13 +251,30 @@ def fp8_amax(x, amax_slot, stream=None):
     _check(_lib.fp8_amax(_p(x), _dt(x), x.numel(), _p(amax_slot), _stream(stream)))
 
 
+def _check_metas(amax_history, scale, scale_inv, formats, recipe, what):
+    """The C call takes the history length from the recipe and the tensor count
+    from the formats: the buffers must hold exactly that many floats (the
+    kernel would otherwise read and roll past the end of the history)."""
+    n, L = len(formats), recipe.history_len
+    if tuple(amax_history.shape) not in ((n, L),) + (((L,),) if n == 1 else ()) or not amax_history.is_contiguous():
+        raise ValueError(f"{what}: amax_history has shape {tuple(amax_history.shape)}, expected a contiguous "
+                         f"({n}, {L}) for {n} tensors and recipe.history_len {L}")
+    for name, t in (("scale", scale), ("scale_inv", scale_inv)):
+        if t.numel() != n or t.dtype != torch.float32:
+            raise ValueError(f"{what}: {name} must hold {n} float32 values")
+    if amax_history.dtype != torch.float32:
+        raise ValueError(f"{what}: amax_history must be float32")
+
+
 def fp8_amax_scale_update(amax_history, scale, scale_inv, formats, recipe, stream=None):
+    _check_metas(amax_history, scale, scale_inv, formats, recipe, "fp8_amax_scale_update")
     fm = (ctypes.c_uint8 * len(formats)).from_buffer_copy(bytes(formats))
     _check(_lib.fp8_amax_scale_update(_p(amax_history), _p(scale), _p(scale_inv), ctypes.cast(fm, ctypes.c_void_p),
                                       len(formats), ctypes.byref(recipe), _stream(stream)))
 
 
 def fp8_scale_from_current_amax(amax_history, scale, scale_inv, formats, recipe, stream=None):
+    _check_metas(amax_history, scale, scale_inv, formats, recipe, "fp8_scale_from_current_amax")
     fm = (ctypes.c_uint8 * len(formats)).from_buffer_copy(bytes(formats))
     _check(_lib.fp8_scale_from_current_amax(_p(amax_history), _p(scale), _p(scale_inv),
                                             ctypes.cast(fm, ctypes.c_void_p), len(formats), ctypes.byref(recipe),

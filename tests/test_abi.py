@@ -256,3 +256,20 @@ def test_attention_validation():
     assert bwd(big[0], big[1], big[2], big[3], 1, 256, 2, 128, big[4], big[3], None) == F.ERR_ARG   # ws on dctx
     assert bwd(big[0], big[1], None, big[3], 1, 256, 2, 128, big[4], big[5], None) == F.ERR_NULL
     assert bwd(big[0], big[1], big[2], big[3], 1, 512, 2, 96, big[4], big[5], None) == F.ERR_UNSUPPORTED
+
+
+def test_binding_checks_meta_buffers_against_the_recipe():
+    """The binding refuses a history buffer whose shape differs from (tensors,
+    recipe.history_len) before calling the library (the kernel would read and
+    roll past its end); host tensors suffice since nothing is launched."""
+    import torch
+    recipe = F.Recipe(F.FORMAT_HYBRID, 16, F.AMAX_MAX, 0)
+    fmts = [F.E4M3, F.E5M2]
+    h, s, si = torch.zeros(2, 8), torch.ones(2), torch.ones(2)
+    for fn in (F.fp8_amax_scale_update, F.fp8_scale_from_current_amax):
+        with pytest.raises(ValueError, match="history_len 16"):
+            fn(h, s, si, fmts, recipe)
+        with pytest.raises(ValueError, match="history_len 16"):
+            fn(torch.zeros(3, 16), torch.ones(3), torch.ones(3), fmts, recipe)
+        with pytest.raises(ValueError, match="scale must hold 2"):
+            fn(torch.zeros(2, 16), torch.ones(1), torch.ones(2), fmts, recipe)

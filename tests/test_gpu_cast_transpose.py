@@ -71,8 +71,18 @@ def test_cast_transpose_dgelu(oracle, dtype, shape):
     rng = np.random.default_rng(rows + cols)
     dh = rng.standard_normal((rows, cols)).astype(np.float32)
     z = (rng.standard_normal((rows, cols)) * 3).astype(np.float32)
+    # planted z: both edges of the bf16 gelu' table (2^-8 <= |z| < 16: 2^-8,
+    # the bf16 value just below it, 16 and the value just below it), values
+    # well outside it, +-0, +-Inf and NaN, each with both signs where it has one
+    edge = [2.0 ** -8, 2.0 ** -8 - 2.0 ** -16, 16.0, 16.0 - 2.0 ** -4, 40.0, 2.0 ** -20, 0.0, np.inf]
+    planted = np.array([s * v for v in edge for s in (1.0, -1.0)] + [np.nan], dtype=np.float32)
+    flat = rng.choice(rows * cols, planted.size, replace=False)
+    z.reshape(-1)[flat] = planted
     if dtype == "bf16":
         dh, z = oracle.bf16_from_f32(dh), oracle.bf16_from_f32(z)
+        zbits = z.reshape(-1)[flat]
+        assert np.array_equal(oracle.bf16_to_f64(zbits)[np.isfinite(planted)],
+                              planted[np.isfinite(planted)].astype(np.float64)), "planted z not bf16 values"
     q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
     qt = torch.empty(cols, rows, dtype=torch.uint8, device="cuda")
     slot = torch.zeros(1, dtype=torch.float32, device="cuda")
@@ -89,6 +99,14 @@ def test_cast_transpose_dgelu(oracle, dtype, shape):
     # exp(-z^2/2) perturbs those functions by about z^2 * 2^-24 relatively.
     dh64 = oracle.bf16_to_f64(dh) if dtype == "bf16" else dh.astype(np.float64)
     z64 = oracle.bf16_to_f64(z) if dtype == "bf16" else z.astype(np.float64)
+    # +-Inf and NaN z give a NaN gelu' on both sides (Inf * phi(Inf) = Inf * 0):
+    # NaN where the oracle has NaN, the bound below on the rest
+    g_all = oracle.bf16_to_f64(got_dz) if dtype == "bf16" else got_dz.astype(np.float64)
+    w_all = oracle.bf16_to_f64(want_dz) if dtype == "bf16" else want_dz.astype(np.float64)
+    nonfin = ~np.isfinite(w_all)
+    assert nonfin.sum() == (~np.isfinite(planted)).sum(), "expected NaN dz exactly at the planted Inf/NaN z"
+    assert np.array_equal(np.isnan(g_all), np.isnan(w_all)), "NaN dz at other places than the oracle's"
+    z64 = np.where(nonfin, 0.0, z64)
     scale = np.abs(dh64) * (0.5 * np.abs(1 + np.vectorize(math.erf)(z64 / math.sqrt(2)))
                             + np.abs(z64) * np.exp(-0.5 * z64 ** 2) / math.sqrt(2 * math.pi))
     if dtype == "bf16":
@@ -96,10 +114,10 @@ def test_cast_transpose_dgelu(oracle, dtype, shape):
         a, b = got_dz.astype(np.int64), want_dz.astype(np.int64)
         ulps = np.abs(np.where(a & 0x8000, -(a & 0x7FFF), a & 0x7FFF) - np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF))
         bound = 2.0 ** -21 * (4 + z64 ** 2) * scale + np.spacing(np.abs(w64).astype(np.float32))
-        ok = (ulps <= 1) | (np.abs(g64 - w64) <= bound)
+        ok = (ulps <= 1) | (np.abs(g64 - w64) <= bound) | nonfin
     else:
         bound = 2.0 ** -21 * (4 + z64 ** 2) * scale + 2 * np.spacing(np.abs(want_dz)) + 1e-44 * np.abs(dh64)
-        ok = np.abs(got_dz - want_dz.astype(np.float64)) <= bound
+        ok = (np.abs(got_dz - want_dz.astype(np.float64)) <= bound) | nonfin
     bad = np.argwhere(~ok)[:5]
     assert ok.all(), [(tuple(i), float(np.asarray(got_dz)[tuple(i)]), float(np.asarray(want_dz)[tuple(i)]),
                        float(dh64[tuple(i)]), float(z64[tuple(i)])) for i in bad]
@@ -108,7 +126,7 @@ def test_cast_transpose_dgelu(oracle, dtype, shape):
     assert_bits_equal(np_of(qt), qt_want, "q_t of dz")
     assert_bits_equal(np_of(slot)[0], oracle.amax(got_dz), "amax of dz")
     ref = oracle.colsum(got_dz)
-    assert np.allclose(np_of(db), ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+    assert np.allclose(np_of(db), ref, rtol=1e-5, atol=1e-5 * np.nanmax(np.abs(ref)), equal_nan=True)
 
 
 def test_cast_transpose_deterministic():

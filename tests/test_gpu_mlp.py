@@ -15,7 +15,8 @@ import torch
 
 import synth
 from fp8_mixed_precision_reduce_amd.blocks import MLP_TENSORS, Fp8MlpBlock
-from helpers import assert_bits_equal, assert_gemm_bf16, assert_gemm_f32, np_of
+from helpers import (GELU_LIPSCHITZ, assert_bits_equal, assert_fast_bf16, assert_fast_f32, assert_gemm_bf16,
+                     assert_gemm_f32, fast_accum_bound, np_of)
 
 pytestmark = pytest.mark.gpu
 E4, E5 = 0, 1
@@ -26,9 +27,41 @@ def _bf16_ulps(a, b):
     return np.abs(np.where(a & 0x8000, -(a & 0x7FFF), a & 0x7FFF) - np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF))
 
 
-def _check_step(oracle, blk, om, rows, wrows, tag):
+class _GemmCheck:
+    """The GEMM comparisons of one step: the fp32-accumulation tolerances of
+    tests/helpers.py for the exact inner product, the group-truncation bound
+    for the fast one (recipe.fast_accum)."""
+
+    def __init__(self, oracle, fast):
+        self.o, self.fast = oracle, fast
+
+    def __call__(self, got, a, af, b, bf, sa, sb, rows, tag, gelu=False, aux=None, f32=False):
+        o = self.o
+        res = o.gemm(a, af, b, bf, sa, sb, gelu=gelu, rows=rows, want_pre=gelu)
+        y, pre = res if gelu else (res, None)
+        sel = slice(None) if rows is None else rows
+        if not self.fast:
+            if f32:
+                assert_gemm_f32(got[sel], y, tag)
+            else:
+                assert_gemm_bf16(got[sel], y, o, tag)
+                if aux is not None:
+                    assert_gemm_bf16(aux[sel], pre, o, tag + " (pre-GeLU)")
+            return
+        a_rows = a if rows is None else a[rows]
+        bound = fast_accum_bound(o.decode_table(af)[a_rows], o.decode_table(bf)[b], sa, sb)
+        if f32:
+            assert_fast_f32(got[sel], y, bound, tag)
+        else:
+            assert_fast_bf16(got[sel], y, bound, tag, lipschitz=GELU_LIPSCHITZ if gelu else 1.0)
+            if aux is not None:
+                assert_fast_bf16(aux[sel], pre, bound, tag + " (pre-GeLU)")
+
+
+def _check_step(oracle, blk, om, rows, wrows, tag, fast=False):
     X, W1, W2, dY = (np_of(t) for t in (blk.x, blk.w1, blk.w2, blk.dy))
     s1, s2 = blk.saved1, blk.saved2
+    gemm = _GemmCheck(oracle, fast)
     # forward FC1: casts and the GEMM with its GeLU epilogue
     xq, xqt = oracle.cast_transpose(X, E4, om["x"].scale)
     w1q, w1qt = oracle.cast_transpose(W1, E4, om["w1"].scale)
@@ -37,12 +70,8 @@ def _check_step(oracle, blk, om, rows, wrows, tag):
     assert_bits_equal(np_of(s1.wq), w1q, tag + " W1q")
     assert_bits_equal(np_of(s1.wq_t), w1qt, tag + " W1q^T")
     assert_bits_equal(np_of(s1.sinv), np.array([om["x"].scale_inv, om["w1"].scale_inv]), tag + " saved sinv 1")
-    h_ref, z_ref = oracle.gemm(xq, E4, w1q, E4, om["x"].scale_inv, om["w1"].scale_inv, gelu=True, rows=rows,
-                               want_pre=True)
     H, Z = np_of(blk.h), np_of(blk.z)
-    sel = slice(None) if rows is None else rows
-    assert_gemm_bf16(H[sel], h_ref, oracle, tag + " H")
-    assert_gemm_bf16(Z[sel], z_ref, oracle, tag + " Z")
+    gemm(H, xq, E4, w1q, E4, om["x"].scale_inv, om["w1"].scale_inv, rows, tag + " H", gelu=True, aux=Z)
     # forward FC2 on the GPU's H
     hq, hqt = oracle.cast_transpose(H, E4, om["h"].scale)
     w2q, w2qt = oracle.cast_transpose(W2, E4, om["w2"].scale)
@@ -50,41 +79,36 @@ def _check_step(oracle, blk, om, rows, wrows, tag):
     assert_bits_equal(np_of(s2.xq_t), hqt, tag + " Hq^T")
     assert_bits_equal(np_of(s2.wq), w2q, tag + " W2q")
     assert_bits_equal(np_of(s2.wq_t), w2qt, tag + " W2q^T")
-    y_ref = oracle.gemm(hq, E4, w2q, E4, om["h"].scale_inv, om["w2"].scale_inv, rows=rows)
-    assert_gemm_bf16(np_of(blk.y)[sel], y_ref, oracle, tag + " Y")
+    gemm(np_of(blk.y), hq, E4, w2q, E4, om["h"].scale_inv, om["w2"].scale_inv, rows, tag + " Y")
     # backward FC2
     gq, gqt = oracle.cast_transpose(dY, E5, om["dy"].scale)
     assert_bits_equal(np_of(blk.dyq), gq, tag + " dYq")
     assert_bits_equal(np_of(blk.dyq_t), gqt, tag + " dYq^T")
-    dh_ref = oracle.gemm(gq, E5, w2qt, E4, om["dy"].scale_inv, om["w2"].scale_inv, rows=rows)
     dH = np_of(blk.dh)
-    assert_gemm_bf16(dH[sel], dh_ref, oracle, tag + " dH")
-    dw2_ref = oracle.gemm(gqt, E5, hqt, E4, om["dy"].scale_inv, om["h"].scale_inv, rows=wrows)
-    assert_gemm_f32(np_of(blk.dw2)[slice(None) if wrows is None else wrows], dw2_ref, tag + " dW2")
+    gemm(dH, gq, E5, w2qt, E4, om["dy"].scale_inv, om["w2"].scale_inv, rows, tag + " dH")
+    gemm(np_of(blk.dw2), gqt, E5, hqt, E4, om["dy"].scale_inv, om["h"].scale_inv, wrows, tag + " dW2", f32=True)
     # GeLU backward fused into the dZ cast, on the GPU's dH and Z
     dZ = np_of(blk.dz)
     assert _bf16_ulps(dZ, oracle.gelu_bwd(dH, Z)).max() <= 1, tag + " dZ"
     zq, zqt = oracle.cast_transpose(dZ, E5, om["dz"].scale)
     assert_bits_equal(np_of(blk.dzq), zq, tag + " dZq")
     assert_bits_equal(np_of(blk.dzq_t), zqt, tag + " dZq^T")
-    dx_ref = oracle.gemm(zq, E5, w1qt, E4, om["dz"].scale_inv, om["w1"].scale_inv, rows=rows)
-    assert_gemm_bf16(np_of(blk.dx)[sel], dx_ref, oracle, tag + " dX")
-    dw1_ref = oracle.gemm(zqt, E5, xqt, E4, om["dz"].scale_inv, om["x"].scale_inv, rows=wrows)
-    assert_gemm_f32(np_of(blk.dw1)[slice(None) if wrows is None else wrows], dw1_ref, tag + " dW1")
+    gemm(np_of(blk.dx), zq, E5, w1qt, E4, om["dz"].scale_inv, om["w1"].scale_inv, rows, tag + " dX")
+    gemm(np_of(blk.dw1), zqt, E5, xqt, E4, om["dz"].scale_inv, om["x"].scale_inv, wrows, tag + " dW1", f32=True)
     # amaxes of the step (slot 0, before the update), from the same tensors
     for name, t in (("x", X), ("w1", W1), ("h", H), ("w2", W2), ("dy", dY), ("dz", dZ)):
         om[name].record(t)
     return om
 
 
-def _run_steps(oracle, blk, steps, rows, wrows):
+def _run_steps(oracle, blk, steps, rows, wrows, fast=False):
     om = {name: oracle.Meta(blk.bank.history_len, E5 if name.startswith("d") else E4) for name in MLP_TENSORS}
     for step in range(steps):
         tag = f"step {step}"
         blk.forward()
         blk.backward()
         torch.cuda.synchronize()
-        _check_step(oracle, blk, om, rows, wrows, tag)
+        _check_step(oracle, blk, om, rows, wrows, tag, fast=fast)
         for i, name in enumerate(MLP_TENSORS):
             assert_bits_equal(np_of(blk.bank.amax_history[i, 0]), om[name].hist[0], f"{tag} amax {name}")
         blk.update()
@@ -104,14 +128,27 @@ def test_mlp_block_small_ragged_all_outputs(oracle, fused):
     _run_steps(oracle, blk, steps=4, rows=None, wrows=None)
 
 
-def test_mlp_block_full_size_sampled(oracle):
-    """8192 tokens x hidden 4096 x FFN 14336 (the benchmark's block), 2 steps."""
+def test_mlp_block_small_ragged_fast_accum(oracle):
+    """The block with the fast inner product (recipe.fast_accum): every code,
+    amax, history and scale bit-exact as with the exact one (stepwise), the
+    GEMM outputs within the group-truncation bound."""
+    m, hidden, ffn = 272, 208, 464
+    x, w1, w2, dy = synth.mlp_inputs(0, device="cpu", m=m, hidden=hidden, ffn=ffn)
+    blk = Fp8MlpBlock(x.cuda(), w1.cuda(), w2.cuda(), dy.cuda(), history_len=16, keep_dz=True, keep_h=True,
+                      fast_accum=True)
+    _run_steps(oracle, blk, steps=4, rows=None, wrows=None, fast=True)
+
+
+@pytest.mark.parametrize("fast", [False, True], ids=["exact", "fast_accum"])
+def test_mlp_block_full_size_sampled(oracle, fast):
+    """8192 tokens x hidden 4096 x FFN 14336 (the benchmark's block), 2 steps,
+    with either inner product."""
     x, w1, w2, dy = synth.mlp_inputs(0, device="cuda")
-    blk = Fp8MlpBlock(x, w1, w2, dy, history_len=1024, keep_dz=True, keep_h=True)
+    blk = Fp8MlpBlock(x, w1, w2, dy, history_len=1024, keep_dz=True, keep_h=True, fast_accum=fast)
     rng = np.random.default_rng(7)
-    rows = np.sort(rng.choice(8192, 12, replace=False))
-    wrows = np.sort(rng.choice(4096, 4, replace=False))
-    _run_steps(oracle, blk, steps=2, rows=rows, wrows=wrows)
+    rows = np.sort(rng.choice(8192, 12 if not fast else 6, replace=False))
+    wrows = np.sort(rng.choice(4096, 4 if not fast else 3, replace=False))
+    _run_steps(oracle, blk, steps=2, rows=rows, wrows=wrows, fast=fast)
 
 
 def test_mlp_block_end_to_end_from_inputs_alone(oracle):
