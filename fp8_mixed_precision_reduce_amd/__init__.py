@@ -32,6 +32,7 @@ ABI_VERSION = 5
 FUNCTIONS = [
     "fp8lin_abi_version", "fp8lin_last_error", "fp8lin_status_name", "fp8lin_dbias_workspace_bytes",
     "fp8_amax", "fp8_amax_scale_update", "fp8_scale_from_current_amax", "fp8_cast", "fp8_cast_transpose", "fp8_cast_transpose_dgelu",
+    "fp8_cast_transpose_dbias_noalloc",
     "fp8_cast_transpose_dual",
     "fp8_dequant", "fp8_gemm", "fp8_linear_fwd", "fp8_linear_bwd", "fp8_loss_scale_update",
     "fp8_loss_scale_apply", "fp8_sgd_step", "fp8lin_timing_enable", "fp8lin_timing_read",
@@ -106,6 +107,7 @@ def _load():
         "fp8_cast": (I32, [P, I32, I64, I32, P, P, P, P]),
         "fp8_cast_transpose": (I32, [P, I32, I64, I64, I32, P, P, P, P, P, P, P]),
         "fp8_cast_transpose_dgelu": (I32, [P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, P]),
+        "fp8_cast_transpose_dbias_noalloc": (I32, [P, I32, I64, I64, I32, P, P, P, P, P, P]),
         "fp8_cast_transpose_dual": (I32, [P, I32, I64, I64, P, P, P, P, P, P, P, P, P]),
         "fp8_dequant": (I32, [P, I32, I64, P, P, I32, P]),
         "fp8_gemm": (I32, [P, I32, P, I32, I64, I64, I64, P, P, P, I32, I32, P, I32, P, P, P, P, P]),
@@ -289,6 +291,14 @@ def fp8_cast_transpose(x, fmt, scale, q, q_t, amax_slot=None, dbias=None, dbias_
     rows, cols = x.shape
     _check(_lib.fp8_cast_transpose(_p(x), _dt(x), rows, cols, fmt, _p(scale), _p(q), _p(q_t), _p(amax_slot),
                                    _p(dbias), _p(dbias_ws), _stream(stream)))
+
+
+def fp8_cast_transpose_dbias_noalloc(x, fmt, scale, q, q_t, dbias, amax_slot=None, stream=None):
+    """fp8_cast_transpose with the bias gradient and no workspace: the library
+    allocates nothing (its partial sums use a scratch array inside it)."""
+    rows, cols = x.shape
+    _check(_lib.fp8_cast_transpose_dbias_noalloc(_p(x), _dt(x), rows, cols, fmt, _p(scale), _p(q), _p(q_t),
+                                                 _p(amax_slot), _p(dbias), _stream(stream)))
 
 
 def fp8_cast_transpose_dgelu(dh, z, fmt, scale, q, q_t, amax_slot=None, dbias=None, dbias_ws=None, dz_out=None,

@@ -271,6 +271,33 @@ int32_t fp8_cast_transpose(const void* x, int32_t x_dtype, int64_t rows, int64_t
                       "fp8_cast_transpose");
 }
 
+int32_t fp8_cast_transpose_dbias_noalloc(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                                         int32_t fp8_dtype, const float* scale, uint8_t* q, uint8_t* q_t,
+                                         float* amax_slot, float* dbias, void* stream) {
+    const char* fn = "fp8_cast_transpose_dbias_noalloc";
+    int32_t v = check_ct(fn, x, nullptr, x_dtype, rows, cols, fp8_dtype, scale, q, q_t, amax_slot, nullptr,
+                         nullptr, nullptr);
+    if (v != FP8LIN_OK) return v;
+    const int64_t n = rows * cols;
+    if (!dbias && cols > 0) return fail(FP8LIN_ERR_NULL, "%s: dbias is null", fn);
+    if (!aligned(dbias, 4)) return fail(FP8LIN_ERR_ALIGN, "%s: misaligned dbias", fn);
+    if (overlap(dbias, cols * 4, x, n * elem_size(x_dtype)) || overlap(dbias, cols * 4, q, n) ||
+        overlap(dbias, cols * 4, q_t, n))
+        return fail(FP8LIN_ERR_ARG, "%s: dbias overlaps another buffer", fn);
+    const int64_t need = cast_transpose_dbias_ws_bytes(rows, cols);
+    if (need > kNoAllocScratchBytes)
+        return fail(FP8LIN_ERR_ARG, "%s: rows=%lld cols=%lld need %lld bytes of scratch, more than its %lld", fn,
+                    (long long)rows, (long long)cols, (long long)need, (long long)kNoAllocScratchBytes);
+    float* ws = nullptr;
+    if (n > 0) {
+        const hipError_t e = noalloc_scratch(as_stream(stream), &ws);
+        if (e != hipSuccess) return hip_status(e, fn);
+    }
+    return hip_status(launch_cast_transpose(x, nullptr, x_dtype, rows, cols, fp8_dtype, scale, q, q_t, amax_slot,
+                                            dbias, ws, nullptr, as_stream(stream)),
+                      fn);
+}
+
 int32_t fp8_cast_transpose_dgelu(const void* dh, const void* z, int32_t x_dtype, int64_t rows, int64_t cols,
                                  int32_t fp8_dtype, const float* scale, uint8_t* q, uint8_t* q_t, float* amax_slot,
                                  float* dbias, float* dbias_ws, void* dz_out, void* stream) {

@@ -37,6 +37,8 @@
 // The dual-format variant encodes every element with two scales, to E4M3 and
 // to E5M2, from one read of the input: four outputs (both formats, both
 // layouts) through two LDS tiles, and one amax for both tensors' metas.
+#include <mutex>
+
 #include "common.h"
 
 namespace fp8lin {
@@ -375,6 +377,39 @@ hipError_t launch_pair_dt_fmt(const void* xa, int64_t rows, int64_t cols, const 
 int64_t cast_transpose_dbias_ws_bytes(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0) return 0;
     return ((rows + kTile - 1) / kTile) * cols * (int64_t)sizeof(float);
+}
+
+// Scratch of the cast-transpose that allocates nothing: the bias gradient's
+// per-row-tile partial sums (every entry is written before it is read, so
+// nothing needs clearing).  Each device holds its own copy until the process
+// ends; calls that overlap on one device share it and race.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(hipStream_t s, float** out) {
+    static std::mutex mu;
+    static float* ptr[kMaxDevices] = {};
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (s && (e = hipStreamGetDevice(s, &dev)) != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!ptr[dev]) {
+        // the symbol's address on the stream's device, looked up with that
+        // device current (each device has its own copy of the array)
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        ptr[dev] = static_cast<float*>(p);
+    }
+    *out = ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_t rows, int64_t cols, int fmt,

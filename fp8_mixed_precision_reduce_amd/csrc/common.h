@@ -63,6 +63,11 @@ hipError_t launch_cast_transpose_dual(const void* x, int dtype, int64_t rows, in
                                       uint8_t* q_e4m3, uint8_t* q_e4m3_t, float* slot_e4m3, const float* scale_e5m2,
                                       uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* slot_e5m2, hipStream_t s);
 int64_t cast_transpose_dbias_ws_bytes(int64_t rows, int64_t cols);
+// The scratch array of fp8_cast_transpose_dbias_noalloc on the device of
+// stream s (its address is looked up once per device).
+constexpr int64_t kNoAllocScratchBytes = int64_t(8) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(hipStream_t s, float** out);
 hipError_t launch_gemm(const uint8_t* a, int afmt, const uint8_t* b, int bfmt, int64_t m, int64_t n,
                        int64_t k, const float* sinv_a, const float* sinv_b, const void* bias,
                        int bias_dtype, int epilogue, void* d, int d_dtype, void* aux, const void* residual,

@@ -248,6 +248,24 @@ int32_t fp8_cast_transpose(const void* x, int32_t x_dtype, int64_t rows, int64_t
                            float* amax_slot, float* dbias, float* dbias_ws, void* stream);
 
 /*
+ * fp8_cast_transpose_dbias_noalloc -- fp8_cast_transpose with the bias
+ * gradient, for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops, harnesses that forbid hipMalloc): it takes no
+ * workspace and allocates nothing; the bias gradient's partial sums go to a
+ * scratch array inside the library, one per device, held until the process
+ * ends.  Arguments as in fp8_cast_transpose; dbias (device float[cols]) is
+ * required.  The scratch holds 8 MiB: rows, cols with
+ * fp8lin_dbias_workspace_bytes(rows, cols) > 8 MiB (more than 2^28 elements
+ * for any cols; e.g. 16384 x 16384 still fits) return FP8LIN_ERR_ARG.  Calls
+ * that overlap in time on one device share that scratch and race: issue them
+ * on one stream (or order them), as the library's other calls on shared
+ * outputs.  The results equal fp8_cast_transpose's bit for bit.
+ */
+int32_t fp8_cast_transpose_dbias_noalloc(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                                         int32_t fp8_dtype, const float* scale, uint8_t* q, uint8_t* q_t,
+                                         float* amax_slot, float* dbias, void* stream);
+
+/*
  * fp8_cast_transpose_dgelu -- the cast-transpose of the gradient entering a
  * GeLU: dz = round_x(dh * gelu'(z)) is formed on the fly (fp32 math, rounded to
  * the element type of dh), then cast and transposed as fp8_cast_transpose does;
@@ -497,6 +515,7 @@ enum {
     FP8LIN_KIND_DBIAS = 6, FP8LIN_KIND_OTHER = 7, FP8LIN_KIND_SGD = 8, FP8LIN_KIND_ATTENTION = 9
 };
 int32_t fp8lin_timing_enable(int32_t capacity);
+
 int32_t fp8lin_timing_read(int32_t* kinds, float* ms, int32_t max);
 
 #ifdef __cplusplus

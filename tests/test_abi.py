@@ -273,3 +273,22 @@ def test_binding_checks_meta_buffers_against_the_recipe():
             fn(torch.zeros(3, 16), torch.ones(3), torch.ones(3), fmts, recipe)
         with pytest.raises(ValueError, match="scale must hold 2"):
             fn(torch.zeros(2, 16), torch.ones(1), torch.ones(2), fmts, recipe)
+
+
+def test_noalloc_cast_transpose_validation():
+    """The allocation-free cast-transpose validates like fp8_cast_transpose,
+    requires dbias, and refuses a shape whose partial sums exceed its 8 MiB
+    scratch -- all before any HIP call."""
+    fn = L.fp8_cast_transpose_dbias_noalloc
+    fn.restype, fn.argtypes = ctypes.c_int32, [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                               P, P, P, P, P, P]
+    D = P(1 << 30)
+    assert _err(fn(A16, F.BF16, 128, 64, F.E4M3, B16, None, C16, None, None, None)) == F.ERR_NULL
+    assert _err(fn(A16, F.BF16, 120, 64, F.E4M3, B16, None, C16, None, D, None)) == F.ERR_SHAPE
+    assert _err(fn(A16, F.BF16, 128, 64, F.E4M3, B16, None, C16, None, P((1 << 30) + 2), None)) == F.ERR_ALIGN
+    assert _err(fn(A16, F.BF16, 128, 64, F.E4M3, B16, None, C16, None, A16, None)) == F.ERR_ARG     # dbias on x
+    # 16384 x 16384 fits (128 row tiles x 16384 columns x 4 bytes = 8 MiB); 16512 rows do not
+    assert L.fp8lin_dbias_workspace_bytes(16384, 16384) == 8 << 20
+    X, QT, DB, S = P(1 << 40), P(1 << 41), P(1 << 42), P(1 << 43)     # far apart: no overlap
+    assert _err(fn(X, F.BF16, 16512, 16384, F.E4M3, S, None, QT, None, DB, None)) == F.ERR_ARG
+    assert b"scratch" in L.fp8lin_last_error()
