@@ -16,19 +16,24 @@ an amax history of 1024 and the "max" algorithm.  Per step:
 Prints one JSON line.  `value` is TFLOP/s of the whole step (inputs resident
 in HBM).  `roofline` is the GEMM kernel: algorithmic flop per launch over its
 average launch time, measured with HIP events around each launch (recorded by
-the library on the launch stream) during a second pass of the same steps.
-`cpu_baseline` times the CPU oracle on a 1024-token slice of the same step.
+the library on the launch stream) during a second pass of the same steps,
+against the dense FP8 matrix-core peak (5.0 PFLOP/s); beside it the fraction
+of the f16 matrix-core ceiling the exact inner product runs on, and the peak
+at the shader clock measured while the GEMMs ran.  `cpu_baseline` times the
+CPU oracle on a 1024-token slice of the same step, plus the quantisation
+tensor in full, the 768-wide linear's steps and a slice of the layer's GEMMs.
 
 `quant` times the standalone quantisation kernels on a 2^28-element bf16
-tensor: amax alone, the dual-format amax+cast+transpose, and dequant, in GB/s
-of algorithmic bytes.
+tensor: amax alone, the dual-format amax+cast+transpose with the two metas'
+scale update in its last workgroup, and dequant, in GB/s of algorithmic bytes,
+beside streaming read and copy kernels of the same size.
 
 `layer_step` reports the FP8 transformer-layer training step beside it: the
 QKV, attention-output, FC1 and FC2 linears (hidden 8192, FFN 28672, 8192
-tokens) forward and backward from fp32 master weights, dynamic loss scaling
-and SGD, 20 iterations with the x100 input spike at iteration 10; 12 GEMMs,
-3.63e13 flop per step.  The attention core is not part of it (its output and
-gradient are seeded stand-in inputs).
+tokens) forward and backward from fp32 master weights, around the bf16
+attention core (64 heads of 128, 2 sequences of 4096 tokens), with dynamic
+loss scaling and SGD, 20 iterations with the x100 input spike at iteration
+10: 12 GEMMs (3.63e13 flop) and 3.30e12 flop of attention products per step.
 """
 import argparse
 import json
@@ -45,6 +50,42 @@ STEP_FLOP = 6 * GEMM_FLOP
 PEAK_F16_TFLOPS = 2500.0      # MI355X dense f16/bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_CLOCK_MHZ = 2400.0       # the engine clock the peaks are quoted at
+
+
+def mfma_roofline(tflops, avg_ms, per_launch_flop, clock_mhz, kernel, f16_inner):
+    """The roofline object of a GEMM kernel against the dense FP8 matrix-core
+    peak; the exact inner product also reports its f16 matrix-core ceiling,
+    and both the peak at the shader clock measured while the GEMMs ran."""
+    r = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+         "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": None, "kernel": kernel,
+         "per_launch_flop": per_launch_flop, "avg_launch_ms": round(avg_ms, 4)}
+    if f16_inner:
+        r["f16_ceiling"] = {"peak": PEAK_F16_TFLOPS, "frac": round(tflops / PEAK_F16_TFLOPS, 4),
+                            "note": "the exact inner product runs on the f16 matrix cores (FP8 codes decoded to f16)"}
+    if clock_mhz:
+        ratio = clock_mhz / PEAK_CLOCK_MHZ
+        ceiling = (PEAK_F16_TFLOPS if f16_inner else PEAK_FP8_TFLOPS) * ratio
+        r["clock_mhz_measured"] = round(clock_mhz, 1)
+        r["peak_at_measured_clock"] = round(PEAK_FP8_TFLOPS * ratio, 1)
+        r["frac_at_measured_clock"] = round(tflops / (PEAK_FP8_TFLOPS * ratio), 4)
+        if f16_inner:
+            r["f16_ceiling"]["peak_at_measured_clock"] = round(ceiling, 1)
+            r["f16_ceiling"]["frac_at_measured_clock"] = round(tflops / ceiling, 4)
+    return r
+
+
+def measure_clock(F, torch, run, window_ms):
+    """Shader clock while `run()` enqueues GPU work: the library's clock
+    sample runs on a stream of its own for window_ms after the work is
+    enqueued."""
+    clk = F.ClockSample()
+    torch.cuda.synchronize()
+    run()
+    clk.start(int(window_ms * 1000))
+    mhz = clk.mhz()
+    torch.cuda.synchronize()
+    return mhz
 
 
 def _exit_multi_gpu(n):
@@ -170,11 +211,18 @@ def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
         n, tot = kb.get(kind, (0, 0.0))
         kb[kind] = (n + 1, tot + ms)
     flop = lay.flops_per_step()
+    attn_flop = lay.attention_flops()
+    gemm_flop = flop - attn_flop
     n_params = lay.master.numel()
     later = sorted(per_it[2:])
     mean_ms = sum(per_it[2:]) / len(per_it[2:])
     n_sgd, t_sgd = kb.get("sgd", (0, 0.0))
     sgd_ms = t_sgd / n_sgd if n_sgd else float("nan")
+    mhz = measure_clock(F, torch, lambda: [lay.step() for _ in range(3)], 1.5 * mean_ms)
+    n_g, t_g = kb.get("gemm", (1, float("nan")))
+    gemm_tflops = gemm_flop * breakdown_steps / (t_g * 1e-3) / 1e12
+    attn_ms = kb.get("attention", (0, float("nan")))[1] / breakdown_steps
+    attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
     out = {
         "workload": "FP8 transformer layer step: QKV, attention-out, FC1, FC2 linears fwd+bwd around the bf16 "
                     "attention core (64 heads of 128, seq 4096 x batch 2, no mask), hidden 8192, FFN 28672, "
@@ -188,10 +236,17 @@ def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
         "flop_per_step": flop,
         "loss_scale_after": state[0],
         "kernels_ms_per_step": {k: round(v[1] / breakdown_steps, 4) for k, v in sorted(kb.items())},
-        "attention": {"flop_per_step": lay.attention_flops(),
-                      "ms_per_step": round(kb.get("attention", (0, 0.0))[1] / breakdown_steps, 4),
-                      "tflops": round(lay.attention_flops() / (kb.get("attention", (0, 1e30))[1] / breakdown_steps
-                                                                * 1e-3) / 1e12, 1),
+        "roofline": mfma_roofline(gemm_tflops, t_g / n_g, gemm_flop / 12, mhz,
+                                  "k_gemm, the step's 12 FP8 GEMM calls (QKV, O, FC1, FC2 fprop, dgrad and wgrad); "
+                                  "achieved = their algorithmic flop over their summed event time",
+                                  not fast_accum),
+        "attention": {"flop_per_step": attn_flop,
+                      "ms_per_step": round(attn_ms, 4),
+                      "tflops": round(attn_tflops, 1),
+                      "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_F16_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_F16_TFLOPS, 4),
+                                   "traffic": None, "kernel": "k_attn_fwd, k_attn_bwd_kv, k_attn_bwd_q (bf16 MFMA)",
+                                   "peak_at_measured_clock": round(PEAK_F16_TFLOPS * mhz / PEAK_CLOCK_MHZ, 1)},
                       "note": "forward (QK^T, PV) and backward (dP, dV, dQ, dK) products over the attention "
                               "kernels' event time; the transposes into the workspaces are under 'other'"},
         "sgd": {"params": n_params, "avg_launch_ms": round(sgd_ms, 4),
@@ -274,10 +329,11 @@ def quant_leg(F, torch, reps=50, first=10):
     """Standalone quantisation of the 2^28-element bf16 tensor (16384 x 16384,
     row magnitudes 2^u, u ~ U[-20, 10]), `reps` repetitions on the same tensor:
     (i) amax alone, (ii) one dual-format cast-transpose (amax fused, E4M3 and
-    E5M2, both layouts) followed by the scale update of the two metas,
-    (iii) dequant of both code tensors back to bf16.  Per-kernel times from
-    the library's launch events; mean (and median) over repetitions
-    `first`..reps-1."""
+    E5M2, both layouts) whose last workgroup runs the scale update of the two
+    metas, (iii) dequant of both code tensors back to bf16; beside them the
+    streaming read and copy kernels over the same 512 MiB (the HBM rate this
+    layout reaches without arithmetic).  Per-kernel times from the library's
+    launch events; mean (and median) over repetitions `first`..reps-1."""
     import synth
     cfg = synth.QUANT
     rows, cols, L = cfg["rows"], cfg["cols"], cfg["history_len"]
@@ -285,20 +341,22 @@ def quant_leg(F, torch, reps=50, first=10):
     x = synth.quant_tensor(device="cuda")
     bank = F.MetaBank([F.E4M3, F.E5M2], L)
     recipe = F.Recipe(F.FORMAT_HYBRID, L, F.AMAX_MAX, 0)
+    ticket = torch.zeros(1, dtype=torch.int32, device="cuda")
     slot = torch.zeros(1, dtype=torch.float32, device="cuda")
     u8 = dict(dtype=torch.uint8, device="cuda")
     q4, q4t, q5, q5t = (torch.empty(rows, cols, **u8), torch.empty(cols, rows, **u8), torch.empty(rows, cols, **u8),
                         torch.empty(cols, rows, **u8))
     out = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda")
+    words = torch.empty(4096, dtype=torch.int32, device="cuda")
     F.timing_enable(8 * reps)
     torch.cuda.synchronize()
     for _ in range(reps):
         F.fp8_amax(x, slot)
-        F.fp8_cast_transpose_dual(x, bank.scale[0:1], bank.scale[1:2], q4, q4t, q5, q5t, bank.amax_history[0, 0:1],
-                                  bank.amax_history[1, 0:1])
-        bank.update(recipe)
+        F.fp8_cast_transpose_dual_update(x, bank, recipe, ticket, q4, q4t, q5, q5t)
         F.fp8_dequant(q4, F.E4M3, bank.scale_inv[0:1], out)
         F.fp8_dequant(q5, F.E5M2, bank.scale_inv[1:2], out)
+        F.stream_probe(x, words, 0)
+        F.stream_probe(x, out, 1)
     torch.cuda.synchronize()
     rec = F.timing_read(8 * reps)
     F.timing_enable(0)
@@ -306,6 +364,7 @@ def quant_leg(F, torch, reps=50, first=10):
     for kind, ms in rec:
         per.setdefault(kind, []).append(ms)
     per["dequant"] = [a + b for a, b in zip(per["dequant"][0::2], per["dequant"][1::2])]
+    per["stream_read"], per["stream_copy"] = per["stream"][0::2], per["stream"][1::2]
 
     def stat(kind, nbytes):
         v = per[kind][first:]
@@ -319,18 +378,40 @@ def quant_leg(F, torch, reps=50, first=10):
         "workload": "bf16 16384x16384 (2^28 elements), row magnitudes 2^u, u~U[-20,10]; "
                     f"{reps} repetitions, mean of {first}..{reps - 1}",
         "amax": stat("amax", 2 * n),
-        "cast_transpose_dual": stat("cast_transpose", (2 + 4) * n),
-        "scale_update": {"mean_ms": round(sum(per["scale_update"][first:]) / (reps - first), 4)},
+        "cast_transpose_dual_update": stat("cast_transpose", (2 + 4) * n),
         "dequant_both": stat("dequant", 2 * (1 + 2) * n),
+        "stream_read": stat("stream_read", 2 * n),
+        "stream_copy": stat("stream_copy", 2 * 2 * n),
         "peak_gbs": PEAK_HBM_GBS,
+        "note": "cast_transpose_dual_update: amax + cast to E4M3 and E5M2 + both transposes + the two metas' scale "
+                "update (last workgroup), one launch; stream_read / stream_copy: the same 16-byte load/store "
+                "layout with no arithmetic, the measured ceiling",
     }
+    for k in ("amax", "cast_transpose_dual_update", "dequant_both"):
+        ceiling = res["stream_read" if k == "amax" else "stream_copy"]["achieved_gbs"]
+        res[k]["frac_of_stream_ceiling"] = round(res[k]["achieved_gbs"] / ceiling, 4)
     del x, q4, q4t, q5, q5t, out
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(torch, rows=1024):
-    """The CPU oracle on a `rows`-token slice of the same step (full weights)."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(torch, rows=1024, layer_rows=32):
+    """The CPU oracle, as it stands, on the host cores: (value) a `rows`-token
+    slice of the MLP block step; beside it the quantisation tensor in full,
+    the 768-wide linear's forward and forward+backward steps in full (median
+    of 5), and `layer_rows` output rows of each of the transformer layer's
+    12 GEMMs (extrapolated to the full step, and labelled so)."""
     import numpy as np
 
     import oracle as O
@@ -343,9 +424,83 @@ def cpu_baseline(torch, rows=1024):
     O.mlp_step(xs, w1n, w2n, dys, O.mlp_metas(HIST))
     dt = time.perf_counter() - t0
     flop = 6 * 2.0 * rows * HID * FFN
+    del xs, dys, w1n, w2n
+    legs = {}
+    # the quantisation tensor, in full: amax, the cast-transpose to both formats
+    # with the update, dequant of both
+    xq = to16(synth.quant_tensor(device="cuda"))
+    n = xq.size
+    metas = [O.Meta(synth.QUANT["history_len"], 0), O.Meta(synth.QUANT["history_len"], 1)]
+    t0 = time.perf_counter()
+    O.amax(xq)
+    ta = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    codes = [O.cast_transpose(xq, f, metas[f].scale)[0] for f in (0, 1)]
+    for m in metas:
+        m.record(xq)
+    O.update_metas(metas)
+    tc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for f in (0, 1):
+        O.dequant(codes[f], f, metas[f].scale_inv, 1)
+    td = time.perf_counter() - t0
+    del xq, codes
+    legs["quant_full"] = {"sample": "the 2^28-element bf16 tensor in full (one repetition)",
+                          "amax_gbs": round(2 * n / ta / 1e9, 3),
+                          "cast_transpose_dual_update_gbs": round(6 * n / tc / 1e9, 3),
+                          "dequant_both_gbs": round(6 * n / td / 1e9, 3),
+                          "seconds": round(ta + tc + td, 2)}
+    # the 768-wide linear, in full
+    w, b = synth.linear768_weights()
+    xl, dyl = synth.linear768_x(0).numpy(), synth.linear768_dy(0).numpy()
+    w, b = w.numpy(), b.numpy()
+
+    def med5(fn):
+        t = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            fn()
+            t.append(time.perf_counter() - t0)
+        return sorted(t)[2]
+
+    def fwd():
+        return O.linear_fwd(xl, w, O.Meta(16, 0), O.Meta(16, 0), bias=b)
+
+    tf = med5(fwd)
+    tfb = med5(lambda: O.linear_bwd(dyl, fwd(), O.Meta(16, 1)))
+    legs["linear768"] = {"sample": "1024x768x768 linear, one step in full, median of 5",
+                         "forward_ms": round(tf * 1e3, 3), "forward_backward_ms": round(tfb * 1e3, 3),
+                         "forward_gflops": round(2.0 * 1024 * 768 * 768 / tf / 1e9, 2),
+                         "forward_backward_gflops": round(3 * 2.0 * 1024 * 768 * 768 / tfb / 1e9, 2)}
+    # the transformer layer's 12 GEMMs on `layer_rows` output rows each
+    cfg = synth.LAYER
+    m_, h_, f_ = cfg["m"], cfg["hidden"], cfg["ffn"]
+    shapes = [(m_, 3 * h_, h_), (m_, h_, h_), (m_, f_, h_), (m_, h_, f_),          # fprop
+              (m_, h_, 3 * h_), (m_, h_, h_), (m_, h_, f_), (m_, f_, h_),          # dgrad
+              (3 * h_, h_, m_), (h_, h_, m_), (f_, h_, m_), (h_, f_, m_)]          # wgrad
+    rng = np.random.default_rng(0)
+    big = rng.integers(0, 0x77, max(n_ * k_ for _, n_, k_ in shapes), dtype=np.uint8)
+    a_rows = rng.integers(0, 0x77, layer_rows * max(k_ for _, _, k_ in shapes), dtype=np.uint8)
+    t_slice, flop_slice, flop_full = 0.0, 0.0, 0.0
+    for mm, nn, kk in shapes:
+        a = a_rows[:layer_rows * kk].reshape(layer_rows, kk)
+        bmat = big[:nn * kk].reshape(nn, kk)
+        t0 = time.perf_counter()
+        O.gemm(a, 0, bmat, 0)
+        t_slice += time.perf_counter() - t0
+        flop_slice += 2.0 * layer_rows * nn * kk
+        flop_full += 2.0 * mm * nn * kk
+    legs["layer_gemms_slice"] = {
+        "sample": f"the transformer layer's 12 GEMMs, {layer_rows} output rows each (operand codes drawn at random: "
+                  "the oracle's GEMM time does not depend on the values)",
+        "gflops": round(flop_slice / t_slice / 1e9, 2), "seconds": round(t_slice, 2),
+        "extrapolated_full_step_s": round(t_slice * flop_full / flop_slice, 1),
+        "extrapolated": True}
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"MLP block fwd+bwd+update on {rows} of {M} tokens (hidden {HID}, FFN {FFN}, full "
-                      f"weights, history {HIST}); {dt:.2f} s for {flop:.3g} flop"}
+                      f"weights, history {HIST}); {dt:.2f} s for {flop:.3g} flop",
+            "legs": legs}
 
 
 def main():
@@ -397,11 +552,20 @@ def main():
     cast_ms = sum(kb.get(k, (0, 0.0))[1] for k in ("cast_transpose", "cast")) / args.steps
     cast_gbs = MlpBlock.cast_bytes_per_step() / (cast_ms * 1e-3) / 1e9
 
-    # the other accumulation mode, for reference
+    mhz = measure_clock(F, torch, lambda: [block.step() for _ in range(10)], 5 * ms)
+    progress("shader clock under the MLP step")
+
+    # the other accumulation mode, for reference, with its own GEMM roofline
     other = MlpBlock(F, torch, fast_accum=not args.fast_accum)
     for _ in range(2):
         other.step()
     other_ms = time_steps(other, torch, max(3, args.steps // 2))
+    kb_o = kernel_breakdown(other, F, torch, max(3, args.steps // 2))
+    n_o, t_o = kb_o.get("gemm", (1, float("nan")))
+    other_mhz = measure_clock(F, torch, lambda: [other.step() for _ in range(10)], 5 * other_ms)
+    other_roof = mfma_roofline(GEMM_FLOP / (t_o / n_o * 1e-3) / 1e12, t_o / n_o, GEMM_FLOP, other_mhz,
+                               "k_gemm (fp8 GEMM, 256x256 tiles), " + ("exact" if args.fast_accum else "fast") +
+                               " inner product", args.fast_accum)
     del other
 
     # just-in-time scaling (every cast preceded by its own amax pass), for reference
@@ -422,7 +586,9 @@ def main():
         progress("quantisation kernels")
 
     value = STEP_FLOP / (ms * 1e-3) / 1e12
-    peak = PEAK_FP8_TFLOPS if args.fast_accum else PEAK_F16_TFLOPS
+    roofline = mfma_roofline(gemm_tflops, gemm_ms, GEMM_FLOP, mhz, "k_gemm (fp8 GEMM, 256x256 tiles), " +
+                             ("fast" if args.fast_accum else "exact") + " inner product", not args.fast_accum)
+    roofline["traffic"] = gemm_traffic()
     line = {
         "metric": "FP8 linear fwd+bwd TFLOP/s (% FP8 MFMA peak); cast/amax GB/s (% HBM)",
         "value": round(value, 2),
@@ -445,23 +611,14 @@ def main():
             else "exact: fp8 codes decoded to f16, f16 MFMA, fp32 accumulation",
             "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 4),
         },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(gemm_tflops, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / peak, 4),
-            "traffic": gemm_traffic(),
-            "kernel": "k_gemm (fp8 GEMM, 256x256 tiles)",
-            "per_launch_flop": GEMM_FLOP,
-            "avg_launch_ms": round(gemm_ms, 4),
-        },
+        "roofline": roofline,
         "kernels_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in sorted(kb.items())},
         "cast_kernels": {"achieved_gbs": round(cast_gbs, 1), "peak_gbs": PEAK_HBM_GBS,
                          "frac": round(cast_gbs / PEAK_HBM_GBS, 4),
                          "algorithmic_bytes_per_step": MlpBlock.cast_bytes_per_step()},
         ("exact_accum" if args.fast_accum else "fast_accum"): {
-            "ms_per_step": round(other_ms, 4), "tflops": round(STEP_FLOP / (other_ms * 1e-3) / 1e12, 2)},
+            "ms_per_step": round(other_ms, 4), "tflops": round(STEP_FLOP / (other_ms * 1e-3) / 1e12, 2),
+            "roofline": other_roof},
         "just_in_time_scaling": {
             "ms_per_step": round(jit_ms, 4), "tflops": round(STEP_FLOP / (jit_ms * 1e-3) / 1e12, 2),
             "note": "same step with every tensor scaled from its own current amax (an extra amax pass each)"},

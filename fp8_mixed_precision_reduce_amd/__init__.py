@@ -26,16 +26,16 @@ FORMAT_E4M3, FORMAT_HYBRID = 0, 1
 AMAX_MAX = 0
 EPI_GELU, EPI_ACCUMULATE, EPI_FAST_ACCUM = 1, 2, 4
 KIND_NAMES = ["amax", "cast", "cast_transpose", "dequant", "scale_update", "gemm", "dbias", "other", "sgd",
-              "attention"]
+              "attention", "stream"]
 ABI_VERSION = 5
 
 FUNCTIONS = [
     "fp8lin_abi_version", "fp8lin_last_error", "fp8lin_status_name", "fp8lin_dbias_workspace_bytes",
     "fp8_amax", "fp8_amax_scale_update", "fp8_scale_from_current_amax", "fp8_cast", "fp8_cast_transpose", "fp8_cast_transpose_dgelu",
     "fp8_cast_transpose_dbias_noalloc",
-    "fp8_cast_transpose_dual",
+    "fp8_cast_transpose_dual", "fp8_cast_transpose_dual_update",
     "fp8_dequant", "fp8_gemm", "fp8_linear_fwd", "fp8_linear_bwd", "fp8_loss_scale_update",
-    "fp8_loss_scale_apply", "fp8_sgd_step", "fp8lin_timing_enable", "fp8lin_timing_read",
+    "fp8_loss_scale_apply", "fp8_sgd_step", "fp8lin_timing_enable", "fp8lin_timing_read", "fp8lin_clock_sample", "fp8lin_stream_probe",
     "bf16_attention_workspace_bytes", "bf16_attention_fwd", "bf16_attention_bwd",
 ]
 
@@ -109,6 +109,8 @@ def _load():
         "fp8_cast_transpose_dgelu": (I32, [P, P, I32, I64, I64, I32, P, P, P, P, P, P, P, P]),
         "fp8_cast_transpose_dbias_noalloc": (I32, [P, I32, I64, I64, I32, P, P, P, P, P, P]),
         "fp8_cast_transpose_dual": (I32, [P, I32, I64, I64, P, P, P, P, P, P, P, P, P]),
+        "fp8_cast_transpose_dual_update": (I32, [P, I32, I64, I64, P, P, P, P, P, P, P, ctypes.POINTER(Recipe), P,
+                                                 P]),
         "fp8_dequant": (I32, [P, I32, I64, P, P, I32, P]),
         "fp8_gemm": (I32, [P, I32, P, I32, I64, I64, I64, P, P, P, I32, I32, P, I32, P, P, P, P, P]),
         "fp8_linear_fwd": (I32, [I64, I64, I64, P, I32, P, I32, P, I32, I32, P, I32, P, P, P, P,
@@ -124,6 +126,8 @@ def _load():
         "bf16_attention_fwd": (I32, [P, I64, I64, I64, I64, P, P, P, P]),
         "bf16_attention_bwd": (I32, [P, P, P, P, I64, I64, I64, I64, P, P, P]),
         "fp8lin_timing_read": (I32, [P, P, I32]),
+        "fp8lin_clock_sample": (I32, [P, I32, P]),
+        "fp8lin_stream_probe": (I32, [P, P, I64, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -316,6 +320,20 @@ def fp8_cast_transpose_dual(x, scale_e4m3, scale_e5m2, q_e4m3=None, q_e4m3_t=Non
                                         _p(amax_slot_e5m2), _stream(stream)))
 
 
+def fp8_cast_transpose_dual_update(x, bank, recipe, ticket, q_e4m3=None, q_e4m3_t=None, q_e5m2=None, q_e5m2_t=None,
+                                   stream=None):
+    """Dual-format cast-transpose into a two-tensor MetaBank (E4M3, E5M2) with
+    the bank's scale update in the same launch; ticket: an int32 device
+    tensor of one element, zero before the first call (left zero)."""
+    if bank.formats != bytes([E4M3, E5M2]):
+        raise ValueError("fp8_cast_transpose_dual_update: the bank must hold (E4M3, E5M2) metas")
+    _check_metas(bank.amax_history, bank.scale, bank.scale_inv, bank.formats, recipe, "fp8_cast_transpose_dual_update")
+    rows, cols = x.shape
+    _check(_lib.fp8_cast_transpose_dual_update(_p(x), _dt(x), rows, cols, _p(q_e4m3), _p(q_e4m3_t), _p(q_e5m2),
+                                               _p(q_e5m2_t), _p(bank.amax_history), _p(bank.scale),
+                                               _p(bank.scale_inv), ctypes.byref(recipe), _p(ticket), _stream(stream)))
+
+
 def fp8_dequant(q, fmt, scale_inv, out, stream=None):
     _check(_lib.fp8_dequant(_p(q), fmt, q.numel(), _p(scale_inv), _p(out), _dt(out), _stream(stream)))
 
@@ -391,6 +409,32 @@ def timing_read(max_records=1 << 16):
     ms = (ctypes.c_float * max_records)()
     n = _lib.fp8lin_timing_read(ctypes.cast(kinds, ctypes.c_void_p), ctypes.cast(ms, ctypes.c_void_p), max_records)
     return [(KIND_NAMES[kinds[i]], ms[i]) for i in range(n)]
+
+
+def stream_probe(src, dst, mode, stream=None):
+    """Streaming reference kernel over src's bytes: mode 0 reads them (dst: a
+    device buffer of at least 8 KiB), mode 1 copies them into dst."""
+    nbytes = src.numel() * src.element_size()
+    _check(_lib.fp8lin_stream_probe(_p(src), _p(dst), nbytes, mode, _stream(stream)))
+
+
+class ClockSample:
+    """The shader clock while other work runs: start() enqueues the library's
+    one-wave clock sample on a stream of its own (it waits wait_us of the
+    constant 100 MHz counter), mhz() waits for it and returns the average
+    shader clock over that window."""
+
+    def __init__(self, device="cuda"):
+        self.buf = torch.zeros(4, dtype=torch.int64, device=device)
+        self.stream = torch.cuda.Stream(device=device)
+
+    def start(self, wait_us):
+        _check(_lib.fp8lin_clock_sample(_p(self.buf), int(wait_us), ctypes.c_void_p(self.stream.cuda_stream)))
+
+    def mhz(self):
+        self.stream.synchronize()
+        c0, c1, r0, r1 = self.buf.cpu().tolist()
+        return (c1 - c0) / max(r1 - r0, 1) * 100.0
 
 
 # ------------------------------------------------------------- attention core

@@ -121,6 +121,26 @@ int64_t fp8lin_dbias_workspace_bytes(int64_t rows, int64_t cols) {
     return cast_transpose_dbias_ws_bytes(rows, cols);
 }
 
+int32_t fp8lin_clock_sample(uint64_t* out, int32_t wait_us, void* stream) {
+    if (!out) return fail(FP8LIN_ERR_NULL, "fp8lin_clock_sample: out is null");
+    if (!aligned(out, 8)) return fail(FP8LIN_ERR_ALIGN, "fp8lin_clock_sample: out not 8-byte aligned");
+    if (wait_us < 1 || wait_us > 1000000)
+        return fail(FP8LIN_ERR_ARG, "fp8lin_clock_sample: wait_us=%d outside 1..1000000", wait_us);
+    return hip_status(launch_clock_sample(reinterpret_cast<unsigned long long*>(out), (int64_t)wait_us * 100,
+                                          as_stream(stream)),
+                      "fp8lin_clock_sample");
+}
+
+int32_t fp8lin_stream_probe(const void* src, void* dst, int64_t bytes, int32_t mode, void* stream) {
+    const char* fn = "fp8lin_stream_probe";
+    if (mode != 0 && mode != 1) return fail(FP8LIN_ERR_ARG, "%s: mode %d is not 0 (read) or 1 (copy)", fn, mode);
+    if (bytes < 0 || bytes % 16 || bytes > kMaxElems) return fail(FP8LIN_ERR_SHAPE, "%s: bytes=%lld", fn, (long long)bytes);
+    if (bytes > 0 && (!src || !dst)) return fail(FP8LIN_ERR_NULL, "%s: null pointer", fn);
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(FP8LIN_ERR_ALIGN, "%s: misaligned pointer", fn);
+    if (overlap(src, bytes, dst, mode == 0 ? 8192 : bytes)) return fail(FP8LIN_ERR_ARG, "%s: dst overlaps src", fn);
+    return hip_status(launch_stream_probe(src, dst, bytes, mode, as_stream(stream)), fn);
+}
+
 int32_t fp8lin_timing_enable(int32_t capacity) {
     std::lock_guard<std::mutex> lk(g_timer.mu);
     for (hipEvent_t e : g_timer.ev) (void)hipEventDestroy(e);
@@ -331,6 +351,44 @@ int32_t fp8_cast_transpose_dual(const void* x, int32_t x_dtype, int64_t rows, in
             if (overlap(a[i], n, b[j], n)) return fail(FP8LIN_ERR_ARG, "%s: outputs overlap", fn);
     return hip_status(launch_cast_transpose_dual(x, x_dtype, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, amax_slot_e4m3,
                                                  scale_e5m2, q_e5m2, q_e5m2_t, amax_slot_e5m2, as_stream(stream)),
+                      fn);
+}
+
+int32_t fp8_cast_transpose_dual_update(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, uint8_t* q_e4m3,
+                                       uint8_t* q_e4m3_t, uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* amax_history,
+                                       float* scale, float* scale_inv, const fp8lin_recipe* recipe, uint32_t* ticket,
+                                       void* stream) {
+    const char* fn = "fp8_cast_transpose_dual_update";
+    static const uint8_t fmts[2] = {FP8LIN_E4M3, FP8LIN_E5M2};
+    int32_t v;
+    if ((v = check_scale_args(fn, amax_history, scale, scale_inv, fmts, 2, recipe))) return v;
+    const int64_t L = recipe->history_len;
+    if ((v = check_ct(fn, x, nullptr, x_dtype, rows, cols, FP8LIN_E4M3, scale, q_e4m3, q_e4m3_t, amax_history,
+                      nullptr, nullptr, nullptr, false)))
+        return v;
+    if ((v = check_ct(fn, x, nullptr, x_dtype, rows, cols, FP8LIN_E5M2, scale + 1, q_e5m2, q_e5m2_t,
+                      amax_history + L, nullptr, nullptr, nullptr, false)))
+        return v;
+    const int64_t n = rows * cols;
+    if (n > 0 && !q_e4m3 && !q_e4m3_t && !q_e5m2 && !q_e5m2_t) return fail(FP8LIN_ERR_NULL, "%s: no output", fn);
+    if (n > 0 && !ticket) return fail(FP8LIN_ERR_NULL, "%s: ticket is null", fn);
+    if (!aligned(ticket, 4)) return fail(FP8LIN_ERR_ALIGN, "%s: misaligned ticket", fn);
+    const uint8_t* outs[4] = {q_e4m3, q_e4m3_t, q_e5m2, q_e5m2_t};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], n, outs[j], n)) return fail(FP8LIN_ERR_ARG, "%s: outputs overlap", fn);
+    const void* state[4] = {amax_history, scale, scale_inv, ticket};
+    const int64_t sb[4] = {2 * L * 4, 8, 8, 4};
+    const int64_t xb = n * elem_size(x_dtype);
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(state[i], sb[i], x, xb)) return fail(FP8LIN_ERR_ARG, "%s: state overlaps the input", fn);
+        for (int j = 0; j < 4; ++j)
+            if (overlap(state[i], sb[i], outs[j], n)) return fail(FP8LIN_ERR_ARG, "%s: state overlaps an output", fn);
+        if (i < 3 && overlap(state[i], sb[i], ticket, 4)) return fail(FP8LIN_ERR_ARG, "%s: ticket overlaps", fn);
+    }
+    return hip_status(launch_cast_transpose_dual_update(x, x_dtype, rows, cols, q_e4m3, q_e4m3_t, q_e5m2, q_e5m2_t,
+                                                        amax_history, scale, scale_inv, (int32_t)L, recipe->margin,
+                                                        ticket, as_stream(stream)),
                       fn);
 }
 

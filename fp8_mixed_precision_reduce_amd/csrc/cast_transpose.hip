@@ -127,12 +127,23 @@ struct CtJob {
     float* amax_slot;
 };
 
+// The scale update the dual-format variant can finish with: the metas of its
+// two formats (0: E4M3, 1: E5M2) in one bank, hist [2][L]; ticket == nullptr:
+// no update.
+struct DualUpdate {
+    float* hist;
+    float* scale;
+    float* sinv;
+    int32_t L, margin;
+    unsigned int* ticket;
+};
+
 template <int DT, int FMT, bool DGELU, bool DBIAS, bool DUAL, bool PAIR = false>
 __global__ void __launch_bounds__(kThreads)
 k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64_t rows_a, int64_t cols_a,
                  int64_t tiles_ca, const float* __restrict__ scale_p, uint8_t* __restrict__ q_a,
                  uint8_t* __restrict__ qt_a, float* amax_slot, float* __restrict__ dbias_ws,
-                 void* __restrict__ dz_out, Second sec, SinvSnap snap, CtJob job_b) {
+                 void* __restrict__ dz_out, Second sec, SinvSnap snap, CtJob job_b, DualUpdate upd) {
     static_assert(!PAIR || (!DGELU && !DBIAS && !DUAL), "the pair variant is a plain cast-transpose");
     using C = CtVec<DT>;
     constexpr int E = C::E, NP = C::NP;
@@ -300,12 +311,50 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
         if (second) m_b = max(m_b, m);
         else m_a = max(m_a, m);
     }
-    if (amax_slot) block_amax_merge(m_a, amax_slot, red);
     if constexpr (DUAL) {
-        if (sec.amax_slot) {
-            __syncthreads();     // red[] is reused
-            block_amax_merge(m_a, sec.amax_slot, red);
+        if (upd.ticket) {
+            // The last workgroup to finish updates both metas ([TE-KR]
+            // "FP8 자동변환(Autocasting)": cast, amax and factor as one step).
+            // Thread 0 merges the workgroup's amax into both slots with
+            // returning atomics and takes its ticket only once both have
+            // returned (the ticket increment depends on their results), so
+            // every merge is performed at the device's coherence point before
+            // the last ticket is taken; no release fence (on this chip an
+            // agent-scope release writes the L2 back, in every workgroup).
+            // The last workgroup then reads the histories with device-scope
+            // loads after an acquire fence, and leaves the ticket at zero.
+            // Every workgroup read the scales before taking its ticket.
+            const uint32_t wm = wave_max_u32(m_a);
+            if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = wm;
+            __syncthreads();
+            __shared__ uint32_t last;
+            if (threadIdx.x == 0) {
+                uint32_t bm = 0;
+                for (int w = 0; w < kThreads / 64; ++w) bm = max(bm, red[w]);
+                const uint32_t o4 = atomicMax(reinterpret_cast<unsigned int*>(amax_slot), bm);
+                const uint32_t o5 = atomicMax(reinterpret_cast<unsigned int*>(sec.amax_slot), bm);
+                uint32_t dep;
+                asm volatile("v_and_b32 %0, 0, %1" : "=v"(dep) : "v"(o4 ^ o5));
+                last = atomicAdd(upd.ticket, 1u + dep) == gridDim.x - 1 ? 1u : 0u;
+            }
+            __syncthreads();
+            if (last) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                float* fred = reinterpret_cast<float*>(red);
+                scale_update_block<true>(upd.hist, upd.scale, upd.sinv, 448.0f, upd.L, upd.margin, fred);
+                scale_update_block<true>(upd.hist + upd.L, upd.scale + 1, upd.sinv + 1, 57344.0f, upd.L, upd.margin,
+                                         fred);
+                if (threadIdx.x == 0) __hip_atomic_store(upd.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            if (amax_slot) block_amax_merge(m_a, amax_slot, red);
+            if (sec.amax_slot) {
+                __syncthreads();     // red[] is reused
+                block_amax_merge(m_a, sec.amax_slot, red);
+            }
         }
+    } else {
+        if (amax_slot) block_amax_merge(m_a, amax_slot, red);
     }
     if constexpr (PAIR) {
         if (job_b.amax_slot) {
@@ -336,27 +385,27 @@ hipError_t launch_dt_fmt(const void* x, const void* z, int64_t rows, int64_t col
     const Second none{nullptr, nullptr, nullptr, nullptr};
     if (!dgelu && !dbias)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{});
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{});
     else if (!dgelu)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, true, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{});
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{});
     else if (!dbias)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, false, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{});
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{});
     else
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, true, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{});
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{});
     return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_dual_dt(const void* x, int64_t rows, int64_t cols, const float* scale4, uint8_t* q4,
-                          uint8_t* q4t, float* slot4, const Second& sec, hipStream_t s) {
+                          uint8_t* q4t, float* slot4, const Second& sec, hipStream_t s, DualUpdate upd = {}) {
     const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
     const int64_t ntiles = tiles_r * tiles_c;
     const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
     hipLaunchKernelGGL((k_cast_transpose<DT, kE4M3, false, false, true>), grid, block, 0, s, x, nullptr, rows,
-                       cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec, SinvSnap{}, CtJob{});
+                       cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec, SinvSnap{}, CtJob{}, upd);
     return hipGetLastError();
 }
 
@@ -368,7 +417,7 @@ hipError_t launch_pair_dt_fmt(const void* xa, int64_t rows, int64_t cols, const 
     const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
     const Second none{nullptr, nullptr, nullptr, nullptr};
     hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false, true>), grid, block, 0, s, xa, nullptr, rows,
-                       cols, tiles_c, scale, q, qt, slot, nullptr, nullptr, none, snap, b);
+                       cols, tiles_c, scale, q, qt, slot, nullptr, nullptr, none, snap, b, DualUpdate{});
     return hipGetLastError();
 }
 
@@ -449,6 +498,24 @@ hipError_t launch_cast_transpose_dual(const void* x, int dtype, int64_t rows, in
     const hipError_t e = dtype == kF32
         ? launch_dual_dt<kF32>(x, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, slot_e4m3, sec, s)
         : launch_dual_dt<kBF16>(x, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, slot_e4m3, sec, s);
+    timing_after(s);
+    return e;
+}
+
+hipError_t launch_cast_transpose_dual_update(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q_e4m3,
+                                             uint8_t* q_e4m3_t, uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* hist,
+                                             float* scale, float* sinv, int32_t L, int32_t margin,
+                                             unsigned int* ticket, hipStream_t s) {
+    if (rows == 0 || cols == 0) {      // nothing to cast: the update alone
+        const uint8_t fmts[2] = {kE4M3, kE5M2};
+        return launch_scale_update(hist, scale, sinv, fmts, 2, L, margin, s);
+    }
+    const Second sec{scale + 1, q_e5m2, q_e5m2_t, hist + L};
+    const DualUpdate upd{hist, scale, sinv, L, margin, ticket};
+    timing_before(kKindCastT, s);
+    const hipError_t e = dtype == kF32
+        ? launch_dual_dt<kF32>(x, rows, cols, scale, q_e4m3, q_e4m3_t, hist, sec, s, upd)
+        : launch_dual_dt<kBF16>(x, rows, cols, scale, q_e4m3, q_e4m3_t, hist, sec, s, upd);
     timing_after(s);
     return e;
 }

@@ -14,7 +14,7 @@ enum Dtype : int32_t { kF32 = 0, kBF16 = 1, kE4M3 = 2, kE5M2 = 3 };
 // Kinds of kernels, as reported by the event timer.
 enum Kind : int32_t { kKindAmax = 0, kKindCast = 1, kKindCastT = 2, kKindDequant = 3,
                       kKindScaleUpdate = 4, kKindGemm = 5, kKindDbias = 6, kKindOther = 7, kKindSgd = 8,
-                      kKindAttn = 9 };
+                      kKindAttn = 9, kKindStream = 10 };
 
 // Host side: record events around a launch when timing is enabled.
 void timing_before(int kind, hipStream_t stream);
@@ -51,6 +51,8 @@ hipError_t launch_scale_from_current(const float* hist, int64_t stride, float* s
                                      const uint8_t* fmts, int32_t n, int32_t margin, hipStream_t s);
 hipError_t launch_copy_scalars(const float* a, const float* b, float* dst2, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+hipError_t launch_clock_sample(unsigned long long* out, int64_t ticks, hipStream_t s);
+hipError_t launch_stream_probe(const void* src, void* dst, int64_t bytes, int mode, hipStream_t s);
 hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_t rows, int64_t cols,
                                  int fmt, const float* scale, uint8_t* q, uint8_t* qt, float* slot,
                                  float* dbias, float* dbias_ws, void* dz_out, hipStream_t s, SinvSnap snap = {});
@@ -62,6 +64,13 @@ hipError_t launch_cast_transpose_pair(const void* xa, const void* xb, int dtype,
 hipError_t launch_cast_transpose_dual(const void* x, int dtype, int64_t rows, int64_t cols, const float* scale_e4m3,
                                       uint8_t* q_e4m3, uint8_t* q_e4m3_t, float* slot_e4m3, const float* scale_e5m2,
                                       uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* slot_e5m2, hipStream_t s);
+// The dual-format cast-transpose into a bank of two metas (0: E4M3, 1: E5M2,
+// histories hist[2][L]) whose last workgroup then runs the scale update of
+// both; `ticket` is a device counter that is zero before and after.
+hipError_t launch_cast_transpose_dual_update(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q_e4m3,
+                                             uint8_t* q_e4m3_t, uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* hist,
+                                             float* scale, float* sinv, int32_t L, int32_t margin,
+                                             unsigned int* ticket, hipStream_t s);
 int64_t cast_transpose_dbias_ws_bytes(int64_t rows, int64_t cols);
 // The scratch array of fp8_cast_transpose_dbias_noalloc on the device of
 // stream s (its address is looked up once per device).
@@ -166,6 +175,65 @@ __device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
 
 // |x| as an unsigned bit pattern: the amax statistic compares these.
 __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// The delayed-scaling scale rule: s = fl32(fl32(fp8_max / a) * 2^-margin),
+// FLT_MAX if that overflowed; 0 means "keep the old scale" (a not > 0, or s
+// underflowed).
+__device__ __forceinline__ float scale_rule(float a, float fmax, int32_t margin) {
+    if (!(a > 0.0f)) return 0.0f;
+    float s = __fdiv_rn(fmax, a);
+    s = ldexpf(s, -margin);
+    if (isinf(s)) s = 3.402823466e+38f;
+    return s;
+}
+
+// The per-step update of one tensor's meta by one workgroup (every thread
+// calls it): the max over the finite history entries, the scale rule, then
+// the roll h[i] <- h[i-1], h[0] <- 0, done top-down in chunks of blockDim.x
+// so every read of a chunk precedes the writes that could clobber it.
+// COHERENT reads the history with device-scope loads (for entries other
+// workgroups of the same launch merged into).  red: LDS, blockDim.x / 64 floats.
+template <bool COHERENT>
+__device__ __forceinline__ float load_hist(const float* p) {
+    if constexpr (COHERENT)
+        return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned int*>(p), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT));
+    else
+        return *p;
+}
+
+template <bool COHERENT>
+__device__ __forceinline__ void scale_update_block(float* h, float* scale, float* sinv, float fmax, int32_t L,
+                                                   int32_t margin, float* red) {
+    const int nt = (int)blockDim.x;
+    float m = -INFINITY;
+    for (int i = threadIdx.x; i < L; i += nt) {
+        const float v = load_hist<COHERENT>(h + i);
+        if (isfinite(v)) m = fmaxf(m, v);
+    }
+    // wave then block max (floats; -inf marks "no finite entry")
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a = red[0];
+        for (int w = 1; w < nt / 64; ++w) a = fmaxf(a, red[w]);
+        const float s = scale_rule(a, fmax, margin);
+        if (s > 0.0f) {
+            *scale = s;
+            *sinv = __fdiv_rn(1.0f, s);
+        }
+    }
+    __syncthreads();
+    for (int base = ((L - 1) / nt) * nt; base >= 0; base -= nt) {
+        const int i = base + threadIdx.x;
+        float prev = 0.0f;
+        if (i < L && i > 0) prev = load_hist<COHERENT>(h + i - 1);
+        __syncthreads();
+        if (i < L) h[i] = prev;
+        __syncthreads();
+    }
+}
 
 // Max over the 64 lanes of a wave: DPP within each row of 16 lanes, then the
 // four row results through readlane.  Every lane returns the wave maximum.

@@ -189,53 +189,14 @@ k_dequant(const uint8_t* __restrict__ q, int64_t n, const float* __restrict__ si
 constexpr int kMaxTensors = 4096;
 struct FmtBits { uint32_t w[kMaxTensors / 32]; };
 
-// One workgroup per tensor: max over the finite history entries, the scale
-// rule, then the roll h[i] <- h[i-1], h[0] <- 0 done top-down in chunks of
-// 256 so every read of a chunk precedes the writes that could clobber it.
-// The scale rule: s = fl32(fl32(fp8_max / a) * 2^-margin), FLT_MAX if that
-// overflowed; 0 means "keep the old scale" (a not > 0, or s underflowed).
-__device__ __forceinline__ float scale_rule(float a, float fmax, int32_t margin) {
-    if (!(a > 0.0f)) return 0.0f;
-    float s = __fdiv_rn(fmax, a);
-    s = ldexpf(s, -margin);
-    if (isinf(s)) s = 3.402823466e+38f;
-    return s;
-}
-
+// One workgroup per tensor (the scale rule and the roll: scale_update_block).
 __global__ void __launch_bounds__(kThreads)
 k_scale_update(float* __restrict__ hist, float* __restrict__ scale, float* __restrict__ sinv,
                FmtBits fmts, int32_t L, int32_t margin) {
     __shared__ float red[kThreads / 64];
     const int t = blockIdx.x;
-    float* h = hist + (int64_t)t * L;
-    float m = -INFINITY;
-    for (int i = threadIdx.x; i < L; i += kThreads) {
-        const float v = h[i];
-        if (isfinite(v)) m = fmaxf(m, v);
-    }
-    // wave then block max (floats; -inf marks "no finite entry")
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float a = red[0];
-        for (int w = 1; w < kThreads / 64; ++w) a = fmaxf(a, red[w]);
-        const bool e5 = (fmts.w[t >> 5] >> (t & 31)) & 1u;
-        const float s = scale_rule(a, e5 ? 57344.0f : 448.0f, margin);
-        if (s > 0.0f) {
-            scale[t] = s;
-            sinv[t] = __fdiv_rn(1.0f, s);
-        }
-    }
-    __syncthreads();
-    for (int base = ((L - 1) / kThreads) * kThreads; base >= 0; base -= kThreads) {
-        const int i = base + threadIdx.x;
-        float prev = 0.0f;
-        if (i < L && i > 0) prev = h[i - 1];
-        __syncthreads();
-        if (i < L) h[i] = prev;
-        __syncthreads();
-    }
+    const bool e5 = (fmts.w[t >> 5] >> (t & 31)) & 1u;
+    scale_update_block<false>(hist + (int64_t)t * L, scale + t, sinv + t, e5 ? 57344.0f : 448.0f, L, margin, red);
 }
 
 // Just-in-time scaling: the scale of tensor t from its current amax alone
@@ -270,6 +231,93 @@ __global__ void __launch_bounds__(kThreads) k_zero_f32(float* p, int64_t n) {
 }
 
 }  // namespace
+
+// Shader-clock sample (a measurement aid, not a step of the method): one
+// wave reads the shader-clock counter and the constant 100 MHz counter,
+// sleeps until `ticks` of the latter have passed (at most 2^22 sleeps of 512
+// cycles), reads both again and writes {clock0, clock1, ref0, ref1}.
+// Launched on a second stream beside running kernels it gives their clock.
+__global__ void __launch_bounds__(64) k_clock_sample(unsigned long long* out, unsigned long long ticks) {
+    const unsigned long long c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    unsigned long long r = r0;
+    for (int i = 0; i < (1 << 22) && r - r0 < ticks; ++i) {
+        __builtin_amdgcn_s_sleep(8);
+        r = __builtin_amdgcn_s_memrealtime();
+    }
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        out[0] = c0;
+        out[1] = c1;
+        out[2] = r0;
+        out[3] = r1;
+    }
+}
+
+// Streaming reference kernels (measurement aids, not steps of the method):
+// the same layout and grid as the elementwise kernels above, without their
+// arithmetic.  Read: every 16-byte vector of src is loaded and folded into an
+// xor per workgroup, written to dst[blockIdx.x] (one word).  Copy: dst = src.
+__global__ void __launch_bounds__(kThreads) k_stream_read(const uint4* __restrict__ p, int64_t nvec,
+                                                         uint32_t* __restrict__ dst) {
+    __shared__ uint32_t red[kThreads / 64];
+    const int lane = threadIdx.x & 63;
+    uint32_t x = 0;
+    for (int64_t b = wave_id() * (64 * kU); b < nvec; b += wave_count() * (64 * kU)) {
+        uint4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            v[u] = i < nvec ? p[i] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (int off = 32; off > 0; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off);
+    if (lane == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kThreads / 64; ++w) x ^= red[w];
+        dst[blockIdx.x] = x;
+    }
+}
+
+__global__ void __launch_bounds__(kThreads) k_stream_copy(const uint4* __restrict__ p, int64_t nvec,
+                                                         uint4* __restrict__ q) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t b = wave_id() * (64 * kU); b < nvec; b += wave_count() * (64 * kU)) {
+        uint4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            v[u] = i < nvec ? p[i] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = b + 64 * u + lane;
+            if (i < nvec) q[i] = v[u];
+        }
+    }
+}
+
+hipError_t launch_stream_probe(const void* src, void* dst, int64_t bytes, int mode, hipStream_t s) {
+    const int64_t nvec = bytes / 16;
+    if (nvec == 0) return hipSuccess;
+    const int g = grid_vec(nvec);
+    timing_before(kKindStream, s);
+    if (mode == 0)
+        hipLaunchKernelGGL(k_stream_read, dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(src), nvec,
+                           static_cast<uint32_t*>(dst));
+    else
+        hipLaunchKernelGGL(k_stream_copy, dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(src), nvec,
+                           static_cast<uint4*>(dst));
+    timing_after(s);
+    return hipGetLastError();
+}
+
+hipError_t launch_clock_sample(unsigned long long* out, int64_t ticks, hipStream_t s) {
+    hipLaunchKernelGGL(k_clock_sample, dim3(1), dim3(64), 0, s, out, (unsigned long long)ticks);
+    return hipGetLastError();
+}
 
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
     if (n == 0) return hipSuccess;

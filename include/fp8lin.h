@@ -299,6 +299,30 @@ int32_t fp8_cast_transpose_dual(const void* x, int32_t x_dtype, int64_t rows, in
                                 void* stream);
 
 /*
+ * fp8_cast_transpose_dual_update -- fp8_cast_transpose_dual into the metas of
+ * a two-tensor bank (tensor 0 E4M3, tensor 1 E5M2), followed in the same
+ * launch by fp8_amax_scale_update of both, run by the last workgroup to
+ * finish: amax, cast to both formats in both layouts, and the new scales as
+ * one step ([TE-KR] "FP8 자동변환(Autocasting)": inputs are cast, their amax
+ * recorded and the factor computed together).  The results equal
+ * fp8_cast_transpose_dual (scales scale[0], scale[1]; amax slots
+ * amax_history[0], amax_history[L]) followed by fp8_amax_scale_update of the
+ * two tensors, bit for bit.
+ *   x              [rows][cols] of x_dtype (F32 or BF16), multiples of 16
+ *   q_e4m3 [rows][cols], q_e4m3_t [cols][rows], q_e5m2, q_e5m2_t: as in
+ *                  fp8_cast_transpose_dual (any may be NULL, not all)
+ *   amax_history   device float[2][L]; scale, scale_inv device float[2]
+ *   recipe         HOST: history_len L, margin, amax_compute_algo
+ *   ticket         device uint32 that is 0 before the first call; every call
+ *                  leaves it 0.  Calls in flight at the same time need
+ *                  tickets of their own.
+ */
+int32_t fp8_cast_transpose_dual_update(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                                       uint8_t* q_e4m3, uint8_t* q_e4m3_t, uint8_t* q_e5m2, uint8_t* q_e5m2_t,
+                                       float* amax_history, float* scale, float* scale_inv,
+                                       const fp8lin_recipe* recipe, uint32_t* ticket, void* stream);
+
+/*
  * fp8_dequant -- out = round_out(fl32(dec_F(q) * scale_inv)) elementwise.
  * [TE-RU] section 3: after the FP8 operation the factor is divided back out;
  * [TE-KR] "정확도(Precision)": the FP8-representable copy of a tensor.
@@ -512,10 +536,31 @@ int32_t bf16_attention_bwd(const void* qkv, const void* ctx, const float* lse, c
 enum {
     FP8LIN_KIND_AMAX = 0, FP8LIN_KIND_CAST = 1, FP8LIN_KIND_CAST_TRANSPOSE = 2,
     FP8LIN_KIND_DEQUANT = 3, FP8LIN_KIND_SCALE_UPDATE = 4, FP8LIN_KIND_GEMM = 5,
-    FP8LIN_KIND_DBIAS = 6, FP8LIN_KIND_OTHER = 7, FP8LIN_KIND_SGD = 8, FP8LIN_KIND_ATTENTION = 9
+    FP8LIN_KIND_DBIAS = 6, FP8LIN_KIND_OTHER = 7, FP8LIN_KIND_SGD = 8, FP8LIN_KIND_ATTENTION = 9,
+    FP8LIN_KIND_STREAM = 10
 };
 int32_t fp8lin_timing_enable(int32_t capacity);
 
+/*
+ * Shader-clock sample, a measurement aid beside the timer: one wave reads the
+ * GPU's shader-clock counter and its constant 100 MHz counter, waits about
+ * wait_us microseconds (1..1000000) of the latter, reads both again and writes
+ * {clock0, clock1, ref0, ref1} to out (device uint64[4]).  Enqueued on a
+ * second stream while other kernels run, (clock1 - clock0) / (ref1 - ref0) *
+ * 100 MHz is the shader clock they ran at.
+ */
+int32_t fp8lin_clock_sample(uint64_t* out, int32_t wait_us, void* stream);
+
+/*
+ * Streaming reference kernels, a measurement aid: the HBM rate that the
+ * elementwise kernels' load/store layout reaches without their arithmetic.
+ * mode 0 reads bytes of src (16-byte vectors, the same grid and layout as
+ * fp8_amax) and writes one 32-bit word per workgroup to dst (at most 2048
+ * words: dst holds 8 KiB); mode 1 copies bytes of src to dst.  bytes is a
+ * multiple of 16; src, dst 16-byte aligned and not overlapping.  Timed as
+ * FP8LIN_KIND_STREAM.
+ */
+int32_t fp8lin_stream_probe(const void* src, void* dst, int64_t bytes, int32_t mode, void* stream);
 int32_t fp8lin_timing_read(int32_t* kinds, float* ms, int32_t max);
 
 #ifdef __cplusplus

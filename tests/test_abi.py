@@ -292,3 +292,37 @@ def test_noalloc_cast_transpose_validation():
     X, QT, DB, S = P(1 << 40), P(1 << 41), P(1 << 42), P(1 << 43)     # far apart: no overlap
     assert _err(fn(X, F.BF16, 16512, 16384, F.E4M3, S, None, QT, None, DB, None)) == F.ERR_ARG
     assert b"scratch" in L.fp8lin_last_error()
+
+
+def test_clock_sample_validation():
+    fn = L.fp8lin_clock_sample
+    fn.restype, fn.argtypes = ctypes.c_int32, [P, ctypes.c_int32, P]
+    assert _err(fn(None, 100, None)) == F.ERR_NULL
+    assert _err(fn(P((1 << 20) + 4), 100, None)) == F.ERR_ALIGN
+    assert _err(fn(A16, 0, None)) == F.ERR_ARG
+    assert _err(fn(A16, 2000000, None)) == F.ERR_ARG
+
+
+def test_dual_update_and_stream_probe_validation():
+    du = L.fp8_cast_transpose_dual_update
+    du.restype = ctypes.c_int32
+    du.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, P, P, P, P, P, P, P,
+                   ctypes.POINTER(F.Recipe), P, P]
+    X, Q, H, S, SI, T = P(1 << 40), P(1 << 41), P(1 << 42), P(1 << 43), P(1 << 44), P(1 << 45)
+    r = F.Recipe(F.FORMAT_HYBRID, 16, F.AMAX_MAX, 0)
+    ok = lambda **kw: du(kw.get("x", X), F.BF16, kw.get("rows", 128), 64, kw.get("q", Q), None, None, None, H, S, SI,
+                         ctypes.byref(kw.get("recipe", r)), kw.get("ticket", T), None)
+    assert _err(ok(ticket=None)) == F.ERR_NULL
+    assert _err(ok(ticket=P((1 << 45) + 2))) == F.ERR_ALIGN
+    assert _err(ok(rows=120)) == F.ERR_SHAPE
+    assert _err(ok(recipe=F.Recipe(F.FORMAT_HYBRID, 0, F.AMAX_MAX, 0))) == F.ERR_ARG
+    assert _err(ok(ticket=P((1 << 42) + 64))) == F.ERR_ARG          # ticket inside the history
+    assert _err(ok(q=P(1 << 40))) == F.ERR_ARG                       # output on the input
+    sp = L.fp8lin_stream_probe
+    sp.restype, sp.argtypes = ctypes.c_int32, [P, P, ctypes.c_int64, ctypes.c_int32, P]
+    assert _err(sp(A16, B16, 1024, 2, None)) == F.ERR_ARG
+    assert _err(sp(A16, B16, 1000, 0, None)) == F.ERR_SHAPE
+    assert _err(sp(None, B16, 1024, 1, None)) == F.ERR_NULL
+    assert _err(sp(ODD, B16, 1024, 1, None)) == F.ERR_ALIGN
+    assert _err(sp(A16, P((1 << 20) + 512), 1024, 1, None)) == F.ERR_ARG
+    assert sp(A16, B16, 0, 1, None) == F.OK

@@ -116,3 +116,43 @@ def test_cast_transpose_dual_full_size(oracle):
         del wqt
     a = oracle.amax(X)
     assert_bits_equal(np_of(bank.amax_history[:, 0]), np.array([a, a], dtype=np.float32), "amax slots")
+
+
+@pytest.mark.parametrize("shape", [(272, 400), (16384, 16384)], ids=["272x400", "16384x16384"])
+def test_cast_transpose_dual_update_matches_oracle(oracle, shape):
+    """The dual-format cast-transpose with the two metas' scale update in its
+    last workgroup: over 4 consecutive calls (histories of 1024 and 16, margin
+    0 and 2, the ticket reused), every code, history entry, scale and inverse
+    scale equals the oracle's cast-transpose of both formats followed by its
+    update, bit for bit; the ticket is left at zero."""
+    rows, cols = shape
+    big = rows * cols > 1 << 20
+    x = synth.quant_tensor(device="cuda", rows=rows, cols=cols)
+    X = np_of(x)
+    ticket = torch.zeros(1, dtype=torch.int32, device="cuda")
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    outs = [torch.empty(rows, cols, **u8), torch.empty(cols, rows, **u8), torch.empty(rows, cols, **u8),
+            torch.empty(cols, rows, **u8)]
+    for L, margin in ((1024, 0), (16, 2)):
+        bank = F.MetaBank([F.E4M3, F.E5M2], L)
+        recipe = F.Recipe(F.FORMAT_HYBRID, L, F.AMAX_MAX, margin)
+        om = [oracle.Meta(L, 0), oracle.Meta(L, 1)]
+        for call in range(4 if not big else 2):
+            xin = x if call % 2 == 0 else x * 3      # the amax changes between calls
+            Xin = X if call % 2 == 0 else np_of(xin)
+            F.fp8_cast_transpose_dual_update(xin, bank, recipe, ticket, *outs)
+            torch.cuda.synchronize()
+            tag = f"L {L} margin {margin} call {call}"
+            for i, fmt in enumerate((0, 1)):
+                wq, wqt = oracle.cast_transpose(Xin, fmt, om[fmt].scale)
+                assert_bits_equal(np_of(outs[2 * i]), wq, f"{tag} fmt {fmt} q")
+                del wq
+                assert_bits_equal(np_of(outs[2 * i + 1]), wqt, f"{tag} fmt {fmt} q^T")
+                del wqt
+                om[fmt].record(Xin)
+            oracle.update_metas(om, margin=margin)
+            for i in range(2):
+                assert_bits_equal(np_of(bank.amax_history[i]), om[i].hist, f"{tag} history {i}")
+                assert_bits_equal(np_of(bank.scale[i]), om[i].scale, f"{tag} scale {i}")
+                assert_bits_equal(np_of(bank.scale_inv[i]), om[i].scale_inv, f"{tag} scale_inv {i}")
+            assert int(ticket.item()) == 0, "ticket not left at zero"
