@@ -348,48 +348,76 @@ def quant_leg(F, torch, reps=50, first=10):
                         torch.empty(cols, rows, **u8))
     out = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda")
     words = torch.empty(4096, dtype=torch.int32, device="cuda")
-    F.timing_enable(8 * reps)
-    torch.cuda.synchronize()
-    for _ in range(reps):
-        F.fp8_amax(x, slot)
-        F.fp8_cast_transpose_dual_update(x, bank, recipe, ticket, q4, q4t, q5, q5t)
-        F.fp8_dequant(q4, F.E4M3, bank.scale_inv[0:1], out)
-        F.fp8_dequant(q5, F.E5M2, bank.scale_inv[1:2], out)
-        F.stream_probe(x, words, 0)
-        F.stream_probe(x, out, 1)
-    torch.cuda.synchronize()
-    rec = F.timing_read(8 * reps)
-    F.timing_enable(0)
-    per = {}
-    for kind, ms in rec:
-        per.setdefault(kind, []).append(ms)
-    per["dequant"] = [a + b for a, b in zip(per["dequant"][0::2], per["dequant"][1::2])]
-    per["stream_read"], per["stream_copy"] = per["stream"][0::2], per["stream"][1::2]
+    seq = [("amax", lambda: F.fp8_amax(x, slot)),
+           ("cast_transpose_dual_update", lambda: F.fp8_cast_transpose_dual_update(x, bank, recipe, ticket,
+                                                                                   q4, q4t, q5, q5t)),
+           ("dequant_both", lambda: (F.fp8_dequant(q4, F.E4M3, bank.scale_inv[0:1], out),
+                                     F.fp8_dequant(q5, F.E5M2, bank.scale_inv[1:2], out)))]
+    ceil = [("stream_read", lambda: F.stream_probe(x, words, 0)), ("stream_copy", lambda: F.stream_probe(x, out, 1)),
+            ("stream_copy_nt", lambda: F.stream_probe(x, out, 2))]
+    nbytes = {"amax": 2 * n, "cast_transpose_dual_update": (2 + 4) * n, "dequant_both": 2 * (1 + 2) * n,
+              "stream_read": 2 * n, "stream_copy": 2 * 2 * n, "stream_copy_nt": 2 * 2 * n}
 
-    def stat(kind, nbytes):
-        v = per[kind][first:]
+    def launches():
+        rec = F.timing_read(16 * reps)
+        F.timing_enable(0)
+        return [ms for _, ms in rec]
+
+    def stat(v, nb):
         mean = sum(v) / len(v)
         med = sorted(v)[len(v) // 2]
-        return {"mean_ms": round(mean, 4), "median_ms": round(med, 4), "bytes": nbytes,
-                "achieved_gbs": round(nbytes / (mean * 1e-3) / 1e9, 1),
-                "frac": round(nbytes / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        return {"mean_ms": round(mean, 4), "median_ms": round(med, 4), "bytes": nb,
+                "achieved_gbs": round(nb / (mean * 1e-3) / 1e9, 1),
+                "frac": round(nb / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
+    # (1) the configuration's sequence: per repetition amax, the fused cast-transpose
+    # with the update, dequant of both; per-kernel times from the library's events
+    F.timing_enable(16 * reps)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for r in range(reps):
+        for _, fn in seq:
+            fn()
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    v = launches()
+    per_rep = [ev[r].elapsed_time(ev[r + 1]) for r in range(first, reps)]
+    per = {"amax": v[0::4][first:], "cast_transpose_dual_update": v[1::4][first:],
+           "dequant_both": [a + b for a, b in zip(v[2::4], v[3::4])][first:]}
     res = {
         "workload": "bf16 16384x16384 (2^28 elements), row magnitudes 2^u, u~U[-20,10]; "
                     f"{reps} repetitions, mean of {first}..{reps - 1}",
-        "amax": stat("amax", 2 * n),
-        "cast_transpose_dual_update": stat("cast_transpose", (2 + 4) * n),
-        "dequant_both": stat("dequant", 2 * (1 + 2) * n),
-        "stream_read": stat("stream_read", 2 * n),
-        "stream_copy": stat("stream_copy", 2 * 2 * n),
-        "peak_gbs": PEAK_HBM_GBS,
-        "note": "cast_transpose_dual_update: amax + cast to E4M3 and E5M2 + both transposes + the two metas' scale "
-                "update (last workgroup), one launch; stream_read / stream_copy: the same 16-byte load/store "
-                "layout with no arithmetic, the measured ceiling",
+        "sequence_ms_per_repetition": round(sum(per_rep) / len(per_rep), 4),
     }
+    for k in per:
+        res[k] = stat(per[k], nbytes[k])
+    # (2) each kernel back to back with itself (its own write-backs included),
+    # beside the streaming read and copy kernels measured the same way
+    steady = {}
+    for name, fn in seq + ceil:
+        for _ in range(3):
+            fn()
+        F.timing_enable(16 * reps)
+        torch.cuda.synchronize()
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        w = launches()
+        if name == "dequant_both":
+            w = [a + b for a, b in zip(w[0::2], w[1::2])]
+        steady[name] = stat(w, nbytes[name])
+    copy_ceiling = max(steady["stream_copy"]["achieved_gbs"], steady["stream_copy_nt"]["achieved_gbs"])
     for k in ("amax", "cast_transpose_dual_update", "dequant_both"):
-        ceiling = res["stream_read" if k == "amax" else "stream_copy"]["achieved_gbs"]
-        res[k]["frac_of_stream_ceiling"] = round(res[k]["achieved_gbs"] / ceiling, 4)
+        ceiling = steady["stream_read"]["achieved_gbs"] if k == "amax" else copy_ceiling
+        steady[k]["frac_of_stream_ceiling"] = round(steady[k]["achieved_gbs"] / ceiling, 4)
+    res["steady_state"] = steady
+    res["peak_gbs"] = PEAK_HBM_GBS
+    res["note"] = ("cast_transpose_dual_update: amax + cast to E4M3 and E5M2 + both transposes + the two metas' "
+                   "scale update (last workgroup), one launch.  steady_state: each kernel 20 times back to back; "
+                   "stream_read / stream_copy / stream_copy_nt: the same 16-byte load/store layout with no arithmetic "
+                   "(the copy with plain or non-temporal stores), the measured ceiling (read for amax, the faster "
+                   "copy for the others)")
     del x, q4, q4t, q5, q5t, out
     torch.cuda.empty_cache()
     return res

@@ -256,7 +256,8 @@ __global__ void __launch_bounds__(64) k_clock_sample(unsigned long long* out, un
 // Streaming reference kernels (measurement aids, not steps of the method):
 // the same layout and grid as the elementwise kernels above, without their
 // arithmetic.  Read: every 16-byte vector of src is loaded and folded into an
-// xor per workgroup, written to dst[blockIdx.x] (one word).  Copy: dst = src.
+// xor per workgroup, written to dst[blockIdx.x] (one word).  Copy: dst = src,
+// with plain or non-temporal stores (the latter as the dequant kernel uses).
 __global__ void __launch_bounds__(kThreads) k_stream_read(const uint4* __restrict__ p, int64_t nvec,
                                                          uint32_t* __restrict__ dst) {
     __shared__ uint32_t red[kThreads / 64];
@@ -281,6 +282,7 @@ __global__ void __launch_bounds__(kThreads) k_stream_read(const uint4* __restric
     }
 }
 
+template <bool NT>
 __global__ void __launch_bounds__(kThreads) k_stream_copy(const uint4* __restrict__ p, int64_t nvec,
                                                          uint4* __restrict__ q) {
     const int lane = threadIdx.x & 63;
@@ -294,7 +296,10 @@ __global__ void __launch_bounds__(kThreads) k_stream_copy(const uint4* __restric
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t i = b + 64 * u + lane;
-            if (i < nvec) q[i] = v[u];
+            if (i < nvec) {
+                if constexpr (NT) store_nt(q + i, v[u]);
+                else q[i] = v[u];
+            }
         }
     }
 }
@@ -307,8 +312,11 @@ hipError_t launch_stream_probe(const void* src, void* dst, int64_t bytes, int mo
     if (mode == 0)
         hipLaunchKernelGGL(k_stream_read, dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(src), nvec,
                            static_cast<uint32_t*>(dst));
+    else if (mode == 1)
+        hipLaunchKernelGGL(k_stream_copy<false>, dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(src), nvec,
+                           static_cast<uint4*>(dst));
     else
-        hipLaunchKernelGGL(k_stream_copy, dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(src), nvec,
+        hipLaunchKernelGGL(k_stream_copy<true>, dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(src), nvec,
                            static_cast<uint4*>(dst));
     timing_after(s);
     return hipGetLastError();

@@ -556,7 +556,8 @@ int32_t fp8lin_clock_sample(uint64_t* out, int32_t wait_us, void* stream);
  * elementwise kernels' load/store layout reaches without their arithmetic.
  * mode 0 reads bytes of src (16-byte vectors, the same grid and layout as
  * fp8_amax) and writes one 32-bit word per workgroup to dst (at most 2048
- * words: dst holds 8 KiB); mode 1 copies bytes of src to dst.  bytes is a
+ * words: dst holds 8 KiB); mode 1 copies bytes of src to dst; mode 2 copies
+ * with non-temporal stores (the stores fp8_dequant uses).  bytes is a
  * multiple of 16; src, dst 16-byte aligned and not overlapping.  Timed as
  * FP8LIN_KIND_STREAM.
  */

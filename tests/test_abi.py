@@ -320,7 +320,7 @@ def test_dual_update_and_stream_probe_validation():
     assert _err(ok(q=P(1 << 40))) == F.ERR_ARG                       # output on the input
     sp = L.fp8lin_stream_probe
     sp.restype, sp.argtypes = ctypes.c_int32, [P, P, ctypes.c_int64, ctypes.c_int32, P]
-    assert _err(sp(A16, B16, 1024, 2, None)) == F.ERR_ARG
+    assert _err(sp(A16, B16, 1024, 3, None)) == F.ERR_ARG
     assert _err(sp(A16, B16, 1000, 0, None)) == F.ERR_SHAPE
     assert _err(sp(None, B16, 1024, 1, None)) == F.ERR_NULL
     assert _err(sp(ODD, B16, 1024, 1, None)) == F.ERR_ALIGN
