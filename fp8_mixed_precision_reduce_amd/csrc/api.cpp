@@ -722,6 +722,12 @@ int32_t check_attn_shape(const char* fn, int64_t batch, int64_t seq, int64_t hea
                     (long long)batch, (long long)heads, (long long)seq);
     if (batch > (1 << 20) || heads > (1 << 20) || seq > (1 << 24) || batch * seq * heads * 128 >= (int64_t(1) << 31))
         return fail(FP8LIN_ERR_SHAPE, "%s: batch*seq*heads*head_dim must be < 2^31", fn);
+    // The kernels stage tiles with buffer loads whose byte offsets, from the
+    // start of one (batch, head), stay below 2^31: a sequence of the qkv rows
+    // (3 * heads * 128 bf16 each) and 128 rows of a transposed operand (row
+    // length batch * seq bf16).
+    if (seq * heads * 768 >= (int64_t(1) << 31) || batch * seq * 256 >= (int64_t(1) << 31))
+        return fail(FP8LIN_ERR_SHAPE, "%s: seq*heads must be < 2796203 and batch*seq < 2^23", fn);
     *n = batch * seq * heads * 128;
     return FP8LIN_OK;
 }

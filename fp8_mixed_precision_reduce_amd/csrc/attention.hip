@@ -50,8 +50,6 @@ __device__ __forceinline__ int sigma(int i) { return (i & ~12) | ((i & 4) << 1) 
 
 __device__ __forceinline__ v8bf lds16(const uint8_t* p) { return __builtin_bit_cast(v8bf, *reinterpret_cast<const v4u*>(p)); }
 __device__ __forceinline__ v8bf as_bf(uint4 u) { return __builtin_bit_cast(v8bf, v4u{u.x, u.y, u.z, u.w}); }
-__device__ __forceinline__ v4u ldg16(const void* p) { return *reinterpret_cast<const v4u*>(p); }
-__device__ __forceinline__ void sts16(uint8_t* p, v4u v) { *reinterpret_cast<v4u*>(p) = v; }
 
 // Eight fp32 accumulators (registers r0 .. r0+7) to eight bf16, RNE.
 __device__ __forceinline__ v8bf pack8(const v16f& a, int r0) {
@@ -103,23 +101,36 @@ struct AttnShape {
 // ------------------------------------------------------------------ forward
 // Workgroup: WAVES waves, 32 queries each, of one (b, h).  Key blocks of 64 go
 // through three LDS buffers (K [64][256 B] and V^T [128][128 B] each), loaded
-// one block ahead through registers.
+// one block ahead by buffer loads that write the LDS directly.
 constexpr int kFwdK = 64;
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBuf = 64 * 256 + 128 * 128;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One wave-instruction of a tile DMA: 16 bytes per lane from the buffer at
+// byte offset off land at lds + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, off, 0, 0, 0);
+}
 
 template <int WAVES>
 __global__ void __launch_bounds__(64 * WAVES, 8 / WAVES)
 k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, uint16_t* __restrict__ ctx,
            float* __restrict__ lse, AttnShape sh) {
-    constexpr int THREADS = 64 * WAVES, BQ = 32 * WAVES, NCH = 1024 / THREADS;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[3 * kFwdBuf];
+    constexpr int BQ = 32 * WAVES, NI = 16 / WAVES;   // DMA wave-instructions per tile and wave
+    // three key-block buffers as separate arrays, the loop unrolled by three, so
+    // the compiler sees that the fragment reads never alias the DMA
+    __shared__ __attribute__((aligned(16))) uint8_t smem0[kFwdBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t smem1[kFwdBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t smem2[kFwdBuf];
     const int S = sh.seq, H = sh.heads;
     const int64_t BS = (int64_t)sh.batch * S, HD = (int64_t)H * kD, ld = 3 * HD;
     const int qblocks = S / BQ;
     const int id = xcd_block(blockIdx.x, gridDim.x);
     const int qb = id % qblocks, h = (id / qblocks) % H, b = id / (qblocks * H);
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+    const int t = threadIdx.x, lane = t & 63, g = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t tok0 = (int64_t)b * S;
     const int q = qb * BQ + w * 32 + l32;          // this lane's query
 
@@ -130,25 +141,26 @@ k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, ui
 #pragma unroll
         for (int st = 0; st < 8; ++st) qf[st] = as_bf(*reinterpret_cast<const uint4*>(qrow + 16 * st + 8 * g));
     }
-    // Tile loads: thread t moves 16-byte chunks t + THREADS u of K (1024 chunks)
-    // and of V^T (1024 chunks).
-    const uint16_t* kbase = qkv + tok0 * ld + HD + (int64_t)h * kD;
-    const uint16_t* vbase = vt + (int64_t)h * kD * BS + tok0;
-    v4u stk[NCH], stv[NCH];
-    auto load = [&](int k0) __attribute__((always_inline)) {
+    // Key-block DMA straight into the LDS (16 bytes per lane, lane l at base +
+    // 16 l): instruction u of wave w fills K rows 4 (w + WAVES u) .. +3 (256 B
+    // each) and V^T rows 8 (w + WAVES u) .. +7 (128 B each), each lane loading
+    // the logical chunk whose swizzled place is its own.
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(qkv + tok0 * ld + HD + (int64_t)h * kD), (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vt + (int64_t)h * kD * BS + tok0), (short)0, 0x7FFFFFFF, 0x00020000);
+    uint32_t o_k[NI], o_v[NI];
 #pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int c = t + u * THREADS;
-            stk[u] = ldg16(kbase + (int64_t)(k0 + (c >> 4)) * ld + (c & 15) * 8);
-            stv[u] = ldg16(vbase + (int64_t)(c >> 3) * BS + k0 + (c & 7) * 8);
-        }
-    };
-    auto store = [&](uint8_t* buf) __attribute__((always_inline)) {
+    for (int u = 0; u < NI; ++u) {
+        const int rk_ = 4 * (w + WAVES * u) + (lane >> 4), rv_ = 8 * (w + WAVES * u) + (lane >> 3);
+        o_k[u] = (uint32_t)(rk_ * ld + (((lane & 15) ^ (rk_ & 15)) * 8)) * 2;
+        o_v[u] = (uint32_t)(rv_ * BS + (((lane & 7) ^ ((rv_ >> 1) & 7)) * 8)) * 2;
+    }
+    auto dma = [&](int k0, uint8_t* buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int c = t + u * THREADS;
-            sts16(buf + off256(c >> 4, c & 15), stk[u]);
-            sts16(buf + 64 * 256 + off128(c >> 3, c & 7), stv[u]);
+        for (int u = 0; u < NI; ++u) {
+            dma16(rk, buf + 1024 * (w + WAVES * u), o_k[u] + (uint32_t)k0 * (uint32_t)ld * 2);
+            dma16(rv, buf + 64 * 256 + 1024 * (w + WAVES * u), o_v[u] + (uint32_t)k0 * 2);
         }
     };
 
@@ -165,13 +177,10 @@ k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, ui
     // core they share.  (Pairing w with w ^ 1 measured 5 % faster than no
     // shift; pairing w with w + 4 gained nothing.)  Three LDS buffers keep
     // block j - 1's V^T for the late waves while block j is used and block
-    // j + 1 is staged.
+    // j + 1 is loaded.
     const int nblk = S / kFwdK;
     const int row = sigma(l32);
     const bool late = (w & 1) != 0;
-    load(0);
-    store(smem);
-    __syncthreads();
     v8bf pl[4];                        // the late waves' P of the previous block
     auto pv = [&](const uint8_t* vb, const v8bf* pb) __attribute__((always_inline)) {
         // O^T += V^T P: keys 16 ks + 8 g + slot = registers 8 (ks & 1) + slot of tile ks / 2
@@ -180,12 +189,9 @@ k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, ui
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) o[dt] = mfma(lds16(vb + off128(32 * dt + l32, 2 * ks + g)), pb[ks], o[dt]);
     };
-    int bj = 0, bp = 2;                // buffers of blocks j and j - 1 (mod 3)
-    for (int j = 0; j < nblk; ++j) {
-        const int bn = bj == 2 ? 0 : bj + 1;
-        const uint8_t* buf = smem + bj * kFwdBuf;
-        if (j + 1 < nblk) load((j + 1) * kFwdK);
-        if (late && j > 0) pv(smem + bp * kFwdBuf + 64 * 256, pl);
+    auto step = [&](int j, const uint8_t* buf, const uint8_t* prev, uint8_t* nxt) __attribute__((always_inline)) {
+        if (j + 1 < nblk) dma((j + 1) * kFwdK, nxt);
+        if (late && j > 0) pv(prev + 64 * 256, pl);
         // S^T tiles: keys kt * 32 + sigma(i) of the block against the lane's query.
         v16f sc[2];
 #pragma unroll
@@ -233,12 +239,18 @@ k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, ui
         } else {
             pv(buf + 64 * 256, pb);
         }
-        if (j + 1 < nblk) store(smem + bn * kFwdBuf);
+        __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0): this wave's DMA of the next block landed
         __syncthreads();
-        bp = bj;
-        bj = bn;
+    };
+    dma(0, smem0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    for (int j = 0; j < nblk; j += 3) {
+        step(j, smem0, smem2, smem1);
+        if (j + 1 < nblk) step(j + 1, smem1, smem0, smem2);
+        if (j + 2 < nblk) step(j + 2, smem2, smem1, smem0);
     }
-    if (late) pv(smem + bp * kFwdBuf + 64 * 256, pl);
+    if (late) pv((nblk - 1) % 3 == 0 ? smem0 + 64 * 256 : (nblk - 1) % 3 == 1 ? smem1 + 64 * 256 : smem2 + 64 * 256, pl);
     const float ltot = pair_sum(lsum);
     const float inv = 1.0f / ltot;
     uint16_t* orow = ctx + (tok0 + q) * HD + (int64_t)h * kD;
@@ -317,9 +329,10 @@ k_attn_rowdot(const uint16_t* __restrict__ dctx, const uint16_t* __restrict__ ct
 
 // ------------------------------------------------------------ dK and dV
 // Workgroup: 8 waves, 256 keys of one (b, h), 32 per wave (each lane one key;
-// its K fragments in registers, the workgroup's V rows in LDS for the whole
-// kernel).  Query blocks of 32 go through a double-buffered LDS tile: Q and dO
-// [32][256 B], Q^T and dO^T [128][64 B], lse2 and Dq [32].
+// its K and V fragments in registers for the whole kernel).  Query blocks of
+// 32 go through a double-buffered LDS tile, loaded by buffer loads that write
+// the LDS directly: Q and dO [32][256 B], Q^T and dO^T [128][64 B], lse2 and
+// Dq [32].
 constexpr int kKvKeys = 256, kKvQ = 32, kKvThreads = 512;
 constexpr int kKvQt = 32 * 256, kKvBuf = 2 * 32 * 256 + 2 * 128 * 64 + 2 * 32 * 4;
 
@@ -327,53 +340,61 @@ __global__ void __launch_bounds__(kKvThreads, 1)
 k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx, const uint16_t* __restrict__ qt,
               const uint16_t* __restrict__ dot, const float* __restrict__ lse, const float* __restrict__ dq_rows,
               uint16_t* __restrict__ dqkv, AttnShape sh) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kKvBuf];
-    __shared__ __attribute__((aligned(16))) uint8_t vtile[kKvKeys * 256];
+    // two query-block buffers as separate arrays, the loop unrolled by two, so
+    // the compiler sees that the fragment reads of one never alias the DMA into
+    // the other
+    __shared__ __attribute__((aligned(16))) uint8_t smem0[kKvBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t smem1[kKvBuf];
     const int S = sh.seq, H = sh.heads;
     const int64_t BS = (int64_t)sh.batch * S, HD = (int64_t)H * kD, ld = 3 * HD;
     const int kblocks = S / kKvKeys;
     const int id = xcd_block(blockIdx.x, gridDim.x);
     const int kb = id % kblocks, h = (id / kblocks) % H, b = id / (kblocks * H);
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+    const int t = threadIdx.x, lane = t & 63, g = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t tok0 = (int64_t)b * S;
     const int key = kb * kKvKeys + w * 32 + l32;
 
-    v8bf kf[8];
+    // the wave's keys: K and V fragments in registers for the whole kernel
+    v8bf kf[8], vf[8];
     {
         const uint16_t* krow = qkv + (tok0 + key) * ld + HD + (int64_t)h * kD;
 #pragma unroll
-        for (int st = 0; st < 8; ++st) kf[st] = as_bf(*reinterpret_cast<const uint4*>(krow + 16 * st + 8 * g));
-        // the workgroup's 256 V rows: 4096 chunks of 16 bytes, 8 per thread
-        const uint16_t* vrows = qkv + (tok0 + kb * kKvKeys) * ld + 2 * HD + (int64_t)h * kD;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int c = t + u * kKvThreads;
-            sts16(vtile + off256(c >> 4, c & 15), ldg16(vrows + (int64_t)(c >> 4) * ld + (c & 15) * 8));
+        for (int st = 0; st < 8; ++st) {
+            kf[st] = as_bf(*reinterpret_cast<const uint4*>(krow + 16 * st + 8 * g));
+            vf[st] = as_bf(*reinterpret_cast<const uint4*>(krow + HD + 16 * st + 8 * g));
         }
     }
-    const int vrow = w * 32 + l32;
-    const uint16_t* qbase = qkv + tok0 * ld + (int64_t)h * kD;
-    const uint16_t* dobase = dctx + tok0 * HD + (int64_t)h * kD;
-    const uint16_t* qtbase = qt + (int64_t)h * kD * BS + tok0;
-    const uint16_t* dotbase = dot + (int64_t)h * kD * BS + tok0;
-    const float* lbase = lse + ((int64_t)b * H + h) * S;
-    const float* dbase = dq_rows + ((int64_t)b * H + h) * S;
-    // 16-byte chunks: 512 of Q (32 rows x 16), 512 of dO, 512 of Q^T (128 rows x 4),
-    // 512 of dO^T; thread t takes chunk t of each; threads 0..15 also lse2 and Dq.
-    v4u st0, st1, st2, st3, sv = {0u, 0u, 0u, 0u};
-    auto load = [&](int q0) __attribute__((always_inline)) {
-        st0 = ldg16(qbase + (int64_t)(q0 + (t >> 4)) * ld + (t & 15) * 8);
-        st1 = ldg16(dobase + (int64_t)(q0 + (t >> 4)) * HD + (t & 15) * 8);
-        st2 = ldg16(qtbase + (int64_t)(t >> 2) * BS + q0 + (t & 3) * 8);
-        st3 = ldg16(dotbase + (int64_t)(t >> 2) * BS + q0 + (t & 3) * 8);
-        if (t < 16) sv = ldg16(t < 8 ? lbase + q0 + 4 * t : dbase + q0 + 4 * (t - 8));
+    // Query-block DMA straight into the LDS (16 bytes per lane, lane l at
+    // base + 16 l): wave w fills Q and dO rows 4 w .. 4 w + 3 (256 B each) and
+    // Q^T and dO^T rows 16 w .. 16 w + 15 (64 B each); lane l loads the logical
+    // chunk whose swizzled place is its own.  Wave 0's lanes 0..15 also load the
+    // block's 32 lse2 and 32 Dq values.
+    const auto rs = [](const void* p) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7FFFFFFF, 0x00020000);
     };
-    auto store = [&](uint8_t* buf) __attribute__((always_inline)) {
-        sts16(buf + off256(t >> 4, t & 15), st0);
-        sts16(buf + kKvQt + off256(t >> 4, t & 15), st1);
-        sts16(buf + 2 * kKvQt + off64(t >> 2, t & 3), st2);
-        sts16(buf + 2 * kKvQt + 128 * 64 + off64(t >> 2, t & 3), st3);
-        if (t < 16) sts16(buf + 2 * kKvQt + 2 * 128 * 64 + 16 * t, sv);
+    const __amdgpu_buffer_rsrc_t rq = rs(qkv + tok0 * ld + (int64_t)h * kD);
+    const __amdgpu_buffer_rsrc_t rdo = rs(dctx + tok0 * HD + (int64_t)h * kD);
+    const __amdgpu_buffer_rsrc_t rqt = rs(qt + (int64_t)h * kD * BS + tok0);
+    const __amdgpu_buffer_rsrc_t rdot = rs(dot + (int64_t)h * kD * BS + tok0);
+    const __amdgpu_buffer_rsrc_t rl = rs(lse + ((int64_t)b * H + h) * S);
+    const __amdgpu_buffer_rsrc_t rd = rs(dq_rows + ((int64_t)b * H + h) * S);
+    const int r256 = 4 * w + (lane >> 4), c256 = (lane & 15) ^ (r256 & 15);
+    const int r64 = 16 * w + (lane >> 2), c64 = (lane & 3) ^ ((r64 >> 2) & 3);
+    const uint32_t o_q = (uint32_t)(r256 * ld + c256 * 8) * 2, o_do = (uint32_t)(r256 * HD + c256 * 8) * 2;
+    const uint32_t o_t = (uint32_t)(r64 * BS + c64 * 8) * 2;
+    auto dma = [&](int q0, uint8_t* buf) __attribute__((always_inline)) {
+        const uint32_t qrow = (uint32_t)q0;
+        dma16(rq, buf + 1024 * w, o_q + qrow * (uint32_t)ld * 2);
+        dma16(rdo, buf + kKvQt + 1024 * w, o_do + qrow * (uint32_t)HD * 2);
+        dma16(rqt, buf + 2 * kKvQt + 1024 * w, o_t + qrow * 2);
+        dma16(rdot, buf + 2 * kKvQt + 128 * 64 + 1024 * w, o_t + qrow * 2);
+        // (a buffer resource is wave-uniform: lse2 by lanes 0..7, Dq by lanes 8..15,
+        // which land 128 bytes further)
+        if (w == 0 && lane < 8)
+            dma16(rl, buf + 2 * kKvQt + 2 * 128 * 64, (qrow + 4 * (uint32_t)lane) * 4);
+        if (w == 0 && lane >= 8 && lane < 16)
+            dma16(rd, buf + 2 * kKvQt + 2 * 128 * 64, (qrow + 4 * (uint32_t)(lane - 8)) * 4);
     };
 
     v16f dk[4], dv[4];
@@ -383,17 +404,13 @@ k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dct
         for (int e = 0; e < 16; ++e) { dk[i][e] = 0.0f; dv[i][e] = 0.0f; }
 
     const int nblk = S / kKvQ;
-    load(0);
-    store(smem);
-    __syncthreads();
-    for (int j = 0; j < nblk; ++j) {
-        const uint8_t* buf = smem + (j & 1) * kKvBuf;
+    auto block = [&](int j, const uint8_t* buf, uint8_t* nxt) __attribute__((always_inline)) {
         const uint8_t* sq = buf;
         const uint8_t* sdo = buf + kKvQt;
         const uint8_t* sqt = buf + 2 * kKvQt;
         const uint8_t* sdot = sqt + 128 * 64;
         const float* sl = reinterpret_cast<const float*>(sqt + 2 * 128 * 64);
-        if (j + 1 < nblk) load((j + 1) * kKvQ);
+        if (j + 1 < nblk) dma((j + 1) * kKvQ, nxt);
         // S and dP tiles, rows = queries sigma(i) of the block, column = the lane's key.
         v16f s, dp;
 #pragma unroll
@@ -402,7 +419,7 @@ k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dct
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
             s = mfma(lds16(sq + off256(row, 2 * st + g)), kf[st], s);
-            dp = mfma(lds16(sdo + off256(row, 2 * st + g)), lds16(vtile + off256(vrow, 2 * st + g)), dp);
+            dp = mfma(lds16(sdo + off256(row, 2 * st + g)), vf[st], dp);
         }
         // register r holds query 16 (r / 8) + 8 g + r % 8 of the block: P and
         // dS for registers 8 hb .. 8 hb + 7 from 8 consecutive lse2 and Dq values
@@ -431,8 +448,15 @@ k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dct
                 dk[dt] = mfma(lds16(sqt + off64(32 * dt + l32, 2 * ks + g)), sb, dk[dt]);
             }
         }
-        if (j + 1 < nblk) store(smem + ((j + 1) & 1) * kKvBuf);
+        __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0): this wave's DMA of the next block landed
         __syncthreads();
+    };
+    dma(0, smem0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    for (int j = 0; j < nblk; j += 2) {
+        block(j, smem0, smem1);
+        if (j + 1 < nblk) block(j + 1, smem1, smem0);
     }
     // register r of tile dt holds d = 32 dt + 8 (r / 4) + 4 g + r % 4 of the lane's key
     uint16_t* krow = dqkv + (tok0 + key) * ld + HD + (int64_t)h * kD;
@@ -461,13 +485,15 @@ __global__ void __launch_bounds__(kQThreads, 1)
 k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx, const uint16_t* __restrict__ kt,
              const float* __restrict__ lse, const float* __restrict__ dq_rows, uint16_t* __restrict__ dqkv,
              AttnShape sh) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kQBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t smem0[kQBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t smem1[kQBuf];
     const int S = sh.seq, H = sh.heads;
     const int64_t BS = (int64_t)sh.batch * S, HD = (int64_t)H * kD, ld = 3 * HD;
     const int qblocks = S / kQQ;
     const int id = xcd_block(blockIdx.x, gridDim.x);
     const int qb = id % qblocks, h = (id / qblocks) % H, b = id / (qblocks * H);
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, l32 = lane & 31;
+    const int t = threadIdx.x, lane = t & 63, g = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t tok0 = (int64_t)b * S;
     const int q = qb * kQQ + w * 32 + l32;
 
@@ -483,19 +509,22 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
     }
     const float lq = lse[((int64_t)b * H + h) * S + q];
     const float dd = dq_rows[((int64_t)b * H + h) * S + q];
-    const uint16_t* kbase = qkv + tok0 * ld + HD + (int64_t)h * kD;
-    const uint16_t* ktbase = kt + (int64_t)h * kD * BS + tok0;
-    // 16-byte chunks: 512 of K (32 rows x 16), 512 of V, 512 of K^T (128 rows x 4).
-    v4u st0, st1, st2;
-    auto load = [&](int k0) __attribute__((always_inline)) {
-        st0 = ldg16(kbase + (int64_t)(k0 + (t >> 4)) * ld + (t & 15) * 8);
-        st1 = ldg16(kbase + HD + (int64_t)(k0 + (t >> 4)) * ld + (t & 15) * 8);
-        st2 = ldg16(ktbase + (int64_t)(t >> 2) * BS + k0 + (t & 3) * 8);
+    // Key-block DMA straight into the LDS: wave w fills K and V rows 4 w .. 4 w + 3
+    // (256 B each) and K^T rows 16 w .. 16 w + 15 (64 B each), each lane loading
+    // the logical chunk whose swizzled place is its own.
+    const auto rs = [](const void* p) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7FFFFFFF, 0x00020000);
     };
-    auto store = [&](uint8_t* buf) __attribute__((always_inline)) {
-        sts16(buf + off256(t >> 4, t & 15), st0);
-        sts16(buf + kQKt + off256(t >> 4, t & 15), st1);
-        sts16(buf + 2 * kQKt + off64(t >> 2, t & 3), st2);
+    const __amdgpu_buffer_rsrc_t rk = rs(qkv + tok0 * ld + HD + (int64_t)h * kD);
+    const __amdgpu_buffer_rsrc_t rkt = rs(kt + (int64_t)h * kD * BS + tok0);
+    const int r256 = 4 * w + (lane >> 4), c256 = (lane & 15) ^ (r256 & 15);
+    const int r64 = 16 * w + (lane >> 2), c64 = (lane & 3) ^ ((r64 >> 2) & 3);
+    const uint32_t o_k = (uint32_t)(r256 * ld + c256 * 8) * 2, o_t = (uint32_t)(r64 * BS + c64 * 8) * 2;
+    auto dma = [&](int k0, uint8_t* buf) __attribute__((always_inline)) {
+        const uint32_t kr = (uint32_t)k0;
+        dma16(rk, buf + 1024 * w, o_k + kr * (uint32_t)ld * 2);
+        dma16(rk, buf + kQKt + 1024 * w, o_k + kr * (uint32_t)ld * 2 + (uint32_t)HD * 2);
+        dma16(rkt, buf + 2 * kQKt + 1024 * w, o_t + kr * 2);
     };
 
     v16f acc[4];
@@ -505,12 +534,8 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
         for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
 
     const int nblk = S / kQK;
-    load(0);
-    store(smem);
-    __syncthreads();
-    for (int j = 0; j < nblk; ++j) {
-        const uint8_t* buf = smem + (j & 1) * kQBuf;
-        if (j + 1 < nblk) load((j + 1) * kQK);
+    auto block = [&](int j, const uint8_t* buf, uint8_t* nxt) __attribute__((always_inline)) {
+        if (j + 1 < nblk) dma((j + 1) * kQK, nxt);
         v16f s, dp;
 #pragma unroll
         for (int e = 0; e < 16; ++e) { s[e] = 0.0f; dp[e] = 0.0f; }
@@ -530,8 +555,15 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
             for (int dt = 0; dt < 4; ++dt)
                 acc[dt] = mfma(lds16(buf + 2 * kQKt + off64(32 * dt + l32, 2 * ks + g)), sb, acc[dt]);
         }
-        if (j + 1 < nblk) store(smem + ((j + 1) & 1) * kQBuf);
+        __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0): this wave's DMA of the next block landed
         __syncthreads();
+    };
+    dma(0, smem0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    for (int j = 0; j < nblk; j += 2) {
+        block(j, smem0, smem1);
+        if (j + 1 < nblk) block(j + 1, smem1, smem0);
     }
     uint16_t* qrow = dqkv + (tok0 + q) * ld + (int64_t)h * kD;
 #pragma unroll

@@ -499,7 +499,9 @@ int32_t fp8_sgd_step(float* w, const float* g, int64_t n, float lr, const float*
  * to bf16 as operands of the second products; outputs rounded to bf16 (RNE).
  * Inf/NaN inputs give unspecified (non-finite) outputs.
  * Supported: head_dim == 128 (else FP8LIN_ERR_UNSUPPORTED), seq a multiple of
- * 256, batch*seq*heads*128 < 2^31.
+ * 256, batch*seq*heads*128 < 2^31, seq*heads*768 < 2^31 and
+ * batch*seq*256 < 2^31 (byte offsets of the tile loads within one (batch,
+ * head)); other shapes give FP8LIN_ERR_SHAPE.
  * Workspaces (caller-owned device memory, 16-byte aligned, contents not
  * preserved): bf16_attention_workspace_bytes(batch, seq, heads, head_dim,
  * backward) bytes: the forward holds V^T, the backward Q^T, K^T, dO^T and

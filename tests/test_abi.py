@@ -248,6 +248,12 @@ def test_attention_validation():
     assert fwd(big[0], 1, 100, 2, 128, big[1], big[2], big[3], None) == F.ERR_SHAPE
     assert fwd(big[0], 0, 256, 2, 128, big[1], big[2], big[3], None) == F.ERR_SHAPE
     assert fwd(big[0], 1 << 12, 4096, 256, 128, big[1], big[2], big[3], None) == F.ERR_SHAPE
+    # tile-load byte offsets within one (batch, head) must stay below 2^31
+    assert ws_bytes(1, 1 << 16, 42, 128, 0) == 1 * (1 << 16) * 42 * 128 * 2
+    assert ws_bytes(1, 1 << 16, 43, 128, 0) == -1                    # seq*heads*768 >= 2^31
+    assert ws_bytes(1 << 7, 1 << 16, 1, 128, 0) == -1                # batch*seq*256 >= 2^31
+    assert ws_bytes((1 << 7) - 1, 1 << 16, 1, 128, 0) > 0
+    assert fwd(big[0], 1, 1 << 16, 43, 128, big[1], big[2], big[3], None) == F.ERR_SHAPE
     assert fwd(None, 1, 256, 2, 128, big[1], big[2], big[3], None) == F.ERR_NULL
     assert fwd(big[0], 1, 256, 2, 128, ODD, big[2], big[3], None) == F.ERR_ALIGN
     assert fwd(big[0], 1, 256, 2, 128, big[0], big[2], big[3], None) == F.ERR_ARG          # ctx on qkv
