@@ -31,6 +31,7 @@ ABI_VERSION = 5
 
 FUNCTIONS = [
     "fp8lin_abi_version", "fp8lin_last_error", "fp8lin_status_name", "fp8lin_dbias_workspace_bytes",
+    "fp8lin_count_saturation",
     "fp8_amax", "fp8_amax_scale_update", "fp8_scale_from_current_amax", "fp8_cast", "fp8_cast_transpose", "fp8_cast_transpose_dgelu",
     "fp8_cast_transpose_dbias_noalloc",
     "fp8_cast_transpose_dual", "fp8_cast_transpose_dual_update",
@@ -101,6 +102,7 @@ def _load():
         "fp8lin_last_error": (ctypes.c_char_p, []),
         "fp8lin_status_name": (ctypes.c_char_p, [I32]),
         "fp8lin_dbias_workspace_bytes": (I64, [I64, I64]),
+        "fp8lin_count_saturation": (I32, [P, P]),
         "fp8_amax": (I32, [P, I32, I64, P, P]),
         "fp8_amax_scale_update": (I32, [P, P, P, P, I32, ctypes.POINTER(Recipe), P]),
         "fp8_scale_from_current_amax": (I32, [P, P, P, P, I32, ctypes.POINTER(Recipe), P]),
@@ -214,6 +216,42 @@ class MetaBank:
     def update(self, recipe, stream=None):
         fp8_amax_scale_update(self.amax_history, self.scale, self.scale_inv, self.formats, recipe, stream)
 
+    def count_saturation(self, enable=True):
+        """Registers (enable) or removes one saturation counter per tensor:
+        self.saturated[i] then accumulates the codes that tensor i's casts
+        saturated (cleared by snapshot(clear=True))."""
+        if enable:
+            if getattr(self, "saturated", None) is None:
+                self.saturated = torch.zeros(len(self.formats), dtype=torch.int32, device=self.scale.device)
+            for i in range(len(self.formats)):
+                count_saturation(self.amax_history[i], self.saturated[i:i + 1])
+        else:
+            for i in range(len(self.formats)):
+                count_saturation(self.amax_history[i], None)
+            self.saturated = None
+
+    def __del__(self):
+        # a registration must not outlive the slot and counter it names
+        if getattr(self, "saturated", None) is not None:
+            try:
+                self.count_saturation(False)
+            except Exception:
+                pass
+
+    def snapshot(self, names=None, clear=True):
+        """Host copy of each tensor's amax slot 0 (between a step's casts and
+        its update: that step's amax), scale and inverse scale (the ones the
+        step's casts used) and, when counting, its saturated codes (cleared
+        for the next step unless clear is False)."""
+        amax = self.amax_history[:, 0].cpu().tolist()
+        scale, sinv = self.scale.cpu().tolist(), self.scale_inv.cpu().tolist()
+        sat = self.saturated.cpu().tolist() if getattr(self, "saturated", None) is not None else None
+        if sat is not None and clear:
+            self.saturated.zero_()
+        names = names or [str(i) for i in range(len(self.formats))]
+        return {n: {"amax": amax[i], "scale": scale[i], "scale_inv": sinv[i],
+                    **({"saturated": sat[i]} if sat is not None else {})} for i, n in enumerate(names)}
+
     def scale_from_current(self, recipe, stream=None):
         fp8_scale_from_current_amax(self.amax_history, self.scale, self.scale_inv, self.formats, recipe, stream)
 
@@ -252,6 +290,15 @@ class Saved:
 
 
 # ------------------------------------------------------------ entry points
+
+def count_saturation(amax_slot, counter):
+    """Registers a device int32 counter (one element; None unregisters) for
+    the casts that use amax_slot (a tensor whose first float is the slot, e.g.
+    a meta's amax_history): they add the number of elements they saturated."""
+    if counter is not None and (counter.dtype != torch.int32 or counter.numel() < 1 or not counter.is_cuda):
+        raise ValueError("count_saturation: counter must be a device int32 tensor")
+    _check(_lib.fp8lin_count_saturation(_p(amax_slot), _p(counter)))
+
 
 def fp8_amax(x, amax_slot, stream=None):
     _check(_lib.fp8_amax(_p(x), _dt(x), x.numel(), _p(amax_slot), _stream(stream)))

@@ -90,10 +90,24 @@ class Fp8MlpBlock:
     def update(self):
         self.bank.update(self.recipe)
 
-    def step(self):
+    def step(self, record=None):
+        """One step; with a list as `record`, appends the step's per-tensor
+        amax, scales and (when counting) saturated codes, taken before the
+        update (see metrics())."""
         self.forward()
         self.backward()
+        if record is not None:
+            record.append(self.metrics())
         self.update()
+
+    def count_saturation(self, enable=True):
+        """Opt-in saturated-code counters for the block's six tensors."""
+        self.bank.count_saturation(enable)
+
+    def metrics(self, clear=True):
+        """Host snapshot per tensor name: amax slot 0, scale, inverse scale and
+        (when counting) saturated codes since the last snapshot."""
+        return self.bank.snapshot(MLP_TENSORS, clear)
 
     def state_dict(self):
         """The block's training state: the delayed-scaling metas (its weights
@@ -261,10 +275,28 @@ class Fp8TransformerLayer:
         self.bank.update(self.recipe)
         fp8_sgd_step(self.master, self.grad, self.lr, self.ls_state)
 
-    def step(self, x=None):
+    def step(self, x=None, record=None):
+        """One step; with a list as `record`, appends the step's per-tensor
+        amax, scales and (when counting) saturated codes, taken before the
+        update (see metrics())."""
         self.forward(x)
         self.backward()
+        if record is not None:
+            record.append(self.metrics())
         self.update()
+
+    def count_saturation(self, enable=True):
+        """Opt-in saturated-code counters for the layer's twelve tensors."""
+        self.bank.count_saturation(enable)
+
+    def metrics(self, clear=True):
+        """Host snapshot per tensor name: amax slot 0 (between backward and
+        update: the step's amax), scale and inverse scale (the ones the step's
+        casts used), the loss scale S, and (when counting) saturated codes
+        since the last snapshot."""
+        m = self.bank.snapshot(LAYER_TENSORS, clear)
+        m["loss_scale"] = self.ls_state[0].item()
+        return m
 
     def state_dict(self):
         """Everything a training run carries from step to step: the fp32

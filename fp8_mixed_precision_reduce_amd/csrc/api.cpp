@@ -183,6 +183,52 @@ int32_t fp8lin_timing_read(int32_t* kinds, float* ms, int32_t max) {
 }
 
 // ------------------------------------------------------------------- amax
+// ------------------------------------------------------ saturation counters
+namespace {
+// Counters registered per amax slot, process-wide.  Looked up at each cast
+// launch; with none registered the lookup is one atomic load.
+constexpr int kMaxSatCounters = 256;
+struct SatEntry {
+    const float* slot;
+    uint32_t* counter;
+};
+std::mutex g_sat_mu;
+SatEntry g_sat[kMaxSatCounters];
+std::atomic<int> g_sat_n{0};
+
+uint32_t* sat_counter(const float* slot) {
+    if (!slot || g_sat_n.load(std::memory_order_acquire) == 0) return nullptr;
+    std::lock_guard<std::mutex> lk(g_sat_mu);
+    const int n = g_sat_n.load(std::memory_order_relaxed);
+    for (int i = 0; i < n; ++i)
+        if (g_sat[i].slot == slot) return g_sat[i].counter;
+    return nullptr;
+}
+}  // namespace
+
+int32_t fp8lin_count_saturation(const float* amax_slot, uint32_t* counter) {
+    const char* fn = "fp8lin_count_saturation";
+    if (!amax_slot) return fail(FP8LIN_ERR_NULL, "%s: null amax slot", fn);
+    if (!aligned(amax_slot, 4) || !aligned(counter, 4)) return fail(FP8LIN_ERR_ALIGN, "%s: misaligned pointer", fn);
+    std::lock_guard<std::mutex> lk(g_sat_mu);
+    const int n = g_sat_n.load(std::memory_order_relaxed);
+    for (int i = 0; i < n; ++i) {
+        if (g_sat[i].slot != amax_slot) continue;
+        if (counter) {
+            g_sat[i].counter = counter;
+        } else {
+            g_sat[i] = g_sat[n - 1];
+            g_sat_n.store(n - 1, std::memory_order_release);
+        }
+        return FP8LIN_OK;
+    }
+    if (!counter) return FP8LIN_OK;
+    if (n == kMaxSatCounters) return fail(FP8LIN_ERR_ARG, "%s: %d counters already registered", fn, n);
+    g_sat[n] = SatEntry{amax_slot, counter};
+    g_sat_n.store(n + 1, std::memory_order_release);
+    return FP8LIN_OK;
+}
+
 int32_t fp8_amax(const void* x, int32_t x_dtype, int64_t n, float* amax_slot, void* stream) {
     if (!is_hp(x_dtype)) return fail(FP8LIN_ERR_DTYPE, "fp8_amax: x_dtype %d must be F32 or BF16", x_dtype);
     if (n < 0 || n > kMaxElems) return fail(FP8LIN_ERR_SHAPE, "fp8_amax: n=%lld out of range", (long long)n);
@@ -247,7 +293,9 @@ int32_t fp8_cast(const void* x, int32_t x_dtype, int64_t n, int32_t fp8_dtype, c
         return fail(FP8LIN_ERR_ALIGN, "fp8_cast: misaligned pointer");
     if (overlap(x, n * elem_size(x_dtype), q, n))
         return fail(FP8LIN_ERR_ARG, "fp8_cast: output overlaps input");
-    return hip_status(launch_cast(x, x_dtype, n, fp8_dtype, scale, q, amax_slot, as_stream(stream)), "fp8_cast");
+    return hip_status(launch_cast(x, x_dtype, n, fp8_dtype, scale, q, amax_slot, as_stream(stream), SinvSnap{},
+                                  SatCounts{sat_counter(amax_slot)}),
+                      "fp8_cast");
 }
 
 namespace {
@@ -288,7 +336,8 @@ int32_t fp8_cast_transpose(const void* x, int32_t x_dtype, int64_t rows, int64_t
                                amax_slot, dbias, dbias_ws, nullptr);
     if (v != FP8LIN_OK) return v;
     return hip_status(launch_cast_transpose(x, nullptr, x_dtype, rows, cols, fp8_dtype, scale, q, q_t, amax_slot,
-                                            dbias, dbias_ws, nullptr, as_stream(stream)),
+                                            dbias, dbias_ws, nullptr, as_stream(stream), SinvSnap{},
+                                            SatCounts{sat_counter(amax_slot)}),
                       "fp8_cast_transpose");
 }
 
@@ -315,7 +364,8 @@ int32_t fp8_cast_transpose_dbias_noalloc(const void* x, int32_t x_dtype, int64_t
         if (e != hipSuccess) return hip_status(e, fn);
     }
     return hip_status(launch_cast_transpose(x, nullptr, x_dtype, rows, cols, fp8_dtype, scale, q, q_t, amax_slot,
-                                            dbias, ws, nullptr, as_stream(stream)),
+                                            dbias, ws, nullptr, as_stream(stream), SinvSnap{},
+                                            SatCounts{sat_counter(amax_slot)}),
                       fn);
 }
 
@@ -327,7 +377,8 @@ int32_t fp8_cast_transpose_dgelu(const void* dh, const void* z, int32_t x_dtype,
                                amax_slot, dbias, dbias_ws, dz_out);
     if (v != FP8LIN_OK) return v;
     return hip_status(launch_cast_transpose(dh, z, x_dtype, rows, cols, fp8_dtype, scale, q, q_t, amax_slot, dbias,
-                                            dbias_ws, dz_out, as_stream(stream)),
+                                            dbias_ws, dz_out, as_stream(stream), SinvSnap{},
+                                            SatCounts{sat_counter(amax_slot)}),
                       "fp8_cast_transpose_dgelu");
 }
 
@@ -351,7 +402,8 @@ int32_t fp8_cast_transpose_dual(const void* x, int32_t x_dtype, int64_t rows, in
         for (int j = 0; j < 2; ++j)
             if (overlap(a[i], n, b[j], n)) return fail(FP8LIN_ERR_ARG, "%s: outputs overlap", fn);
     return hip_status(launch_cast_transpose_dual(x, x_dtype, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, amax_slot_e4m3,
-                                                 scale_e5m2, q_e5m2, q_e5m2_t, amax_slot_e5m2, as_stream(stream)),
+                                                 scale_e5m2, q_e5m2, q_e5m2_t, amax_slot_e5m2, as_stream(stream),
+                                                 SatCounts{sat_counter(amax_slot_e4m3), sat_counter(amax_slot_e5m2)}),
                       fn);
 }
 
@@ -389,7 +441,9 @@ int32_t fp8_cast_transpose_dual_update(const void* x, int32_t x_dtype, int64_t r
     }
     return hip_status(launch_cast_transpose_dual_update(x, x_dtype, rows, cols, q_e4m3, q_e4m3_t, q_e5m2, q_e5m2_t,
                                                         amax_history, scale, scale_inv, (int32_t)L, recipe->margin,
-                                                        ticket, as_stream(stream)),
+                                                        ticket, as_stream(stream),
+                                                        SatCounts{sat_counter(amax_history),
+                                                                  sat_counter(amax_history + L)}),
                       fn);
 }
 
@@ -578,7 +632,8 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
             return hip_status(e, "fp8_linear_fwd: just-in-time scale of W");
         e = launch_cast_transpose_pair(x, w, x_dtype, m, k, n, k, FP8LIN_E4M3, mx->scale, saved->xq, saved->xq_t,
                                        jit ? nullptr : mx->amax_history, mw->scale, saved->wq, saved->wq_t,
-                                       jit ? nullptr : mw->amax_history, s, snap);
+                                       jit ? nullptr : mw->amax_history, s, snap,
+                                       SatCounts{sat_counter(mx->amax_history), sat_counter(mw->amax_history)});
         if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast X and W");
         return hip_status(launch_gemm(saved->xq, FP8LIN_E4M3, saved->wq, FP8LIN_E4M3, m, n, k, saved->sinv,
                                       saved->sinv + 1, bias, bias_dtype, epilogue | fast, y, y_dtype, y_aux, residual,
@@ -590,17 +645,19 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
         if (jit && (e = jit_scale(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx, recipe->margin, s)) != hipSuccess)
             return hip_status(e, "fp8_linear_fwd: just-in-time scale of X");
         float* xslot = jit ? nullptr : mx->amax_history;
+        const SatCounts xsat{sat_counter(mx->amax_history)};
         if (saved->xq_t) e = launch_cast_transpose(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx->scale, saved->xq,
-                                                   saved->xq_t, xslot, nullptr, nullptr, nullptr, s);
-        else e = launch_cast(x, x_dtype, m * k, FP8LIN_E4M3, mx->scale, saved->xq, xslot, s);
+                                                   saved->xq_t, xslot, nullptr, nullptr, nullptr, s, SinvSnap{}, xsat);
+        else e = launch_cast(x, x_dtype, m * k, FP8LIN_E4M3, mx->scale, saved->xq, xslot, s, SinvSnap{}, xsat);
         if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast X");
     }
     if (jit && (e = jit_scale(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw, recipe->margin, s)) != hipSuccess)
         return hip_status(e, "fp8_linear_fwd: just-in-time scale of W");
     float* wslot = jit ? nullptr : mw->amax_history;
+    const SatCounts wsat{sat_counter(mw->amax_history)};
     if (saved->wq_t) e = launch_cast_transpose(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw->scale, saved->wq,
-                                               saved->wq_t, wslot, nullptr, nullptr, nullptr, s, snap);
-    else e = launch_cast(w, w_dtype, n * k, FP8LIN_E4M3, mw->scale, saved->wq, wslot, s, snap);
+                                               saved->wq_t, wslot, nullptr, nullptr, nullptr, s, snap, wsat);
+    else e = launch_cast(w, w_dtype, n * k, FP8LIN_E4M3, mw->scale, saved->wq, wslot, s, snap, wsat);
     if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast W");
     if (n * k == 0) {
         e = launch_copy_scalars(mx->scale_inv, mw->scale_inv, saved->sinv, s);
@@ -658,7 +715,7 @@ int32_t fp8_linear_bwd(int64_t m, int64_t n, int64_t k, const void* dy, int32_t 
     if (jit && (e = jit_scale(dy, gelu_z, dy_dtype, m, n, gfmt, mdy, recipe->margin, s)) != hipSuccess)
         return hip_status(e, "fp8_linear_bwd: just-in-time scale of dY");
     e = launch_cast_transpose(dy, gelu_z, dy_dtype, m, n, gfmt, mdy->scale, qr, qt, jit ? nullptr : mdy->amax_history,
-                              dbias, dbias_ws, dz_out, s);
+                              dbias, dbias_ws, dz_out, s, SinvSnap{}, SatCounts{sat_counter(mdy->amax_history)});
     if (e != hipSuccess) return hip_status(e, "fp8_linear_bwd: cast dY");
     if (dx) {
         e = launch_gemm(dyq_ws, gfmt, saved->wq_t, FP8LIN_E4M3, m, k, n, mdy->scale_inv, saved->sinv + 1, nullptr,

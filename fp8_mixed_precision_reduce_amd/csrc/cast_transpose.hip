@@ -143,7 +143,7 @@ __global__ void __launch_bounds__(kThreads)
 k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64_t rows_a, int64_t cols_a,
                  int64_t tiles_ca, const float* __restrict__ scale_p, uint8_t* __restrict__ q_a,
                  uint8_t* __restrict__ qt_a, float* amax_slot, float* __restrict__ dbias_ws,
-                 void* __restrict__ dz_out, Second sec, SinvSnap snap, CtJob job_b, DualUpdate upd) {
+                 void* __restrict__ dz_out, Second sec, SinvSnap snap, CtJob job_b, DualUpdate upd, SatCounts sat) {
     static_assert(!PAIR || (!DGELU && !DBIAS && !DUAL), "the pair variant is a plain cast-transpose");
     using C = CtVec<DT>;
     constexpr int E = C::E, NP = C::NP;
@@ -175,6 +175,7 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
     const int64_t ntiles_a = ((rows_a + kTile - 1) / kTile) * tiles_ca;
     const int64_t ntiles = ntiles_a + (PAIR ? ((job_b.rows + kTile - 1) / kTile) * job_b.tiles_c : 0);
     uint32_t m_a = 0, m_b = 0;
+    uint32_t n_a = 0, n_b = 0;        // saturated elements (of the second tensor or format: n_b)
     for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
         const bool second = PAIR && tile_id >= ntiles_a;        // uniform per workgroup
         const void* const x = second ? job_b.x : x_a;
@@ -184,6 +185,7 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
         uint8_t* const q = second ? job_b.q : q_a;
         uint8_t* const qt = second ? job_b.qt : qt_a;
         const int64_t local_id = second ? tile_id - ntiles_a : tile_id;
+        const bool count = (second ? sat.b : sat.a) != nullptr;      // uniform per workgroup
         uint32_t m = 0;
         const int64_t tr = local_id / tiles_c, tc = local_id % tiles_c;
         const int64_t r0 = tr * kTile, c0 = tc * kTile;
@@ -249,6 +251,14 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
             }
             const int lds = lds_word(lrow, vc * (E / 4));
             const uint2 codes = enc_vec<FMT, E>(v, s);
+            if (count) {
+                const uint32_t c = sat_count<FMT, E>(v, s);
+                if (second) n_b += c;
+                else n_a += c;
+            }
+            if constexpr (DUAL) {
+                if (sat.b) n_b += sat_count<kE5M2, E>(v, s2);
+            }
             if constexpr (E == 8) {
                 if (q && ok) *reinterpret_cast<uint2*>(q + row * cols + col) = codes;
                 if (qt) *reinterpret_cast<uint2*>(tile + lds) = codes;
@@ -362,6 +372,10 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
             block_amax_merge(m_b, job_b.amax_slot, red);
         }
     }
+    if (sat.a) wave_count_add(n_a, sat.a);
+    if constexpr (DUAL || PAIR) {
+        if (sat.b) wave_count_add(n_b, sat.b);
+    }
 }
 
 // dbias[c] = sum over row tiles of the partials, in row-tile order.
@@ -377,7 +391,7 @@ k_dbias_reduce(const float* __restrict__ ws, int64_t tiles_r, int64_t cols, floa
 template <int DT, int FMT>
 hipError_t launch_dt_fmt(const void* x, const void* z, int64_t rows, int64_t cols, const float* scale,
                          uint8_t* q, uint8_t* qt, float* slot, float* dbias_ws, void* dz_out, hipStream_t s,
-                         SinvSnap snap) {
+                         SinvSnap snap, SatCounts sat) {
     const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
     const int64_t ntiles = tiles_r * tiles_c;
     const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
@@ -385,39 +399,39 @@ hipError_t launch_dt_fmt(const void* x, const void* z, int64_t rows, int64_t col
     const Second none{nullptr, nullptr, nullptr, nullptr};
     if (!dgelu && !dbias)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{});
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat);
     else if (!dgelu)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, true, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{});
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat);
     else if (!dbias)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, false, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{});
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat);
     else
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, true, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{});
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat);
     return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_dual_dt(const void* x, int64_t rows, int64_t cols, const float* scale4, uint8_t* q4,
-                          uint8_t* q4t, float* slot4, const Second& sec, hipStream_t s, DualUpdate upd = {}) {
+                          uint8_t* q4t, float* slot4, const Second& sec, hipStream_t s, DualUpdate upd, SatCounts sat) {
     const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
     const int64_t ntiles = tiles_r * tiles_c;
     const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
     hipLaunchKernelGGL((k_cast_transpose<DT, kE4M3, false, false, true>), grid, block, 0, s, x, nullptr, rows,
-                       cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec, SinvSnap{}, CtJob{}, upd);
+                       cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec, SinvSnap{}, CtJob{}, upd, sat);
     return hipGetLastError();
 }
 
 template <int DT, int FMT>
 hipError_t launch_pair_dt_fmt(const void* xa, int64_t rows, int64_t cols, const float* scale, uint8_t* q, uint8_t* qt,
-                              float* slot, const CtJob& b, hipStream_t s, SinvSnap snap) {
+                              float* slot, const CtJob& b, hipStream_t s, SinvSnap snap, SatCounts sat) {
     const int64_t tiles_c = (cols + kTile - 1) / kTile;
     const int64_t ntiles = ((rows + kTile - 1) / kTile) * tiles_c + ((b.rows + kTile - 1) / kTile) * b.tiles_c;
     const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
     const Second none{nullptr, nullptr, nullptr, nullptr};
     hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false, true>), grid, block, 0, s, xa, nullptr, rows,
-                       cols, tiles_c, scale, q, qt, slot, nullptr, nullptr, none, snap, b, DualUpdate{});
+                       cols, tiles_c, scale, q, qt, slot, nullptr, nullptr, none, snap, b, DualUpdate{}, sat);
     return hipGetLastError();
 }
 
@@ -463,7 +477,7 @@ hipError_t noalloc_scratch(hipStream_t s, float** out) {
 
 hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_t rows, int64_t cols, int fmt,
                                  const float* scale, uint8_t* q, uint8_t* qt, float* slot, float* dbias,
-                                 float* dbias_ws, void* dz_out, hipStream_t s, SinvSnap snap) {
+                                 float* dbias_ws, void* dz_out, hipStream_t s, SinvSnap snap, SatCounts sat) {
     if (rows == 0 || cols == 0) {
         if (dbias && cols > 0) return launch_zero_f32(dbias, cols, s);
         return hipSuccess;
@@ -472,13 +486,13 @@ hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_
     hipError_t e;
     timing_before(kKindCastT, s);
     if (dtype == kF32 && fmt == kE4M3)
-        e = launch_dt_fmt<kF32, kE4M3>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap);
+        e = launch_dt_fmt<kF32, kE4M3>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap, sat);
     else if (dtype == kF32)
-        e = launch_dt_fmt<kF32, kE5M2>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap);
+        e = launch_dt_fmt<kF32, kE5M2>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap, sat);
     else if (fmt == kE4M3)
-        e = launch_dt_fmt<kBF16, kE4M3>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap);
+        e = launch_dt_fmt<kBF16, kE4M3>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap, sat);
     else
-        e = launch_dt_fmt<kBF16, kE5M2>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap);
+        e = launch_dt_fmt<kBF16, kE5M2>(x, z, rows, cols, scale, q, qt, slot, ws, dz_out, s, snap, sat);
     timing_after(s);
     if (e != hipSuccess || !dbias) return e;
     const int64_t tiles_r = (rows + kTile - 1) / kTile;
@@ -491,13 +505,14 @@ hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_
 
 hipError_t launch_cast_transpose_dual(const void* x, int dtype, int64_t rows, int64_t cols, const float* scale_e4m3,
                                       uint8_t* q_e4m3, uint8_t* q_e4m3_t, float* slot_e4m3, const float* scale_e5m2,
-                                      uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* slot_e5m2, hipStream_t s) {
+                                      uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* slot_e5m2, hipStream_t s,
+                                      SatCounts sat) {
     if (rows == 0 || cols == 0) return hipSuccess;
     const Second sec{scale_e5m2, q_e5m2, q_e5m2_t, slot_e5m2};
     timing_before(kKindCastT, s);
     const hipError_t e = dtype == kF32
-        ? launch_dual_dt<kF32>(x, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, slot_e4m3, sec, s)
-        : launch_dual_dt<kBF16>(x, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, slot_e4m3, sec, s);
+        ? launch_dual_dt<kF32>(x, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, slot_e4m3, sec, s, DualUpdate{}, sat)
+        : launch_dual_dt<kBF16>(x, rows, cols, scale_e4m3, q_e4m3, q_e4m3_t, slot_e4m3, sec, s, DualUpdate{}, sat);
     timing_after(s);
     return e;
 }
@@ -505,7 +520,7 @@ hipError_t launch_cast_transpose_dual(const void* x, int dtype, int64_t rows, in
 hipError_t launch_cast_transpose_dual_update(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q_e4m3,
                                              uint8_t* q_e4m3_t, uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* hist,
                                              float* scale, float* sinv, int32_t L, int32_t margin,
-                                             unsigned int* ticket, hipStream_t s) {
+                                             unsigned int* ticket, hipStream_t s, SatCounts sat) {
     if (rows == 0 || cols == 0) {      // nothing to cast: the update alone
         const uint8_t fmts[2] = {kE4M3, kE5M2};
         return launch_scale_update(hist, scale, sinv, fmts, 2, L, margin, s);
@@ -514,8 +529,8 @@ hipError_t launch_cast_transpose_dual_update(const void* x, int dtype, int64_t r
     const DualUpdate upd{hist, scale, sinv, L, margin, ticket};
     timing_before(kKindCastT, s);
     const hipError_t e = dtype == kF32
-        ? launch_dual_dt<kF32>(x, rows, cols, scale, q_e4m3, q_e4m3_t, hist, sec, s, upd)
-        : launch_dual_dt<kBF16>(x, rows, cols, scale, q_e4m3, q_e4m3_t, hist, sec, s, upd);
+        ? launch_dual_dt<kF32>(x, rows, cols, scale, q_e4m3, q_e4m3_t, hist, sec, s, upd, sat)
+        : launch_dual_dt<kBF16>(x, rows, cols, scale, q_e4m3, q_e4m3_t, hist, sec, s, upd, sat);
     timing_after(s);
     return e;
 }
@@ -523,18 +538,18 @@ hipError_t launch_cast_transpose_dual_update(const void* x, int dtype, int64_t r
 hipError_t launch_cast_transpose_pair(const void* xa, const void* xb, int dtype, int64_t rows_a, int64_t cols_a,
                                       int64_t rows_b, int64_t cols_b, int fmt, const float* scale_a, uint8_t* q_a,
                                       uint8_t* qt_a, float* slot_a, const float* scale_b, uint8_t* q_b, uint8_t* qt_b,
-                                      float* slot_b, hipStream_t s, SinvSnap snap) {
+                                      float* slot_b, hipStream_t s, SinvSnap snap, SatCounts sat) {
     const CtJob b{xb, rows_b, cols_b, (cols_b + kTile - 1) / kTile, scale_b, q_b, qt_b, slot_b};
     hipError_t e;
     timing_before(kKindCastT, s);
     if (dtype == kF32 && fmt == kE4M3)
-        e = launch_pair_dt_fmt<kF32, kE4M3>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap);
+        e = launch_pair_dt_fmt<kF32, kE4M3>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap, sat);
     else if (dtype == kF32)
-        e = launch_pair_dt_fmt<kF32, kE5M2>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap);
+        e = launch_pair_dt_fmt<kF32, kE5M2>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap, sat);
     else if (fmt == kE4M3)
-        e = launch_pair_dt_fmt<kBF16, kE4M3>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap);
+        e = launch_pair_dt_fmt<kBF16, kE4M3>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap, sat);
     else
-        e = launch_pair_dt_fmt<kBF16, kE5M2>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap);
+        e = launch_pair_dt_fmt<kBF16, kE5M2>(xa, rows_a, cols_a, scale_a, q_a, qt_a, slot_a, b, s, snap, sat);
     timing_after(s);
     return e;
 }

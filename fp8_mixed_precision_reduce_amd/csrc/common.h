@@ -28,6 +28,14 @@ struct SinvSnap {
     const float* b;
     float* dst;
 };
+// Saturation counters of a cast (fp8lin_count_saturation): device counters
+// that the cast adds its number of saturated elements to -- those whose scaled
+// value fl32(x * scale) exceeds the format's largest finite magnitude, the
+// values the saturating encode clamps.  nullptr: not counted.
+struct SatCounts {
+    uint32_t* a = nullptr;     // the tensor (dual cast: its E4M3 copy; pair cast: the first tensor)
+    uint32_t* b = nullptr;     // dual cast: the E5M2 copy; pair cast: the second tensor
+};
 #ifdef __HIPCC__
 __device__ __forceinline__ void take_snapshot(const SinvSnap& snap) {
     if (snap.dst && blockIdx.x == 0 && threadIdx.x == 0) {
@@ -42,7 +50,7 @@ __device__ __forceinline__ void take_snapshot(const SinvSnap& snap) {
 // C entry points before these are called.
 hipError_t launch_amax(const void* x, int dtype, int64_t n, float* slot, hipStream_t s);
 hipError_t launch_cast(const void* x, int dtype, int64_t n, int fmt, const float* scale,
-                       uint8_t* q, float* slot, hipStream_t s, SinvSnap snap = {});
+                       uint8_t* q, float* slot, hipStream_t s, SinvSnap snap = {}, SatCounts sat = {});
 hipError_t launch_dequant(const uint8_t* q, int fmt, int64_t n, const float* sinv, void* out,
                           int out_dtype, hipStream_t s);
 hipError_t launch_scale_update(float* hist, float* scale, float* sinv, const uint8_t* fmts,
@@ -55,22 +63,24 @@ hipError_t launch_clock_sample(unsigned long long* out, int64_t ticks, hipStream
 hipError_t launch_stream_probe(const void* src, void* dst, int64_t bytes, int mode, hipStream_t s);
 hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_t rows, int64_t cols,
                                  int fmt, const float* scale, uint8_t* q, uint8_t* qt, float* slot,
-                                 float* dbias, float* dbias_ws, void* dz_out, hipStream_t s, SinvSnap snap = {});
+                                 float* dbias, float* dbias_ws, void* dz_out, hipStream_t s, SinvSnap snap = {},
+                                 SatCounts sat = {});
 // Two non-empty tensors of one element type cast to one format in one launch.
 hipError_t launch_cast_transpose_pair(const void* xa, const void* xb, int dtype, int64_t rows_a, int64_t cols_a,
                                       int64_t rows_b, int64_t cols_b, int fmt, const float* scale_a, uint8_t* q_a,
                                       uint8_t* qt_a, float* slot_a, const float* scale_b, uint8_t* q_b, uint8_t* qt_b,
-                                      float* slot_b, hipStream_t s, SinvSnap snap);
+                                      float* slot_b, hipStream_t s, SinvSnap snap, SatCounts sat = {});
 hipError_t launch_cast_transpose_dual(const void* x, int dtype, int64_t rows, int64_t cols, const float* scale_e4m3,
                                       uint8_t* q_e4m3, uint8_t* q_e4m3_t, float* slot_e4m3, const float* scale_e5m2,
-                                      uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* slot_e5m2, hipStream_t s);
+                                      uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* slot_e5m2, hipStream_t s,
+                                      SatCounts sat = {});
 // The dual-format cast-transpose into a bank of two metas (0: E4M3, 1: E5M2,
 // histories hist[2][L]) whose last workgroup then runs the scale update of
 // both; `ticket` is a device counter that is zero before and after.
 hipError_t launch_cast_transpose_dual_update(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q_e4m3,
                                              uint8_t* q_e4m3_t, uint8_t* q_e5m2, uint8_t* q_e5m2_t, float* hist,
                                              float* scale, float* sinv, int32_t L, int32_t margin,
-                                             unsigned int* ticket, hipStream_t s);
+                                             unsigned int* ticket, hipStream_t s, SatCounts sat = {});
 int64_t cast_transpose_dbias_ws_bytes(int64_t rows, int64_t cols);
 // The scratch array of fp8_cast_transpose_dbias_noalloc on the device of
 // stream s (its address is looked up once per device).
@@ -112,6 +122,23 @@ __device__ __forceinline__ float round_to_bf16(float v) {
 template <int FMT> struct Fp8Max;
 template <> struct Fp8Max<kE4M3> { static constexpr float value = 448.0f; };
 template <> struct Fp8Max<kE5M2> { static constexpr float value = 57344.0f; };
+
+// Number of the E values whose product with s exceeds the format's largest
+// finite magnitude (the same fp32 products the encode rounds; NaN not counted).
+template <int FMT, int E>
+__device__ __forceinline__ uint32_t sat_count(const float* v, float s) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) n += fabsf(v[j] * s) > Fp8Max<FMT>::value ? 1u : 0u;
+    return n;
+}
+
+// Sum a per-thread count over the wave and add it to a device counter (one
+// atomic per wave, none for a zero sum).  Every lane of the wave must call it.
+__device__ __forceinline__ void wave_count_add(uint32_t v, uint32_t* ctr) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0 && v != 0u) atomicAdd(ctr, v);
+}
 
 // Saturating clamp that lets NaN through: |p| >= max -> +-max.
 template <int FMT>

@@ -95,11 +95,13 @@ __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, i
 
 // Codes of the E elements of one vector, written with one store (4 or 8 bytes).
 template <int DT, int FMT>
-__device__ __forceinline__ void cast_vec(uint4 w, float s, uint8_t* q, int64_t i, uint32_t& m) {
+__device__ __forceinline__ void cast_vec(uint4 w, float s, uint8_t* q, int64_t i, uint32_t& m, bool count,
+                                         uint32_t& nsat) {
     constexpr int E = InVec<DT>::elems;
     float v[E];
     unpack_vec<DT>(w, v);
     m = max(m, absmax_vec<DT>(w));
+    if (count) nsat += sat_count<FMT, E>(v, s);
     if constexpr (E == 4) {
         reinterpret_cast<uint32_t*>(q)[i] = enc4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
     } else {
@@ -111,9 +113,11 @@ __device__ __forceinline__ void cast_vec(uint4 w, float s, uint8_t* q, int64_t i
 template <int DT, int FMT>
 __global__ void __launch_bounds__(kThreads)
 k_cast(const void* __restrict__ x, int64_t n, const float* __restrict__ scale_p, uint8_t* __restrict__ q,
-       float* slot, SinvSnap snap) {
+       float* slot, SinvSnap snap, uint32_t* sat) {
     __shared__ uint32_t red[kThreads / 64];
     take_snapshot(snap);
+    const bool count = sat != nullptr;
+    uint32_t nsat = 0;
     constexpr int E = InVec<DT>::elems;
     const float s = *scale_p;
     const uint4* p = static_cast<const uint4*>(x);
@@ -130,15 +134,17 @@ k_cast(const void* __restrict__ x, int64_t n, const float* __restrict__ scale_p,
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t i = b + 64 * u + lane;
-            if (i < nvec) cast_vec<DT, FMT>(v[u], s, q, i, m);
+            if (i < nvec) cast_vec<DT, FMT>(v[u], s, q, i, m, count, nsat);
         }
     }
     for (int64_t i = nvec * E + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
         const float v = load1<DT>(x, i);
         m = max(m, abs_bits(v));
         q[i] = (uint8_t)(enc4<FMT>(v * s, 0.0f, 0.0f, 0.0f) & 0xFFu);
+        if (count) nsat += sat_count<FMT, 1>(&v, s);
     }
     if (slot) block_amax_merge(m, slot, red);
+    if (count) wave_count_add(nsat, sat);
 }
 
 // Dequant: a lane decodes the codes of one 16-byte output vector per step (8
@@ -348,18 +354,18 @@ hipError_t launch_amax(const void* x, int dtype, int64_t n, float* slot, hipStre
 }
 
 hipError_t launch_cast(const void* x, int dtype, int64_t n, int fmt, const float* scale, uint8_t* q,
-                       float* slot, hipStream_t s, SinvSnap snap) {
+                       float* slot, hipStream_t s, SinvSnap snap, SatCounts sat) {
     if (n == 0) return hipSuccess;
     const int g = grid_vec(n / (dtype == kF32 ? 4 : 8));
     timing_before(kKindCast, s);
     if (dtype == kF32 && fmt == kE4M3)
-        hipLaunchKernelGGL((k_cast<kF32, kE4M3>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap);
+        hipLaunchKernelGGL((k_cast<kF32, kE4M3>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap, sat.a);
     else if (dtype == kF32)
-        hipLaunchKernelGGL((k_cast<kF32, kE5M2>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap);
+        hipLaunchKernelGGL((k_cast<kF32, kE5M2>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap, sat.a);
     else if (fmt == kE4M3)
-        hipLaunchKernelGGL((k_cast<kBF16, kE4M3>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap);
+        hipLaunchKernelGGL((k_cast<kBF16, kE4M3>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap, sat.a);
     else
-        hipLaunchKernelGGL((k_cast<kBF16, kE5M2>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap);
+        hipLaunchKernelGGL((k_cast<kBF16, kE5M2>), dim3(g), dim3(kThreads), 0, s, x, n, scale, q, slot, snap, sat.a);
     timing_after(s);
     return hipGetLastError();
 }

@@ -212,6 +212,34 @@ int32_t fp8_scale_from_current_amax(float* amax_history, float* scale, float* sc
                                     const fp8lin_recipe* recipe, void* stream);
 
 /*
+ * fp8lin_count_saturation -- opt-in count of saturated codes per tensor, for
+ * inspecting how a tensor's values sit against its scale ([TE-KR]
+ * "정확도(Precision)": FP8 results differ from higher-precision ones, and
+ * debugging needs to see where).  While a counter is registered for amax_slot
+ * (a tensor's amax slot: its history's slot 0), every cast of this library
+ * that uses that slot for the tensor -- fp8_cast, the fp8_cast_transpose
+ * family, and the casts inside fp8_linear_fwd / fp8_linear_bwd of the meta
+ * whose amax_history starts at amax_slot, also under just-in-time scaling --
+ * adds to *counter the number of elements whose scaled value fl32(x * scale)
+ * has a magnitude above the format's largest finite value (448 for E4M3,
+ * 57344 for E5M2): the elements the saturating encode clamped (NaN is not
+ * counted, +-Inf is).  The FP8 copy written by a GEMM epilogue (q_out) is not
+ * counted.  A dual-format cast counts each format into the counter of its own
+ * slot.
+ *   amax_slot  device float (the key; not dereferenced here)
+ *   counter    device uint32, 4-byte aligned, on the device the casts run
+ *              on; NULL removes the registration.  Counts accumulate: the
+ *              caller clears the counter between steps.  Registering a slot
+ *              again replaces its counter.
+ * Registrations are process-wide (every device and stream), at most 256 at a
+ * time (FP8LIN_ERR_ARG beyond); counting costs a compare per element and one
+ * atomic per wave in the casts it applies to, nothing elsewhere.  Remove a
+ * registration before freeing its slot or counter: a later cast whose amax
+ * slot reused the address would add into whatever then holds the counter's.
+ */
+int32_t fp8lin_count_saturation(const float* amax_slot, uint32_t* counter);
+
+/*
  * fp8_cast -- q = enc_F(fl32(x * scale)) elementwise, with amax(x) fused.
  * [TE-KR] "FP8 자동변환(Autocasting)": inputs are converted to FP8 and their
  * amax recorded in the same step; [TE-RU] section 3.  enc_F is the saturating

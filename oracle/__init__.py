@@ -68,6 +68,7 @@ def _load():
         "orc_amax": (F, [P, ctypes.c_int, I64]),
         "orc_scale_update": (None, [P, P, P, P, I32, I32, I32]),
         "orc_cast": (None, [P, ctypes.c_int, I64, ctypes.c_int, F, P]),
+        "orc_count_saturated": (I64, [P, ctypes.c_int, I64, ctypes.c_int, F]),
         "orc_cast_transpose": (None, [P, ctypes.c_int, I64, I64, ctypes.c_int, F, P, P]),
         "orc_transpose_u8": (None, [P, I64, I64, P]),
         "orc_dequant": (None, [P, ctypes.c_int, I64, F, P, ctypes.c_int]),
@@ -233,6 +234,14 @@ def cast(x, fmt, scale):
     q = np.empty(x.shape, dtype=np.uint8)
     _load().orc_cast(_ptr(x), _dtype_code(x), x.size, fmt, float(np.float32(scale)), _ptr(q))
     return q
+
+
+def count_saturated(x, fmt, scale):
+    """Number of elements whose fp32 product with scale exceeds the format's
+    largest finite magnitude (the ones the saturating cast clamps; NaN not
+    counted) -- [TE-KR] "정확도(Precision)"."""
+    x = _c(x)
+    return int(_load().orc_count_saturated(_ptr(x), _dtype_code(x), x.size, fmt, float(np.float32(scale))))
 
 
 def cast_transpose(x, fmt, scale):

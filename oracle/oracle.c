@@ -375,6 +375,22 @@ void orc_cast(const void* x, int dtype, int64_t n, int fmt, float scale, uint8_t
     }
 }
 
+/* Saturated elements of a cast: those whose fp32 product with the scale has a
+ * magnitude above the format's largest finite value -- the values the
+ * saturating encode clamps to +-max, where the FP8 copy parts most from the
+ * higher-precision tensor ([TE-KR] "정확도(Precision)").  NaN products are not
+ * counted, infinite ones are. */
+int64_t orc_count_saturated(const void* x, int dtype, int64_t n, int fmt, float scale) {
+    const double fmax = orc_fp8_max(fmt);
+    int64_t c = 0;
+#pragma omp parallel for schedule(static) reduction(+ : c)
+    for (int64_t i = 0; i < n; ++i) {
+        const float prod = load_elem(x, dtype, i) * scale;
+        if (fabs((double)prod) > fmax) ++c;
+    }
+    return c;
+}
+
 void orc_transpose_u8(const uint8_t* q, int64_t rows, int64_t cols, uint8_t* q_t) {
 #pragma omp parallel for schedule(static)
     for (int64_t c = 0; c < cols; ++c)

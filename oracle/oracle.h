@@ -66,6 +66,7 @@ void     orc_scale_update(float* hist, float* scale, float* scale_inv, const uin
 
 /* ---- cast, cast-transpose, dequant, column sums ---- */
 void     orc_cast(const void* x, int dtype, int64_t n, int fmt, float scale, uint8_t* q);
+int64_t  orc_count_saturated(const void* x, int dtype, int64_t n, int fmt, float scale);
 void     orc_cast_transpose(const void* x, int dtype, int64_t rows, int64_t cols, int fmt,
                             float scale, uint8_t* q, uint8_t* q_t);
 void     orc_transpose_u8(const uint8_t* q, int64_t rows, int64_t cols, uint8_t* q_t);

@@ -264,6 +264,31 @@ def test_attention_validation():
     assert bwd(big[0], big[1], big[2], big[3], 1, 512, 2, 96, big[4], big[5], None) == F.ERR_UNSUPPORTED
 
 
+def test_saturation_counter_registry():
+    """fp8lin_count_saturation keeps at most 256 registrations keyed by amax
+    slot; re-registering replaces, NULL removes (also for a slot never
+    registered); the pointers are not dereferenced."""
+    f = L.fp8lin_count_saturation
+    f.argtypes = [P, P]
+    slots = [P((1 << 40) + 4 * i) for i in range(257)]
+    ctrs = [P((1 << 41) + 4 * i) for i in range(257)]
+    try:
+        assert f(None, ctrs[0]) == F.ERR_NULL
+        assert f(slots[0], P((1 << 41) + 2)) == F.ERR_ALIGN
+        assert f(P((1 << 40) + 1), ctrs[0]) == F.ERR_ALIGN
+        for i in range(256):
+            assert f(slots[i], ctrs[i]) == F.OK
+        assert f(slots[256], ctrs[256]) == F.ERR_ARG and b"256" in L.fp8lin_last_error()
+        assert f(slots[3], ctrs[256]) == F.OK                 # replace: no new entry
+        assert f(slots[256], None) == F.OK                    # never registered
+        assert f(slots[5], None) == F.OK                      # frees one entry
+        assert f(slots[256], ctrs[256]) == F.OK
+    finally:
+        for i in range(257):
+            f(slots[i], None)
+    assert f(slots[0], ctrs[0]) == F.OK and f(slots[0], None) == F.OK
+
+
 def test_binding_checks_meta_buffers_against_the_recipe():
     """The binding refuses a history buffer whose shape differs from (tensors,
     recipe.history_len) before calling the library (the kernel would read and

@@ -121,32 +121,57 @@ def _check_attention(lay, ctx, dqkv, tag, heads_sample=((0, 0), (1, 37)), nrows=
 def _check_step(oracle, lay, om, ols, X, rows, wrows, tag):
     """One step of the layer (already run on the GPU up to the update) checked
     sub-step by sub-step; then the update is run on both sides and compared.
-    The layer's recipe decides delayed or just-in-time scaling."""
+    The layer's recipe decides delayed or just-in-time scaling.  With the
+    layer's saturation counters on, each tensor's count is checked against the
+    oracle's and the counts are returned (else None)."""
     jit = bool(lay.recipe.just_in_time)
     mt, sv = om, lay.saved
     W = {n: np_of(lay.w[n]) for n in LAYER_WEIGHTS}
+    # With the layer's saturation counters on: the oracle's count of each
+    # tensor's saturated elements, over the values its cast saw and the scale
+    # it used (after the sub-step's check, the oracle meta holds that scale).
+    counting = getattr(lay.bank, "saturated", None) is not None
+    want_sat, counts = {}, None
+
+    def sat(name, values):
+        if counting:
+            want_sat[name] = oracle.count_saturated(values, mt[name].fmt, mt[name].scale)
+
     f_q = _check_fwd(oracle, X, W["wqkv"], mt["x"], mt["wqkv"], sv["qkv"], lay.qkv, rows, tag + " QKV", jit=jit)
+    sat("x", X)
+    sat("wqkv", W["wqkv"])
     ctx = np_of(lay.ctx)
     f_o = _check_fwd(oracle, ctx, W["wo"], mt["ctx"], mt["wo"], sv["o"], lay.y1, rows, tag + " O", residual=X, jit=jit)
+    sat("ctx", ctx)
+    sat("wo", W["wo"])
     Y1 = np_of(lay.y1)
     f_1 = _check_fwd(oracle, Y1, W["w1"], mt["y1"], mt["w1"], sv["fc1"], lay.h, rows, tag + " FC1", z_gpu=lay.z, jit=jit)
-    f_2 = _check_fwd(oracle, np_of(lay.h), W["w2"], mt["h"], mt["w2"], sv["fc2"], lay.y, rows, tag + " FC2",
+    sat("y1", Y1)
+    sat("w1", W["w1"])
+    H = np_of(lay.h)
+    f_2 = _check_fwd(oracle, H, W["w2"], mt["h"], mt["w2"], sv["fc2"], lay.y, rows, tag + " FC2",
                      residual=Y1, jit=jit)
+    sat("h", H)
+    sat("w2", W["w2"])
+    del H
     S = np.float32(ols.state[0])
     assert_bits_equal(np_of(lay.ls_state), ols.state, tag + " loss-scale state before the update")
     dY = np_of(lay.dy)
     assert_bits_equal(dY, oracle.scale_by(np_of(lay.g), S), tag + " dY = G*S")
     _check_bwd(oracle, dY, mt["g_fc2"], f_2, lay.gws["fc2"], lay.dh, lay.dw["w2"], rows, wrows,
                tag + " bwd FC2", jit=jit)
+    sat("g_fc2", dY)
     dH, Z, dZ = np_of(lay.dh), np_of(lay.z), np_of(lay.dz)
     assert _bf16_ulps(dZ, oracle.gelu_bwd(dH, Z)).max() <= 1, tag + " dZ"
     del dH, Z
     _check_bwd(oracle, dZ, mt["g_fc1"], f_1, lay.gws["fc1"], lay.dy1, lay.dw["w1"], rows, wrows,
                tag + " bwd FC1", residual=dY, jit=jit)
+    sat("g_fc1", dZ)
     del dZ
     dY1 = np_of(lay.dy1)
     _check_bwd(oracle, dY1, mt["g_o"], f_o, lay.gws["o"], lay.dctx, lay.dw["wo"], rows, wrows,
                tag + " bwd O", jit=jit)
+    sat("g_o", dY1)
     dQ = np_of(lay.dqkv)
     if lay.heads is None:
         assert_bits_equal(dQ, oracle.scale_by(np_of(lay.dqkv_in), S), tag + " dqkv*S")
@@ -154,8 +179,14 @@ def _check_step(oracle, lay, om, ols, X, rows, wrows, tag):
         _check_attention(lay, ctx, dQ, tag)
     _check_bwd(oracle, dQ, mt["g_qkv"], f_q, lay.gws["qkv"], lay.dx, lay.dw["wqkv"], rows, wrows,
                tag + " bwd QKV", residual=dY1, jit=jit)
+    sat("g_qkv", dQ)
     for i, name in enumerate(LAYER_TENSORS):
         assert_bits_equal(np_of(lay.bank.amax_history[i, 0]), om[name].hist[0], f"{tag} amax {name}")
+    if counting:
+        got = lay.metrics()          # the step's counts (cleared for the next step)
+        for name in LAYER_TENSORS:
+            assert got[name]["saturated"] == want_sat[name], (tag, name, got[name]["saturated"], want_sat[name])
+        counts = {n: got[n]["saturated"] for n in LAYER_TENSORS}
     # update: loss scale from the four gradient amaxes, the twelve metas, SGD
     grads = np_of(lay.grad)
     masters = np_of(lay.master)
@@ -170,6 +201,7 @@ def _check_step(oracle, lay, om, ols, X, rows, wrows, tag):
         assert_bits_equal(np_of(lay.bank.scale[i]), om[name].scale, f"{tag} scale {name}")
         assert_bits_equal(np_of(lay.bank.scale_inv[i]), om[name].scale_inv, f"{tag} scale_inv {name}")
     assert_bits_equal(np_of(lay.master), masters, tag + " masters after SGD")
+    return counts
 
 
 def _layer(inp, history_len, **kw):
@@ -180,18 +212,28 @@ def _layer(inp, history_len, **kw):
 def test_layer_small_attention_with_spike(oracle):
     """The layer with its bf16 attention core: 2 sequences of 256 tokens, two
     heads of 128 (hidden 256), FFN 464 (ragged), history 16; steps 0..4 with the
-    x100 spike at step 2."""
+    x100 spike at step 2.  The library's saturation counters are on: every
+    tensor's count per step equals the oracle's; X saturates only at the spike
+    (the scale from the clean history), and there for most of its elements."""
     inp = {k: v.cuda() for k, v in synth.layer_inputs(device="cpu", m=512, hidden=256, ffn=464).items()}
     lay = _layer(inp, 16, heads=2, batch=2)
     om, ols = oracle.layer_metas(16), oracle.LossScale(2.0 ** 16, interval=5)
     spiked = synth.layer_spike(inp["x"])
-    for step in range(5):
-        x_in = spiked if step == 2 else inp["x"]
-        lay.forward(x_in)
-        lay.backward()
-        torch.cuda.synchronize()
-        _check_step(oracle, lay, om, ols, np_of(x_in), None, None, f"attention step {step}")
+    lay.count_saturation()
+    try:
+        x_sat = []
+        for step in range(5):
+            x_in = spiked if step == 2 else inp["x"]
+            lay.forward(x_in)
+            lay.backward()
+            torch.cuda.synchronize()
+            counts = _check_step(oracle, lay, om, ols, np_of(x_in), None, None, f"attention step {step}")
+            x_sat.append(counts["x"])
+    finally:
+        lay.count_saturation(False)
     assert om["x"].hist[3] == oracle.amax(np_of(spiked))    # the spike's amax, rolled by three updates
+    print("saturated codes of X per step:", x_sat, flush=True)
+    assert x_sat[:2] == [0, 0] and x_sat[3:] == [0, 0] and x_sat[2] > spiked.numel() // 2
 
 
 def _oracle_state_from(oracle, lay):
@@ -314,23 +356,28 @@ def test_layer_spike_just_in_time_versus_delayed(oracle):
     for jit in (False, True):
         lay = _layer(inp, 16)
         om, ols = oracle.layer_metas(16), oracle.LossScale(2.0 ** 16, interval=5)
-        for step in range(3):
-            lay.forward()
+        lay.count_saturation()          # the saturated-code counts come from the library's casts
+        try:
+            for step in range(3):
+                lay.forward()
+                lay.backward()
+                torch.cuda.synchronize()
+                _check_step(oracle, lay, om, ols, np_of(inp["x"]), None, None, f"jit={jit} step {step}")
+            lay.recipe.just_in_time = int(jit)
+            lay.forward(spiked)
             lay.backward()
             torch.cuda.synchronize()
-            _check_step(oracle, lay, om, ols, np_of(inp["x"]), None, None, f"jit={jit} step {step}")
-        lay.recipe.just_in_time = int(jit)
-        lay.forward(spiked)
-        lay.backward()
-        torch.cuda.synchronize()
-        _check_step(oracle, lay, om, ols, S, None, None, f"jit={jit} spike step")
+            counts = _check_step(oracle, lay, om, ols, S, None, None, f"jit={jit} spike step")
+        finally:
+            lay.count_saturation(False)
         codes = np_of(lay.saved["qkv"].xq)
         deq = oracle.bf16_to_f64(oracle.dequant(codes, E4, np.float32(np_of(lay.saved["qkv"].sinv)[0]), 1))
         xs = oracle.bf16_to_f64(S)
-        res[jit] = (int(np.count_nonzero((codes & 0x7F) == 0x7E)), np.linalg.norm(deq - xs) / np.linalg.norm(xs))
+        res[jit] = (counts["x"], np.linalg.norm(deq - xs) / np.linalg.norm(xs))
     print(f"spike step: delayed saturated {res[False][0]} codes, error {res[False][1]:.3e}; "
           f"just-in-time saturated {res[True][0]}, error {res[True][1]:.3e}", flush=True)
-    assert res[False][0] > 0.5 * S.size and res[True][0] <= 2
+    # just in time, the largest element maps to the top code exactly: nothing is clamped
+    assert res[False][0] > 0.5 * S.size and res[True][0] == 0
     assert res[True][1] < 0.1 * res[False][1]
 
 

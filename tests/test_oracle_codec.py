@@ -170,6 +170,39 @@ def test_saturation(oracle, fmt, maxc, mx):
         assert code == (0x7F | (0x80 if nan_bits >> 31 else 0))
 
 
+@pytest.mark.parametrize("fmt,mx", [(0, 448.0), (1, 57344.0)])
+def test_count_saturated(oracle, fmt, mx):
+    """The saturated-element count: planted products at the boundary (exactly
+    the maximum is exact, not clamped; one step above is clamped), +-Inf
+    counted, NaN and zero not, for fp32 and bf16 inputs; then, on random
+    data spanning the boundary, the count equals the number of products that
+    the encoder maps to the top code while lying above the maximum, and the
+    count of numpy's fp32 products above it."""
+    s = np.float32(128.0)                        # power of two: the planted products are exact
+    at = np.float32(mx / 128.0)                  # 3.5 (E4M3) and 448 (E5M2): bf16-exact
+    above = np.float32(np.nextafter(at, np.float32(np.inf)))
+    above_bf16 = np.float32(at + (2.0 ** (math.floor(math.log2(at)) - 7)))   # one bf16 step up
+    planted = np.array([at, -at, above, -above, np.inf, -np.inf, np.nan, 0.0, -0.0, 1e30, 1.0], dtype=np.float32)
+    assert oracle.count_saturated(planted, fmt, s) == 5          # +-above, +-inf, 1e30 (fp32 product 1.28e32)
+    assert oracle.count_saturated(planted[:2], fmt, s) == 0
+    planted16 = np.array([at, -at, above_bf16, -above_bf16, np.inf, np.nan, 0.0], dtype=np.float32)
+    bits = oracle.bf16_from_f32(planted16)
+    assert np.array_equal(oracle.bf16_to_f64(bits), planted16.astype(np.float64), equal_nan=True)
+    assert oracle.count_saturated(bits, fmt, s) == 3
+    assert oracle.count_saturated(np.zeros(0, dtype=np.float32), fmt, s) == 0
+    rng = np.random.default_rng(19)
+    x = (rng.standard_normal(1 << 16) * (mx / 3.0)).astype(np.float32)
+    sc = np.float32(1.37)
+    p = x * sc                                   # numpy's fp32 products (IEEE RNE)
+    top = 0x7E if fmt == 0 else 0x7B
+    codes = oracle.encode_array(p, fmt) & 0x7F
+    want = int(np.count_nonzero(np.abs(p) > np.float32(mx)))
+    assert want > 100
+    assert oracle.count_saturated(x, fmt, sc) == want
+    assert want == int(np.count_nonzero((codes == top) & (np.abs(p) > np.float32(mx))))
+    assert int(np.count_nonzero(codes == top)) >= want
+
+
 # ------------------------------------------- textbook formats via library ----
 
 def _pattern_set(n_random, seed):
