@@ -257,14 +257,16 @@ def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
     return out
 
 
-def linear768_leg(F, torch, iters=200):
+def linear768_leg(F, torch, iters=200, steps_per_graph=20):
     """The 768-wide linear (1024 x 768 x 768, fp32 in and out, history 16): one
     forward step (amax + cast of X and W, FP8 GEMM with bias, scale update) and
     one forward + backward step in HYBRID (adds the E5M2 cast-transpose of dY,
     dgrad and wgrad), each timed launched one call at a time (eager) and
-    replayed from a captured HIP graph.  At 1.2 GFLOP per GEMM these steps are
-    bound by launch latency, not by the matrix cores or HBM, so they are
-    reported in microseconds per step."""
+    replayed from a captured HIP graph of `steps_per_graph` consecutive steps
+    (one replay launches them all; a graph of a single step would time the
+    graph launch itself, which costs more than the step's few small kernels).
+    At 1.2 GFLOP per GEMM these steps are bound by launch latency, not by the
+    matrix cores or HBM, so they are reported in microseconds per step."""
     import synth
     m, n, k = 1024, 768, 768
     w, b = (t.cuda() for t in synth.linear768_weights())
@@ -285,28 +287,29 @@ def linear768_leg(F, torch, iters=200):
         F.fp8_linear_bwd(dy, k, recipe, bank.meta(2), saved, gq, gqt, dx, dw)
         bank.update(recipe)
 
-    def timed(fn, batches=5):
-        # median over batches of iters / batches steps: a one-off stall (a clock
-        # change, the first replay's upload) does not move the figure
+    def timed(fn, calls, batches=5):
+        # median over batches of `calls` calls (us per call): a one-off stall (a
+        # clock change, the first replay's upload) does not move the figure
         per = []
         for _ in range(batches):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             ev[0].record()
-            for _ in range(iters // batches):
+            for _ in range(calls):
                 fn()
             ev[1].record()
             torch.cuda.synchronize()
-            per.append(ev[0].elapsed_time(ev[1]) * 1e3 / (iters // batches))
+            per.append(ev[0].elapsed_time(ev[1]) * 1e3 / calls)
         return sorted(per)[batches // 2]
 
     out = {"workload": "linear 1024x768x768 fp32 in/out, E4M3 (forward) / HYBRID (forward+backward), "
-                       "history 16, launch-latency bound", "iterations": iters,
-           "statistic": "median over 5 batches of iterations / 5 steps"}
+                       "history 16, launch-latency bound", "iterations": iters, "steps_per_graph": steps_per_graph,
+           "statistic": "median over 5 batches of iterations / 5 steps (graph: replays of steps_per_graph "
+                        "steps, per step)"}
     for name, fn in (("forward", fwd), ("forward_backward", fwd_bwd)):
         for _ in range(5):
             fn()
         torch.cuda.synchronize()
-        eager = timed(fn)
+        eager = timed(fn, iters // 5)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -315,11 +318,12 @@ def linear768_leg(F, torch, iters=200):
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            fn()
-        for _ in range(5):
+            for _ in range(steps_per_graph):
+                fn()
+        for _ in range(3):
             g.replay()
         torch.cuda.synchronize()
-        graph = timed(g.replay)
+        graph = timed(g.replay, max(1, iters // (5 * steps_per_graph))) / steps_per_graph
         out[name] = {"us_per_step_eager": round(eager, 2), "us_per_step_graph": round(graph, 2)}
         del g
     return out
