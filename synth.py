@@ -1,9 +1,18 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
 
 This module holds only input recipes -- shapes, value distributions and seeds --
-and none of the FP8 method's arithmetic.  Values are drawn with torch's seeded
-generators (on the CPU for small tensors, on the GPU for large ones) and then
-rounded once to the element type.  Both the HIP path and the oracle consume the
+and none of the FP8 method's arithmetic.  Random values come from splitmix64
+used as a counter generator (Steele, Lea and Flood, "Fast splittable
+pseudorandom number generators", 2014): draw i of a seed is the splitmix64
+output of state seed + (i + 1) * 0x9E3779B97F4A7C15, computed with 64-bit
+integer operations that give the same integers on the CPU and the GPU and in
+any torch version.  A uniform value takes the top 24 bits (k / 2^24, exact in
+fp32); a normal value takes two draws, 53 bits each, through the Box-Muller
+transform in fp64 (sqrt(-2 ln u1) cos(2 pi u2), u1 in (0, 1]), is scaled in
+fp64 and rounded to fp32, then to the element type (a last-bit difference
+between two libraries' fp64 log or cos changes a value only where it straddles
+an fp32 rounding boundary).  Small tensors are drawn on the CPU, large ones on
+the GPU.  Both the HIP path and the oracle consume the
 same tensors (the oracle after a copy to the host).
 
 Seed of a tensor: 12345 + 1000 * config + 10 * iteration + tensor_id (12345 is
@@ -37,20 +46,52 @@ def seed_of(config, iteration, tensor_id):
     return SEED0 + 1000 * config + 10 * iteration + tensor_id
 
 
-def _gen(seed, device):
-    g = torch.Generator(device=device)
-    g.manual_seed(seed)
-    return g
+def _s64(v):
+    """A 64-bit pattern as the signed int64 torch stores."""
+    v &= (1 << 64) - 1
+    return v - (1 << 64) if v >> 63 else v
+
+
+_GAMMA, _M1, _M2 = _s64(0x9E3779B97F4A7C15), _s64(0xBF58476D1CE4E5B9), _s64(0x94D049BB133111EB)
+
+
+def _srl(z, s):
+    """Logical right shift of int64 patterns."""
+    return (z >> s) & ((1 << (64 - s)) - 1)
+
+
+def splitmix64(seed, n, device="cpu"):
+    """Draws 0 .. n-1 of the seed as int64 bit patterns (multiplication wraps
+    mod 2^64, as the generator's definition requires)."""
+    z = torch.arange(1, n + 1, dtype=torch.int64, device=device) * _GAMMA + _s64(seed)
+    z = (z ^ _srl(z, 30)) * _M1
+    z = (z ^ _srl(z, 27)) * _M2
+    return z ^ _srl(z, 31)
+
+
+def _numel(shape):
+    return math.prod(shape) if isinstance(shape, (tuple, list)) else int(shape)
 
 
 def uniform(shape, lo, hi, seed, dtype=torch.float32, device="cpu"):
-    u = torch.rand(shape, generator=_gen(seed, device), device=device, dtype=torch.float32)
-    return (u * (hi - lo) + lo).to(dtype)
+    u = _srl(splitmix64(seed, _numel(shape), device), 40).to(torch.float32) * 2.0 ** -24
+    return (u * (hi - lo) + lo).reshape(shape).to(dtype)
 
 
 def normal(shape, std, seed, dtype=torch.float32, device="cpu"):
-    x = torch.randn(shape, generator=_gen(seed, device), device=device, dtype=torch.float32)
-    return (x * std).to(dtype)
+    n = _numel(shape)
+    z = splitmix64(seed, 2 * n, device).view(n, 2)
+    u1 = (_srl(z[:, 0], 11).to(torch.float64) + 1.0) * 2.0 ** -53
+    u2 = _srl(z[:, 1], 11).to(torch.float64) * 2.0 ** -53
+    del z
+    x = torch.sqrt(-2.0 * torch.log(u1)) * torch.cos((2.0 * math.pi) * u2)
+    del u1, u2
+    return (x * std).to(torch.float32).reshape(shape).to(dtype)
+
+
+def permutation(n, seed):
+    """A seeded permutation of 0 .. n-1: the indices ordered by their draws."""
+    return torch.argsort(splitmix64(seed, n), stable=True)
 
 
 # ------------------------------------------------------------ linear768 ----
@@ -82,8 +123,7 @@ def mlp_inputs(iteration=0, device="cpu", m=8192, hidden=4096, ffn=14336):
     """X (with outlier channels), W1, W2 and the upstream gradient dY, all bf16."""
     x = normal((m, hidden), 1.0, seed_of(3, iteration, 0), device=device)
     n_out = round(0.001 * hidden)
-    perm = torch.randperm(hidden, generator=_gen(seed_of(3, 0, 9), "cpu"))
-    cols = perm[:n_out].to(device)
+    cols = permutation(hidden, seed_of(3, 0, 9))[:n_out].to(device)
     x[:, cols] *= 50.0
     x = x.to(torch.bfloat16)
     w1 = normal((ffn, hidden), 0.02, seed_of(3, 0, 1), torch.bfloat16, device)
@@ -94,8 +134,7 @@ def mlp_inputs(iteration=0, device="cpu", m=8192, hidden=4096, ffn=14336):
 
 def mlp_outlier_channels(hidden=4096):
     n_out = round(0.001 * hidden)
-    perm = torch.randperm(hidden, generator=_gen(seed_of(3, 0, 9), "cpu"))
-    return perm[:n_out]
+    return permutation(hidden, seed_of(3, 0, 9))[:n_out]
 
 
 # ---------------------------------------------------------------- quant ----
