@@ -89,7 +89,7 @@ def measure_clock(F, torch, run, window_ms):
 
 
 def _exit_multi_gpu(n):
-    print(f"bench.py runs on one GPU only (asked for {n}); the multi-GPU path is not part of this build.",
+    print(f"bench.py runs on one GPU only (asked for {n}): the library has no multi-GPU path.",
           file=sys.stderr, flush=True)
     sys.exit(2)
 

@@ -52,7 +52,7 @@ enum {
     FP8LIN_ERR_DTYPE = 4,       /* an element type or format is not accepted by this call */
     FP8LIN_ERR_ARG = 5,         /* any other invalid argument (flags, history length, margin, aliasing) */
     FP8LIN_ERR_HIP = 6,         /* the HIP runtime refused a launch */
-    FP8LIN_ERR_UNSUPPORTED = 7  /* a valid request this build does not implement */
+    FP8LIN_ERR_UNSUPPORTED = 7  /* a valid request the library does not implement */
 };
 
 /* Element types. */
