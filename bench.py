@@ -218,6 +218,8 @@ def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
     mean_ms = sum(per_it[2:]) / len(per_it[2:])
     n_sgd, t_sgd = kb.get("sgd", (0, 0.0))
     sgd_ms = t_sgd / n_sgd if n_sgd else float("nan")
+    sgd_step_ms = t_sgd / breakdown_steps
+    sgd_bytes = (14 if lay.fuse_sgd_cast else 12) * n_params
     mhz = measure_clock(F, torch, lambda: [lay.step() for _ in range(3)], 1.5 * mean_ms)
     n_g, t_g = kb.get("gemm", (1, float("nan")))
     gemm_tflops = gemm_flop * breakdown_steps / (t_g * 1e-3) / 1e12
@@ -249,8 +251,14 @@ def layer_leg(F, torch, fast_accum=False, iterations=20, breakdown_steps=3):
                                    "peak_at_measured_clock": round(PEAK_F16_TFLOPS * mhz / PEAK_CLOCK_MHZ, 1)},
                       "note": "forward (QK^T, PV) and backward (dP, dV, dQ, dK) products over the attention "
                               "kernels' event time; the transposes into the workspaces are under 'other'"},
-        "sgd": {"params": n_params, "avg_launch_ms": round(sgd_ms, 4),
-                "achieved_gbs": round(12.0 * n_params / (sgd_ms * 1e-3) / 1e9, 1), "peak_gbs": PEAK_HBM_GBS},
+        "sgd": {"params": n_params, "fused_with_weight_cast": lay.fuse_sgd_cast,
+                "launches_per_step": n_sgd // breakdown_steps, "avg_launch_ms": round(sgd_ms, 4),
+                "ms_per_step": round(sgd_step_ms, 4), "bytes_per_step": sgd_bytes,
+                "achieved_gbs": round(sgd_bytes / (sgd_step_ms * 1e-3) / 1e9, 1), "peak_gbs": PEAK_HBM_GBS,
+                "frac": round(sgd_bytes / (sgd_step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "note": "fused: fp8_sgd_step_cast per weight matrix (master read and written, gradient read, E4M3 "
+                        "codes written row-major and transposed: 14 B per parameter), the next forward taking W "
+                        "pre-cast; unfused: fp8_sgd_step over all masters (12 B per parameter)"},
     }
     del lay, inp, spiked
     torch.cuda.empty_cache()

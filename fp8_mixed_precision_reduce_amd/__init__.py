@@ -36,7 +36,7 @@ FUNCTIONS = [
     "fp8_cast_transpose_dbias_noalloc",
     "fp8_cast_transpose_dual", "fp8_cast_transpose_dual_update",
     "fp8_dequant", "fp8_gemm", "fp8_linear_fwd", "fp8_linear_bwd", "fp8_loss_scale_update",
-    "fp8_loss_scale_apply", "fp8_sgd_step", "fp8lin_timing_enable", "fp8lin_timing_read", "fp8lin_clock_sample", "fp8lin_stream_probe",
+    "fp8_loss_scale_apply", "fp8_sgd_step", "fp8_sgd_step_cast", "fp8lin_timing_enable", "fp8lin_timing_read", "fp8lin_clock_sample", "fp8lin_stream_probe",
     "bf16_attention_workspace_bytes", "bf16_attention_fwd", "bf16_attention_bwd",
 ]
 
@@ -123,6 +123,7 @@ def _load():
         "fp8_loss_scale_update": (I32, [P, I32, I64, P, I32, ctypes.c_float, ctypes.c_float, P]),
         "fp8_loss_scale_apply": (I32, [P, I32, I64, P, P, P]),
         "fp8_sgd_step": (I32, [P, P, I64, ctypes.c_float, P, P]),
+        "fp8_sgd_step_cast": (I32, [P, P, I64, I64, ctypes.c_float, P, P, P, P, P, P]),
         "fp8lin_timing_enable": (I32, [I32]),
         "bf16_attention_workspace_bytes": (I64, [I64, I64, I64, I64, I32]),
         "bf16_attention_fwd": (I32, [P, I64, I64, I64, I64, P, P, P, P]),
@@ -399,14 +400,16 @@ def fp8_gemm(a, a_fmt, b, b_fmt, sinv_a, sinv_b, d, bias=None, epilogue=0, aux=N
 def fp8_linear_fwd(x, w, y, recipe, mx, mw, saved, bias=None, epilogue=0, y_aux=None, residual=None,
                    y_amax_slot=None, y_q=None, stream=None):
     """x None: X's codes are already in saved (written by the producer's y_q).
+    w None: W's codes are already in saved (written by fp8_sgd_step_cast).
     y None: only the FP8 copy y_q is written (y_dtype bf16)."""
     m, k = saved.xq.shape if x is None else x.shape
-    n = w.shape[0]
+    n = saved.wq.shape[0] if w is None else w.shape[0]
     bias_dt = _dt(bias) if bias is not None else F32
     x_dt = _dt(x) if x is not None else BF16
     y_dt = _dt(y) if y is not None else BF16
     cx, cw, cs = mx.c(), mw.c(), saved.c()
-    _check(_lib.fp8_linear_fwd(m, n, k, _p(x), x_dt, _p(w), _dt(w), _p(bias), bias_dt, epilogue, _p(y), y_dt,
+    w_dt = _dt(w) if w is not None else F32
+    _check(_lib.fp8_linear_fwd(m, n, k, _p(x), x_dt, _p(w), w_dt, _p(bias), bias_dt, epilogue, _p(y), y_dt,
                                _p(y_aux), _p(residual), _p(y_amax_slot), _qref(y_q), ctypes.byref(recipe),
                                ctypes.byref(cx), ctypes.byref(cw), ctypes.byref(cs), _stream(stream)))
 
@@ -440,6 +443,17 @@ def fp8_sgd_step(w, g, lr, state, stream=None):
     if w.dtype != torch.float32 or g.dtype != torch.float32:
         raise TypeError("fp8_sgd_step: w and g must be float32")
     _check(_lib.fp8_sgd_step(_p(w), _p(g), w.numel(), lr, _p(state), _stream(stream)))
+
+
+def fp8_sgd_step_cast(w, g, lr, state, scale, q, q_t, amax_slot=None, stream=None):
+    """fp8_sgd_step on the fp32 weight matrix w [rows][cols] fused with its E4M3
+    cast-transpose for the next forward (codes q [rows][cols] or None, q_t
+    [cols][rows]; amax of the updated w max-merged into amax_slot)."""
+    if w.dtype != torch.float32 or g.dtype != torch.float32 or w.dim() != 2 or g.shape != w.shape:
+        raise TypeError("fp8_sgd_step_cast: w and g must be float32 matrices of one shape")
+    rows, cols = w.shape
+    _check(_lib.fp8_sgd_step_cast(_p(w), _p(g), rows, cols, lr, _p(state), _p(scale), _p(q), _p(q_t),
+                                  _p(amax_slot), _stream(stream)))
 
 
 def dbias_workspace_bytes(rows, cols):

@@ -30,7 +30,7 @@ import torch
 
 from . import (AMAX_MAX, E4M3, E5M2, EPI_GELU, FORMAT_HYBRID, MetaBank, QOut, Recipe, Saved, attention_workspace_bytes,
                bf16_attention_bwd, bf16_attention_fwd, fp8_linear_bwd, fp8_linear_fwd, fp8_loss_scale_apply,
-               fp8_loss_scale_update, fp8_sgd_step)
+               fp8_loss_scale_update, fp8_sgd_step, fp8_sgd_step_cast)
 
 MLP_TENSORS = ("x", "w1", "h", "w2", "dy", "dz")
 
@@ -149,10 +149,15 @@ class Fp8TransformerLayer:
     for the per-step history update after backward):
         fp8_loss_scale_update from the four gradient amax slots (Inf/NaN ->
         found_inf, S halves), fp8_amax_scale_update of the twelve metas, then
-        fp8_sgd_step on all masters at once (skipped on found_inf).
+        the SGD step on the masters (skipped on found_inf).  Under delayed
+        scaling (fuse_sgd_cast, the default) each weight's SGD step also casts
+        the updated master to E4M3 with the scale the update just set and
+        merges its amax into the rolled history, i.e. the cast the next
+        forward would make, done while the master is in registers
+        (fp8_sgd_step_cast); that forward then takes W pre-cast.  Otherwise
+        fp8_sgd_step runs on all masters at once and every forward casts W.
 
-    The masters live in one fp32 buffer and their gradients in another, so the
-    SGD step is one launch over all parameters.  x, g (and the stand-ins ctx,
+    The masters live in one fp32 buffer and their gradients in another.  x, g (and the stand-ins ctx,
     dqkv) are bf16 device tensors of the caller; forward(x_in) may take another
     input of x's shape (the spiked one).  Residual adds happen in the GEMM
     epilogues; with fuse_casts (delayed scaling only; off by default, see the
@@ -163,7 +168,7 @@ class Fp8TransformerLayer:
 
     def __init__(self, x, ctx, g, dqkv, wqkv, wo, w1, w2, history_len=1024, lr=2.0 ** -10, loss_scale=2.0 ** 16,
                  growth_interval=5, fast_accum=False, keep_dz=False, keep_codes=False, fuse_casts=False,
-                 keep_h=False, heads=None, batch=1):
+                 keep_h=False, heads=None, batch=1, fuse_sgd_cast=True):
         m, hid = x.shape
         ffn = w1.shape[0]
         assert wqkv.shape == (3 * hid, hid) and wo.shape == (hid, hid) and w1.shape == (ffn, hid)
@@ -189,6 +194,8 @@ class Fp8TransformerLayer:
             off += n          # every size is a multiple of 256 elements: the views stay 16-byte aligned
         act = dict(dtype=x.dtype, device=dev)
         self.fuse_casts = fuse_casts and x.dtype == torch.bfloat16
+        self.fuse_sgd_cast = fuse_sgd_cast
+        self._w_cast = False        # the saved W codes hold the masters cast with the current W scales
         self.qkv = torch.empty(m, 3 * hid, **act)
         self.y1 = torch.empty(m, hid, **act)
         self.z = torch.empty(m, ffn, **act)
@@ -233,7 +240,10 @@ class Fp8TransformerLayer:
 
     def forward(self, x=None):
         x = self.x if x is None else x
-        r, mt, sv, w = self.recipe, self.meta, self.saved, self.w
+        r, mt, sv = self.recipe, self.meta, self.saved
+        # W is passed as None where the last update already cast it (delayed scaling)
+        pre = self._w_cast and not r.just_in_time
+        w = {n: (None if pre else t) for n, t in self.w.items()}
         fp8_linear_fwd(x, w["wqkv"], self.qkv, r, mt["x"], mt["wqkv"], sv["qkv"])
         if self.heads is not None:
             bf16_attention_fwd(self.qkv, self.batch, self.heads, self.ctx, self.lse, self.attn_ws)
@@ -273,7 +283,15 @@ class Fp8TransformerLayer:
         fp8_loss_scale_update(self._grad_amaxes, self.ls_state, stride=self.bank.history_len, n=len(LAYER_GRADS),
                               growth_interval=self.growth_interval)
         self.bank.update(self.recipe)
-        fp8_sgd_step(self.master, self.grad, self.lr, self.ls_state)
+        if self.fuse_sgd_cast and not self.recipe.just_in_time:
+            mt, sv = self.meta, self.saved
+            for name, lin in zip(LAYER_WEIGHTS, ("qkv", "o", "fc1", "fc2")):
+                fp8_sgd_step_cast(self.w[name], self.dw[name], self.lr, self.ls_state, mt[name].scale, sv[lin].wq,
+                                  sv[lin].wq_t, mt[name].amax_history[0:1])
+            self._w_cast = True
+        else:
+            fp8_sgd_step(self.master, self.grad, self.lr, self.ls_state)
+            self._w_cast = False
 
     def step(self, x=None, record=None):
         """One step; with a list as `record`, appends the step's per-tensor
@@ -314,6 +332,7 @@ class Fp8TransformerLayer:
         self.master.copy_(state["master"])
         self.bank.load_state_dict(state["bank"])
         self.ls_state.copy_(state["ls_state"])
+        self._w_cast = False        # the next forward casts W from the restored masters
 
     def flops_per_step(self):
         """Algorithmic flops of one step: the twelve FP8 GEMMs (2 m n k each)

@@ -590,9 +590,9 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
         return fail(FP8LIN_ERR_SHAPE, "%s: m=%lld n=%lld k=%lld must be >= 0 multiples of 16", fn, (long long)m,
                     (long long)n, (long long)k);
     const bool x_quantised = x == nullptr;      // X's codes are already in saved (cast by the producer)
-    if (x_quantised && recipe->just_in_time)
-        return fail(FP8LIN_ERR_ARG, "%s: a pre-quantised X cannot be scaled just in time", fn);
-    if (n * k > 0 && !w) return fail(FP8LIN_ERR_NULL, "%s: null w", fn);
+    const bool w_quantised = w == nullptr;      // W's codes are already in saved (cast by fp8_sgd_step_cast)
+    if ((x_quantised || w_quantised) && recipe->just_in_time)
+        return fail(FP8LIN_ERR_ARG, "%s: a pre-quantised X or W cannot be scaled just in time", fn);
     if (!aligned(saved->sinv, 4)) return fail(FP8LIN_ERR_ALIGN, "%s: saved->sinv misaligned", fn);
     // Validate every sub-call before launching any of them.
     if (!x_quantised && (v = check_ct(fn, x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx->scale, saved->xq, saved->xq_t,
@@ -600,9 +600,11 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
         return v;
     if (x_quantised && (!aligned(saved->xq, 16) || !aligned(saved->xq_t, 16)))
         return fail(FP8LIN_ERR_ALIGN, "%s: saved codes misaligned", fn);
-    if ((v = check_ct(fn, w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw->scale, saved->wq, saved->wq_t,
-                      mw->amax_history, nullptr, nullptr, nullptr, false)))
+    if (!w_quantised && (v = check_ct(fn, w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw->scale, saved->wq, saved->wq_t,
+                                      mw->amax_history, nullptr, nullptr, nullptr, false)))
         return v;
+    if (w_quantised && (!aligned(saved->wq, 16) || !aligned(saved->wq_t, 16)))
+        return fail(FP8LIN_ERR_ALIGN, "%s: saved codes misaligned", fn);
     if ((v = check_gemm(fn, saved->xq, FP8LIN_E4M3, saved->wq, FP8LIN_E4M3, m, n, k, saved->sinv, saved->sinv + 1,
                         bias, bias_dtype, epilogue | fast, y, y_dtype, y_aux, residual, y_amax_slot, y_q)))
         return v;
@@ -624,7 +626,7 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
     // the W cast also snapshots the two inverse scales into saved->sinv (an
     // empty W launches no cast, so a one-thread copy does it)
     const SinvSnap snap{mx->scale_inv, mw->scale_inv, saved->sinv};
-    if (!x_quantised && saved->xq_t && saved->wq_t && x_dtype == w_dtype && m * k > 0 && n * k > 0) {
+    if (!x_quantised && !w_quantised && saved->xq_t && saved->wq_t && x_dtype == w_dtype && m * k > 0 && n * k > 0) {
         // X and W in one launch (same kernel variant, independent tensors)
         if (jit && (e = jit_scale(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx, recipe->margin, s)) != hipSuccess)
             return hip_status(e, "fp8_linear_fwd: just-in-time scale of X");
@@ -641,25 +643,31 @@ int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k, const void* x, int32_t x
                                       y_q ? y_q->q_t : nullptr, y_q ? y_q->fp8_dtype : 0, s),
                           "fp8_linear_fwd: gemm");
     }
+    // the snapshot of the inverse scales rides on the last cast of the call
+    // (none of an empty tensor), else a one-thread copy takes it
+    const bool w_cast = !w_quantised && n * k > 0;
     if (!x_quantised) {
         if (jit && (e = jit_scale(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx, recipe->margin, s)) != hipSuccess)
             return hip_status(e, "fp8_linear_fwd: just-in-time scale of X");
         float* xslot = jit ? nullptr : mx->amax_history;
         const SatCounts xsat{sat_counter(mx->amax_history)};
+        const SinvSnap xsnap = !w_cast && m * k > 0 ? snap : SinvSnap{};
         if (saved->xq_t) e = launch_cast_transpose(x, nullptr, x_dtype, m, k, FP8LIN_E4M3, mx->scale, saved->xq,
-                                                   saved->xq_t, xslot, nullptr, nullptr, nullptr, s, SinvSnap{}, xsat);
-        else e = launch_cast(x, x_dtype, m * k, FP8LIN_E4M3, mx->scale, saved->xq, xslot, s, SinvSnap{}, xsat);
+                                                   saved->xq_t, xslot, nullptr, nullptr, nullptr, s, xsnap, xsat);
+        else e = launch_cast(x, x_dtype, m * k, FP8LIN_E4M3, mx->scale, saved->xq, xslot, s, xsnap, xsat);
         if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast X");
     }
-    if (jit && (e = jit_scale(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw, recipe->margin, s)) != hipSuccess)
-        return hip_status(e, "fp8_linear_fwd: just-in-time scale of W");
-    float* wslot = jit ? nullptr : mw->amax_history;
-    const SatCounts wsat{sat_counter(mw->amax_history)};
-    if (saved->wq_t) e = launch_cast_transpose(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw->scale, saved->wq,
-                                               saved->wq_t, wslot, nullptr, nullptr, nullptr, s, snap, wsat);
-    else e = launch_cast(w, w_dtype, n * k, FP8LIN_E4M3, mw->scale, saved->wq, wslot, s, snap, wsat);
-    if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast W");
-    if (n * k == 0) {
+    if (!w_quantised) {
+        if (jit && (e = jit_scale(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw, recipe->margin, s)) != hipSuccess)
+            return hip_status(e, "fp8_linear_fwd: just-in-time scale of W");
+        float* wslot = jit ? nullptr : mw->amax_history;
+        const SatCounts wsat{sat_counter(mw->amax_history)};
+        if (saved->wq_t) e = launch_cast_transpose(w, nullptr, w_dtype, n, k, FP8LIN_E4M3, mw->scale, saved->wq,
+                                                   saved->wq_t, wslot, nullptr, nullptr, nullptr, s, snap, wsat);
+        else e = launch_cast(w, w_dtype, n * k, FP8LIN_E4M3, mw->scale, saved->wq, wslot, s, snap, wsat);
+        if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: cast W");
+    }
+    if (!w_cast && (x_quantised || m * k == 0)) {
         e = launch_copy_scalars(mx->scale_inv, mw->scale_inv, saved->sinv, s);
         if (e != hipSuccess) return hip_status(e, "fp8_linear_fwd: save scale_inv");
     }
@@ -765,6 +773,29 @@ int32_t fp8_sgd_step(float* w, const float* g, int64_t n, float lr, const float*
     if (overlap(w, n * 4, g, n * 4) || overlap(w, n * 4, state, 16))
         return fail(FP8LIN_ERR_ARG, "%s: w overlaps g or the state", fn);
     return hip_status(launch_sgd(w, g, n, lr, state, as_stream(stream)), fn);
+}
+
+int32_t fp8_sgd_step_cast(float* w, const float* g, int64_t rows, int64_t cols, float lr, const float* state,
+                          const float* scale, uint8_t* q, uint8_t* q_t, float* amax_slot, void* stream) {
+    const char* fn = "fp8_sgd_step_cast";
+    int32_t v = check_ct(fn, w, nullptr, FP8LIN_F32, rows, cols, FP8LIN_E4M3, scale, q, q_t, amax_slot, nullptr,
+                         nullptr, nullptr);
+    if (v != FP8LIN_OK) return v;
+    const int64_t n = rows * cols;
+    if (!state || (n > 0 && !g)) return fail(FP8LIN_ERR_NULL, "%s: null pointer", fn);
+    if (!aligned(g, 16) || !aligned(state, 4)) return fail(FP8LIN_ERR_ALIGN, "%s: misaligned", fn);
+    // w is written: nothing else may share its bytes; g, state and scale are read
+    if (overlap(w, n * 4, g, n * 4) || overlap(w, n * 4, state, 16) || overlap(w, n * 4, scale, 4) ||
+        overlap(w, n * 4, amax_slot, 4))
+        return fail(FP8LIN_ERR_ARG, "%s: w overlaps g, the state, the scale or the amax slot", fn);
+    const void* outs[3] = {q, q_t, amax_slot};
+    const int64_t ob[3] = {n, n, 4};
+    for (int i = 0; i < 3; ++i)
+        if (overlap(outs[i], ob[i], g, n * 4) || overlap(outs[i], ob[i], state, 16))
+            return fail(FP8LIN_ERR_ARG, "%s: an output overlaps g or the state", fn);
+    return hip_status(launch_sgd_cast_transpose(w, g, rows, cols, lr, state, scale, q, q_t, amax_slot,
+                                                as_stream(stream), SatCounts{sat_counter(amax_slot)}),
+                      fn);
 }
 
 

@@ -138,13 +138,25 @@ struct DualUpdate {
     unsigned int* ticket;
 };
 
-template <int DT, int FMT, bool DGELU, bool DBIAS, bool DUAL, bool PAIR = false>
+// The optimizer step the SGD variant applies to an fp32 weight matrix before
+// casting it: w <- w - lr * (g * (1 / S)) in place (the arithmetic of
+// k_sgd), skipped when the step found Inf/NaN gradients (state[2] != 0).
+struct SgdPre {
+    float* w;
+    const float* g;
+    float lr;
+    const float* state;
+};
+
+template <int DT, int FMT, bool DGELU, bool DBIAS, bool DUAL, bool PAIR = false, bool SGD = false>
 __global__ void __launch_bounds__(kThreads)
 k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64_t rows_a, int64_t cols_a,
                  int64_t tiles_ca, const float* __restrict__ scale_p, uint8_t* __restrict__ q_a,
                  uint8_t* __restrict__ qt_a, float* amax_slot, float* __restrict__ dbias_ws,
-                 void* __restrict__ dz_out, Second sec, SinvSnap snap, CtJob job_b, DualUpdate upd, SatCounts sat) {
+                 void* __restrict__ dz_out, Second sec, SinvSnap snap, CtJob job_b, DualUpdate upd, SatCounts sat,
+                 SgdPre sgd) {
     static_assert(!PAIR || (!DGELU && !DBIAS && !DUAL), "the pair variant is a plain cast-transpose");
+    static_assert(!SGD || (DT == kF32 && !PAIR && !DGELU && !DBIAS && !DUAL), "the SGD variant casts fp32 weights");
     using C = CtVec<DT>;
     constexpr int E = C::E, NP = C::NP;
     constexpr int NF = DUAL ? 2 : 1;
@@ -172,6 +184,8 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
     const float s_a = *scale_p;
     const float s_b = PAIR ? *job_b.scale : 0.0f;
     const float s2 = DUAL ? *sec.scale : 0.0f;
+    const bool sgd_update = SGD && sgd.state[2] == 0.0f;                    // uniform: the step's found_inf
+    const float sgd_inv = SGD ? __fdiv_rn(1.0f, sgd.state[3]) : 0.0f;
     const int64_t ntiles_a = ((rows_a + kTile - 1) / kTile) * tiles_ca;
     const int64_t ntiles = ntiles_a + (PAIR ? ((job_b.rows + kTile - 1) / kTile) * job_b.tiles_c : 0);
     uint32_t m_a = 0, m_b = 0;
@@ -193,13 +207,40 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
         const bool col_ok = col < cols;
 
         uint4 rv[NP], rz[DGELU ? NP : 1];
+        if constexpr (SGD) {
+            // the weights (read and written through sgd.w, not x) and their gradients
+            uint4 rg[NP];
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int64_t row = r0 + r_first + C::RS * p;
-            const bool ok = col_ok && row < rows;
-            rv[p] = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) +
-                                                         (row * cols + col) * (DT == kF32 ? 4 : 2))
-                       : make_uint4(0, 0, 0, 0);
+            for (int p = 0; p < NP; ++p) {
+                const int64_t row = r0 + r_first + C::RS * p;
+                const bool ok = col_ok && row < rows;
+                rv[p] = ok ? *reinterpret_cast<const uint4*>(sgd.w + row * cols + col) : make_uint4(0, 0, 0, 0);
+                rg[p] = ok && sgd_update ? *reinterpret_cast<const uint4*>(sgd.g + row * cols + col)
+                                         : make_uint4(0, 0, 0, 0);
+            }
+            if (sgd_update) {
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    const int64_t row = r0 + r_first + C::RS * p;
+                    float4 wv = __builtin_bit_cast(float4, rv[p]);
+                    const float4 gv = __builtin_bit_cast(float4, rg[p]);
+                    wv.x = wv.x - sgd.lr * (gv.x * sgd_inv);
+                    wv.y = wv.y - sgd.lr * (gv.y * sgd_inv);
+                    wv.z = wv.z - sgd.lr * (gv.z * sgd_inv);
+                    wv.w = wv.w - sgd.lr * (gv.w * sgd_inv);
+                    rv[p] = __builtin_bit_cast(uint4, wv);
+                    if (col_ok && row < rows) *reinterpret_cast<float4*>(sgd.w + row * cols + col) = wv;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int64_t row = r0 + r_first + C::RS * p;
+                const bool ok = col_ok && row < rows;
+                rv[p] = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) +
+                                                             (row * cols + col) * (DT == kF32 ? 4 : 2))
+                           : make_uint4(0, 0, 0, 0);
+            }
         }
         if constexpr (DGELU) {
 #pragma unroll
@@ -399,16 +440,16 @@ hipError_t launch_dt_fmt(const void* x, const void* z, int64_t rows, int64_t col
     const Second none{nullptr, nullptr, nullptr, nullptr};
     if (!dgelu && !dbias)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat, SgdPre{});
     else if (!dgelu)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, true, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat, SgdPre{});
     else if (!dbias)
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, false, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat, SgdPre{});
     else
         hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, true, false>), grid, block, 0, s, x, z, rows, cols,
-                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat);
+                           tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat, SgdPre{});
     return hipGetLastError();
 }
 
@@ -419,7 +460,7 @@ hipError_t launch_dual_dt(const void* x, int64_t rows, int64_t cols, const float
     const int64_t ntiles = tiles_r * tiles_c;
     const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
     hipLaunchKernelGGL((k_cast_transpose<DT, kE4M3, false, false, true>), grid, block, 0, s, x, nullptr, rows,
-                       cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec, SinvSnap{}, CtJob{}, upd, sat);
+                       cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec, SinvSnap{}, CtJob{}, upd, sat, SgdPre{});
     return hipGetLastError();
 }
 
@@ -431,11 +472,27 @@ hipError_t launch_pair_dt_fmt(const void* xa, int64_t rows, int64_t cols, const 
     const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
     const Second none{nullptr, nullptr, nullptr, nullptr};
     hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false, true>), grid, block, 0, s, xa, nullptr, rows,
-                       cols, tiles_c, scale, q, qt, slot, nullptr, nullptr, none, snap, b, DualUpdate{}, sat);
+                       cols, tiles_c, scale, q, qt, slot, nullptr, nullptr, none, snap, b, DualUpdate{}, sat, SgdPre{});
     return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_sgd_cast_transpose(float* w, const float* g, int64_t rows, int64_t cols, float lr,
+                                     const float* state, const float* scale, uint8_t* q, uint8_t* qt, float* slot,
+                                     hipStream_t s, SatCounts sat) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
+    const int64_t ntiles = tiles_r * tiles_c;
+    const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
+    const Second none{nullptr, nullptr, nullptr, nullptr};
+    timing_before(kKindSgd, s);
+    hipLaunchKernelGGL((k_cast_transpose<kF32, kE4M3, false, false, false, false, true>), grid, block, 0, s, w,
+                       nullptr, rows, cols, tiles_c, scale, q, qt, slot, nullptr, nullptr, none, SinvSnap{}, CtJob{},
+                       DualUpdate{}, sat, SgdPre{w, g, lr, state});
+    timing_after(s);
+    return hipGetLastError();
+}
 
 int64_t cast_transpose_dbias_ws_bytes(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0) return 0;

@@ -65,6 +65,11 @@ hipError_t launch_cast_transpose(const void* x, const void* z, int dtype, int64_
                                  int fmt, const float* scale, uint8_t* q, uint8_t* qt, float* slot,
                                  float* dbias, float* dbias_ws, void* dz_out, hipStream_t s, SinvSnap snap = {},
                                  SatCounts sat = {});
+// The fp32 weight matrix w [rows][cols] updated by SGD (as launch_sgd) and
+// cast-transposed to E4M3 in the same pass (the cast the next forward needs).
+hipError_t launch_sgd_cast_transpose(float* w, const float* g, int64_t rows, int64_t cols, float lr,
+                                     const float* state, const float* scale, uint8_t* q, uint8_t* qt, float* slot,
+                                     hipStream_t s, SatCounts sat = {});
 // Two non-empty tensors of one element type cast to one format in one launch.
 hipError_t launch_cast_transpose_pair(const void* xa, const void* xb, int dtype, int64_t rows_a, int64_t cols_a,
                                       int64_t rows_b, int64_t cols_b, int fmt, const float* scale_a, uint8_t* q_a,

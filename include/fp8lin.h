@@ -420,7 +420,10 @@ int32_t fp8_gemm(const uint8_t* a, int32_t a_dtype, const uint8_t* b, int32_t b_
  *   saved     HOST struct of device pointers; xq, wq, sinv required
  * x may be NULL: X's codes are then already in saved->xq (and saved->xq_t),
  * cast with mx->scale by the producer's y_q; the call copies *mx->scale_inv
- * into saved->sinv[0] and records no amax of X (the producer did).  Not with
+ * into saved->sinv[0] and records no amax of X (the producer did).  w may be
+ * NULL likewise: W's codes are then already in saved->wq and saved->wq_t, cast
+ * with mw->scale by the previous step's fp8_sgd_step_cast, which also recorded
+ * W's amax; the call copies *mw->scale_inv into saved->sinv[1].  Neither with
  * recipe->just_in_time.
  */
 int32_t fp8_linear_fwd(int64_t m, int64_t n, int64_t k,
@@ -506,6 +509,31 @@ int32_t fp8_loss_scale_apply(const void* g, int32_t dtype, int64_t n, const floa
  *          weight gradient);  state  device float[4];  n >= 0
  */
 int32_t fp8_sgd_step(float* w, const float* g, int64_t n, float lr, const float* state, void* stream);
+
+/*
+ * fp8_sgd_step_cast -- fp8_sgd_step on one fp32 weight matrix fused with the
+ * E4M3 cast-transpose that the next forward makes of it: the master weight is
+ * read once, updated, written, and cast from registers.  [MP-KR] "FP32 Master
+ * Copy of Weights" (the update on the fp32 masters) and [TE-KR] "FP8
+ * 자동변환(Autocasting)" (cast and amax in one step): under delayed scaling the
+ * scale the next forward casts with is fixed by the metas' update, which runs
+ * before this call, so the cast need not wait for that forward.
+ *   w       device float[rows][cols], updated in place as fp8_sgd_step does
+ *           (a found_inf step leaves it and still casts it)
+ *   g       device float[rows][cols];  state  device float[4] (loss-scale state)
+ *   scale   device float: the E4M3 scale of W for the next forward (its meta's
+ *           scale after the update)
+ *   q       [rows][cols] codes, row-major, or NULL;  q_t  [cols][rows] codes
+ *   amax_slot device float or NULL: amax of the updated w is max-merged into it
+ *           (the meta's slot 0 after the update's roll)
+ * rows, cols >= 0, multiples of 16.  q and q_t equal fp8_cast_transpose of the
+ * updated w with the same scale bit for bit, and w equals fp8_sgd_step's
+ * result bit for bit.  The next fp8_linear_fwd then takes w = NULL (its W
+ * codes are in saved->wq / saved->wq_t).  Not for just-in-time scaling, whose
+ * scale comes from the updated w's own amax.
+ */
+int32_t fp8_sgd_step_cast(float* w, const float* g, int64_t rows, int64_t cols, float lr, const float* state,
+                          const float* scale, uint8_t* q, uint8_t* q_t, float* amax_slot, void* stream);
 
 /*
  * bf16 attention core between the fused QKV projection and the output

@@ -202,6 +202,34 @@ def test_linear_prequantised_x_validation():
     fwd = L.fp8_linear_fwd
     assert _err(fwd(64, 64, 64, None, F.BF16, B16, F.F32, None, F.F32, 0, C16, F.F32, None, None, None, None,
                     ctypes.byref(r), ctypes.byref(meta), ctypes.byref(meta), ctypes.byref(saved), None)) == F.ERR_ARG
+    # W pre-cast (w = NULL) is refused under just-in-time scaling too, and needs aligned saved codes
+    assert _err(fwd(64, 64, 64, A16, F.BF16, None, F.F32, None, F.F32, 0, C16, F.F32, None, None, None, None,
+                    ctypes.byref(r), ctypes.byref(meta), ctypes.byref(meta), ctypes.byref(saved), None)) == F.ERR_ARG
+    delayed = F.Recipe()
+    bad_saved = F._SavedC(1 << 37, 1 << 38, (1 << 39) + 8, 1 << 40, 1 << 41)
+    assert _err(fwd(64, 64, 64, A16, F.BF16, None, F.F32, None, F.F32, 0, C16, F.F32, None, None, None, None,
+                    ctypes.byref(delayed), ctypes.byref(meta), ctypes.byref(meta), ctypes.byref(bad_saved),
+                    None)) == F.ERR_ALIGN
+
+
+def test_sgd_step_cast_validation():
+    f = L.fp8_sgd_step_cast
+    f.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_float, P, P, P, P, P, P]
+    w, g, st, sc = P(1 << 36), P(1 << 37), P(1 << 38), P(1 << 39)
+    q, qt, slot = P(1 << 40), P(1 << 41), P(1 << 42)
+    assert _err(f(w, g, 64, 60, 1e-3, st, sc, q, qt, slot, None)) == F.ERR_SHAPE
+    assert _err(f(w, g, 64, 64, 1e-3, None, sc, q, qt, slot, None)) == F.ERR_NULL         # no state
+    assert _err(f(w, None, 64, 64, 1e-3, st, sc, q, qt, slot, None)) == F.ERR_NULL        # no gradient
+    assert _err(f(w, g, 64, 64, 1e-3, st, None, q, qt, slot, None)) == F.ERR_NULL         # no scale
+    assert _err(f(w, g, 64, 64, 1e-3, st, sc, q, None, slot, None)) == F.ERR_NULL         # q_t is required
+    assert _err(f(w, P((1 << 37) + 8), 64, 64, 1e-3, st, sc, q, qt, slot, None)) == F.ERR_ALIGN
+    assert _err(f(w, g, 64, 64, 1e-3, st, sc, P((1 << 40) + 4), qt, slot, None)) == F.ERR_ALIGN
+    assert _err(f(w, P((1 << 36) + 4096), 64, 64, 1e-3, st, sc, q, qt, slot, None)) == F.ERR_ARG    # g inside w
+    assert _err(f(w, g, 64, 64, 1e-3, P((1 << 36) + 64), sc, q, qt, slot, None)) == F.ERR_ARG       # state in w
+    assert _err(f(w, g, 64, 64, 1e-3, st, sc, P((1 << 36) + 1024), qt, slot, None)) == F.ERR_ARG    # codes in w
+    assert _err(f(w, g, 64, 64, 1e-3, st, sc, q, qt, P((1 << 36) + 256), None)) == F.ERR_ARG        # slot in w
+    assert _err(f(w, g, 64, 64, 1e-3, st, sc, P((1 << 37) + 1024), qt, slot, None)) == F.ERR_ARG    # codes in g
+    assert f(w, g, 0, 64, 1e-3, st, sc, q, qt, slot, None) == F.OK                                 # empty: nothing runs
 
 
 def test_loss_scale_and_sgd_validation():

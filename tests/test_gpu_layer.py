@@ -183,6 +183,12 @@ def _check_step(oracle, lay, om, ols, X, rows, wrows, tag):
     for i, name in enumerate(LAYER_TENSORS):
         assert_bits_equal(np_of(lay.bank.amax_history[i, 0]), om[name].hist[0], f"{tag} amax {name}")
     if counting:
+        # a forward that re-cast W (just in time) after a fused update adds to
+        # the window the fused update's own cast of W, made with the delayed scale
+        for name in LAYER_WEIGHTS:
+            if jit:
+                want_sat[name] += getattr(mt[name], "fused_sat", 0)
+            mt[name].fused_sat = 0
         got = lay.metrics()          # the step's counts (cleared for the next step)
         for name in LAYER_TENSORS:
             assert got[name]["saturated"] == want_sat[name], (tag, name, got[name]["saturated"], want_sat[name])
@@ -190,11 +196,22 @@ def _check_step(oracle, lay, om, ols, X, rows, wrows, tag):
     # update: loss scale from the four gradient amaxes, the twelve metas, SGD
     grads = np_of(lay.grad)
     masters = np_of(lay.master)
+    fused = lay.fuse_sgd_cast and not lay.recipe.just_in_time
     lay.update()
     torch.cuda.synchronize()
     ols.update([om[n].hist[0] for n in LAYER_GRADS])
     oracle.update_metas([om[n] for n in LAYER_TENSORS])
     oracle.sgd(masters, grads, LR, ols)
+    if fused:
+        # the fused SGD step already cast each updated master for the next
+        # forward and merged its amax into the rolled slot 0
+        off = 0
+        for name in LAYER_WEIGHTS:
+            n = W[name].size
+            om[name].record(masters[off:off + n])
+            if counting:
+                om[name].fused_sat = oracle.count_saturated(masters[off:off + n], om[name].fmt, om[name].scale)
+            off += n
     assert_bits_equal(np_of(lay.ls_state), ols.state, tag + " loss-scale state")
     for i, name in enumerate(LAYER_TENSORS):
         assert_bits_equal(np_of(lay.bank.amax_history[i]), om[name].hist, f"{tag} history {name}")
