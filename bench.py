@@ -359,6 +359,7 @@ def quant_leg(F, torch, reps=50, first=10):
     q4, q4t, q5, q5t = (torch.empty(rows, cols, **u8), torch.empty(cols, rows, **u8), torch.empty(rows, cols, **u8),
                         torch.empty(cols, rows, **u8))
     out = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty(2, rows, cols, dtype=torch.bfloat16, device="cuda")
     words = torch.empty(4096, dtype=torch.int32, device="cuda")
     seq = [("amax", lambda: F.fp8_amax(x, slot)),
            ("cast_transpose_dual_update", lambda: F.fp8_cast_transpose_dual_update(x, bank, recipe, ticket,
@@ -366,9 +367,12 @@ def quant_leg(F, torch, reps=50, first=10):
            ("dequant_both", lambda: (F.fp8_dequant(q4, F.E4M3, bank.scale_inv[0:1], out),
                                      F.fp8_dequant(q5, F.E5M2, bank.scale_inv[1:2], out)))]
     ceil = [("stream_read", lambda: F.stream_probe(x, words, 0)), ("stream_copy", lambda: F.stream_probe(x, out, 1)),
-            ("stream_copy_nt", lambda: F.stream_probe(x, out, 2))]
+            ("stream_copy_nt", lambda: F.stream_probe(x, out, 2)),
+            ("stream_copy_twice", lambda: F.stream_probe(x, out2, 3)),
+            ("stream_copy_twice_nt", lambda: F.stream_probe(x, out2, 4))]
     nbytes = {"amax": 2 * n, "cast_transpose_dual_update": (2 + 4) * n, "dequant_both": 2 * (1 + 2) * n,
-              "stream_read": 2 * n, "stream_copy": 2 * 2 * n, "stream_copy_nt": 2 * 2 * n}
+              "stream_read": 2 * n, "stream_copy": 2 * 2 * n, "stream_copy_nt": 2 * 2 * n,
+              "stream_copy_twice": 3 * 2 * n, "stream_copy_twice_nt": 3 * 2 * n}
 
     def launches():
         rec = F.timing_read(16 * reps)
@@ -420,17 +424,25 @@ def quant_leg(F, torch, reps=50, first=10):
             w = [a + b for a, b in zip(w[0::2], w[1::2])]
         steady[name] = stat(w, nbytes[name])
     copy_ceiling = max(steady["stream_copy"]["achieved_gbs"], steady["stream_copy_nt"]["achieved_gbs"])
+    twice_ceiling = max(steady["stream_copy_twice"]["achieved_gbs"], steady["stream_copy_twice_nt"]["achieved_gbs"])
     for k in ("amax", "cast_transpose_dual_update", "dequant_both"):
-        ceiling = steady["stream_read"]["achieved_gbs"] if k == "amax" else copy_ceiling
+        # the ceiling of the same read:write ratio: read only for amax, one read
+        # and two writes for the dual cast (2 B in, 4 B out) and the dequant (1 B in,
+        # 2 B out); the 1:1 copy beside it
+        ceiling = steady["stream_read"]["achieved_gbs"] if k == "amax" else twice_ceiling
         steady[k]["frac_of_stream_ceiling"] = round(steady[k]["achieved_gbs"] / ceiling, 4)
+        if k != "amax":
+            steady[k]["frac_of_copy_ceiling"] = round(steady[k]["achieved_gbs"] / copy_ceiling, 4)
     res["steady_state"] = steady
     res["peak_gbs"] = PEAK_HBM_GBS
     res["note"] = ("cast_transpose_dual_update: amax + cast to E4M3 and E5M2 + both transposes + the two metas' "
                    "scale update (last workgroup), one launch.  steady_state: each kernel 20 times back to back; "
-                   "stream_read / stream_copy / stream_copy_nt: the same 16-byte load/store layout with no arithmetic "
-                   "(the copy with plain or non-temporal stores), the measured ceiling (read for amax, the faster "
-                   "copy for the others)")
-    del x, q4, q4t, q5, q5t, out
+                   "stream_read / stream_copy(_nt) / stream_copy_twice(_nt): the same 16-byte load/store layout with "
+                   "no arithmetic (the copies with plain or non-temporal stores, the twice variants writing every "
+                   "vector to two places); frac_of_stream_ceiling is against the pattern of the same read:write "
+                   "ratio (read for amax, the faster copy-twice for the dual cast-transpose and the dequant), "
+                   "frac_of_copy_ceiling against the faster 1:1 copy")
+    del x, q4, q4t, q5, q5t, out, out2
     torch.cuda.empty_cache()
     return res
 

@@ -475,7 +475,8 @@ def timing_read(max_records=1 << 16):
 def stream_probe(src, dst, mode, stream=None):
     """Streaming reference kernel over src's bytes: mode 0 reads them (dst: a
     device buffer of at least 8 KiB), mode 1 copies them into dst, mode 2
-    copies them with non-temporal stores."""
+    copies them with non-temporal stores, modes 3 and 4 copy them twice (dst
+    holds twice src's bytes), with plain and with non-temporal stores."""
     nbytes = src.numel() * src.element_size()
     _check(_lib.fp8lin_stream_probe(_p(src), _p(dst), nbytes, mode, _stream(stream)))
 

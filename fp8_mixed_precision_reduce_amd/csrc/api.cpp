@@ -133,12 +133,13 @@ int32_t fp8lin_clock_sample(uint64_t* out, int32_t wait_us, void* stream) {
 
 int32_t fp8lin_stream_probe(const void* src, void* dst, int64_t bytes, int32_t mode, void* stream) {
     const char* fn = "fp8lin_stream_probe";
-    if (mode < 0 || mode > 2)
-        return fail(FP8LIN_ERR_ARG, "%s: mode %d is not 0 (read), 1 (copy) or 2 (copy, non-temporal stores)", fn, mode);
+    if (mode < 0 || mode > 4)
+        return fail(FP8LIN_ERR_ARG, "%s: mode %d is not 0 (read), 1 / 2 (copy) or 3 / 4 (copy twice)", fn, mode);
     if (bytes < 0 || bytes % 16 || bytes > kMaxElems) return fail(FP8LIN_ERR_SHAPE, "%s: bytes=%lld", fn, (long long)bytes);
     if (bytes > 0 && (!src || !dst)) return fail(FP8LIN_ERR_NULL, "%s: null pointer", fn);
     if (!aligned(src, 16) || !aligned(dst, 16)) return fail(FP8LIN_ERR_ALIGN, "%s: misaligned pointer", fn);
-    if (overlap(src, bytes, dst, mode == 0 ? 8192 : bytes)) return fail(FP8LIN_ERR_ARG, "%s: dst overlaps src", fn);
+    if (overlap(src, bytes, dst, mode == 0 ? 8192 : mode <= 2 ? bytes : 2 * bytes))
+        return fail(FP8LIN_ERR_ARG, "%s: dst overlaps src", fn);
     return hip_status(launch_stream_probe(src, dst, bytes, mode, as_stream(stream)), fn);
 }
 

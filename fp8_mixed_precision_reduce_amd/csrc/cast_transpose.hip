@@ -46,7 +46,7 @@ namespace {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
-constexpr int64_t kMaxGrid = 256 * 8;     // workgroups loop over tiles beyond this
+
 constexpr int kGeluExpLo = 119, kGeluExps = 12;                  // bf16 exponent fields of the gelu' table
 constexpr int kGeluTabHalf = kGeluExps * 128, kGeluTabN = 2 * kGeluTabHalf;
 
@@ -429,26 +429,48 @@ k_dbias_reduce(const float* __restrict__ ws, int64_t tiles_r, int64_t cols, floa
     dbias[c] = acc;
 }
 
+// Grid of a cast-transpose instance: the workgroups that are resident at once
+// (its occupancy times the compute units), at most one per tile.  Each
+// workgroup loops over tiles with the grid as stride, so every workgroup takes
+// within one as many tiles as any other (a grid of more than one resident
+// wave of workgroups would leave the last wave part-empty).
+template <int DT, int FMT, bool DGELU, bool DBIAS, bool DUAL, bool PAIR, bool SGD>
+dim3 ct_grid(int64_t ntiles) {
+    static const int per_cu = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_cast_transpose<DT, FMT, DGELU, DBIAS, DUAL, PAIR, SGD>,
+                                                         kThreads, 0) != hipSuccess || n < 1)
+            n = 1;
+        return n;
+    }();
+    const int64_t resident = (int64_t)cu_count() * per_cu;
+    return dim3((unsigned)(ntiles < resident ? ntiles : resident));
+}
+
 template <int DT, int FMT>
 hipError_t launch_dt_fmt(const void* x, const void* z, int64_t rows, int64_t cols, const float* scale,
                          uint8_t* q, uint8_t* qt, float* slot, float* dbias_ws, void* dz_out, hipStream_t s,
                          SinvSnap snap, SatCounts sat) {
     const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
     const int64_t ntiles = tiles_r * tiles_c;
-    const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
+    const dim3 block(kThreads);
     const bool dgelu = z != nullptr, dbias = dbias_ws != nullptr;
     const Second none{nullptr, nullptr, nullptr, nullptr};
     if (!dgelu && !dbias)
-        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false>), grid, block, 0, s, x, z, rows, cols,
+        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false>),
+                           (ct_grid<DT, FMT, false, false, false, false, false>(ntiles)), block, 0, s, x, z, rows, cols,
                            tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat, SgdPre{});
     else if (!dgelu)
-        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, true, false>), grid, block, 0, s, x, z, rows, cols,
+        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, true, false>),
+                           (ct_grid<DT, FMT, false, true, false, false, false>(ntiles)), block, 0, s, x, z, rows, cols,
                            tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat, SgdPre{});
     else if (!dbias)
-        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, false, false>), grid, block, 0, s, x, z, rows, cols,
+        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, false, false>),
+                           (ct_grid<DT, FMT, true, false, false, false, false>(ntiles)), block, 0, s, x, z, rows, cols,
                            tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat, SgdPre{});
     else
-        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, true, false>), grid, block, 0, s, x, z, rows, cols,
+        hipLaunchKernelGGL((k_cast_transpose<DT, FMT, true, true, false>),
+                           (ct_grid<DT, FMT, true, true, false, false, false>(ntiles)), block, 0, s, x, z, rows, cols,
                            tiles_c, scale, q, qt, slot, dbias_ws, dz_out, none, snap, CtJob{}, DualUpdate{}, sat, SgdPre{});
     return hipGetLastError();
 }
@@ -458,7 +480,7 @@ hipError_t launch_dual_dt(const void* x, int64_t rows, int64_t cols, const float
                           uint8_t* q4t, float* slot4, const Second& sec, hipStream_t s, DualUpdate upd, SatCounts sat) {
     const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
     const int64_t ntiles = tiles_r * tiles_c;
-    const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
+    const dim3 grid = ct_grid<DT, kE4M3, false, false, true, false, false>(ntiles), block(kThreads);
     hipLaunchKernelGGL((k_cast_transpose<DT, kE4M3, false, false, true>), grid, block, 0, s, x, nullptr, rows,
                        cols, tiles_c, scale4, q4, q4t, slot4, nullptr, nullptr, sec, SinvSnap{}, CtJob{}, upd, sat, SgdPre{});
     return hipGetLastError();
@@ -469,7 +491,7 @@ hipError_t launch_pair_dt_fmt(const void* xa, int64_t rows, int64_t cols, const 
                               float* slot, const CtJob& b, hipStream_t s, SinvSnap snap, SatCounts sat) {
     const int64_t tiles_c = (cols + kTile - 1) / kTile;
     const int64_t ntiles = ((rows + kTile - 1) / kTile) * tiles_c + ((b.rows + kTile - 1) / kTile) * b.tiles_c;
-    const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
+    const dim3 grid = ct_grid<DT, FMT, false, false, false, true, false>(ntiles), block(kThreads);
     const Second none{nullptr, nullptr, nullptr, nullptr};
     hipLaunchKernelGGL((k_cast_transpose<DT, FMT, false, false, false, true>), grid, block, 0, s, xa, nullptr, rows,
                        cols, tiles_c, scale, q, qt, slot, nullptr, nullptr, none, snap, b, DualUpdate{}, sat, SgdPre{});
@@ -484,7 +506,7 @@ hipError_t launch_sgd_cast_transpose(float* w, const float* g, int64_t rows, int
     if (rows == 0 || cols == 0) return hipSuccess;
     const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
     const int64_t ntiles = tiles_r * tiles_c;
-    const dim3 grid((unsigned)(ntiles < kMaxGrid ? ntiles : kMaxGrid)), block(kThreads);
+    const dim3 grid = ct_grid<kF32, kE4M3, false, false, false, false, true>(ntiles), block(kThreads);
     const Second none{nullptr, nullptr, nullptr, nullptr};
     timing_before(kKindSgd, s);
     hipLaunchKernelGGL((k_cast_transpose<kF32, kE4M3, false, false, false, false, true>), grid, block, 0, s, w,

@@ -45,6 +45,9 @@ __device__ __forceinline__ void take_snapshot(const SinvSnap& snap) {
 }
 #endif
 
+// Compute units of the current device (the persistent kernels size their grids by it).
+int cu_count();
+
 // ------------------------------------------------------------------ launchers
 // Each returns the hipError_t of its launch.  Arguments are validated by the
 // C entry points before these are called.

@@ -14,6 +14,8 @@
 // vector is handled one element per thread.  amax is an unsigned max over |x|
 // bit patterns: DPP within the wave, LDS across waves, one atomic per
 // workgroup.
+#include <atomic>
+
 #include "common.h"
 
 namespace fp8lin {
@@ -288,7 +290,9 @@ __global__ void __launch_bounds__(kThreads) k_stream_read(const uint4* __restric
     }
 }
 
-template <bool NT>
+// TWICE: each vector is also written nvec vectors further on (one read, two
+// writes: the read:write ratio of the dual-format cast and of the dequant).
+template <bool NT, bool TWICE = false>
 __global__ void __launch_bounds__(kThreads) k_stream_copy(const uint4* __restrict__ p, int64_t nvec,
                                                          uint4* __restrict__ q) {
     const int lane = threadIdx.x & 63;
@@ -305,6 +309,10 @@ __global__ void __launch_bounds__(kThreads) k_stream_copy(const uint4* __restric
             if (i < nvec) {
                 if constexpr (NT) store_nt(q + i, v[u]);
                 else q[i] = v[u];
+                if constexpr (TWICE) {
+                    if constexpr (NT) store_nt(q + nvec + i, v[u]);
+                    else q[nvec + i] = v[u];
+                }
             }
         }
     }
@@ -321,11 +329,31 @@ hipError_t launch_stream_probe(const void* src, void* dst, int64_t bytes, int mo
     else if (mode == 1)
         hipLaunchKernelGGL(k_stream_copy<false>, dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(src), nvec,
                            static_cast<uint4*>(dst));
-    else
+    else if (mode == 2)
         hipLaunchKernelGGL(k_stream_copy<true>, dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(src), nvec,
                            static_cast<uint4*>(dst));
+    else if (mode == 3)
+        hipLaunchKernelGGL((k_stream_copy<false, true>), dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(src),
+                           nvec, static_cast<uint4*>(dst));
+    else
+        hipLaunchKernelGGL((k_stream_copy<true, true>), dim3(g), dim3(kThreads), 0, s, static_cast<const uint4*>(src),
+                           nvec, static_cast<uint4*>(dst));
     timing_after(s);
     return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device; callers on several
+// host threads may race to fill an entry, with the same value).
+int cu_count() {
+    static std::atomic<int> cached[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 hipError_t launch_clock_sample(unsigned long long* out, int64_t ticks, hipStream_t s) {

@@ -632,19 +632,6 @@ k_gemm(GemmParams p) {
     if (p.amax) block_amax_merge(amax, p.amax, red);
 }
 
-// Compute units of the current device (cached per device; callers on several
-// host threads may race to fill an entry, with the same value).
-int cu_count() {
-    static std::atomic<int> cached[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
 
 template <typename Kern>
 int resident_per_cu(Kern kern, int threads) {

@@ -615,9 +615,11 @@ int32_t fp8lin_clock_sample(uint64_t* out, int32_t wait_us, void* stream);
  * mode 0 reads bytes of src (16-byte vectors, the same grid and layout as
  * fp8_amax) and writes one 32-bit word per workgroup to dst (at most 2048
  * words: dst holds 8 KiB); mode 1 copies bytes of src to dst; mode 2 copies
- * with non-temporal stores (the stores fp8_dequant uses).  bytes is a
- * multiple of 16; src, dst 16-byte aligned and not overlapping.  Timed as
- * FP8LIN_KIND_STREAM.
+ * with non-temporal stores (the stores fp8_dequant uses); modes 3 and 4 copy
+ * twice, to dst and to dst + bytes (dst holds 2 * bytes), with plain and with
+ * non-temporal stores: one read and two writes, the read:write ratio of the
+ * dual-format cast-transpose and of the dequant.  bytes is a multiple of 16;
+ * src, dst 16-byte aligned and not overlapping.  Timed as FP8LIN_KIND_STREAM.
  */
 int32_t fp8lin_stream_probe(const void* src, void* dst, int64_t bytes, int32_t mode, void* stream);
 int32_t fp8lin_timing_read(int32_t* kinds, float* ms, int32_t max);

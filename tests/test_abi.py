@@ -379,7 +379,12 @@ def test_dual_update_and_stream_probe_validation():
     assert _err(ok(q=P(1 << 40))) == F.ERR_ARG                       # output on the input
     sp = L.fp8lin_stream_probe
     sp.restype, sp.argtypes = ctypes.c_int32, [P, P, ctypes.c_int64, ctypes.c_int32, P]
-    assert _err(sp(A16, B16, 1024, 3, None)) == F.ERR_ARG
+    assert _err(sp(A16, B16, 1024, 5, None)) == F.ERR_ARG
+    assert _err(sp(A16, B16, 1024, -1, None)) == F.ERR_ARG
+    # the copy-twice modes write 2 * bytes: a dst whose second copy would reach src is refused
+    assert _err(sp(P((1 << 20) + 1536), P(1 << 20), 1024, 3, None)) == F.ERR_ARG
+    assert _err(sp(P((1 << 20) + 1024), P(1 << 20), 1024, 4, None)) == F.ERR_ARG
+    assert sp(P((1 << 20) + 2048), P(1 << 20), 0, 3, None) == F.OK
     assert _err(sp(A16, B16, 1000, 0, None)) == F.ERR_SHAPE
     assert _err(sp(None, B16, 1024, 1, None)) == F.ERR_NULL
     assert _err(sp(ODD, B16, 1024, 1, None)) == F.ERR_ALIGN
