@@ -54,6 +54,7 @@ bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 }
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kCtMaxRows = int64_t(1) << 24, kCtMaxCols = int64_t(1) << 22;
 constexpr int64_t kMaxK = int64_t(1) << 23;
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -308,6 +309,10 @@ int32_t check_ct(const char* fn, const void* x, const void* z, int32_t x_dtype, 
     if (rows < 0 || cols < 0 || rows % 16 || cols % 16 || rows * cols > kMaxElems)
         return fail(FP8LIN_ERR_SHAPE, "%s: rows=%lld cols=%lld must be >= 0 multiples of 16", fn, (long long)rows,
                     (long long)cols);
+    // The kernels address a 128 x 128 tile with 32-bit byte offsets below 2^31.
+    if (cols >= kCtMaxCols || rows >= kCtMaxRows)
+        return fail(FP8LIN_ERR_SHAPE, "%s: rows=%lld cols=%lld (cast-transpose needs rows < 2^24, cols < 2^22)", fn,
+                    (long long)rows, (long long)cols);
     const int64_t n = rows * cols;
     if (!scale || (n > 0 && (!x || (need_qt && !q_t)))) return fail(FP8LIN_ERR_NULL, "%s: null pointer", fn);
     if (dbias && cols > 0 && !dbias_ws && rows > 0) return fail(FP8LIN_ERR_NULL, "%s: dbias needs dbias_ws", fn);

@@ -50,6 +50,28 @@ constexpr int kThreads = 256;
 constexpr int kGeluExpLo = 119, kGeluExps = 12;                  // bf16 exponent fields of the gelu' table
 constexpr int kGeluTabHalf = kGeluExps * 128, kGeluTabN = 2 * kGeluTabHalf;
 
+// Buffer accesses (raw, unswizzled): an access whose offset is at or past the
+// resource's num_records loads zeros or stores nothing.
+constexpr uint32_t kOob = 0x80000000u;       // an offset past every bound in use (all below 2^31)
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)num_bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+
 template <int DT> struct CtVec {
     static constexpr int E = DT == kF32 ? 4 : 8;       // elements per 16-byte vector
     static constexpr int V = kTile / E;                // vectors per tile row
@@ -82,12 +104,20 @@ __device__ __forceinline__ uint4 pack_vec(const float v[CtVec<DT>::E]) {
                           pack_bf16x2(v[6], v[7]));
 }
 
-// Codes of one vector: 4 codes in a word, or 8 codes in two words.
+// Codes of one vector: 4 codes in a word, or 8 codes in two words.  any_nan:
+// some scaled value v * s is NaN (always so when some v is NaN).
+template <int FMT, int E>
+__device__ __forceinline__ uint2 enc_vec(const float v[E], float s, bool& any_nan) {
+    bool n0, n1 = false;
+    const uint32_t lo = enc4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s, n0);
+    const uint32_t hi = E == 4 ? 0u : enc4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s, n1);
+    any_nan = n0 | n1;
+    return make_uint2(lo, hi);
+}
 template <int FMT, int E>
 __device__ __forceinline__ uint2 enc_vec(const float v[E], float s) {
-    const uint32_t lo = enc4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
-    if constexpr (E == 4) return make_uint2(lo, 0u);
-    else return make_uint2(lo, enc4<FMT>(v[4] * s, v[5] * s, v[6] * s, v[7] * s));
+    bool any_nan;
+    return enc_vec<FMT, E>(v, s, any_nan);
 }
 
 // Byte offset in the LDS tile of the 4-byte word `w` (0..31) of tile row `r`.
@@ -194,64 +224,70 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
         const bool second = PAIR && tile_id >= ntiles_a;        // uniform per workgroup
         const void* const x = second ? job_b.x : x_a;
         const int64_t rows = second ? job_b.rows : rows_a, cols = second ? job_b.cols : cols_a;
-        const int64_t tiles_c = second ? job_b.tiles_c : tiles_ca;
+        const uint32_t tiles_c = (uint32_t)(second ? job_b.tiles_c : tiles_ca);
         const float s = second ? s_b : s_a;
         uint8_t* const q = second ? job_b.q : q_a;
         uint8_t* const qt = second ? job_b.qt : qt_a;
-        const int64_t local_id = second ? tile_id - ntiles_a : tile_id;
+        const uint32_t local_id = (uint32_t)(second ? tile_id - ntiles_a : tile_id);
         const bool count = (second ? sat.b : sat.a) != nullptr;      // uniform per workgroup
-        uint32_t m = 0;
-        const int64_t tr = local_id / tiles_c, tc = local_id % tiles_c;
-        const int64_t r0 = tr * kTile, c0 = tc * kTile;
-        const int64_t col = c0 + vc * E;
-        const bool col_ok = col < cols;
+        // The tile's amax as the unsigned max of |v|'s bit patterns: for a
+        // vector without NaN that is the float max of |v| (non-negative
+        // floats order as their bits), taken two elements per instruction;
+        // a vector whose scaled values hold a NaN (so every vector with a NaN
+        // element) adds its exact bit patterns instead.
+        float mf = 0.0f;
+        uint32_t mb = 0;
+        const uint32_t tr = local_id / tiles_c, tc = local_id - tr * tiles_c;
+        const int64_t r0 = (int64_t)tr * kTile, c0 = (int64_t)tc * kTile;
+        const uint32_t trows = (uint32_t)min(rows - r0, (int64_t)kTile), tcols = (uint32_t)min(cols - c0, (int64_t)kTile);
+        const uint32_t ucols = (uint32_t)cols, urows = (uint32_t)rows;
+
+        // Every global access of the tile is a buffer access relative to the
+        // tile's first element, bounded by the tile's rows (num_records): a
+        // lane past the last row lands beyond the bound, a lane past the last
+        // column is given the offset kOob; such loads return zeros and such
+        // stores are dropped.  Offsets stay below 2^32 (the launcher admits
+        // cols < 2^22 and rows < 2^24).
+        const uint32_t e0 = vc * E < tcols ? (uint32_t)r_first * ucols + vc * E : kOob;   // element offset
+        const uint32_t estep = C::RS * ucols;                                            // between vectors
+        const int64_t tile0 = r0 * cols + c0;
+        constexpr uint32_t XB = DT == kF32 ? 4 : 2;
+        const uint32_t xnum = trows * ucols * XB;
+        auto xoff = [&](int p) { return e0 == kOob ? kOob : (e0 + (uint32_t)p * estep) * XB; };
+        auto qoff = [&](int p) { return e0 == kOob ? kOob : e0 + (uint32_t)p * estep; };
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const uint8_t*>(SGD ? (const void*)sgd.w : x) + tile0 * XB, xnum);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(q ? q + tile0 : nullptr, q ? trows * ucols : 0u);
 
         uint4 rv[NP], rz[DGELU ? NP : 1];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) rv[p] = buf_load16(rx, xoff(p));
         if constexpr (SGD) {
             // the weights (read and written through sgd.w, not x) and their gradients
-            uint4 rg[NP];
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const int64_t row = r0 + r_first + C::RS * p;
-                const bool ok = col_ok && row < rows;
-                rv[p] = ok ? *reinterpret_cast<const uint4*>(sgd.w + row * cols + col) : make_uint4(0, 0, 0, 0);
-                rg[p] = ok && sgd_update ? *reinterpret_cast<const uint4*>(sgd.g + row * cols + col)
-                                         : make_uint4(0, 0, 0, 0);
-            }
             if (sgd_update) {
+                const __amdgpu_buffer_rsrc_t rg = make_rsrc(reinterpret_cast<const uint8_t*>(sgd.g) + tile0 * 4, xnum);
+                uint4 rg_v[NP];
+#pragma unroll
+                for (int p = 0; p < NP; ++p) rg_v[p] = buf_load16(rg, xoff(p));
 #pragma unroll
                 for (int p = 0; p < NP; ++p) {
-                    const int64_t row = r0 + r_first + C::RS * p;
                     float4 wv = __builtin_bit_cast(float4, rv[p]);
-                    const float4 gv = __builtin_bit_cast(float4, rg[p]);
+                    const float4 gv = __builtin_bit_cast(float4, rg_v[p]);
                     wv.x = wv.x - sgd.lr * (gv.x * sgd_inv);
                     wv.y = wv.y - sgd.lr * (gv.y * sgd_inv);
                     wv.z = wv.z - sgd.lr * (gv.z * sgd_inv);
                     wv.w = wv.w - sgd.lr * (gv.w * sgd_inv);
                     rv[p] = __builtin_bit_cast(uint4, wv);
-                    if (col_ok && row < rows) *reinterpret_cast<float4*>(sgd.w + row * cols + col) = wv;
+                    buf_store16(rx, xoff(p), rv[p]);
                 }
-            }
-        } else {
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const int64_t row = r0 + r_first + C::RS * p;
-                const bool ok = col_ok && row < rows;
-                rv[p] = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) +
-                                                             (row * cols + col) * (DT == kF32 ? 4 : 2))
-                           : make_uint4(0, 0, 0, 0);
             }
         }
         if constexpr (DGELU) {
+            const __amdgpu_buffer_rsrc_t rzs = make_rsrc(static_cast<const uint8_t*>(z) + tile0 * XB, xnum);
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const int64_t row = r0 + r_first + C::RS * p;
-                const bool ok = col_ok && row < rows;
-                rz[p] = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(z) +
-                                                             (row * cols + col) * (DT == kF32 ? 4 : 2))
-                           : make_uint4(0, 0, 0, 0);
-            }
+            for (int p = 0; p < NP; ++p) rz[p] = buf_load16(rzs, xoff(p));
         }
+        const __amdgpu_buffer_rsrc_t rdz = make_rsrc(DGELU && dz_out ? static_cast<uint8_t*>(dz_out) + tile0 * XB : nullptr,
+                                                     DGELU && dz_out ? xnum : 0u);
 
         float csum[E];
 #pragma unroll
@@ -259,8 +295,6 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int lrow = r_first + C::RS * p;
-            const int64_t row = r0 + lrow;
-            const bool ok = col_ok && row < rows;
             float v[E];
             unpack_vec<DT>(rv[p], v);
             if constexpr (DGELU) {
@@ -281,17 +315,23 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
                     const float g = v[j] * gz;
                     v[j] = DT == kF32 ? g : round_to_bf16(g);
                 }
-                if (dz_out && ok)
-                    *reinterpret_cast<uint4*>(static_cast<uint8_t*>(dz_out) + (row * cols + col) * (DT == kF32 ? 4 : 2)) =
-                        pack_vec<DT>(v);
-            }
-#pragma unroll
-            for (int j = 0; j < E; ++j) {
-                m = max(m, abs_bits(v[j]));
-                if constexpr (DBIAS) csum[j] += v[j];
+                if (dz_out) buf_store16(rdz, xoff(p), pack_vec<DT>(v));
             }
             const int lds = lds_word(lrow, vc * (E / 4));
-            const uint2 codes = enc_vec<FMT, E>(v, s);
+            bool vnan;
+            const uint2 codes = enc_vec<FMT, E>(v, s, vnan);
+            float vm = mf;
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                vm = fmaxf(vm, fabsf(v[j]));
+                if constexpr (DBIAS) csum[j] += v[j];
+            }
+            mf = vnan ? mf : vm;
+            asm volatile("" : "+v"(mf));      // keeps the max here (not sunk to the tile's end with every |v| live)
+            if (vnan) {
+#pragma unroll
+                for (int j = 0; j < E; ++j) mb = max(mb, abs_bits(v[j]));
+            }
             if (count) {
                 const uint32_t c = sat_count<FMT, E>(v, s);
                 if (second) n_b += c;
@@ -301,19 +341,20 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
                 if (sat.b) n_b += sat_count<kE5M2, E>(v, s2);
             }
             if constexpr (E == 8) {
-                if (q && ok) *reinterpret_cast<uint2*>(q + row * cols + col) = codes;
+                if (q) buf_store8(rq, qoff(p), codes);
                 if (qt) *reinterpret_cast<uint2*>(tile + lds) = codes;
             } else {
-                if (q && ok) *reinterpret_cast<uint32_t*>(q + row * cols + col) = codes.x;
+                if (q) buf_store4(rq, qoff(p), codes.x);
                 if (qt) *reinterpret_cast<uint32_t*>(tile + lds) = codes.x;
             }
             if constexpr (DUAL) {
+                const __amdgpu_buffer_rsrc_t rq2 = make_rsrc(sec.q ? sec.q + tile0 : nullptr, sec.q ? trows * ucols : 0u);
                 const uint2 c2 = enc_vec<kE5M2, E>(v, s2);
                 if constexpr (E == 8) {
-                    if (sec.q && ok) *reinterpret_cast<uint2*>(sec.q + row * cols + col) = c2;
+                    if (sec.q) buf_store8(rq2, qoff(p), c2);
                     if (sec.qt) *reinterpret_cast<uint2*>(tile + kTile * kTile + lds) = c2;
                 } else {
-                    if (sec.q && ok) *reinterpret_cast<uint32_t*>(sec.q + row * cols + col) = c2.x;
+                    if (sec.q) buf_store4(rq2, qoff(p), c2.x);
                     if (sec.qt) *reinterpret_cast<uint32_t*>(tile + kTile * kTile + lds) = c2.x;
                 }
             }
@@ -321,11 +362,15 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
         __syncthreads();
 
         // Transposed write: four q_t rows (input columns c0 + 4 cg ..) x one
-        // 16-byte strip (input rows r0 + 16 strip ..) per thread and format.
+        // 16-byte strip (input rows r0 + 16 strip ..) per thread and format,
+        // as buffer stores relative to q_t's element (c0, r0) bounded by the
+        // tile's columns; a strip past the last row gets kOob.
+        const uint32_t t0 = (uint32_t)strip * 16 < trows ? (uint32_t)(4 * cg) * urows + strip * 16 : kOob;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
             uint8_t* const qtf = f == 0 ? qt : sec.qt;
             if (!qtf) continue;
+            const __amdgpu_buffer_rsrc_t rt = make_rsrc(qtf + c0 * rows + r0, tcols * urows);
             const uint8_t* const tf = tile + f * kTile * kTile;
             uint32_t w[16];
 #pragma unroll
@@ -334,13 +379,9 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 transpose4x4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3], o[0][k], o[1][k], o[2][k], o[3][k]);
-            const int64_t ocol = r0 + strip * 16;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t orow = c0 + 4 * cg + j;
-                if (orow < cols && ocol < rows)
-                    *reinterpret_cast<uint4*>(qtf + orow * rows + ocol) = make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]);
-            }
+            for (int j = 0; j < 4; ++j)
+                buf_store16(rt, t0 == kOob ? kOob : t0 + (uint32_t)j * urows, make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]));
         }
 
         if constexpr (DBIAS) {
@@ -359,6 +400,7 @@ k_cast_transpose(const void* __restrict__ x_a, const void* __restrict__ z, int64
             }
         }
         __syncthreads();             // the LDS tile is rewritten by the next tile
+        const uint32_t m = max(__float_as_uint(mf), mb);
         if (second) m_b = max(m_b, m);
         else m_a = max(m_a, m);
     }

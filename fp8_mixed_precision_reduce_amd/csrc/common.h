@@ -148,17 +148,20 @@ __device__ __forceinline__ void wave_count_add(uint32_t v, uint32_t* ctr) {
     if ((threadIdx.x & 63) == 0 && v != 0u) atomicAdd(ctr, v);
 }
 
-// Saturating clamp that lets NaN through: |p| >= max -> +-max.
+// Saturating clamp, one median-of-three: |p| >= max -> +-max, any other
+// non-NaN p (-0 and subnormals included) unchanged.  A NaN p comes out as some
+// finite value; the encoders below replace its code.
 template <int FMT>
 __device__ __forceinline__ float sat_fp8(float p) {
-    return fabsf(p) >= Fp8Max<FMT>::value ? copysignf(Fp8Max<FMT>::value, p) : p;
+    return __builtin_amdgcn_fmed3f(p, -Fp8Max<FMT>::value, Fp8Max<FMT>::value);
 }
 
 // Encode four fp32 values (already scaled) into four codes, byte i = value i.
 // The hardware converts round to nearest-even; the clamp gives saturation and
-// NaN is mapped to sign|0x7F explicitly.
+// NaN is mapped to sign|0x7F explicitly.  any_nan: set when one of the four
+// values is NaN.
 template <int FMT>
-__device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
+__device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d, bool& any_nan) {
     const float sa = sat_fp8<FMT>(a), sb = sat_fp8<FMT>(b), sc = sat_fp8<FMT>(c), sd = sat_fp8<FMT>(d);
     int v;
     if constexpr (FMT == kE4M3) {
@@ -170,7 +173,8 @@ __device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
     }
     uint32_t r = (uint32_t)v;
     const bool na = a != a, nb = b != b, nc = c != c, nd = d != d;
-    if (__builtin_expect(na | nb | nc | nd, 0)) {
+    any_nan = na | nb | nc | nd;
+    if (__builtin_expect(any_nan, 0)) {
         const uint32_t nan_mask = (na ? 0xFFu : 0u) | (nb ? 0xFF00u : 0u) | (nc ? 0xFF0000u : 0u) |
                                   (nd ? 0xFF000000u : 0u);
         const uint32_t signs = ((__float_as_uint(a) >> 31) << 7) | ((__float_as_uint(b) >> 31) << 15) |
@@ -178,6 +182,11 @@ __device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
         r = (r & ~nan_mask) | (nan_mask & (0x7F7F7F7Fu | signs));
     }
     return r;
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
+    bool any_nan;
+    return enc4<FMT>(a, b, c, d, any_nan);
 }
 
 // Decode four codes (bytes of w) to fp32, exactly.

@@ -263,7 +263,9 @@ int32_t fp8_cast(const void* x, int32_t x_dtype, int64_t n, int32_t fp8_dtype,
  * [TE-KR] "Backward Pass 처리" (backward consumes the forward's FP8 copies);
  * [PT-VI] torch._scaled_mm example (the second operand enters transposed).
  *   rows, cols  >= 0 and multiples of 16 ([TE-KR] caution note: FP8 linear
- *               layers need both dimensions divisible by 16)
+ *               layers need both dimensions divisible by 16); rows < 2^24 and
+ *               cols < 2^22 (every cast-transpose entry point), else
+ *               FP8LIN_ERR_SHAPE
  *   q           [rows][cols] or NULL (only the transpose is written)
  *   q_t         [cols][rows]
  *   amax_slot   device float or NULL

@@ -68,6 +68,11 @@ def test_cast_transpose_validation():
     ct = L.fp8_cast_transpose
     assert _err(ct(A16, F.BF16, 17, 32, F.E4M3, B16, C16, P(1 << 30), None, None, None, None)) == F.ERR_SHAPE
     assert _err(ct(A16, F.BF16, 32, 24, F.E4M3, B16, C16, P(1 << 30), None, None, None, None)) == F.ERR_SHAPE
+    # the kernels' 32-bit tile offsets: rows < 2^24, cols < 2^22 (checked before any pointer is used)
+    assert _err(ct(A16, F.BF16, 16, 1 << 22, F.E4M3, B16, C16, P(1 << 30), None, None, None, None)) == F.ERR_SHAPE
+    assert _err(ct(A16, F.BF16, 1 << 24, 16, F.E4M3, B16, C16, P(1 << 30), None, None, None, None)) == F.ERR_SHAPE
+    assert _err(L.fp8_cast_transpose_dgelu(A16, B16, F.BF16, 16, 1 << 22, F.E4M3, C16, P(1 << 29), P(1 << 30),
+                                           None, None, None, None, None)) == F.ERR_SHAPE
     assert _err(ct(A16, F.BF16, 32, 32, F.E4M3, B16, C16, None, None, None, None, None)) == F.ERR_NULL
     assert _err(ct(A16, F.BF16, 32, 32, F.E4M3, B16, C16, P(1 << 30), None, P(1 << 31), None, None)) == F.ERR_NULL
     assert _err(ct(A16, F.BF16, 32, 32, F.E4M3, B16, ODD, P(1 << 30), None, None, None, None)) == F.ERR_ALIGN

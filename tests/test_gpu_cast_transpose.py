@@ -62,6 +62,62 @@ def test_cast_transpose_only_transpose_and_special_values(oracle, dtype):
     assert np.isnan(np_of(slot)[0])
 
 
+def _with_bits(x, dtype, bits):
+    """x (fp32 values, or bf16 bit patterns as uint16) with the given raw bit
+    patterns planted at seeded places, one per 128-row tile band."""
+    x = x.copy()
+    flat = x.reshape(-1).view(np.uint32 if dtype == "f32" else np.uint16)
+    rng = np.random.default_rng(len(bits))
+    idx = rng.choice(flat.size, len(bits), replace=False)
+    flat[idx] = np.array(bits, dtype=flat.dtype)
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["nan_payloads", "subnormal"])
+def test_cast_transpose_amax_bit_patterns(oracle, dtype, kind):
+    """The amax is the unsigned max of |x|'s bit patterns, also where NaN
+    payloads decide it (quiet and signalling NaNs of both signs, the largest
+    payload in one vector of one tile) and where only subnormals and zeros of
+    both signs are present: plain, dual and code outputs against the oracle."""
+    rows, cols = 272, 400
+    rng = np.random.default_rng(17 + (dtype == "bf16"))
+    if kind == "nan_payloads":
+        x = rng.standard_normal((rows, cols)).astype(np.float32)
+        bits = ([0x7FC00001, 0xFFC0ABCD, 0x7F800001, 0xFF800000, 0x7FFFFFFF] if dtype == "f32"
+                else [0x7FC1, 0xFFC5, 0x7F81, 0xFF80, 0x7FF0])
+    else:
+        x = (rng.integers(0, 1 << 20, (rows, cols)) * np.float32(2.0 ** -149)).astype(np.float32)
+        x[rng.random((rows, cols)) < 0.3] = -0.0
+        bits = [0x807FFF00, 0x00000001] if dtype == "f32" else [0x807E, 0x0001]
+    if dtype == "bf16":
+        x = oracle.bf16_from_f32(x)
+    x = _with_bits(x, dtype, bits)
+    want = oracle.amax(x)
+    if kind == "nan_payloads":
+        assert np.float32(want).view(np.uint32) == (0x7FFFFFFF if dtype == "f32" else 0x7FF00000)
+    else:
+        assert 0 < np.float32(want).view(np.uint32) < 0x00800000
+    s = np.float32(448.0 / 3.0)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    q, qt = torch.empty(rows, cols, **u8), torch.empty(cols, rows, **u8)
+    slot = torch.zeros(1, device="cuda")
+    F.fp8_cast_transpose(dev(x), F.E4M3, _scalar(float(s)), q, qt, slot)
+    want_q, want_qt = oracle.cast_transpose(x, 0, s)
+    assert_bits_equal(np_of(q), want_q, "q")
+    assert_bits_equal(np_of(qt), want_qt, "q_t")
+    assert_bits_equal(np_of(slot)[0], want, "amax")
+    outs = [torch.empty(rows, cols, **u8), torch.empty(cols, rows, **u8), torch.empty(rows, cols, **u8),
+            torch.empty(cols, rows, **u8)]
+    slots = torch.zeros(2, device="cuda")
+    s5 = np.float32(57344.0 / 3.0)
+    F.fp8_cast_transpose_dual(dev(x), _scalar(float(s)), _scalar(float(s5)), *outs, slots[0:1], slots[1:2])
+    assert_bits_equal(np_of(outs[1]), want_qt, "dual E4M3 q_t")
+    assert_bits_equal(np_of(outs[2]), oracle.cast_transpose(x, 1, s5)[0], "dual E5M2 q")
+    assert_bits_equal(np_of(slots)[0], want, "dual amax (E4M3 slot)")
+    assert_bits_equal(np_of(slots)[1], want, "dual amax (E5M2 slot)")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(48, 80), (272, 1040)], ids=lambda s: f"{s[0]}x{s[1]}")
 def test_cast_transpose_dgelu(oracle, dtype, shape):
