@@ -6,15 +6,20 @@
 // (the second GEMM operand enters transposed).
 //
 // One workgroup (256 threads, 4 waves) owns a 128 x 128 tile of the
-// [rows][cols] input and loops over tiles (at most 2048 workgroups run, so the
-// amax merge costs one, usually skipped, atomic per workgroup).
+// [rows][cols] input and loops over tiles; the grid is one resident round of
+// workgroups (the occupancy the compiled kernel allows, times the CU count),
+// so the amax merge costs one, usually skipped, atomic per workgroup.
 //
 // Load phase: the tile is read as 16-byte vectors (8 bf16 or 4 fp32
 // elements); thread t owns vector column t % V of rows t / V + (256 / V) p
 // (V vectors per tile row), so each load instruction of a wave covers whole
-// 256- or 512-byte row segments.  Every load of the tile (and of z for the
-// GeLU backward) is issued before any is used.  Each vector's codes go to q
-// with one 8- or 4-byte store and to an LDS tile [128][128] bytes.
+// 256- or 512-byte row segments.  Every access is a buffer access relative to
+// the tile with 32-bit offsets, bounded by the tile (out-of-range lanes load
+// zeros and drop their stores), so the loads carry no branches: every load of
+// the tile (and of z for the GeLU backward) is issued before any is used, and
+// each vector is encoded as soon as its own load has returned.  Each vector's
+// codes go to q with one 8- or 4-byte store and to an LDS tile [128][128]
+// bytes.
 //
 // Transpose phase: thread t owns input columns 4 cg .. 4 cg + 3 (cg = t / 8)
 // of the 16-row strip s = t % 8: it reads one 4-byte LDS word from each of the
