@@ -1,5 +1,6 @@
 """GPU parity past 2^31 elements: the 64-bit indexing of the amax, cast,
-cast-transpose and dequant kernels.
+cast-transpose and dequant kernels; and the cast-transpose at the largest
+dimensions its entry points admit (its tiles use 32-bit offsets).
 
 The bf16 tensors (just over 2^31 elements, with a ragged tail) are drawn on the
 GPU from a seeded generator.  The cast and the dequant are elementwise, so the
@@ -13,6 +14,7 @@ import pytest
 import torch
 
 import fp8_mixed_precision_reduce_amd as F
+import synth
 from helpers import assert_bits_equal, np_of
 
 pytestmark = pytest.mark.gpu
@@ -76,3 +78,43 @@ def test_cast_transpose_past_2_31_elements(oracle):
     want = oracle.cast(xs, 1, scale)
     assert_bits_equal(np_of(q.index_select(0, tr).index_select(1, tc)), want, "row-major codes")
     assert_bits_equal(np_of(qt.index_select(0, tc).index_select(1, tr)), want.T, "transposed codes")
+
+
+def test_cast_transpose_largest_admitted_dims(oracle):
+    """The cast-transpose kernels address a tile with 32-bit offsets; the
+    entry points admit cols < 2^22 and rows < 2^24.  At the largest admitted
+    width (16 x (2^22 - 16), fp32) and height ((2^24 - 16) x 16, bf16, the
+    dual-format kernel) every code, both layouts, and the amax equal the
+    oracle's."""
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    # widest: fp32, one row of tiles, the last tile ragged (2^22 - 16 = 32767 * 128 + 112)
+    rows, cols = 16, (1 << 22) - 16
+    x = synth.normal((rows, cols), 3.0, synth.seed_of(7, 0, 0), device="cuda")
+    x[rows - 1, cols - 1] = -500.0                       # the maximum, in the last (ragged) tile
+    s = np.float32(448.0 / 4.0)
+    q, qt = torch.empty(rows, cols, **u8), torch.empty(cols, rows, **u8)
+    slot = torch.zeros(1, device="cuda")
+    F.fp8_cast_transpose(x, F.E4M3, _scalar(float(s)), q, qt, slot)
+    torch.cuda.synchronize()
+    xh = np_of(x)
+    want_q, want_qt = oracle.cast_transpose(xh, 0, s)
+    assert_bits_equal(np_of(q), want_q, "q, widest")
+    assert_bits_equal(np_of(qt), want_qt, "q_t, widest")
+    assert_bits_equal(np_of(slot)[0], np.float32(500.0), "amax, widest")
+    del x, q, qt, xh, want_q, want_qt
+    # tallest: bf16, one column of tiles, dual format (both layouts of both formats)
+    rows, cols = (1 << 24) - 16, 16
+    x = synth.normal((rows, cols), 1.0, synth.seed_of(7, 0, 1), torch.bfloat16, "cuda")
+    x[rows - 1, 0] = 200.0
+    s4, s5 = np.float32(448.0 / 8.0), np.float32(57344.0 / 8.0)
+    outs = [torch.empty(rows, cols, **u8), torch.empty(cols, rows, **u8), torch.empty(rows, cols, **u8),
+            torch.empty(cols, rows, **u8)]
+    slots = torch.zeros(2, device="cuda")
+    F.fp8_cast_transpose_dual(x, _scalar(float(s4)), _scalar(float(s5)), *outs, slots[0:1], slots[1:2])
+    torch.cuda.synchronize()
+    xh = np_of(x)
+    for k, (fmt, sc) in enumerate(((0, s4), (1, s5))):
+        want_q, want_qt = oracle.cast_transpose(xh, fmt, sc)
+        assert_bits_equal(np_of(outs[2 * k]), want_q, f"q, tallest, format {fmt}")
+        assert_bits_equal(np_of(outs[2 * k + 1]), want_qt, f"q_t, tallest, format {fmt}")
+    assert_bits_equal(np_of(slots), np.array([200.0, 200.0], dtype=np.float32), "amax, tallest")
