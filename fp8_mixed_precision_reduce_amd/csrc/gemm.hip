@@ -365,16 +365,26 @@ k_gemm(GemmParams p) {
     }
 
     // ---------------------------------------------------------------- epilogue
-    // y = acc * sinv_a * sinv_b + bias, in place.  Lane (r32, g) of block (i, j)
-    // holds row i * 32 + r32 and, for q4 = 0..3, the four columns
-    // j * 32 + 8 q4 + 4 g .. + 3 of its wave's sub-tile.
+    // On the exact path (and with FP8 output) the epilogue's lane indices come
+    // from an opaque copy of the thread index made inside the tile loop:
+    // otherwise the compiler hoists the epilogue's per-lane LDS addresses out
+    // of the tile loop, where they stay live across the k loop and are spilled
+    // to scratch (one reload per store, each followed by a wait for all of the
+    // wave's memory operations).  The fast path's k loop leaves room for them
+    // and is measured 1-3 % faster with them hoisted.
+    int te = t;
+    if constexpr (!FAST || QOUT) asm volatile("" : "+v"(te));
+    const int lane_e = te & 63, r32e = lane_e & 31, ge = lane_e >> 5;
+    // y = acc * sinv_a * sinv_b + bias, in place.  Lane (r32e, ge) of block (i, j)
+    // holds row i * 32 + r32e and, for q4 = 0..3, the four columns
+    // j * 32 + 8 q4 + 4 ge .. + 3 of its wave's sub-tile.
     const bool gelu = p.epilogue & 1, accum = p.epilogue & 2;
     const bool want_amax = p.amax != nullptr;      // the output amax costs VALU work per element
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const int64_t ncol = n0 + wn * NB * 32 + j * 32 + 8 * q4 + 4 * g;
+            const int64_t ncol = n0 + wn * NB * 32 + j * 32 + 8 * q4 + 4 * ge;
             float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if (p.bias && ncol < N) {
                 if (p.bias_dtype == kF32) {
@@ -405,10 +415,10 @@ k_gemm(GemmParams p) {
             __syncthreads();
             constexpr int CPR = C::BN / 8;              // 16-byte chunks per row
             constexpr int RPP = C::THREADS / CPR;       // rows per pass
-            const int c = t % CPR;
+            const int c = te % CPR;
 #pragma unroll
             for (int pass = 0; pass < C::BM / RPP; ++pass) {
-                const int r = t / CPR + RPP * pass;
+                const int r = te / CPR + RPP * pass;
                 const int lr = r % (C::BM / 2);
                 const uint8_t* src = (r < C::BM / 2 ? smem0 : smem1) + lds_unit(lr, 2 * c);
                 const uint4 v = *reinterpret_cast<const uint4*>(src);
@@ -424,8 +434,8 @@ k_gemm(GemmParams p) {
                 for (int j = 0; j < NB; ++j)
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
-                        const int lr = i * 32 + r32;
-                        const int unit = (wn * NB * 32 + j * 32 + 8 * q4 + 4 * g) / 4;
+                        const int lr = i * 32 + r32e;
+                        const int unit = (wn * NB * 32 + j * 32 + 8 * q4 + 4 * ge) / 4;
                         *reinterpret_cast<uint2*>(half + lds_unit(lr, unit)) =
                             make_uint2(pack_bf16x2(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1]),
                                        pack_bf16x2(acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]));
@@ -434,12 +444,12 @@ k_gemm(GemmParams p) {
         }
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-            const int64_t mrow = m0 + wm * MB * 32 + i * 32 + r32;
+            const int64_t mrow = m0 + wm * MB * 32 + i * 32 + r32e;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const int64_t ncol = n0 + wn * NB * 32 + j * 32 + 8 * q4 + 4 * g;
+                    const int64_t ncol = n0 + wn * NB * 32 + j * 32 + 8 * q4 + 4 * ge;
                     const bool inside = mrow < M && ncol < N;
                     float y[4];
 #pragma unroll
@@ -454,8 +464,8 @@ k_gemm(GemmParams p) {
                     if (want_amax && inside)
                         amax = max(amax, max(max(abs_bits(bf16_to_f32(o.x & 0xFFFFu)), abs_bits(bf16_to_f32(o.x >> 16))),
                                              max(abs_bits(bf16_to_f32(o.y & 0xFFFFu)), abs_bits(bf16_to_f32(o.y >> 16)))));
-                    const int unit = (wn * NB * 32 + j * 32 + 8 * q4 + 4 * g) / 4;
-                    *reinterpret_cast<uint2*>(half + lds_unit(i * 32 + r32, unit)) = o;
+                    const int unit = (wn * NB * 32 + j * 32 + 8 * q4 + 4 * ge) / 4;
+                    *reinterpret_cast<uint2*>(half + lds_unit(i * 32 + r32e, unit)) = o;
                 }
             }
         }
@@ -480,13 +490,13 @@ k_gemm(GemmParams p) {
             __shared__ __attribute__((aligned(16))) uint8_t codes[SEG * C::BN];
             auto code_word = [&](int r, int w) { return r * C::BN + ((w ^ (((r >> 4) << 1) & (WPR - 1))) << 2); };
             const float qs = *p.q_scale;
-            const int c = t % CPR;
+            const int c = te % CPR;
             __syncthreads();
 #pragma unroll
             for (int sg = 0; sg < C::BM / SEG; ++sg) {
 #pragma unroll
                 for (int pass = 0; pass < NPASS; ++pass) {
-                    const int lr = t / CPR + RPP * pass;        // row within the segment
+                    const int lr = te / CPR + RPP * pass;        // row within the segment
                     const int r = sg * SEG + lr;
                     const uint4 v = *reinterpret_cast<const uint4*>((r < HALF ? smem0 : smem1) + lds_unit(r % HALF, 2 * c));
                     const int64_t row = m0 + r, col = n0 + 8 * c;
@@ -506,7 +516,7 @@ k_gemm(GemmParams p) {
                 if (p.qt) {
                     __syncthreads();
                     constexpr int STRIPS = SEG / 16;
-                    for (int u = t; u < WPR * STRIPS; u += C::THREADS) {
+                    for (int u = te; u < WPR * STRIPS; u += C::THREADS) {
                         const int cg = u / STRIPS, strip = u % STRIPS;
                         uint32_t w[16];
 #pragma unroll
@@ -550,7 +560,7 @@ k_gemm(GemmParams p) {
         auto f32_unit = [&](int lr, int unit) {
             return (lr < QR ? smem0 : smem1) + (lr % QR) * (C::BN * 4) + ((unit ^ (lr & 15)) << 4);
         };
-        const int c = t % UPR;
+        const int c = te % UPR;
 #pragma unroll
         for (int pass = 0; pass < WM; ++pass) {
             __syncthreads();
@@ -561,14 +571,14 @@ k_gemm(GemmParams p) {
                     for (int j = 0; j < NB; ++j)
 #pragma unroll
                         for (int q4 = 0; q4 < 4; ++q4)
-                            *reinterpret_cast<float4*>(f32_unit(i * 32 + r32, (wn * NB * 32 + j * 32 + 8 * q4 + 4 * g) / 4)) =
+                            *reinterpret_cast<float4*>(f32_unit(i * 32 + r32e, (wn * NB * 32 + j * 32 + 8 * q4 + 4 * ge) / 4)) =
                                 make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
                                             acc[i][j][4 * q4 + 3]);
             }
             __syncthreads();
 #pragma unroll
             for (int st = 0; st < (C::BM / 2) / RPP; ++st) {
-                const int lr = t / UPR + RPP * st;
+                const int lr = te / UPR + RPP * st;
                 const int64_t mrow = m0 + pass * (C::BM / 2) + lr, ncol = n0 + 4 * c;
                 if (mrow >= M || ncol >= N) continue;
                 const float4 v = *reinterpret_cast<const float4*>(f32_unit(lr, c));
@@ -590,16 +600,16 @@ k_gemm(GemmParams p) {
         }
         __syncthreads();     // the next tile's DMA rewrites the LDS
     } else {
-        // fp32 outputs from registers: lane (r32, g) writes four consecutive
+        // fp32 outputs from registers: lane (r32e, ge) writes four consecutive
         // columns of its row per 32 x 32 block.
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-            const int64_t mrow = m0 + wm * MB * 32 + i * 32 + r32;
+            const int64_t mrow = m0 + wm * MB * 32 + i * 32 + r32e;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const int64_t ncol = n0 + wn * NB * 32 + j * 32 + 8 * q4 + 4 * g;
+                    const int64_t ncol = n0 + wn * NB * 32 + j * 32 + 8 * q4 + 4 * ge;
                     if (mrow >= M || ncol >= N) continue;
                     float y[4];
                     const int64_t off = mrow * LDD + ncol;
