@@ -69,6 +69,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 128;
 constexpr int kGroupM = 8;
@@ -415,16 +416,30 @@ k_gemm(GemmParams p) {
             __syncthreads();
             constexpr int CPR = C::BN / 8;              // 16-byte chunks per row
             constexpr int RPP = C::THREADS / CPR;       // rows per pass
-            const int c = te % CPR;
+            constexpr int NPASS = C::BM / RPP, NH = NPASS / 2;
+            static_assert(NPASS % 2 == 0 && RPP % 16 == 0, "passes split over the two stage arrays");
+            const int c = te % CPR, r0 = te / CPR;
+            // Every LDS read of the thread first (rows r0 + RPP pass: the
+            // first half from stage array 0, the second from array 1, at
+            // constant offsets from one address), one wait, then the stores.
+            uint4 v[NPASS];
 #pragma unroll
-            for (int pass = 0; pass < C::BM / RPP; ++pass) {
-                const int r = te / CPR + RPP * pass;
-                const int lr = r % (C::BM / 2);
-                const uint8_t* src = (r < C::BM / 2 ? smem0 : smem1) + lds_unit(lr, 2 * c);
-                const uint4 v = *reinterpret_cast<const uint4*>(src);
-                const int64_t row = m0 + r, col = n0 + 8 * c;
-                if (row < M && col < N) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + row * LDD + col) = v;
+            for (int pass = 0; pass < NPASS; ++pass)
+                v[pass] = *reinterpret_cast<const uint4*>((pass < NH ? smem0 : smem1) +
+                                                          lds_unit(r0 + RPP * (pass % NH), 2 * c));
+            // (the reads stay here, not sunk into the conditional stores)
+#pragma unroll
+            for (int pass = 0; pass < NPASS; ++pass) {
+                v4u w = __builtin_bit_cast(v4u, v[pass]);
+                asm volatile("" : "+v"(w));
+                v[pass] = __builtin_bit_cast(uint4, w);
             }
+            const int64_t col = n0 + 8 * c;
+            uint16_t* const out = static_cast<uint16_t*>(dst) + (m0 + r0) * LDD + col;
+#pragma unroll
+            for (int pass = 0; pass < NPASS; ++pass)
+                if (m0 + r0 + RPP * pass < M && col < N)
+                    *reinterpret_cast<uint4*>(out + (int64_t)(RPP * pass) * LDD) = v[pass];
             __syncthreads();
         };
         if (gelu && p.aux) {
