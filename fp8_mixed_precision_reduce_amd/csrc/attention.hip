@@ -185,9 +185,21 @@ k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, ui
     auto pv = [&](const uint8_t* vb, const v8bf* pb) __attribute__((always_inline)) {
         // O^T += V^T P: keys 16 ks + 8 g + slot = registers 8 (ks & 1) + slot of tile ks / 2
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks) {
+            v8bf vf[4];
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[dt] = mfma(lds16(vb + off128(32 * dt + l32, 2 * ks + g)), pb[ks], o[dt]);
+            for (int dt = 0; dt < 4; ++dt) vf[dt] = lds16(vb + off128(32 * dt + l32, 2 * ks + g));
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] = mfma(vf[dt], pb[ks], o[dt]);
+        }
+        // reads of step ks + 1 ahead of the MFMAs of step ks
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int ks = 0; ks < 3; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     };
     auto step = [&](int j, const uint8_t* buf, const uint8_t* prev, uint8_t* nxt) __attribute__((always_inline)) {
         if (j + 1 < nblk) dma((j + 1) * kFwdK, nxt);
@@ -197,10 +209,21 @@ k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, ui
 #pragma unroll
         for (int e = 0; e < 16; ++e) { sc[0][e] = 0.0f; sc[1][e] = 0.0f; }
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            sc[0] = mfma(lds16(buf + off256(row, 2 * st + g)), qf[st], sc[0]);
-            sc[1] = mfma(lds16(buf + off256(32 + row, 2 * st + g)), qf[st], sc[1]);
+        for (int s2 = 0; s2 < 4; ++s2) {
+            v8bf kf[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kf[u] = lds16(buf + off256(32 * (u & 1) + row, 2 * (2 * s2 + (u >> 1)) + g));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sc[u & 1] = mfma(kf[u], qf[2 * s2 + (u >> 1)], sc[u & 1]);
         }
+        // reads of group s2 + 1 ahead of the MFMAs of group s2
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // block j's maximum; the reference maximum m2 moves only when the block
         // exceeds it by more than kLazy (then every P of the block is <= 2^kLazy,
         // harmless in fp32 and bf16), and O and l are rescaled with it -- exact in
@@ -506,9 +529,16 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
             qf[st] = as_bf(*reinterpret_cast<const uint4*>(qrow + 16 * st + 8 * g));
             df[st] = as_bf(*reinterpret_cast<const uint4*>(drow + 16 * st + 8 * g));
         }
+        // The fragments land before the loop: left to the scheduler, these
+        // loads move past the first barrier and the loop's first uses wait on
+        // the memory counter, which then (in every iteration) also waits for
+        // the next block's DMA in the middle of the products.
+#pragma unroll
+        for (int st = 0; st < 8; ++st) asm volatile("" ::"v"(qf[st]), "v"(df[st]));
     }
-    const float lq = lse[((int64_t)b * H + h) * S + q];
-    const float dd = dq_rows[((int64_t)b * H + h) * S + q];
+    float lq = lse[((int64_t)b * H + h) * S + q];
+    float dd = dq_rows[((int64_t)b * H + h) * S + q];
+    asm volatile("" : "+v"(lq), "+v"(dd));        // (as the fragments: landed before the loop)
     // Key-block DMA straight into the LDS: wave w fills K and V rows 4 w .. 4 w + 3
     // (256 B each) and K^T rows 16 w .. 16 w + 15 (64 B each), each lane loading
     // the logical chunk whose swizzled place is its own.
@@ -541,19 +571,37 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
         for (int e = 0; e < 16; ++e) { s[e] = 0.0f; dp[e] = 0.0f; }
         const int row = sigma(l32);
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            s = mfma(lds16(buf + off256(row, 2 * st + g)), qf[st], s);
-            dp = mfma(lds16(buf + kQKt + off256(row, 2 * st + g)), df[st], dp);
+        for (int s2 = 0; s2 < 4; ++s2) {
+            v8bf f[4];      // K and V fragments of steps 2 s2 and 2 s2 + 1
+#pragma unroll
+            for (int u = 0; u < 4; ++u) f[u] = lds16(buf + (u & 1) * kQKt + off256(row, 2 * (2 * s2 + (u >> 1)) + g));
+#pragma unroll
+            for (int u = 0; u < 4; u += 2) {
+                s = mfma(f[u], qf[2 * s2 + (u >> 1)], s);
+                dp = mfma(f[u + 1], df[2 * s2 + (u >> 1)], dp);
+            }
         }
+        // reads of group s2 + 1 ahead of the MFMAs of group s2
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int s2 = 0; s2 < 3; ++s2) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 #pragma unroll
         for (int e = 0; e < 16; ++e) dp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sh.c2, -lq)) * (dp[e] - dd);
         // dQ^T += K^T dS: keys 16 ks + 8 g + slot = registers 8 ks + slot
+        v8bf kt_f[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) kt_f[ks][dt] = lds16(buf + 2 * kQKt + off64(32 * dt + l32, 2 * ks + g));
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const v8bf sb = pack8(dp, 8 * ks);
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-                acc[dt] = mfma(lds16(buf + 2 * kQKt + off64(32 * dt + l32, 2 * ks + g)), sb, acc[dt]);
+            for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(kt_f[ks][dt], sb, acc[dt]);
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0): this wave's DMA of the next block landed
         __syncthreads();
