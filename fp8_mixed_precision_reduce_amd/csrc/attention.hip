@@ -267,6 +267,8 @@ k_attn_fwd(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ vt, ui
     };
     dma(0, smem0);
     __builtin_amdgcn_s_waitcnt(0x0f70);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) asm volatile("" ::"v"(qf[st]));     // the Q fragments land with the first block
     __syncthreads();
     for (int j = 0; j < nblk; j += 3) {
         step(j, smem0, smem2, smem1);
@@ -529,16 +531,9 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
             qf[st] = as_bf(*reinterpret_cast<const uint4*>(qrow + 16 * st + 8 * g));
             df[st] = as_bf(*reinterpret_cast<const uint4*>(drow + 16 * st + 8 * g));
         }
-        // The fragments land before the loop: left to the scheduler, these
-        // loads move past the first barrier and the loop's first uses wait on
-        // the memory counter, which then (in every iteration) also waits for
-        // the next block's DMA in the middle of the products.
-#pragma unroll
-        for (int st = 0; st < 8; ++st) asm volatile("" ::"v"(qf[st]), "v"(df[st]));
     }
     float lq = lse[((int64_t)b * H + h) * S + q];
     float dd = dq_rows[((int64_t)b * H + h) * S + q];
-    asm volatile("" : "+v"(lq), "+v"(dd));        // (as the fragments: landed before the loop)
     // Key-block DMA straight into the LDS: wave w fills K and V rows 4 w .. 4 w + 3
     // (256 B each) and K^T rows 16 w .. 16 w + 15 (64 B each), each lane loading
     // the logical chunk whose swizzled place is its own.
@@ -608,6 +603,14 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
     };
     dma(0, smem0);
     __builtin_amdgcn_s_waitcnt(0x0f70);
+    // The per-query fragments and row statistics land together with the first
+    // block: left to the scheduler, their loads move past this barrier and the
+    // loop's first uses wait on the memory counter, which then (in every
+    // iteration) also waits for the next block's DMA in the middle of the
+    // products.
+#pragma unroll
+    for (int st = 0; st < 8; ++st) asm volatile("" ::"v"(qf[st]), "v"(df[st]));
+    asm volatile("" : "+v"(lq), "+v"(dd));
     __syncthreads();
     for (int j = 0; j < nblk; j += 2) {
         block(j, smem0, smem1);
