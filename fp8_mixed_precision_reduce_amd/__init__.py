@@ -503,8 +503,9 @@ class ClockSample:
 # ------------------------------------------------------------- attention core
 
 def attention_workspace_bytes(batch, seq, heads, head_dim=128, backward=False):
-    """Bytes of device workspace bf16_attention_fwd (backward=False) or
-    bf16_attention_bwd needs; -1 for an unsupported shape."""
+    """Bytes of device workspace bf16_attention_fwd (backward=False: V^T) or
+    bf16_attention_bwd (the per-query rowsum(dO * O), fp32) needs; -1 for an
+    unsupported shape."""
     return _lib.bf16_attention_workspace_bytes(batch, seq, heads, head_dim, int(bool(backward)))
 
 
@@ -517,18 +518,31 @@ def _attn_shape(qkv, batch, heads):
     return tokens // batch, cols // (3 * heads)
 
 
+def _check_workspace(workspace, batch, seq, heads, d, backward):
+    """The library cannot see the workspace's size: an undersized one would be
+    written past its end, so it is refused here."""
+    need = attention_workspace_bytes(batch, seq, heads, d, backward)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if need > 0 and have < need:
+        raise ValueError(f"attention {'backward' if backward else 'forward'}: workspace of {have} bytes, "
+                         f"needs {need} (attention_workspace_bytes)")
+
+
 def bf16_attention_fwd(qkv, batch, heads, ctx, lse, workspace, stream=None):
     """ctx [batch*seq, heads*D] bf16 = softmax(Q K^T / sqrt(D)) V per (batch,
     head) from qkv [batch*seq, 3*heads*D] ([Q | K | V], head-major); lse
     float32 [batch, heads, seq] (base-2 log-sum-exp, kept for the backward);
     workspace: a uint8 device tensor of attention_workspace_bytes(...) bytes."""
     seq, d = _attn_shape(qkv, batch, heads)
+    _check_workspace(workspace, batch, seq, heads, d, False)
     _check(_lib.bf16_attention_fwd(_p(qkv), batch, seq, heads, d, _p(ctx), _p(lse), _p(workspace), _stream(stream)))
 
 
 def bf16_attention_bwd(qkv, ctx, lse, dctx, batch, heads, dqkv, workspace, stream=None):
     """dqkv [batch*seq, 3*heads*D] bf16 = the gradient of <ctx, dctx> with
-    respect to qkv (all three parts written), from the forward's qkv, ctx, lse."""
+    respect to qkv (all three parts written), from the forward's qkv, ctx, lse;
+    workspace: a uint8 device tensor of attention_workspace_bytes(..., backward=True) bytes."""
     seq, d = _attn_shape(qkv, batch, heads)
+    _check_workspace(workspace, batch, seq, heads, d, True)
     _check(_lib.bf16_attention_bwd(_p(qkv), _p(ctx), _p(lse), _p(dctx), batch, seq, heads, d, _p(dqkv),
                                    _p(workspace), _stream(stream)))

@@ -210,7 +210,8 @@ class Fp8TransformerLayer:
         self.heads, self.batch = heads, batch
         if heads is not None:
             seq = m // batch
-            wsb = attention_workspace_bytes(batch, seq, heads, hid // heads, backward=True)
+            # one workspace serves the forward (V^T) and the backward (row sums): the larger figure
+            wsb = max(attention_workspace_bytes(batch, seq, heads, hid // heads, backward=bw) for bw in (False, True))
             if wsb < 0:
                 raise ValueError(f"attention core: unsupported shape batch={batch} seq={seq} heads={heads} "
                                  f"head width {hid // heads}")

@@ -560,10 +560,13 @@ int32_t fp8_sgd_step_cast(float* w, const float* g, int64_t rows, int64_t cols, 
  * 256, batch*seq*heads*128 < 2^31, seq*heads*768 < 2^31 and
  * batch*seq*256 < 2^31 (byte offsets of the tile loads within one (batch,
  * head)); other shapes give FP8LIN_ERR_SHAPE.
- * Workspaces (caller-owned device memory, 16-byte aligned, contents not
+ * Workspace (caller-owned device memory, 16-byte aligned, contents not
  * preserved): bf16_attention_workspace_bytes(batch, seq, heads, head_dim,
- * backward) bytes: the forward holds V^T, the backward Q^T, K^T, dO^T and
- * rowsum(dO * O).
+ * backward) bytes: the forward holds V^T (batch*seq*heads*D bf16), the
+ * backward rowsum(dO * O) (batch*heads*seq fp32; its transposed operands are
+ * read from the row-major tiles in the LDS, so it makes no transposed copy).
+ * The library cannot see the workspace's size; a caller that shares one
+ * workspace between the two calls sizes it as the larger figure.
  */
 int64_t bf16_attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
                                        int32_t backward);

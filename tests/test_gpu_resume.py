@@ -99,7 +99,8 @@ def test_attention_is_deterministic():
     give identical bytes (no floating-point atomics anywhere)."""
     batch, seq, heads = 2, 4096, 64
     qkv, dctx = synth.attention_inputs(batch, seq, heads, device="cuda")
-    ws = torch.empty(F.attention_workspace_bytes(batch, seq, heads, backward=True), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(F.attention_workspace_bytes(batch, seq, heads, backward=bw) for bw in (False, True)),
+                     dtype=torch.uint8, device="cuda")
     outs = []
     for _ in range(2):
         ctx = torch.empty(batch * seq, heads * 128, dtype=torch.bfloat16, device="cuda")
