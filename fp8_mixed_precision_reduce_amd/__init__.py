@@ -504,8 +504,8 @@ class ClockSample:
 
 def attention_workspace_bytes(batch, seq, heads, head_dim=128, backward=False):
     """Bytes of device workspace bf16_attention_fwd (backward=False: V^T) or
-    bf16_attention_bwd (the per-query rowsum(dO * O), fp32) needs; -1 for an
-    unsupported shape."""
+    bf16_attention_bwd (Q^T, dO^T and the per-query rowsum(dO * O)) needs; -1
+    for an unsupported shape."""
     return _lib.bf16_attention_workspace_bytes(batch, seq, heads, head_dim, int(bool(backward)))
 
 

@@ -830,7 +830,7 @@ int32_t check_attn_shape(const char* fn, int64_t batch, int64_t seq, int64_t hea
 int64_t bf16_attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, int32_t backward) {
     int64_t n = 0;
     if (check_attn_shape("bf16_attention_workspace_bytes", batch, seq, heads, head_dim, &n) != FP8LIN_OK) return -1;
-    return backward ? batch * heads * seq * 4 : n * 2;
+    return backward ? 2 * n * 2 + batch * heads * seq * 4 : n * 2;
 }
 
 int32_t bf16_attention_fwd(const void* qkv, int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void* ctx,
@@ -864,7 +864,7 @@ int32_t bf16_attention_bwd(const void* qkv, const void* ctx, const float* lse, c
         !aligned(workspace, 16))
         return fail(FP8LIN_ERR_ALIGN, "%s: misaligned pointer", fn);
     const int64_t lb = batch * heads * seq * 4;
-    const int64_t wsb = lb;                       // rowsum(dO * O), fp32 per (batch, head, query)
+    const int64_t wsb = 2 * n * 2 + lb;           // Q^T and dO^T (bf16), then rowsum(dO * O) (fp32)
     const void* ins[4] = {qkv, ctx, lse, dctx};
     const int64_t inb[4] = {3 * n * 2, n * 2, lb, n * 2};
     for (int i = 0; i < 4; ++i)
@@ -873,7 +873,9 @@ int32_t bf16_attention_bwd(const void* qkv, const void* ctx, const float* lse, c
     if (overlap(dqkv, 3 * n * 2, workspace, wsb)) return fail(FP8LIN_ERR_ARG, "%s: dqkv overlaps the workspace", fn);
     return hip_status(launch_attention_bwd(static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(ctx), lse,
                                            static_cast<const uint16_t*>(dctx), batch, seq, heads,
-                                           static_cast<uint16_t*>(dqkv), static_cast<float*>(workspace),
+                                           static_cast<uint16_t*>(dqkv), static_cast<uint16_t*>(workspace),
+                                           static_cast<uint16_t*>(workspace) + n,
+                                           reinterpret_cast<float*>(static_cast<uint16_t*>(workspace) + 2 * n),
                                            as_stream(stream)),
                       fn);
 }

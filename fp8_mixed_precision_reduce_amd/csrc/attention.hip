@@ -88,9 +88,11 @@ __device__ __forceinline__ v16f mfma(v8bf a, v8bf b, v16f c) {
 // r + 8 .. r + 11) hits every bank group twice, its minimum.
 __device__ __forceinline__ int swz256(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int off256(int row, int chunk) { return row * 256 + ((chunk ^ swz256(row)) << 4); }
-// The forward's K tile (no transposing reads) keeps the plain swizzle by the
-// row's low 4 bits.
+// The forward's and the dK/dV kernel's tiles (no transposing reads) keep the
+// plain swizzle by the row's low 4 bits.
 __device__ __forceinline__ int off256f(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+// 64-byte rows (32 tokens): chunk swizzled by (row >> 2) & 3 (four rows span the 64 banks).
+__device__ __forceinline__ int off64(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 // 128-byte rows (64 tokens): chunk swizzled by (row >> 1) & 7 (two rows span the 64 banks).
 __device__ __forceinline__ int off128(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
@@ -389,14 +391,14 @@ k_attn_rowdot(const uint16_t* __restrict__ dctx, const uint16_t* __restrict__ ct
 // Workgroup: 8 waves, 256 keys of one (b, h), 32 per wave (each lane one key;
 // its K and V fragments in registers for the whole kernel).  Query blocks of
 // 32 go through a double-buffered LDS tile, loaded by buffer loads that write
-// the LDS directly: Q and dO [32][256 B] (Q^T and dO^T fragments read from
-// them by transposing reads), lse2 and Dq [32].
+// the LDS directly: Q and dO [32][256 B], Q^T and dO^T [128][64 B], lse2 and
+// Dq [32].
 constexpr int kKvKeys = 256, kKvQ = 32, kKvThreads = 512;
-constexpr int kKvQt = 32 * 256, kKvBuf = 2 * 32 * 256 + 2 * 32 * 4;
+constexpr int kKvQt = 32 * 256, kKvBuf = 2 * 32 * 256 + 2 * 128 * 64 + 2 * 32 * 4;
 
 __global__ void __launch_bounds__(kKvThreads, 1)
-k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx, const float* __restrict__ lse,
-              const float* __restrict__ dq_rows,
+k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx, const uint16_t* __restrict__ qt,
+              const uint16_t* __restrict__ dot, const float* __restrict__ lse, const float* __restrict__ dq_rows,
               uint16_t* __restrict__ dqkv, AttnShape sh) {
     // two query-block buffers as separate arrays, the loop unrolled by two, so
     // the compiler sees that the fragment reads of one never alias the DMA into
@@ -424,28 +426,35 @@ k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dct
         }
     }
     // Query-block DMA straight into the LDS (16 bytes per lane, lane l at
-    // base + 16 l): wave w fills Q and dO rows 4 w .. 4 w + 3 (256 B each);
-    // lane l loads the logical chunk whose swizzled place is its own.  Wave 0's lanes 0..15 also load the
+    // base + 16 l): wave w fills Q and dO rows 4 w .. 4 w + 3 (256 B each) and
+    // Q^T and dO^T rows 16 w .. 16 w + 15 (64 B each); lane l loads the logical
+    // chunk whose swizzled place is its own.  Wave 0's lanes 0..15 also load the
     // block's 32 lse2 and 32 Dq values.
     const auto rs = [](const void* p) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7FFFFFFF, 0x00020000);
     };
     const __amdgpu_buffer_rsrc_t rq = rs(qkv + tok0 * ld + (int64_t)h * kD);
     const __amdgpu_buffer_rsrc_t rdo = rs(dctx + tok0 * HD + (int64_t)h * kD);
+    const __amdgpu_buffer_rsrc_t rqt = rs(qt + (int64_t)h * kD * BS + tok0);
+    const __amdgpu_buffer_rsrc_t rdot = rs(dot + (int64_t)h * kD * BS + tok0);
     const __amdgpu_buffer_rsrc_t rl = rs(lse + ((int64_t)b * H + h) * S);
     const __amdgpu_buffer_rsrc_t rd = rs(dq_rows + ((int64_t)b * H + h) * S);
-    const int r256 = 4 * w + (lane >> 4), c256 = (lane & 15) ^ swz256(r256);
+    const int r256 = 4 * w + (lane >> 4), c256 = (lane & 15) ^ (r256 & 15);
+    const int r64 = 16 * w + (lane >> 2), c64 = (lane & 3) ^ ((r64 >> 2) & 3);
     const uint32_t o_q = (uint32_t)(r256 * ld + c256 * 8) * 2, o_do = (uint32_t)(r256 * HD + c256 * 8) * 2;
+    const uint32_t o_t = (uint32_t)(r64 * BS + c64 * 8) * 2;
     auto dma = [&](int q0, uint8_t* buf) __attribute__((always_inline)) {
         const uint32_t qrow = (uint32_t)q0;
         dma16(rq, buf + 1024 * w, o_q + qrow * (uint32_t)ld * 2);
         dma16(rdo, buf + kKvQt + 1024 * w, o_do + qrow * (uint32_t)HD * 2);
+        dma16(rqt, buf + 2 * kKvQt + 1024 * w, o_t + qrow * 2);
+        dma16(rdot, buf + 2 * kKvQt + 128 * 64 + 1024 * w, o_t + qrow * 2);
         // (a buffer resource is wave-uniform: lse2 by lanes 0..7, Dq by lanes 8..15,
         // which land 128 bytes further)
         if (w == 0 && lane < 8)
-            dma16(rl, buf + 2 * kKvQt, (qrow + 4 * (uint32_t)lane) * 4);
+            dma16(rl, buf + 2 * kKvQt + 2 * 128 * 64, (qrow + 4 * (uint32_t)lane) * 4);
         if (w == 0 && lane >= 8 && lane < 16)
-            dma16(rd, buf + 2 * kKvQt, (qrow + 4 * (uint32_t)(lane - 8)) * 4);
+            dma16(rd, buf + 2 * kKvQt + 2 * 128 * 64, (qrow + 4 * (uint32_t)(lane - 8)) * 4);
     };
 
     v16f dk[4], dv[4];
@@ -458,22 +467,19 @@ k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dct
     auto block = [&](int j, const uint8_t* buf, uint8_t* nxt) __attribute__((always_inline)) {
         const uint8_t* sq = buf;
         const uint8_t* sdo = buf + kKvQt;
-        const float* sl = reinterpret_cast<const float*>(buf + 2 * kKvQt);
+        const uint8_t* sqt = buf + 2 * kKvQt;
+        const uint8_t* sdot = sqt + 128 * 64;
+        const float* sl = reinterpret_cast<const float*>(sqt + 2 * 128 * 64);
         if (j + 1 < nblk) dma((j + 1) * kKvQ, nxt);
-        // The per-lane LDS addresses of this block's reads come from an opaque
-        // copy of the lane index: hoisted out of the loop they would be spilled.
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int gl = ln >> 5;
         // S and dP tiles, rows = queries sigma(i) of the block, column = the lane's key.
         v16f s, dp;
 #pragma unroll
         for (int e = 0; e < 16; ++e) { s[e] = 0.0f; dp[e] = 0.0f; }
-        const int row = sigma(ln & 31);
+        const int row = sigma(l32);
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-            s = mfma(lds16(sq + off256(row, 2 * st + gl)), kf[st], s);
-            dp = mfma(lds16(sdo + off256(row, 2 * st + gl)), vf[st], dp);
+            s = mfma(lds16(sq + off256f(row, 2 * st + g)), kf[st], s);
+            dp = mfma(lds16(sdo + off256f(row, 2 * st + g)), vf[st], dp);
         }
         // register r holds query 16 (r / 8) + 8 g + r % 8 of the block: P and
         // dS for registers 8 hb .. 8 hb + 7 from 8 consecutive lse2 and Dq values
@@ -495,15 +501,12 @@ k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dct
         // dV^T += dO^T P and dK^T += Q^T dS: queries 16 ks + 8 g + slot = registers 8 ks + slot.
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const v8bf pb = pack8(s, 8 * ks);
+            const v8bf pb = pack8(s, 8 * ks), sb = pack8(dp, 8 * ks);
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) dv[dt] = mfma(lds_tr(sdo, 16 * ks, 32 * dt, ln), pb, dv[dt]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const v8bf sb = pack8(dp, 8 * ks);
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) dk[dt] = mfma(lds_tr(sq, 16 * ks, 32 * dt, ln), sb, dk[dt]);
+            for (int dt = 0; dt < 4; ++dt) {
+                dv[dt] = mfma(lds16(sdot + off64(32 * dt + l32, 2 * ks + g)), pb, dv[dt]);
+                dk[dt] = mfma(lds16(sqt + off64(32 * dt + l32, 2 * ks + g)), sb, dk[dt]);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0): this wave's DMA of the next block landed
         __syncthreads();
@@ -694,20 +697,24 @@ hipError_t launch_attention_fwd(const uint16_t* qkv, int64_t batch, int64_t seq,
 }
 
 hipError_t launch_attention_bwd(const uint16_t* qkv, const uint16_t* ctx, const float* lse, const uint16_t* dctx,
-                                int64_t batch, int64_t seq, int64_t heads, uint16_t* dqkv, float* rows_ws,
-                                hipStream_t s) {
+                                int64_t batch, int64_t seq, int64_t heads, uint16_t* dqkv, uint16_t* qt_ws,
+                                uint16_t* dot_ws, float* rows_ws, hipStream_t s) {
     const AttnShape sh = make_shape(batch, seq, heads);
-    const int64_t BS = batch * seq;
+    const int64_t BS = batch * seq, HD = heads * kD;
     timing_before(kKindOther, s);
-    const int64_t units = BS * heads;
-    hipLaunchKernelGGL(k_attn_rowdot, dim3((unsigned)((units * 16 + 255) / 256)), dim3(256), 0, s, dctx, ctx, rows_ws,
-                       sh);
-    hipError_t e = hipGetLastError();
+    hipError_t e = transpose(qkv, 3 * HD, BS, HD, qt_ws, s);
+    if (e == hipSuccess) e = transpose(dctx, HD, BS, HD, dot_ws, s);
+    if (e == hipSuccess) {
+        const int64_t units = BS * heads;
+        hipLaunchKernelGGL(k_attn_rowdot, dim3((unsigned)((units * 16 + 255) / 256)), dim3(256), 0, s, dctx, ctx,
+                           rows_ws, sh);
+        e = hipGetLastError();
+    }
     timing_after(s);
     if (e != hipSuccess) return e;
     timing_before(kKindAttn, s);
     hipLaunchKernelGGL(k_attn_bwd_kv, dim3((unsigned)(batch * heads * (seq / kKvKeys))), dim3(kKvThreads), 0, s, qkv,
-                       dctx, lse, rows_ws, dqkv, sh);
+                       dctx, qt_ws, dot_ws, lse, rows_ws, dqkv, sh);
     e = hipGetLastError();
     timing_after(s);
     if (e != hipSuccess) return e;

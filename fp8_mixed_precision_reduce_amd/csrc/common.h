@@ -106,8 +106,8 @@ hipError_t launch_scale_by(const void* x, int dtype, int64_t n, const float* sta
 hipError_t launch_attention_fwd(const uint16_t* qkv, int64_t batch, int64_t seq, int64_t heads, uint16_t* ctx,
                                 float* lse, uint16_t* vt_ws, hipStream_t s);
 hipError_t launch_attention_bwd(const uint16_t* qkv, const uint16_t* ctx, const float* lse, const uint16_t* dctx,
-                                int64_t batch, int64_t seq, int64_t heads, uint16_t* dqkv, float* rows_ws,
-                                hipStream_t s);
+                                int64_t batch, int64_t seq, int64_t heads, uint16_t* dqkv, uint16_t* qt_ws,
+                                uint16_t* dot_ws, float* rows_ws, hipStream_t s);
 
 #ifdef __HIPCC__
 // ------------------------------------------------------------ device helpers

@@ -563,8 +563,9 @@ int32_t fp8_sgd_step_cast(float* w, const float* g, int64_t rows, int64_t cols, 
  * Workspace (caller-owned device memory, 16-byte aligned, contents not
  * preserved): bf16_attention_workspace_bytes(batch, seq, heads, head_dim,
  * backward) bytes: the forward holds V^T (batch*seq*heads*D bf16), the
- * backward rowsum(dO * O) (batch*heads*seq fp32; its transposed operands are
- * read from the row-major tiles in the LDS, so it makes no transposed copy).
+ * backward Q^T and dO^T (2 * batch*seq*heads*D bf16) and rowsum(dO * O)
+ * (batch*heads*seq fp32); K^T is read from the row-major K tile in the LDS
+ * with transposing reads, so no copy of it is made.
  * The library cannot see the workspace's size; a caller that shares one
  * workspace between the two calls sizes it as the larger figure.
  */

@@ -271,7 +271,7 @@ def test_attention_validation():
     ws_bytes.restype = I64
     ws_bytes.argtypes = [I64, I64, I64, I64, ctypes.c_int32]
     assert ws_bytes(2, 4096, 64, 128, 0) == 2 * 4096 * 64 * 128 * 2   # V^T
-    assert ws_bytes(2, 4096, 64, 128, 1) == 2 * 64 * 4096 * 4         # rowsum(dO * O), fp32
+    assert ws_bytes(2, 4096, 64, 128, 1) == 2 * 2 * 4096 * 64 * 128 * 2 + 2 * 64 * 4096 * 4   # Q^T, dO^T, rowsum
     assert ws_bytes(2, 4096, 64, 64, 0) == -1 and ws_bytes(1, 100, 2, 128, 1) == -1
     fwd, bwd = L.bf16_attention_fwd, L.bf16_attention_bwd
     fwd.argtypes = [P, I64, I64, I64, I64, P, P, P, P]
@@ -282,7 +282,7 @@ def test_attention_validation():
     assert fwd(big[0], 0, 256, 2, 128, big[1], big[2], big[3], None) == F.ERR_SHAPE
     assert fwd(big[0], 1 << 12, 4096, 256, 128, big[1], big[2], big[3], None) == F.ERR_SHAPE
     # tile-load byte offsets within one (batch, head) must stay below 2^31
-    assert ws_bytes(1, 1 << 16, 42, 128, 1) == 1 * 42 * (1 << 16) * 4
+    assert ws_bytes(1, 1 << 16, 42, 128, 1) == 2 * (1 << 16) * 42 * 128 * 2 + 42 * (1 << 16) * 4
     assert ws_bytes(1, 1 << 16, 43, 128, 0) == -1                    # seq*heads*768 >= 2^31
     assert ws_bytes(1 << 7, 1 << 16, 1, 128, 0) == -1                # batch*seq*256 >= 2^31
     assert ws_bytes((1 << 7) - 1, 1 << 16, 1, 128, 1) > 0
@@ -409,9 +409,9 @@ def test_attention_workspace_too_small_is_refused():
     dqkv = torch.zeros_like(qkv)
     need_f = F.attention_workspace_bytes(batch, seq, heads)
     need_b = F.attention_workspace_bytes(batch, seq, heads, backward=True)
-    assert need_f == batch * seq * heads * 128 * 2 and need_b == batch * heads * seq * 4
+    assert need_f == batch * seq * heads * 128 * 2 and need_b == 2 * need_f + batch * heads * seq * 4
     with pytest.raises(ValueError, match="forward: workspace of"):
-        F.bf16_attention_fwd(qkv, batch, heads, ctx, lse, torch.zeros(need_b, dtype=torch.uint8))
+        F.bf16_attention_fwd(qkv, batch, heads, ctx, lse, torch.zeros(need_f - 16, dtype=torch.uint8))
     with pytest.raises(ValueError, match="backward: workspace of"):
         F.bf16_attention_bwd(qkv, ctx, lse, ctx, batch, heads, dqkv, torch.zeros(need_b - 4, dtype=torch.uint8))
     with pytest.raises(ValueError):
