@@ -32,11 +32,12 @@
 //
 // V (forward), Q, K and dO (backward) are also needed transposed (the token
 // index as the contraction index of P V, dO^T P, Q^T dS and K^T dS).  The
-// backward reads Q^T, K^T and dO^T fragments from the same row-major LDS tiles
-// with transposing LDS reads (ds_read_b64_tr_b16), so it makes no transposed
-// copy; the forward, bound by its LDS traffic, keeps a V^T tile, written by a
-// transpose kernel into the caller's workspace first (one 16-byte read per
-// fragment instead of two 8-byte transposing reads: measured 10 % faster).
+// kernels bound by their LDS traffic (the forward and the dK/dV kernel) read
+// V^T, Q^T and dO^T tiles that a transpose kernel first writes into the
+// caller's workspace (one 16-byte LDS read per fragment instead of two 8-byte
+// transposing reads: measured 10 % and 15 % faster); the dQ kernel reads its
+// K^T fragments from the row-major K tile with transposing LDS reads
+// (ds_read_b64_tr_b16), so K needs no transposed copy.
 #include "common.h"
 
 namespace fp8lin {
