@@ -48,13 +48,13 @@
 // whole next-stage DMA is issued at the start of a stage (the longest lead).
 // The MFMA takes the B tile as
 // its first operand, so each lane's accumulators run along n: four
-// consecutive outputs of one row.  fp32 outputs are written from there with
-// one 16-byte store per lane, except where the output's row stride is a
-// multiple of 32 KiB; those, and bf16 outputs (and the pre-GeLU copy), are
-// first staged in the LDS, which is free after the k loop, and then written by
-// the whole workgroup in 16-byte pieces that cover complete row segments.  A
-// launch may cover a column range of a wider output (its row stride is then
-// the full width).  Tiles are rasterised in groups of 8 tile-rows, and the
+// consecutive outputs of one row.  The outputs (bf16, fp32, and the pre-GeLU
+// copy) are first staged in the LDS, which is free after the k loop, and then
+// written by the whole workgroup in 16-byte pieces that cover complete row
+// segments, with non-temporal stores (only fp32 outputs with GeLU are written
+// straight from the registers, 32 bytes per row per store).  A launch may
+// cover a column range of a wider output (its row stride is then the full
+// width).  Tiles are rasterised in groups of 8 tile-rows, and the
 // workgroup index is remapped so that each XCD (workgroups are dealt
 // round-robin over 8 XCDs) works on a contiguous range of tiles that share
 // operands in its own L2.
@@ -70,6 +70,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 128;
 constexpr int kGroupM = 8;
@@ -408,6 +409,10 @@ k_gemm(GemmParams p) {
         // bf16 outputs go through LDS (free after the k loop) so that the global
         // stores write whole row segments: rows of the wave-row wm go to stage
         // array wm, BN * 2 bytes per row, 8-byte units XOR-swizzled by row.
+        // The stores are non-temporal: all workgroups store a tile at about
+        // the same time, and the burst drained that way measured 5-14 %
+        // faster on the fast path's bf16-output GEMMs (1-3 % on the exact
+        // path's), outputs unchanged.
         static_assert(WM == 2 && (C::BM / 2) * C::BN * 2 <= C::STAGE, "bf16 staging must fit one stage array");
         constexpr int UPR = C::BN / 4;                  // 8-byte units per LDS row
         auto lds_unit = [&](int lr, int unit) { return lr * (C::BN * 2) + ((unit ^ (((lr & 15) << 1) & (UPR - 1))) << 3); };
@@ -422,24 +427,20 @@ k_gemm(GemmParams p) {
             // Every LDS read of the thread first (rows r0 + RPP pass: the
             // first half from stage array 0, the second from array 1, at
             // constant offsets from one address), one wait, then the stores.
-            uint4 v[NPASS];
+            v4u v[NPASS];
 #pragma unroll
             for (int pass = 0; pass < NPASS; ++pass)
-                v[pass] = *reinterpret_cast<const uint4*>((pass < NH ? smem0 : smem1) +
-                                                          lds_unit(r0 + RPP * (pass % NH), 2 * c));
+                v[pass] = *reinterpret_cast<const v4u*>((pass < NH ? smem0 : smem1) +
+                                                        lds_unit(r0 + RPP * (pass % NH), 2 * c));
             // (the reads stay here, not sunk into the conditional stores)
 #pragma unroll
-            for (int pass = 0; pass < NPASS; ++pass) {
-                v4u w = __builtin_bit_cast(v4u, v[pass]);
-                asm volatile("" : "+v"(w));
-                v[pass] = __builtin_bit_cast(uint4, w);
-            }
+            for (int pass = 0; pass < NPASS; ++pass) asm volatile("" : "+v"(v[pass]));
             const int64_t col = n0 + 8 * c;
             uint16_t* const out = static_cast<uint16_t*>(dst) + (m0 + r0) * LDD + col;
 #pragma unroll
             for (int pass = 0; pass < NPASS; ++pass)
                 if (m0 + r0 + RPP * pass < M && col < N)
-                    *reinterpret_cast<uint4*>(out + (int64_t)(RPP * pass) * LDD) = v[pass];
+                    __builtin_nontemporal_store(v[pass], reinterpret_cast<v4u*>(out + (int64_t)(RPP * pass) * LDD));
             __syncthreads();
         };
         if (gelu && p.aux) {
@@ -557,17 +558,14 @@ k_gemm(GemmParams p) {
             __syncthreads();               // the staged values are read; the next tile may DMA
         }
     } else if (OUT == kOutF32Staged) {
-        // fp32 outputs whose row stride is a multiple of 32 KiB go through LDS
-        // as well: written from registers, each wave store puts 32 bytes into
-        // each of 32 rows one stride apart, which such strides map onto one
-        // memory channel (measured 9-11% slower on 8192- and 16384-column
-        // outputs; 4096- and 12288-column outputs are not affected and keep
-        // the register path).  One wave-row (BM / 2 rows) per pass, its rows
-        // split over the two stage arrays, 1 KiB per row for BN = 256,
-        // 16-byte units XOR-swizzled by the row's low 4 bits; then the whole
-        // workgroup applies the residual and the accumulate in the same order
-        // as the register path and writes complete row segments.  Never
-        // launched with GeLU.
+        // fp32 outputs go through LDS as well (written from registers, each
+        // wave store would put 32 bytes into each of 32 rows).  One wave-row
+        // (BM / 2 rows) per pass, its rows split over the two stage arrays,
+        // 1 KiB per row for BN = 256, 16-byte units XOR-swizzled by the row's
+        // low 4 bits; then the whole workgroup applies the residual and the
+        // accumulate in the same order as the register path and writes
+        // complete row segments with non-temporal stores.  Never launched with
+        // GeLU.
         static_assert(WM == 2 && (C::BM / 4) * C::BN * 4 <= C::STAGE && C::BN >= 64, "fp32 staging layout");
         constexpr int UPR = C::BN / 4;                  // 16-byte units (4 floats) per row
         constexpr int QR = C::BM / 4;                   // rows per stage array in one pass
@@ -608,7 +606,7 @@ k_gemm(GemmParams p) {
                     const float4 old = *dp;
                     y[0] = old.x + y[0]; y[1] = old.y + y[1]; y[2] = old.z + y[2]; y[3] = old.w + y[3];
                 }
-                *dp = make_float4(y[0], y[1], y[2], y[3]);
+                __builtin_nontemporal_store(v4f{y[0], y[1], y[2], y[3]}, reinterpret_cast<v4f*>(dp));
                 if (want_amax)
                     amax = max(amax, max(max(abs_bits(y[0]), abs_bits(y[1])), max(abs_bits(y[2]), abs_bits(y[3]))));
             }
@@ -683,13 +681,17 @@ hipError_t launch_out(const GemmParams& p, hipStream_t s) {
 // The staged fp32 epilogue is an instance of its own: with it in the same
 // kernel as the bf16 and register fp32 epilogues, the register allocation of
 // the whole kernel changed (37 spilled registers instead of 14 on the exact
-// path) and bf16-output GEMMs measured 2-5% slower.
+// path) and bf16-output GEMMs measured 2-5% slower.  Every fp32 output without
+// GeLU takes it: its whole-row, non-temporal stores measured 8-17 % faster on
+// the fast path's weight gradients and 1.5-3 % on the exact path's, against
+// the register path's 32-byte pieces (which non-temporal stores make slower
+// still: partial lines then miss the L2's write combining).
 template <int WM, int WN, int MB, int NB, int AF, int BF, bool FAST, bool QOUT = false>
 hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
     if constexpr (QOUT) {
         return launch_out<WM, WN, MB, NB, AF, BF, FAST, true, kOutDirect>(p, s);     // bf16 outputs only
     } else {
-        if (p.d_dtype == kF32 && !(p.epilogue & 1) && (p.ldd * 4) % 32768 == 0)
+        if (p.d_dtype == kF32 && !(p.epilogue & 1))
             return launch_out<WM, WN, MB, NB, AF, BF, FAST, false, kOutF32Staged>(p, s);
         return launch_out<WM, WN, MB, NB, AF, BF, FAST, false, kOutDirect>(p, s);
     }
