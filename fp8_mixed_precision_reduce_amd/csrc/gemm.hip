@@ -71,6 +71,7 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;
 constexpr int kGroupM = 8;
@@ -490,8 +491,9 @@ k_gemm(GemmParams p) {
         } else {
             // The output as written (bf16) is also cast to FP8 with the scale of the
             // tensor it becomes: codes = enc(fl32(bf16 value * scale)), the same
-            // arithmetic as a separate cast of d.  Row-major codes are stored
-            // straight from the staged values; for the transposed codes each
+            // arithmetic as a separate cast of d.  The bf16 values and the row-major
+            // codes are stored straight from the staged values (non-temporal, whole
+            // row segments, as the other staged outputs); for the transposed codes each
             // segment of SEG rows goes through a byte tile in an LDS region of its
             // own (16 KiB; 4-byte words XOR-swizzled by an even function of the
             // row, so 8-byte pairs stay together) and 4 x 4 byte transposes, as in
@@ -517,7 +519,9 @@ k_gemm(GemmParams p) {
                     const uint4 v = *reinterpret_cast<const uint4*>((r < HALF ? smem0 : smem1) + lds_unit(r % HALF, 2 * c));
                     const int64_t row = m0 + r, col = n0 + 8 * c;
                     const bool inside = row < M && col < N;
-                    if (p.d && inside) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.d) + row * LDD + col) = v;
+                    if (p.d && inside)
+                        __builtin_nontemporal_store(__builtin_bit_cast(v4u, v),
+                                                    reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.d) + row * LDD + col));
                     const float f[8] = {bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
                                         bf16_to_f32(v.y >> 16),     bf16_to_f32(v.z & 0xFFFFu), bf16_to_f32(v.z >> 16),
                                         bf16_to_f32(v.w & 0xFFFFu), bf16_to_f32(v.w >> 16)};
@@ -526,7 +530,7 @@ k_gemm(GemmParams p) {
                                      enc4<kE4M3>(f[4] * qs, f[5] * qs, f[6] * qs, f[7] * qs))
                         : make_uint2(enc4<kE5M2>(f[0] * qs, f[1] * qs, f[2] * qs, f[3] * qs),
                                      enc4<kE5M2>(f[4] * qs, f[5] * qs, f[6] * qs, f[7] * qs));
-                    if (p.q && inside) *reinterpret_cast<uint2*>(p.q + row * N + col) = q8;
+                    if (p.q && inside) __builtin_nontemporal_store(__builtin_bit_cast(v2u, q8), reinterpret_cast<v2u*>(p.q + row * N + col));
                     if (p.qt) *reinterpret_cast<uint2*>(codes + code_word(lr, 2 * c)) = q8;
                 }
                 if (p.qt) {
