@@ -28,8 +28,9 @@
 // Tiling.  Both operands are contiguous along k ("TN").  A workgroup of
 // WM x WN waves computes a BM x BN tile; each wave owns MB x NB blocks of
 // 32 x 32.  The kernel is persistent: one resident wave of workgroups loops
-// over the tiles, so one tile's output stores drain while the next tile's k
-// loop runs.  k advances in stages of 128 bytes through a double-buffered LDS
+// over the tiles (a tile's output stores are still in flight when the next
+// tile's first stage is fetched; vector-memory operations retire in issue
+// order, so that stage's wait covers them).  k advances in stages of 128 bytes through a double-buffered LDS
 // tile.  The next stage is fetched while the current one is multiplied, with
 // buffer loads that write straight into LDS (buffer_load_dwordx4 ... lds: no
 // staging registers, out-of-range rows and the k tail read as zero).  LDS rows
@@ -207,8 +208,7 @@ k_gemm(GemmParams p) {
     const float sc = (*p.sinv_a) * (*p.sinv_b);
     uint32_t amax = 0;
 
-    // Persistent: each workgroup takes tiles blockIdx.x, + gridDim.x, ...; the
-    // output stores of one tile drain while the next tile's k loop runs.
+    // Persistent: each workgroup takes tiles blockIdx.x, + gridDim.x, ....
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     int tm, tn;
     tile_coords(tile, p.tiles_m, p.tiles_n, tm, tn);
