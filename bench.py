@@ -448,14 +448,21 @@ def quant_leg(F, torch, reps=50, first=10):
 
 
 def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, with its family and model
+    numbers (a virtualised host may report only a generic name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break                      # the first processor's block is enough
+                key, _, val = line.partition(":")
+                fields.setdefault(key.strip(), val.strip())
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    extra = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    return f"{name} ({extra})" if extra else name
 
 
 def cpu_baseline(torch, rows=1024, layer_rows=32):
