@@ -237,6 +237,43 @@ k_gemm(GemmParams p) {
                   kb < (uint32_t)K ? off : 0x80000000u);
         }
     };
+    // The next stage's DMA during the k loop.  On the FP8-MFMA path with eight
+    // waves, waves w and w ^ 4 share a SIMD; in each stage one of them issues
+    // both waves' DMA wave-instructions (alternating by stage) while the other
+    // goes straight on to its fragment reads and MFMAs, so one wave keeps the
+    // SIMD's matrix core fed while the other waits to issue into a backed-up
+    // memory pipeline (the MLP block step 3.5 % faster, same data in the same
+    // LDS places; on the exact path, whose converts already fill the other
+    // wave's time, it measured 1-2 % slower, so that path keeps every wave
+    // issuing its own share).  The pair's rows are those of wave
+    // w & 3 and the same rows + 32 (the swizzle repeats every 16 rows), so the
+    // second offset is the first + 32 K; every offset stays in the vector
+    // offset, which the buffer range check covers (a k-tail lane's 2^31 + 32 K
+    // is past every tile's rows * K and below 2^32, since K < 2^23).
+    auto dma_stage = [&](int kt, uint8_t* sa) {
+        if constexpr (FAST && C::WAVES == 8) {
+            static_assert(C::A_DMA * 8 * C::WAVES == C::BM && C::B_DMA * 8 * C::WAVES == C::BN, "DMA row layout");
+            if (((wave >> 2) ^ (kt & 1)) != 0) return;
+            const int wb = wave & 3;
+            const uint32_t dk = 32u * (uint32_t)K;
+            uint8_t* sb = sa + C::BM * kBK;
+            const uint32_t k0 = (uint32_t)kt * kBK;
+#pragma unroll
+            for (int q = 0; q < NDMA; ++q) {
+                const bool is_a = q < C::A_DMA;
+                const int i = is_a ? q : q - C::A_DMA;
+                const int row = 8 * (wb + C::WAVES * i) + lrow;
+                const uint32_t kb = k0 + (uint32_t)((lpc ^ swz(row)) << 4);
+                const uint32_t off = kb < (uint32_t)K ? (uint32_t)row * (uint32_t)K + kb : 0x80000000u;
+                uint8_t* dst = (is_a ? sa : sb) + (row - lrow) * kBK;
+                const __amdgpu_buffer_rsrc_t r = is_a ? ra_rsrc : rb_rsrc;
+                dma16(r, dst, off);
+                dma16(r, dst + 32 * kBK, off + dk);
+            }
+        } else {
+            dma_part(kt, sa, 0, NDMA);
+        }
+    };
 
     v16f acc[MB][NB];
 #pragma unroll
@@ -281,7 +318,7 @@ k_gemm(GemmParams p) {
                     const uint4 hi = *reinterpret_cast<const uint4*>(sb + lds_off(row, c0 + 1));
                     bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 }
-                if (more && kb == 0) dma_part(kt + 1, nxt, 0, NDMA);
+                if (more && kb == 0) dma_stage(kt + 1, nxt);
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -336,7 +373,7 @@ k_gemm(GemmParams p) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x002, (NCV + NMF - 1) / NMF, 0);
                 }
-                if (more && kb == 0) dma_part(kt + 1, nxt, 0, NDMA);
+                if (more && kb == 0) dma_stage(kt + 1, nxt);
                 if (kb + 1 < kBK / 32) {
                     rd(kb + 1);
                     cvt_h1();
@@ -368,15 +405,13 @@ k_gemm(GemmParams p) {
     }
 
     // ---------------------------------------------------------------- epilogue
-    // On the exact path (and with FP8 output) the epilogue's lane indices come
-    // from an opaque copy of the thread index made inside the tile loop:
-    // otherwise the compiler hoists the epilogue's per-lane LDS addresses out
-    // of the tile loop, where they stay live across the k loop and are spilled
-    // to scratch (one reload per store, each followed by a wait for all of the
-    // wave's memory operations).  The fast path's k loop leaves room for them
-    // and is measured 1-3 % faster with them hoisted.
+    // The epilogue's lane indices come from an opaque copy of the thread index
+    // made inside the tile loop: otherwise the compiler hoists the epilogue's
+    // per-lane LDS addresses out of the tile loop, where they stay live across
+    // the k loop and are spilled to scratch (one reload per store, each
+    // followed by a wait for all of the wave's memory operations).
     int te = t;
-    if constexpr (!FAST || QOUT) asm volatile("" : "+v"(te));
+    asm volatile("" : "+v"(te));
     const int lane_e = te & 63, r32e = lane_e & 31, ge = lane_e >> 5;
     // y = acc * sinv_a * sinv_b + bias, in place.  Lane (r32e, ge) of block (i, j)
     // holds row i * 32 + r32e and, for q4 = 0..3, the four columns
