@@ -538,8 +538,7 @@ k_attn_bwd_kv(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dct
 
 // ------------------------------------------------------------------- dQ
 // Workgroup: 8 waves, 256 queries of one (b, h), 32 per wave (Q and dO
-// fragments in registers).  Key blocks of 32: K and V [32][256 B], through
-// three LDS buffers.
+// fragments in registers).  Key blocks of 32: K and V [32][256 B].
 constexpr int kQQ = 256, kQK = 32, kQThreads = 512;
 constexpr int kQKt = 32 * 256, kQBuf = 2 * 32 * 256;
 
@@ -549,7 +548,6 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
              AttnShape sh) {
     __shared__ __attribute__((aligned(16))) uint8_t smem0[kQBuf];
     __shared__ __attribute__((aligned(16))) uint8_t smem1[kQBuf];
-    __shared__ __attribute__((aligned(16))) uint8_t smem2[kQBuf];
     const int S = sh.seq, H = sh.heads;
     const int64_t BS = (int64_t)sh.batch * S, HD = (int64_t)H * kD, ld = 3 * HD;
     const int qblocks = S / kQQ;
@@ -594,30 +592,8 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
         for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
 
     const int nblk = S / kQK;
-    // Neighbouring waves run in opposite phases, as in the forward: the odd
-    // ("late") waves multiply dQ^T += K^T dS one block behind their scores, so
-    // that one wave's exponentials (VALU) overlap its neighbour's products on
-    // the matrix core they share (measured 5 % faster for this kernel, outputs
-    // identical: every wave still adds the blocks in order).  Three LDS
-    // buffers keep block j - 1's K for the late waves while block j is used
-    // and block j + 1 is loaded.
-    const bool late = (w & 1) != 0;
-    v8bf sbl[2];
-    auto dq = [&](const uint8_t* kbuf, const v8bf* sb) __attribute__((always_inline)) {
-        // dQ^T += K^T dS: keys 16 ks + 8 g + slot = registers 8 ks + slot
-        v8bf kt_f[2][4];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) kt_f[ks][dt] = lds_tr(kbuf, 16 * ks, 32 * dt, lane);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(kt_f[ks][dt], sb[ks], acc[dt]);
-    };
-    auto block = [&](int j, const uint8_t* buf, const uint8_t* prev, uint8_t* nxt) __attribute__((always_inline)) {
+    auto block = [&](int j, const uint8_t* buf, uint8_t* nxt) __attribute__((always_inline)) {
         if (j + 1 < nblk) dma((j + 1) * kQK, nxt);
-        if (late && j > 0) dq(prev, sbl);
         v16f s, dp;
 #pragma unroll
         for (int e = 0; e < 16; ++e) { s[e] = 0.0f; dp[e] = 0.0f; }
@@ -643,12 +619,17 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 #pragma unroll
         for (int e = 0; e < 16; ++e) dp[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sh.c2, -lq)) * (dp[e] - dd);
-        const v8bf sb[2] = {pack8(dp, 0), pack8(dp, 8)};
-        if (late) {
-            sbl[0] = sb[0];
-            sbl[1] = sb[1];
-        } else {
-            dq(buf, sb);
+        // dQ^T += K^T dS: keys 16 ks + 8 g + slot = registers 8 ks + slot
+        v8bf kt_f[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) kt_f[ks][dt] = lds_tr(buf, 16 * ks, 32 * dt, lane);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const v8bf sb = pack8(dp, 8 * ks);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma(kt_f[ks][dt], sb, acc[dt]);
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0): this wave's DMA of the next block landed
         __syncthreads();
@@ -664,12 +645,10 @@ k_attn_bwd_q(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dctx
     for (int st = 0; st < 8; ++st) asm volatile("" ::"v"(qf[st]), "v"(df[st]));
     asm volatile("" : "+v"(lq), "+v"(dd));
     __syncthreads();
-    for (int j = 0; j < nblk; j += 3) {
-        block(j, smem0, smem2, smem1);
-        if (j + 1 < nblk) block(j + 1, smem1, smem0, smem2);
-        if (j + 2 < nblk) block(j + 2, smem2, smem1, smem0);
+    for (int j = 0; j < nblk; j += 2) {
+        block(j, smem0, smem1);
+        if (j + 1 < nblk) block(j + 1, smem1, smem0);
     }
-    if (late) dq((nblk - 1) % 3 == 0 ? smem0 : (nblk - 1) % 3 == 1 ? smem1 : smem2, sbl);
     uint16_t* qrow = dqkv + (tok0 + q) * ld + (int64_t)h * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)

@@ -242,7 +242,7 @@ k_gemm(GemmParams p) {
     // both waves' DMA wave-instructions (alternating by stage) while the other
     // goes straight on to its fragment reads and MFMAs, so one wave keeps the
     // SIMD's matrix core fed while the other waits to issue into a backed-up
-    // memory pipeline (the MLP block step 2.6-3.5 % faster, same data in the same
+    // memory pipeline (every GEMM 1-2 % faster, same data in the same
     // LDS places; on the exact path, whose converts already fill the other
     // wave's time, it measured 1-2 % slower, so that path keeps every wave
     // issuing its own share).  The pair's rows are those of wave
